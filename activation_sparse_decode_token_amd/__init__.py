@@ -1,0 +1,240 @@
+"""Python binding of libspax (three-tier activation-sparse decode on gfx950).
+
+Argument marshalling only: every step of the method runs in the HIP kernels
+behind the C ABI declared in include/spax.h. Device buffers are torch tensors
+(or raw integer addresses); streams are torch.cuda.Stream objects or raw
+hipStream_t handles. Loading fails loudly when the library is not built.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Sequence
+
+__all__ = [
+    "SpaxError", "lib", "library_path",
+    "FMT_NONE", "FMT_FP16", "FMT_INT4_G128", "FMT_INT2_G128",
+    "RES_DEVICE", "RES_HOST_PINNED", "LAYOUT_PLAIN", "LAYOUT_GLU_INTERLEAVED",
+    "GROUP_QKV", "GROUP_O", "GROUP_GATE_UP", "GROUP_DOWN",
+    "Matrix", "Layer", "LayerIO",
+    "plan_tiers", "tiered_gemv", "gemv_workspace_bytes", "layer_step",
+    "layer_workspace_bytes", "pack_g128", "workspace_clear", "version",
+    "status_string", "last_error", "EXPORTS",
+]
+
+FMT_NONE, FMT_FP16, FMT_INT4_G128, FMT_INT2_G128 = 0, 1, 2, 3
+RES_DEVICE, RES_HOST_PINNED = 0, 1
+LAYOUT_PLAIN, LAYOUT_GLU_INTERLEAVED = 0, 1
+GROUP_QKV, GROUP_O, GROUP_GATE_UP, GROUP_DOWN = 0, 1, 2, 3
+
+STATUS = {0: "SPAX_OK", -1: "SPAX_EINVAL", -2: "SPAX_ENULL", -3: "SPAX_EALIGN",
+          -4: "SPAX_EFORMAT", -5: "SPAX_EWORKSPACE", -6: "SPAX_ESTREAM", -7: "SPAX_EHIP"}
+
+# Every entry point declared in include/spax.h.
+EXPORTS = (
+    "spax_plan_tiers", "spax_gemv_workspace_bytes", "spax_tiered_gemv",
+    "spax_layer_workspace_bytes", "spax_layer_step", "spax_pack_g128",
+    "spax_workspace_clear", "spax_status_string", "spax_last_error", "spax_version",
+)
+
+library_path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libspax.so")
+
+
+class SpaxError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        msg = f"{where}: {STATUS.get(status, status)} ({_status_text(status)})"
+        if status == -7:
+            msg += f": {_last_error_text()}"
+        super().__init__(msg)
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load libspax.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(library_path):
+            raise ImportError(
+                f"{library_path} is missing; build it with "
+                "`python -m activation_sparse_decode_token_amd.build`")
+        L = ctypes.CDLL(library_path)
+        _declare(L)
+        _lib = L
+    return _lib
+
+
+class Matrix(ctypes.Structure):
+    """spax_matrix. Keeps Python references to the tensors it points to."""
+    _fields_ = [
+        ("rows", ctypes.c_int32), ("cols", ctypes.c_int32),
+        ("full_fmt", ctypes.c_int32), ("approx_fmt", ctypes.c_int32),
+        ("residency", ctypes.c_int32), ("layout", ctypes.c_int32),
+        ("full_data", ctypes.c_void_p), ("full_scales", ctypes.c_void_p),
+        ("approx_codes", ctypes.c_void_p), ("approx_scales", ctypes.c_void_p),
+    ]
+
+    @classmethod
+    def make(cls, rows, cols, full_fmt, approx_fmt, full_data, full_scales=None,
+             approx_codes=None, approx_scales=None, residency=RES_DEVICE,
+             layout=LAYOUT_PLAIN) -> "Matrix":
+        m = cls(rows, cols, full_fmt, approx_fmt, residency, layout,
+                _ptr(full_data), _ptr(full_scales), _ptr(approx_codes), _ptr(approx_scales))
+        m._keep = (full_data, full_scales, approx_codes, approx_scales)
+        return m
+
+
+class Layer(ctypes.Structure):
+    _fields_ = [("group", Matrix * 4), ("k_full", ctypes.c_int32 * 4),
+                ("k_approx", ctypes.c_int32 * 4)]
+
+    @classmethod
+    def make(cls, groups: Sequence[Optional[Matrix]], k_full: Sequence[int],
+             k_approx: Sequence[int]) -> "Layer":
+        L = cls()
+        for g in range(4):
+            if groups[g] is not None:
+                L.group[g] = groups[g]
+            L.k_full[g] = int(k_full[g])
+            L.k_approx[g] = int(k_approx[g])
+        L._keep = tuple(groups)
+        return L
+
+
+class LayerIO(ctypes.Structure):
+    _fields_ = [
+        ("h", ctypes.c_void_p), ("z", ctypes.c_void_p), ("x", ctypes.c_void_p),
+        ("qkv", ctypes.c_void_p), ("o", ctypes.c_void_p), ("g", ctypes.c_void_p),
+        ("u", ctypes.c_void_p), ("a", ctypes.c_void_p), ("down", ctypes.c_void_p),
+        ("full_idx", ctypes.c_void_p * 4), ("approx_idx", ctypes.c_void_p * 4),
+    ]
+
+    @classmethod
+    def make(cls, h=None, z=None, x=None, qkv=None, o=None, g=None, u=None, a=None,
+             down=None, full_idx=(None,) * 4, approx_idx=(None,) * 4) -> "LayerIO":
+        io = cls(_ptr(h), _ptr(z), _ptr(x), _ptr(qkv), _ptr(o), _ptr(g), _ptr(u), _ptr(a),
+                 _ptr(down))
+        for i in range(4):
+            io.full_idx[i] = _ptr(full_idx[i])
+            io.approx_idx[i] = _ptr(approx_idx[i])
+        io._keep = (h, z, x, qkv, o, g, u, a, down, tuple(full_idx), tuple(approx_idx))
+        return io
+
+
+def _ptr(t) -> Optional[int]:
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    return t.data_ptr()
+
+
+def _stream(s) -> Optional[int]:
+    if s is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(s, int):
+        return s
+    return s.cuda_stream
+
+
+def _check(status: int, where: str) -> None:
+    if status != 0:
+        raise SpaxError(status, where)
+
+
+def _status_text(status: int) -> str:
+    return lib().spax_status_string(status).decode()
+
+
+def _last_error_text() -> str:
+    return lib().spax_last_error().decode()
+
+
+def _declare(L: ctypes.CDLL) -> None:
+    vp, i32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
+    L.spax_plan_tiers.argtypes = [vp, i32, i32, i32, vp, vp, vp]
+    L.spax_plan_tiers.restype = ctypes.c_int
+    L.spax_gemv_workspace_bytes.argtypes = [ctypes.POINTER(Matrix)]
+    L.spax_gemv_workspace_bytes.restype = sz
+    L.spax_tiered_gemv.argtypes = [ctypes.POINTER(Matrix), vp, vp, i32, vp, i32, vp, vp, sz,
+                                   vp, vp]
+    L.spax_tiered_gemv.restype = ctypes.c_int
+    L.spax_layer_workspace_bytes.argtypes = [ctypes.POINTER(Layer)]
+    L.spax_layer_workspace_bytes.restype = sz
+    L.spax_layer_step.argtypes = [ctypes.POINTER(Layer), ctypes.POINTER(LayerIO), vp, sz, vp, vp]
+    L.spax_layer_step.restype = ctypes.c_int
+    L.spax_pack_g128.argtypes = [vp, i32, i32, i32, vp, vp, vp]
+    L.spax_pack_g128.restype = ctypes.c_int
+    L.spax_workspace_clear.argtypes = [vp, sz, vp]
+    L.spax_workspace_clear.restype = ctypes.c_int
+    L.spax_status_string.argtypes = [ctypes.c_int]
+    L.spax_status_string.restype = ctypes.c_char_p
+    L.spax_last_error.argtypes = []
+    L.spax_last_error.restype = ctypes.c_char_p
+    L.spax_version.argtypes = []
+    L.spax_version.restype = ctypes.c_int
+
+
+# ---------------------------------------------------------------- entry points
+
+def version() -> int:
+    return lib().spax_version()
+
+
+def status_string(status: int) -> str:
+    return _status_text(status)
+
+
+def last_error() -> str:
+    return _last_error_text()
+
+
+def plan_tiers(x, n, k_full, k_approx, full_idx, approx_idx, stream=None) -> None:
+    """spax_plan_tiers: ascending full / approx index lists of x (fp16[n])."""
+    _check(lib().spax_plan_tiers(_ptr(x), int(n), int(k_full), int(k_approx),
+                                 _ptr(full_idx), _ptr(approx_idx), _stream(stream)),
+           "spax_plan_tiers")
+
+
+def gemv_workspace_bytes(W: Matrix) -> int:
+    return int(lib().spax_gemv_workspace_bytes(ctypes.byref(W)))
+
+
+def tiered_gemv(W: Matrix, x, full_idx, k_full, approx_idx, k_approx, y, ws, ws_bytes=None,
+                stream=None, copy_stream=None) -> None:
+    """spax_tiered_gemv: y = W[:,F] x_F + W^[:,A] x_A (fp32 accumulate, fp16 out)."""
+    nbytes = ws.numel() * ws.element_size() if ws_bytes is None else ws_bytes
+    cs = None if copy_stream is None else _stream(copy_stream)
+    _check(lib().spax_tiered_gemv(ctypes.byref(W), _ptr(x), _ptr(full_idx), int(k_full),
+                                  _ptr(approx_idx), int(k_approx), _ptr(y), _ptr(ws),
+                                  int(nbytes), _stream(stream), cs),
+           "spax_tiered_gemv")
+
+
+def layer_workspace_bytes(L: Layer) -> int:
+    return int(lib().spax_layer_workspace_bytes(ctypes.byref(L)))
+
+
+def layer_step(L: Layer, io: LayerIO, ws, ws_bytes=None, compute_stream=None,
+               copy_stream=None) -> None:
+    """spax_layer_step: the four ranking groups of one decoder layer."""
+    nbytes = ws.numel() * ws.element_size() if ws_bytes is None else ws_bytes
+    cs = None if copy_stream is None else _stream(copy_stream)
+    _check(lib().spax_layer_step(ctypes.byref(L), ctypes.byref(io), _ptr(ws), int(nbytes),
+                                 _stream(compute_stream), cs),
+           "spax_layer_step")
+
+
+def pack_g128(w, rows, cols, fmt, codes, scales, stream=None) -> None:
+    """spax_pack_g128: int4 / int2 group-128 codes and fp16 scales of w."""
+    _check(lib().spax_pack_g128(_ptr(w), int(rows), int(cols), int(fmt), _ptr(codes),
+                                _ptr(scales), _stream(stream)),
+           "spax_pack_g128")
+
+
+def workspace_clear(ws, nbytes=None, stream=None) -> None:
+    n = ws.numel() * ws.element_size() if nbytes is None else nbytes
+    _check(lib().spax_workspace_clear(_ptr(ws), int(n), _stream(stream)), "spax_workspace_clear")

@@ -1,0 +1,383 @@
+// C ABI of the three-tier activation-sparse decode library: argument
+// validation, launch planning, workspace layout and the layer sequence.
+// All arithmetic of the method runs in the kernels (plan.hip, gemv.hip,
+// aux.hip); this file only checks arguments and enqueues work.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstdint>
+#include <string>
+
+#include "spax.h"
+#include "spax_internal.h"
+
+namespace {
+
+using namespace spax;
+
+thread_local std::string g_last_error = "no error";
+
+int hip_fail(hipError_t e) {
+  g_last_error = hipGetErrorString(e);
+  return SPAX_EHIP;
+}
+
+inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+inline size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
+
+// Bytes of one stored column (codes only for code formats).
+int64_t col_bytes(int32_t fmt, int64_t rows) {
+  switch (fmt) {
+    case kFp16: return 2 * rows;
+    case kInt4: return rows / 2;
+    case kInt2: return rows / 4;
+    default: return 0;
+  }
+}
+// fp16 scales per stored column (0 for fp16 values).
+int64_t col_scales(int32_t fmt, int64_t rows) {
+  return (fmt == kInt4 || fmt == kInt2) ? rows / kGroup : 0;
+}
+// Bytes one 512-row tile of a column costs, used to balance the splits.
+int64_t tile_bytes(int32_t fmt) {
+  switch (fmt) {
+    case kFp16: return 2 * kTileRows;
+    case kInt4: return kTileRows / 2 + 2 * (kTileRows / kGroup);
+    case kInt2: return kTileRows / 4 + 2 * (kTileRows / kGroup);
+    default: return 0;
+  }
+}
+
+int validate_matrix(const spax_matrix* W) {
+  if (!W) return SPAX_ENULL;
+  if (W->rows <= 0 || W->cols <= 0 || W->rows % kGroup) return SPAX_EINVAL;
+  if (W->full_fmt != kFp16 && W->full_fmt != kInt4) return SPAX_EFORMAT;
+  if (W->approx_fmt != kNone && W->approx_fmt != kInt4 && W->approx_fmt != kInt2)
+    return SPAX_EFORMAT;
+  if (W->residency != SPAX_RES_DEVICE && W->residency != SPAX_RES_HOST_PINNED)
+    return SPAX_EINVAL;
+  if (W->layout != SPAX_LAYOUT_PLAIN && W->layout != SPAX_LAYOUT_GLU_INTERLEAVED)
+    return SPAX_EINVAL;
+  if (W->layout == SPAX_LAYOUT_GLU_INTERLEAVED && W->rows % (2 * kGroup)) return SPAX_EINVAL;
+  if (!W->full_data) return SPAX_ENULL;
+  if (W->full_fmt == kInt4 && !W->full_scales) return SPAX_ENULL;
+  if (W->approx_fmt != kNone && (!W->approx_codes || !W->approx_scales)) return SPAX_ENULL;
+  if (!aligned16(W->full_data) || !aligned16(W->full_scales) || !aligned16(W->approx_codes) ||
+      !aligned16(W->approx_scales))
+    return SPAX_EALIGN;
+  return SPAX_OK;
+}
+
+struct ProductPlan {
+  int32_t tiles = 1;
+  int32_t splits = 1;
+  int64_t wf = 0, wa = 0;
+};
+
+// Number of column splits: about two workgroups per compute unit, at least
+// 16 KB of weights per workgroup, a multiple of 8 (one XCD per split group).
+ProductPlan plan_product(const spax_matrix* W, int32_t kf, int32_t ka) {
+  constexpr int64_t kTargetBlocks = 512;
+  constexpr int64_t kMinSplitBytes = 16384;
+  ProductPlan p;
+  p.tiles = (W->rows + kTileRows - 1) / kTileRows;
+  p.wf = tile_bytes(W->full_fmt);
+  p.wa = tile_bytes(W->approx_fmt);
+  const int64_t total = kf * p.wf + ka * p.wa;
+  if (total == 0) return p;
+  int64_t s = (kTargetBlocks + p.tiles - 1) / p.tiles;
+  s = std::min<int64_t>(s, std::max<int64_t>(1, total / kMinSplitBytes));
+  s = std::min<int64_t>(s, kMaxSplits);
+  s = std::min<int64_t>(s, (int64_t)kf + ka);
+  if (s >= 8) s = s / 8 * 8;
+  p.splits = (int32_t)std::max<int64_t>(1, s);
+  return p;
+}
+
+size_t counters_bytes(const spax_matrix* W) {
+  return align256(sizeof(uint32_t) * ((W->rows + kTileRows - 1) / kTileRows));
+}
+size_t partials_bytes(const spax_matrix* W) {
+  return align256(sizeof(float) * (size_t)kMaxSplits * W->rows);
+}
+size_t staging_bytes(const spax_matrix* W) {
+  if (W->residency != SPAX_RES_HOST_PINNED) return 0;
+  const int64_t per_full = col_bytes(W->full_fmt, W->rows) + 2 * col_scales(W->full_fmt, W->rows);
+  const int64_t per_apx =
+      col_bytes(W->approx_fmt, W->rows) + 2 * col_scales(W->approx_fmt, W->rows);
+  return align256((size_t)W->cols * std::max(per_full, per_apx)) + 4 * 256;
+}
+size_t gemv_ws(const spax_matrix* W) {
+  return counters_bytes(W) + partials_bytes(W) + staging_bytes(W);
+}
+
+// Events for the host-resident copy pipeline, one set per thread and device.
+constexpr int kChunks = 4;
+struct EventSet {
+  int device = -1;
+  hipEvent_t ready = nullptr;
+  hipEvent_t chunk[kChunks] = {};
+};
+thread_local EventSet g_events;
+
+hipError_t events_for_current_device(EventSet** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  EventSet& es = g_events;
+  if (es.device != dev) {
+    // events of another device are kept alive; a thread that moves between
+    // devices re-creates its set on the new one
+    es = EventSet{};
+    e = hipEventCreateWithFlags(&es.ready, hipEventDisableTiming);
+    if (e != hipSuccess) return e;
+    for (auto& c : es.chunk) {
+      e = hipEventCreateWithFlags(&c, hipEventDisableTiming);
+      if (e != hipSuccess) return e;
+    }
+    es.device = dev;
+  }
+  *out = &es;
+  return hipSuccess;
+}
+
+int run_product(const spax_matrix* W, const uint16_t* x, const int32_t* fidx, int32_t kf,
+                const int32_t* aidx, int32_t ka, int32_t epi, uint16_t* y, uint16_t* ga,
+                uint16_t* gg, uint16_t* gu, void* ws, hipStream_t s, hipStream_t cs) {
+  const ProductPlan p = plan_product(W, kf, ka);
+  uint8_t* wsb = static_cast<uint8_t*>(ws);
+  GemvArgs a{};
+  a.rows = W->rows;
+  a.n_tiles = p.tiles;
+  a.n_splits = p.splits;
+  a.k_full = kf;
+  a.k_approx = ka;
+  a.w_full = p.wf;
+  a.w_approx = p.wa;
+  a.x = x;
+  a.full_idx = fidx;
+  a.approx_idx = aidx;
+  a.counters = reinterpret_cast<uint32_t*>(wsb);
+  a.partials = reinterpret_cast<float*>(wsb + counters_bytes(W));
+  a.y = y;
+  a.glu_a = ga;
+  a.glu_g = gg;
+  a.glu_u = gu;
+  const int64_t fb = col_bytes(W->full_fmt, W->rows), fsn = col_scales(W->full_fmt, W->rows);
+  const int64_t ab = col_bytes(W->approx_fmt, W->rows), asn = col_scales(W->approx_fmt, W->rows);
+  a.full_stride = fb;
+  a.full_sstride = fsn;
+  a.approx_stride = ab;
+  a.approx_sstride = asn;
+
+  if (W->residency == SPAX_RES_DEVICE) {
+    a.full_base = static_cast<const uint8_t*>(W->full_data);
+    a.full_scales = W->full_scales;
+    a.approx_base = W->approx_codes;
+    a.approx_scales = W->approx_scales;
+    a.split_lo = 0;
+    a.splits_here = p.splits;
+    const hipError_t e = launch_gemv(a, W->full_fmt, W->approx_fmt, false, epi, s);
+    return e == hipSuccess ? SPAX_OK : hip_fail(e);
+  }
+
+  // Host-resident: copy the selected columns into staging in chunks on the
+  // copy stream; the product consumes each chunk's splits as it lands.
+  uint8_t* st = wsb + counters_bytes(W) + partials_bytes(W);
+  size_t off = 0;
+  uint8_t* full_dst = st + off;
+  off = align256(off + (size_t)kf * fb);
+  uint16_t* fscale_dst = reinterpret_cast<uint16_t*>(st + off);
+  off = align256(off + (size_t)kf * fsn * 2);
+  uint8_t* approx_dst = st + off;
+  off = align256(off + (size_t)ka * ab);
+  uint16_t* ascale_dst = reinterpret_cast<uint16_t*>(st + off);
+
+  a.full_base = full_dst;
+  a.full_scales = fscale_dst;
+  a.approx_base = approx_dst;
+  a.approx_scales = ascale_dst;
+
+  CopyArgs c{};
+  c.k_full = kf;
+  c.k_approx = ka;
+  c.full_idx = fidx;
+  c.approx_idx = aidx;
+  c.full_src = static_cast<const uint8_t*>(W->full_data);
+  c.full_bytes = fb;
+  c.fscale_src = W->full_scales;
+  c.fscale_n = (int32_t)fsn;
+  c.approx_src = W->approx_codes;
+  c.approx_bytes = ab;
+  c.ascale_src = W->approx_scales;
+  c.ascale_n = (int32_t)asn;
+  c.full_dst = full_dst;
+  c.fscale_dst = fscale_dst;
+  c.approx_dst = approx_dst;
+  c.ascale_dst = ascale_dst;
+
+  EventSet* ev = nullptr;
+  hipError_t e = events_for_current_device(&ev);
+  if (e != hipSuccess) return hip_fail(e);
+  // the lists (and the previous use of the staging) are ready on `s`
+  if ((e = hipEventRecord(ev->ready, s)) != hipSuccess) return hip_fail(e);
+  if ((e = hipStreamWaitEvent(cs, ev->ready, 0)) != hipSuccess) return hip_fail(e);
+  const int chunks = std::min(kChunks, p.splits);
+  for (int k = 0; k < chunks; ++k) {
+    const int s_lo = (int)((int64_t)p.splits * k / chunks);
+    const int s_hi = (int)((int64_t)p.splits * (k + 1) / chunks);
+    c.e_lo = split_start(s_lo, p.splits, kf, ka, p.wf, p.wa);
+    c.e_hi = split_start(s_hi, p.splits, kf, ka, p.wf, p.wa);
+    if ((e = launch_copy(c, cs)) != hipSuccess) return hip_fail(e);
+    if ((e = hipEventRecord(ev->chunk[k], cs)) != hipSuccess) return hip_fail(e);
+    if ((e = hipStreamWaitEvent(s, ev->chunk[k], 0)) != hipSuccess) return hip_fail(e);
+    a.split_lo = s_lo;
+    a.splits_here = s_hi - s_lo;
+    if ((e = launch_gemv(a, W->full_fmt, W->approx_fmt, true, epi, s)) != hipSuccess)
+      return hip_fail(e);
+  }
+  return SPAX_OK;
+}
+
+int check_counts(int32_t n, int32_t kf, int32_t ka) {
+  if (kf < 0 || ka < 0 || (int64_t)kf + ka > n) return SPAX_EINVAL;
+  return SPAX_OK;
+}
+
+int validate_product(const spax_matrix* W, const uint16_t* x, const int32_t* fidx, int32_t kf,
+                     const int32_t* aidx, int32_t ka, const void* ws, size_t ws_bytes,
+                     hipStream_t cs) {
+  int st = validate_matrix(W);
+  if (st) return st;
+  if ((st = check_counts(W->cols, kf, ka))) return st;
+  if (ka > 0 && W->approx_fmt == kNone) return SPAX_EINVAL;
+  if (!x || (kf > 0 && !fidx) || (ka > 0 && !aidx) || !ws) return SPAX_ENULL;
+  if (!aligned16(x) || !aligned16(fidx) || !aligned16(aidx) || !aligned16(ws)) return SPAX_EALIGN;
+  if (ws_bytes < gemv_ws(W)) return SPAX_EWORKSPACE;
+  if (W->residency == SPAX_RES_HOST_PINNED && !cs) return SPAX_ESTREAM;
+  return SPAX_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int spax_version(void) { return 100; }
+
+const char* spax_status_string(int status) {
+  switch (status) {
+    case SPAX_OK: return "ok";
+    case SPAX_EINVAL: return "invalid size or tier count";
+    case SPAX_ENULL: return "required pointer is null";
+    case SPAX_EALIGN: return "device pointer is not 16-byte aligned";
+    case SPAX_EFORMAT: return "unknown or unsupported format";
+    case SPAX_EWORKSPACE: return "workspace too small";
+    case SPAX_ESTREAM: return "host-resident matrix needs a copy stream";
+    case SPAX_EHIP: return "HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+const char* spax_last_error(void) { return g_last_error.c_str(); }
+
+int spax_plan_tiers(const uint16_t* x, int32_t n, int32_t k_full, int32_t k_approx,
+                    int32_t* full_idx, int32_t* approx_idx, hipStream_t stream) {
+  if (n < 1 || n > 65536) return SPAX_EINVAL;
+  int st = check_counts(n, k_full, k_approx);
+  if (st) return st;
+  if (!x || (k_full > 0 && !full_idx) || (k_approx > 0 && !approx_idx)) return SPAX_ENULL;
+  if (!aligned16(x) || !aligned16(full_idx) || !aligned16(approx_idx)) return SPAX_EALIGN;
+  const hipError_t e = launch_plan(x, n, k_full, k_approx, full_idx, approx_idx, stream);
+  return e == hipSuccess ? SPAX_OK : hip_fail(e);
+}
+
+size_t spax_gemv_workspace_bytes(const spax_matrix* W) {
+  if (validate_matrix(W) != SPAX_OK) return 0;
+  return gemv_ws(W);
+}
+
+int spax_tiered_gemv(const spax_matrix* W, const uint16_t* x, const int32_t* full_idx,
+                     int32_t k_full, const int32_t* approx_idx, int32_t k_approx, uint16_t* y,
+                     void* ws, size_t ws_bytes, hipStream_t stream, hipStream_t copy_stream) {
+  int st = validate_product(W, x, full_idx, k_full, approx_idx, k_approx, ws, ws_bytes,
+                            copy_stream);
+  if (st) return st;
+  if (!y) return SPAX_ENULL;
+  if (!aligned16(y)) return SPAX_EALIGN;
+  return run_product(W, x, full_idx, k_full, approx_idx, k_approx, kEpiPlain, y, nullptr,
+                     nullptr, nullptr, ws, stream, copy_stream);
+}
+
+size_t spax_layer_workspace_bytes(const spax_layer* L) {
+  if (!L) return 0;
+  size_t m = 0;
+  for (int g = 0; g < 4; ++g)
+    if (L->group[g].cols > 0 && validate_matrix(&L->group[g]) == SPAX_OK)
+      m = std::max(m, gemv_ws(&L->group[g]));
+  return m;
+}
+
+int spax_layer_step(const spax_layer* L, const spax_layer_io* io, void* ws, size_t ws_bytes,
+                    hipStream_t compute_stream, hipStream_t copy_stream) {
+  if (!L || !io) return SPAX_ENULL;
+  const spax_matrix* G = L->group;
+  const bool ffn = G[SPAX_GROUP_GATE_UP].cols > 0;
+  if (ffn != (G[SPAX_GROUP_DOWN].cols > 0)) return SPAX_EINVAL;
+  if (ffn) {
+    if (G[SPAX_GROUP_GATE_UP].layout != SPAX_LAYOUT_GLU_INTERLEAVED) return SPAX_EINVAL;
+    if (G[SPAX_GROUP_DOWN].cols != G[SPAX_GROUP_GATE_UP].rows / 2) return SPAX_EINVAL;
+    if (G[SPAX_GROUP_DOWN].layout != SPAX_LAYOUT_PLAIN) return SPAX_EINVAL;
+  }
+  const uint16_t* inputs[4] = {io->h, io->z, io->x, io->a};
+  uint16_t* outputs[4] = {io->qkv, io->o, io->a, io->down};
+  if (ws_bytes < spax_layer_workspace_bytes(L)) return SPAX_EWORKSPACE;
+  // validate everything before enqueuing anything
+  for (int g = 0; g < 4; ++g) {
+    if (G[g].cols <= 0) continue;
+    if (g != SPAX_GROUP_GATE_UP && G[g].layout != SPAX_LAYOUT_PLAIN) return SPAX_EINVAL;
+    int st = validate_product(&G[g], inputs[g], io->full_idx[g], L->k_full[g],
+                              io->approx_idx[g], L->k_approx[g], ws, ws_bytes, copy_stream);
+    if (st) return st;
+    if (G[g].cols > 65536) return SPAX_EINVAL;
+    if (!outputs[g]) return SPAX_ENULL;
+    if (!aligned16(outputs[g]) || !aligned16(io->g) || !aligned16(io->u)) return SPAX_EALIGN;
+  }
+  for (int g = 0; g < 4; ++g) {
+    if (G[g].cols <= 0) continue;
+    hipError_t e = launch_plan(inputs[g], G[g].cols, L->k_full[g], L->k_approx[g],
+                               io->full_idx[g], io->approx_idx[g], compute_stream);
+    if (e != hipSuccess) return hip_fail(e);
+    int st;
+    if (g == SPAX_GROUP_GATE_UP)
+      st = run_product(&G[g], inputs[g], io->full_idx[g], L->k_full[g], io->approx_idx[g],
+                       L->k_approx[g], kEpiGlu, nullptr, io->a, io->g, io->u, ws,
+                       compute_stream, copy_stream);
+    else
+      st = run_product(&G[g], inputs[g], io->full_idx[g], L->k_full[g], io->approx_idx[g],
+                       L->k_approx[g], kEpiPlain, outputs[g], nullptr, nullptr, nullptr, ws,
+                       compute_stream, copy_stream);
+    if (st) return st;
+  }
+  return SPAX_OK;
+}
+
+int spax_pack_g128(const uint16_t* w, int32_t rows, int32_t cols, int32_t fmt, uint8_t* codes,
+                   uint16_t* scales, hipStream_t stream) {
+  if (fmt != kInt4 && fmt != kInt2) return SPAX_EFORMAT;
+  if (rows <= 0 || cols <= 0 || rows % kGroup) return SPAX_EINVAL;
+  if (!w || !codes || !scales) return SPAX_ENULL;
+  if (!aligned16(w) || !aligned16(codes) || !aligned16(scales)) return SPAX_EALIGN;
+  const hipError_t e = launch_pack(w, rows, cols, fmt, codes, scales, stream);
+  return e == hipSuccess ? SPAX_OK : hip_fail(e);
+}
+
+int spax_workspace_clear(void* ws, size_t bytes, hipStream_t stream) {
+  if (bytes % 4) return SPAX_EINVAL;
+  if (bytes == 0) return SPAX_OK;
+  if (!ws) return SPAX_ENULL;
+  if (!aligned16(ws)) return SPAX_EALIGN;
+  const hipError_t e = launch_clear(ws, bytes, stream);
+  return e == hipSuccess ? SPAX_OK : hip_fail(e);
+}
+
+}  // extern "C"

@@ -1,0 +1,159 @@
+// Selected-column copy, packer and workspace clear (gfx950).
+#include <hip/hip_fp16.h>
+#include <hip/hip_runtime.h>
+
+#include "spax_internal.h"
+
+namespace spax {
+namespace {
+
+// ---------------------------------------------------------------------------
+// Selected-column copy for host-resident weights.
+// SpAx page, section 5 Figure 2 step 4 (only the top-tier columns and the
+// middle-tier codes of the selected entries are fetched into GPU memory) and
+// section 5.3 (each entry's data is a contiguous range; ranges of one tier
+// are read as whole runs). Each wave moves whole columns from pinned host
+// memory (device-addressable) into device staging, slot = list position, so
+// the product reads the staging in list order. Adjacent columns of a run
+// stream back to back from the same wave-wide loads, so no per-range request
+// is issued by the host.
+// ---------------------------------------------------------------------------
+constexpr int kCopyThreads = 256;
+
+__device__ __forceinline__ void copy_bytes(uint8_t* __restrict__ dst,
+                                           const uint8_t* __restrict__ src, int64_t nbytes,
+                                           int lane) {
+  // nbytes is a multiple of 16; 8 loads in flight per lane
+  const int64_t n16 = nbytes >> 4;
+  const uint4* s = reinterpret_cast<const uint4*>(src);
+  uint4* d = reinterpret_cast<uint4*>(dst);
+  int64_t i = lane;
+  for (; i + 7 * 64 < n16; i += 8 * 64) {
+    uint4 v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) v[u] = s[i + u * 64];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) d[i + u * 64] = v[u];
+  }
+  for (; i < n16; i += 64) d[i] = s[i];
+}
+
+__global__ __launch_bounds__(kCopyThreads) void copy_kernel(CopyArgs a) {
+  const int lane = threadIdx.x & 63;
+  const int64_t gw = (int64_t)blockIdx.x * (kCopyThreads / 64) + (threadIdx.x >> 6);
+  const int64_t nw = (int64_t)gridDim.x * (kCopyThreads / 64);
+  for (int64_t e = a.e_lo + gw; e < a.e_hi; e += nw) {
+    if (e < a.k_full) {
+      const int64_t col = a.full_idx[e];
+      copy_bytes(a.full_dst + e * a.full_bytes, a.full_src + col * a.full_bytes, a.full_bytes,
+                 lane);
+      for (int i = lane; i < a.fscale_n; i += 64)
+        a.fscale_dst[e * a.fscale_n + i] = a.fscale_src[col * a.fscale_n + i];
+    } else {
+      const int64_t p = e - a.k_full;
+      const int64_t col = a.approx_idx[p];
+      copy_bytes(a.approx_dst + p * a.approx_bytes, a.approx_src + col * a.approx_bytes,
+                 a.approx_bytes, lane);
+      for (int i = lane; i < a.ascale_n; i += 64)
+        a.ascale_dst[p * a.ascale_n + i] = a.ascale_src[col * a.ascale_n + i];
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Group-128 packer (offline). SpAx page section 5, Figure 2 step 1 and
+// section 5.1: every column is encoded on its own, in groups of 128 rows with
+// one fp16 scale.
+//   int4: s = fp16(m / 7),   q = clamp(rne(w / s), -8, 7)
+//   int2: s = fp16(m / 1.5), u = clamp(rne(w / s + 1.5), 0, 3)
+// The quotients are taken in fp64 and rounded once (to fp16 through fp32, or
+// to an integer with ties to even); for fp16 operands neither rounding can
+// land on a tie the exact quotient does not have.
+// One wave per (column, group); lane l reads rows 2l and 2l+1.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ float h2f(uint16_t b) { return __half2float(__ushort_as_half(b)); }
+
+__global__ __launch_bounds__(256) void pack_kernel(const uint16_t* __restrict__ w, int rows,
+                                                   int cols, int fmt, uint8_t* __restrict__ codes,
+                                                   uint16_t* __restrict__ scales) {
+  const int lane = threadIdx.x & 63;
+  const int64_t item = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int groups = rows / kGroup;
+  if (item >= (int64_t)cols * groups) return;
+  const int64_t col = item / groups;
+  const int g = (int)(item - col * groups);
+  const uint16_t* src = w + col * rows + (int64_t)g * kGroup;
+  const float w0 = h2f(src[2 * lane]), w1 = h2f(src[2 * lane + 1]);
+  float m = fmaxf(fabsf(w0), fabsf(w1));
+#pragma unroll
+  for (int d = 32; d >= 1; d >>= 1) m = fmaxf(m, __shfl_xor(m, d, 64));
+  const double top = fmt == kInt4 ? 7.0 : 1.5;
+  const __half sh = __float2half_rn((float)((double)m / top));
+  const uint16_t sbits = __half_as_ushort(sh);
+  const double s = (double)__half2float(sh);
+  if (lane == 0) scales[col * groups + g] = sbits;
+  if (fmt == kInt4) {
+    int q0 = 0, q1 = 0;
+    if (s > 0.0) {
+      q0 = (int)rint((double)w0 / s);
+      q1 = (int)rint((double)w1 / s);
+      q0 = min(7, max(-8, q0));
+      q1 = min(7, max(-8, q1));
+    }
+    codes[col * (rows / 2) + (int64_t)g * 64 + lane] =
+        (uint8_t)((q0 & 0xF) | ((q1 & 0xF) << 4));
+  } else {
+    // lanes 0..31 each build one byte from rows 4l .. 4l+3
+    if (lane < 32) {
+      uint32_t byte = 0;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const double wv = (double)h2f(src[4 * lane + r]);
+        int u = 2;
+        if (s > 0.0) u = min(3, max(0, (int)rint(wv / s + 1.5)));
+        byte |= (uint32_t)u << (2 * r);
+      }
+      codes[col * (rows / 4) + (int64_t)g * 32 + lane] = (uint8_t)byte;
+    }
+  }
+}
+
+__global__ void clear_kernel(uint32_t* __restrict__ p, int64_t n) {
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
+       i += (int64_t)gridDim.x * blockDim.x)
+    p[i] = 0u;
+}
+
+}  // namespace
+
+hipError_t launch_copy(const CopyArgs& a, hipStream_t s) {
+  const int64_t cols = a.e_hi - a.e_lo;
+  if (cols <= 0) return hipSuccess;
+  const int64_t waves = (kCopyThreads / 64);
+  int64_t blocks = (cols + waves - 1) / waves;
+  if (blocks > 512) blocks = 512;
+  hipLaunchKernelGGL(copy_kernel, dim3((unsigned)blocks), dim3(kCopyThreads), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_pack(const uint16_t* w, int32_t rows, int32_t cols, int32_t fmt,
+                       uint8_t* codes, uint16_t* scales, hipStream_t s) {
+  const int64_t items = (int64_t)cols * (rows / kGroup);
+  if (items == 0) return hipSuccess;
+  const int64_t blocks = (items + 3) / 4;
+  hipLaunchKernelGGL(pack_kernel, dim3((unsigned)blocks), dim3(256), 0, s, w, rows, cols, fmt,
+                     codes, scales);
+  return hipGetLastError();
+}
+
+hipError_t launch_clear(void* ws, size_t bytes, hipStream_t s) {
+  const int64_t n = (int64_t)(bytes / 4);
+  if (n == 0) return hipSuccess;
+  int64_t blocks = (n + 255) / 256;
+  if (blocks > 4096) blocks = 4096;
+  hipLaunchKernelGGL(clear_kernel, dim3((unsigned)blocks), dim3(256), 0, s,
+                     reinterpret_cast<uint32_t*>(ws), n);
+  return hipGetLastError();
+}
+
+}  // namespace spax

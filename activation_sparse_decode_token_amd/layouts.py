@@ -1,0 +1,84 @@
+"""Offline weight preparation for the library's storage layouts.
+
+Weights are column-major: a matrix of R rows and n columns is a tensor of
+shape [n, R] whose row j is column j (contiguous). Matrices that share an
+input are stored as one matrix so that the columns one activation entry
+indexes are adjacent (SpAx page, section 5.3, Figure 4):
+  * q, k, v: rows stacked, column j = [q_j; k_j; v_j];
+  * gate, up: rows interleaved in 128-row blocks (SPAX_LAYOUT_GLU_INTERLEAVED).
+The compressed copies are produced by the library's packer (spax_pack_g128).
+These helpers only move data; nothing here is on the per-token path.
+"""
+from __future__ import annotations
+
+from typing import Optional, Sequence
+
+import torch
+
+from . import (FMT_FP16, FMT_INT2_G128, FMT_INT4_G128, FMT_NONE, LAYOUT_GLU_INTERLEAVED,
+               LAYOUT_PLAIN, RES_DEVICE, RES_HOST_PINNED, Matrix, pack_g128)
+
+GROUP = 128
+
+
+def stack_rows(cols_major: Sequence[torch.Tensor]) -> torch.Tensor:
+    """[n, R_i] tensors -> [n, sum R_i]: column j holds every matrix's column j."""
+    return torch.cat(list(cols_major), dim=1).contiguous()
+
+
+def glu_interleave(gate: torch.Tensor, up: torch.Tensor) -> torch.Tensor:
+    """[n, I] gate and up -> [n, 2I] interleaved in 128-row blocks."""
+    n, I = gate.shape
+    if up.shape != gate.shape or I % GROUP:
+        raise ValueError("gate and up must share a shape with I % 128 == 0")
+    g = gate.reshape(n, I // GROUP, 1, GROUP)
+    u = up.reshape(n, I // GROUP, 1, GROUP)
+    return torch.cat([g, u], dim=2).reshape(n, 2 * I).contiguous()
+
+
+def glu_deinterleave(stacked: torch.Tensor):
+    """Inverse of glu_interleave along the last dimension (rows)."""
+    *lead, R2 = stacked.shape
+    v = stacked.reshape(*lead, R2 // (2 * GROUP), 2, GROUP)
+    return v[..., 0, :].reshape(*lead, R2 // 2), v[..., 1, :].reshape(*lead, R2 // 2)
+
+
+def pack(w_cm: torch.Tensor, fmt: int, stream=None):
+    """Codes and scales of a column-major fp16 device tensor [n, R]."""
+    n, R = w_cm.shape
+    per = {FMT_INT4_G128: 2, FMT_INT2_G128: 4}[fmt]
+    codes = torch.empty((n, R // per), dtype=torch.uint8, device=w_cm.device)
+    scales = torch.empty((n, R // GROUP), dtype=torch.float16, device=w_cm.device)
+    pack_g128(w_cm, R, n, fmt, codes, scales, stream)
+    return codes, scales
+
+
+def _pin(t: Optional[torch.Tensor]) -> Optional[torch.Tensor]:
+    if t is None:
+        return None
+    h = torch.empty(t.shape, dtype=t.dtype, pin_memory=True)
+    h.copy_(t)
+    return h
+
+
+def build_matrix(w_cm: torch.Tensor, full_fmt: int = FMT_FP16,
+                 approx_fmt: int = FMT_INT4_G128, layout: int = LAYOUT_PLAIN,
+                 residency: int = RES_DEVICE, stream=None) -> Matrix:
+    """A spax_matrix for a column-major fp16 device tensor [n, R].
+
+    The full tier is w_cm itself (fp16) or its int4 code; the approx tier is
+    the int4 / int2 code of w_cm. With RES_HOST_PINNED every buffer is copied
+    to pinned host memory and the device copies are dropped."""
+    n, R = w_cm.shape
+    fs = None
+    if full_fmt == FMT_FP16:
+        fd = w_cm
+    else:
+        fd, fs = pack(w_cm, full_fmt, stream)
+    ac = asc = None
+    if approx_fmt != FMT_NONE:
+        ac, asc = pack(w_cm, approx_fmt, stream)
+    if residency == RES_HOST_PINNED:
+        torch.cuda.synchronize()
+        fd, fs, ac, asc = _pin(fd), _pin(fs), _pin(ac), _pin(asc)
+    return Matrix.make(R, n, full_fmt, approx_fmt, fd, fs, ac, asc, residency, layout)

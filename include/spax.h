@@ -1,0 +1,220 @@
+/*
+ * spax.h -- C ABI of the three-tier activation-sparse decode library (gfx950).
+ *
+ * Method: "Activation Sparsity with Weight Approximation for Faster LLM
+ * Decoding on Offloaded Weights" (the SpAx page). For each token and each
+ * projection the input activations are ranked by magnitude; the columns of
+ * the smallest are skipped, the next ones are read from a compressed copy and
+ * the largest ones are read in full precision (section 1; section 5,
+ * Figure 2 steps 3-5), giving y = W[:,F] x_F + W^[:,A] x_A (section 2 Eq. 1
+ * restricted to the kept columns).
+ *
+ * Conventions shared by every call
+ *   - fp16 values travel as uint16_t bit patterns; indices are int32_t.
+ *   - Matrices are column-major: column j of an R-row matrix is contiguous.
+ *     One column per activation entry keeps a selected column readable on
+ *     its own (section 1, challenge 1; section 5.1).
+ *   - Group-128 codes: a group is 128 consecutive rows of one column with one
+ *     fp16 scale, so each column is rebuilt from its own codes (section 5.1).
+ *       int4: s = fp16(max|w| / 7), q = clamp(rne(w / s), -8, 7), w^ = q s;
+ *             row 2i in bits 0-3 of byte i of the column, row 2i+1 in 4-7.
+ *       int2: s = fp16(max|w| / 1.5), u = clamp(rne(w / s + 1.5), 0, 3),
+ *             w^ = (u - 1.5) s  (the sign-pair form of section 5.1 Eq. 4
+ *             with scales s and s/2); row 4i+r in bits 2r..2r+1 of byte i.
+ *       codes: [cols][rows/2] (int4) or [cols][rows/4] (int2) bytes;
+ *       scales: [cols][rows/128] fp16.
+ *   - rows must be a multiple of 128 for every format.
+ *   - Every device pointer must be 16-byte aligned.
+ *   - The caller owns every buffer. Calls validate their arguments on the
+ *     host, enqueue kernels on the given stream(s) and return; results are
+ *     valid once the stream has reached that point. No call allocates memory.
+ *   - A status code is returned; 0 is success. Validation errors return
+ *     before anything is enqueued. No exception crosses the ABI.
+ */
+#ifndef SPAX_H_
+#define SPAX_H_
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ---- status codes ------------------------------------------------------ */
+#define SPAX_OK          0
+#define SPAX_EINVAL     -1  /* a size or a tier count is out of range          */
+#define SPAX_ENULL      -2  /* a required pointer is null                      */
+#define SPAX_EALIGN     -3  /* a device pointer is not 16-byte aligned         */
+#define SPAX_EFORMAT    -4  /* unknown format or unsupported combination       */
+#define SPAX_EWORKSPACE -5  /* workspace smaller than the *_workspace_bytes()  */
+#define SPAX_ESTREAM    -6  /* host-resident matrix but no copy stream given   */
+#define SPAX_EHIP       -7  /* the HIP runtime reported an error; see
+                               spax_last_error()                               */
+
+/* ---- formats, residency, layout ---------------------------------------- */
+#define SPAX_FMT_NONE       0  /* tier absent (its count must be 0)          */
+#define SPAX_FMT_FP16       1  /* fp16 values, rows*2 bytes per column        */
+#define SPAX_FMT_INT4_G128  2  /* int4 codes + fp16 scale per 128 rows        */
+#define SPAX_FMT_INT2_G128  3  /* int2 codes + fp16 scale per 128 rows        */
+
+#define SPAX_RES_DEVICE       0  /* weights in device memory (HBM)            */
+#define SPAX_RES_HOST_PINNED  1  /* weights in pinned host memory that the GPU
+                                    can address (hipHostMalloc); only the
+                                    selected columns cross the host link       */
+
+#define SPAX_LAYOUT_PLAIN           0
+/* Gate and up projections of a gated FFN (section 2: a = silu(W_gate x) *
+ * W_up x) stored as ONE matrix of 2*I rows whose column j holds the two
+ * column-j segments interleaved in 128-row blocks:
+ *   stored rows [256b, 256b+128)     = gate rows [128b, 128b+128)
+ *   stored rows [256b+128, 256b+256) = up   rows [128b, 128b+128)
+ * The two matrices share one ranking and one request per entry (section 5.3,
+ * Figure 4: the columns that one activation entry indexes are adjacent). */
+#define SPAX_LAYOUT_GLU_INTERLEAVED 1
+
+/* One projection (or one group of projections stacked row-wise). */
+typedef struct spax_matrix {
+  int32_t rows;            /* output length R (multiple of 128)            */
+  int32_t cols;            /* input length n                                */
+  int32_t full_fmt;        /* SPAX_FMT_FP16 or SPAX_FMT_INT4_G128           */
+  int32_t approx_fmt;      /* SPAX_FMT_NONE, _INT4_G128 or _INT2_G128       */
+  int32_t residency;       /* SPAX_RES_*                                    */
+  int32_t layout;          /* SPAX_LAYOUT_*                                 */
+  const void* full_data;   /* fp16 [cols][rows] or int4 codes [cols][rows/2] */
+  const uint16_t* full_scales;   /* int4 full tier only: [cols][rows/128]   */
+  const uint8_t* approx_codes;   /* approx codes, layout per approx_fmt     */
+  const uint16_t* approx_scales; /* [cols][rows/128]                        */
+} spax_matrix;
+
+/* ---- tier selection ----------------------------------------------------- */
+/* spax_plan_tiers -- rank x by magnitude and split its entries into tiers.
+ *   SpAx page section 2 (magnitude top-k keeps the largest |x_i|) and
+ *   section 5, Figure 2 step 3 with section 5.2 (a second boundary divides
+ *   the kept entries; k_top and k_mid are integers per group).
+ *   x          device, fp16[n], 16-byte aligned; read only.
+ *   n          1 .. 65536.
+ *   k_full     number of full-tier entries (k_top), >= 0.
+ *   k_approx   number of middle-tier entries (k_mid), >= 0, k_full+k_approx <= n.
+ *   full_idx   device int32[k_full]   out: ascending indices of the k_full
+ *              largest |x_j|.
+ *   approx_idx device int32[k_approx] out: ascending indices of the next
+ *              k_approx.
+ *   Ties in |x| rank the lower index first; +0 and -0 are equal; the order
+ *   key is the fp16 magnitude bit pattern (inf above every finite value).
+ *   The result is deterministic and bit-exact.
+ *   Errors: SPAX_ENULL, SPAX_EINVAL (sizes), SPAX_EALIGN, SPAX_EHIP.       */
+int spax_plan_tiers(const uint16_t* x, int32_t n, int32_t k_full, int32_t k_approx,
+                    int32_t* full_idx, int32_t* approx_idx, hipStream_t stream);
+
+/* ---- tiered product ----------------------------------------------------- */
+/* Workspace bytes one spax_tiered_gemv call on W needs (any tier counts). */
+size_t spax_gemv_workspace_bytes(const spax_matrix* W);
+
+/* spax_tiered_gemv -- y = sum_{j in F} x_j W~[:,j] + sum_{j in A} x_j W^[:,j].
+ *   SpAx page section 2 Eq. 1 and section 5, Figure 2 steps 4-5: the full
+ *   tier is read in its stored format (fp16, or int4 dequantised), the middle
+ *   tier is rebuilt from its codes on the GPU, the skipped columns are never
+ *   read. Products and sums in fp32, y rounded once to fp16 (nearest even).
+ *   W          matrix descriptor (host struct, read during the call only).
+ *   x          device fp16[W->cols].
+ *   full_idx   device int32[k_full], approx_idx device int32[k_approx]:
+ *              in-range, disjoint; any order is accepted, the fp32 summation
+ *              follows list order.
+ *   y          device fp16[W->rows] out (stored row order; for the
+ *              GLU-interleaved layout this is the interleaved order).
+ *   ws         device workspace of spax_gemv_workspace_bytes(W) bytes. It
+ *              must be all zero before its first use (spax_workspace_clear);
+ *              every call leaves its counters at zero again. Calls that share
+ *              a workspace must be ordered on one stream.
+ *   stream     compute stream. copy_stream: required when W is
+ *              SPAX_RES_HOST_PINNED (only the selected columns are copied to
+ *              device staging inside ws, in chunks overlapped with the
+ *              product), ignored otherwise.
+ *   k_full = k_approx = 0 writes zeros. The result is deterministic: the
+ *   same inputs give the same bits, in both residency modes.
+ *   Errors: SPAX_ENULL, SPAX_EINVAL, SPAX_EALIGN, SPAX_EFORMAT,
+ *   SPAX_EWORKSPACE, SPAX_ESTREAM, SPAX_EHIP.                                */
+int spax_tiered_gemv(const spax_matrix* W, const uint16_t* x,
+                     const int32_t* full_idx, int32_t k_full,
+                     const int32_t* approx_idx, int32_t k_approx,
+                     uint16_t* y, void* ws, size_t ws_bytes,
+                     hipStream_t stream, hipStream_t copy_stream);
+
+/* ---- one decoder layer -------------------------------------------------- */
+#define SPAX_GROUP_QKV     0  /* W_q, W_k, W_v stacked row-wise; input h   */
+#define SPAX_GROUP_O       1  /* W_o; input z                               */
+#define SPAX_GROUP_GATE_UP 2  /* W_gate, W_up, GLU-interleaved; input x     */
+#define SPAX_GROUP_DOWN    3  /* W_down; input a = silu(g) * u              */
+
+/* The seven matrices of a layer in the four groups that share a ranking
+ * (section 2; section 5.2 step 1; section 5.3 Figure 4). A group whose
+ * matrix has cols == 0 is absent and skipped. GATE_UP must use
+ * SPAX_LAYOUT_GLU_INTERLEAVED and DOWN must have cols == GATE_UP.rows / 2;
+ * GATE_UP and DOWN are present together or not at all. */
+typedef struct spax_layer {
+  spax_matrix group[4];
+  int32_t k_full[4];
+  int32_t k_approx[4];
+} spax_layer;
+
+/* Inputs, outputs and per-group tier lists (all device pointers). */
+typedef struct spax_layer_io {
+  const uint16_t* h;       /* fp16[QKV.cols]                                 */
+  const uint16_t* z;       /* fp16[O.cols]                                   */
+  const uint16_t* x;       /* fp16[GATE_UP.cols]                             */
+  uint16_t* qkv;           /* out fp16[QKV.rows] (q, k, v in stored order)   */
+  uint16_t* o;             /* out fp16[O.rows]                               */
+  uint16_t* g;             /* out fp16[I] gate output, may be null           */
+  uint16_t* u;             /* out fp16[I] up output, may be null             */
+  uint16_t* a;             /* out fp16[I] = fp16(silu(g) * u)                */
+  uint16_t* down;          /* out fp16[DOWN.rows]                            */
+  int32_t* full_idx[4];    /* out per group, int32[k_full[g]]                */
+  int32_t* approx_idx[4];  /* out per group, int32[k_approx[g]]              */
+} spax_layer_io;
+
+size_t spax_layer_workspace_bytes(const spax_layer* L);
+
+/* spax_layer_step -- rank each group's input once, then run the group's
+ * tiered product with the shared lists: h -> q,k,v; z -> o; x -> gate,up;
+ * a = silu(g) * u is formed in the gate/up product's final reduction (fp32
+ * math on the fp16 g and u, one rounding); a -> down.
+ *   SpAx page section 2 (matrices and inputs), sections 5.2-5.3 (groups).
+ *   ws / ws_bytes as for spax_tiered_gemv, sized by
+ *   spax_layer_workspace_bytes(L). copy_stream is required when any group is
+ *   host-resident. Deterministic. Errors: as spax_tiered_gemv.              */
+int spax_layer_step(const spax_layer* L, const spax_layer_io* io,
+                    void* ws, size_t ws_bytes,
+                    hipStream_t compute_stream, hipStream_t copy_stream);
+
+/* ---- offline helpers ---------------------------------------------------- */
+/* spax_pack_g128 -- encode the compressed copy of a matrix (SpAx page
+ * section 5, Figure 2 step 1: every column is encoded offline, on its own).
+ *   w      device fp16 [cols][rows] (column-major), rows % 128 == 0.
+ *   fmt    SPAX_FMT_INT4_G128 or SPAX_FMT_INT2_G128.
+ *   codes  device out, [cols][rows/2] or [cols][rows/4] bytes.
+ *   scales device out, fp16 [cols][rows/128].
+ *   Bit-exact to the rules in the header comment above.
+ *   Errors: SPAX_ENULL, SPAX_EINVAL, SPAX_EALIGN, SPAX_EFORMAT, SPAX_EHIP.  */
+int spax_pack_g128(const uint16_t* w, int32_t rows, int32_t cols, int32_t fmt,
+                   uint8_t* codes, uint16_t* scales, hipStream_t stream);
+
+/* spax_workspace_clear -- zero `bytes` bytes of ws with a kernel (no memset
+ * node, so it may be captured in a graph). bytes % 4 == 0. */
+int spax_workspace_clear(void* ws, size_t bytes, hipStream_t stream);
+
+/* Text for a status code (static storage). */
+const char* spax_status_string(int status);
+
+/* Text of the last HIP error seen by this thread (static per thread). */
+const char* spax_last_error(void);
+
+/* Library version, major*10000 + minor*100 + patch. */
+int spax_version(void);
+
+#ifdef __cplusplus
+}  /* extern "C" */
+#endif
+
+#endif  /* SPAX_H_ */

@@ -1,0 +1,115 @@
+"""Helpers shared by the GPU parity tests (not collected by pytest)."""
+from __future__ import annotations
+
+import math
+import sys
+
+import numpy as np
+
+import oracle as O
+
+GROUP = 128
+# Stated tolerance for fp16 outputs with fp32 accumulation: max relative error
+# 2e-3, norm-wise (|y - r|_inf / |r|_inf).
+REL_TOL = 2e-3
+U24 = 2.0 ** -24
+
+
+def log(msg: str) -> None:
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def torch_dev():
+    import torch
+    return torch.device("cuda:0")
+
+
+def to_dev(a: np.ndarray):
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(a)).to(torch_dev())
+
+
+def to_host(t) -> np.ndarray:
+    return t.detach().cpu().numpy()
+
+
+def ulp16(v: np.ndarray) -> np.ndarray:
+    a = np.abs(np.asarray(v, dtype=np.float64))
+    e = np.floor(np.log2(np.maximum(a, 2.0 ** -14)))
+    return 2.0 ** (e - 10)
+
+
+def abs_sum(x, F, A, full: O.ColumnStore, approx) -> np.ndarray:
+    """Per-row sum of the magnitudes the fp32 accumulation adds: |x_j W_ij|
+    for full fp16 columns, and |x_j s_jg| (u_ij + offset) for code columns
+    (the kernel sums c*u and c*offset separately)."""
+    xf = np.asarray(x, dtype=np.float16).astype(np.float64)
+    S = np.zeros(full.rows)
+
+    def code_part(store, idx):
+        if store.fmt == "int4":
+            nib = np.empty((len(idx), store.rows), dtype=np.int64)
+            c = store.codes[idx]
+            nib[:, 0::2] = c & 0xF
+            nib[:, 1::2] = c >> 4
+            u = (nib ^ 8).astype(np.float64)
+            off = 8.0
+        else:
+            c = store.codes[idx]
+            u = np.empty((len(idx), store.rows), dtype=np.float64)
+            for r in range(4):
+                u[:, r::4] = (c >> (2 * r)) & 3
+            off = 1.5
+        s = np.repeat(store.scales[idx].astype(np.float64), GROUP, axis=1)
+        return np.abs(xf[idx])[:, None] * s * (u + off)
+
+    if len(F):
+        if full.fmt == "fp16":
+            S += np.abs(xf[F]) @ np.abs(full.columns(F))
+        else:
+            S += code_part(full, F).sum(axis=0)
+    if len(A):
+        S += code_part(approx, A).sum(axis=0)
+    return S
+
+
+def check_product(y16: np.ndarray, x, F, A, full, approx, label: str = "",
+                  rows: np.ndarray | None = None) -> float:
+    """Compare a GPU fp16 output with the oracle.
+
+    Gate: |y - r|_inf <= 2e-3 |r|_inf. Also every element must sit within
+    the order-independent bound gamma_m * S_i + ulp16(y_i)/2 of the exact
+    value r_i (m = terms summed, S_i = abs_sum); an all-zero r needs y == 0.
+    `rows` optionally names the stored rows the stores were cut to.
+    Returns the norm-wise error."""
+    r = O.tiered_product(x, F, A, full, approx)
+    y = np.asarray(y16, dtype=np.float16).astype(np.float64)
+    if rows is not None:
+        y = y[rows]
+    assert y.shape == r.shape
+    rmax = np.abs(r).max() if r.size else 0.0
+    if rmax == 0.0:
+        assert np.all(y == 0), f"{label}: expected zeros"
+        return 0.0
+    err = np.abs(y - r).max() / rmax
+    assert err <= REL_TOL, f"{label}: norm-wise error {err:.3e} > {REL_TOL}"
+    m = len(F) + len(A) + 80
+    gamma = m * U24 / (1 - m * U24)
+    S = abs_sum(x, F, A, full, approx)
+    bound = gamma * S + 0.5 * ulp16(y) + 2.0 ** -25
+    bad = np.abs(y - r) > bound
+    assert not bad.any(), (f"{label}: {bad.sum()} elements outside the fp32 bound, "
+                           f"first at {np.argmax(bad)}")
+    return float(err)
+
+
+def sample_groups(R: int, n_groups: int, seed: int) -> np.ndarray:
+    """Stored rows of a few whole 128-row groups: the first, the last, both
+    sides of every 512-row tile boundary near the start, and random ones."""
+    G = R // GROUP
+    rs = np.random.default_rng(seed)
+    pick = {0, G - 1, min(3, G - 1), min(4, G - 1)}
+    pick |= set(rs.choice(G, size=min(n_groups, G), replace=False).tolist())
+    g = np.array(sorted(pick))
+    return (g[:, None] * GROUP + np.arange(GROUP)[None, :]).ravel()

@@ -1,0 +1,177 @@
+"""spax_layer_step and the host-resident mode on the GPU."""
+import numpy as np
+import pytest
+
+import oracle as O
+import workloads as WL
+from tests.spax_testlib import check_product, log, sample_groups, to_dev, to_host
+
+pytestmark = pytest.mark.gpu
+
+
+def _spax():
+    import activation_sparse_decode_token_amd as spax
+    return spax
+
+
+class LayerWeights:
+    """Column-major fp16 weights of one layer, drawn on the host."""
+
+    def __init__(self, cfg, layer, hidden, inter, std):
+        self.hidden, self.inter = hidden, inter
+        self.q = WL.weights_fp16(cfg, layer, "q", hidden, hidden, std)
+        self.k = WL.weights_fp16(cfg, layer, "k", hidden, hidden, std)
+        self.v = WL.weights_fp16(cfg, layer, "v", hidden, hidden, std)
+        self.o = WL.weights_fp16(cfg, layer, "o", hidden, hidden, std)
+        self.gate = WL.weights_fp16(cfg, layer, "gate", inter, hidden, std)
+        self.up = WL.weights_fp16(cfg, layer, "up", inter, hidden, std)
+        self.down = WL.weights_fp16(cfg, layer, "down", hidden, inter, std)
+
+
+def _build_layer(w: LayerWeights, ff, af, residency, ks):
+    import torch
+    spax = _spax()
+    from activation_sparse_decode_token_amd.layouts import build_matrix, glu_interleave, stack_rows
+    F = {"fp16": 1, "int4": 2}[ff]
+    A = {"int4": 2, "int2": 3}[af]
+    qkv = build_matrix(stack_rows([to_dev(w.q), to_dev(w.k), to_dev(w.v)]), F, A,
+                       residency=residency)
+    o = build_matrix(to_dev(w.o), F, A, residency=residency)
+    gu = build_matrix(glu_interleave(to_dev(w.gate), to_dev(w.up)), F, A,
+                      layout=spax.LAYOUT_GLU_INTERLEAVED, residency=residency)
+    dn = build_matrix(to_dev(w.down), F, A, residency=residency)
+    torch.cuda.synchronize()
+    kf = [ks[g][0] for g in ("qkv", "o", "ffn", "down")]
+    ka = [ks[g][1] for g in ("qkv", "o", "ffn", "down")]
+    return spax.Layer.make([qkv, o, gu, dn], kf, ka)
+
+
+def _io(L, h, z, x):
+    import torch
+    spax = _spax()
+    dev = torch.device("cuda:0")
+    G = L.group
+    out = {
+        "qkv": torch.empty(G[0].rows, dtype=torch.float16, device=dev),
+        "o": torch.empty(G[1].rows, dtype=torch.float16, device=dev),
+        "g": torch.empty(G[2].rows // 2, dtype=torch.float16, device=dev),
+        "u": torch.empty(G[2].rows // 2, dtype=torch.float16, device=dev),
+        "a": torch.empty(G[2].rows // 2, dtype=torch.float16, device=dev),
+        "down": torch.empty(G[3].rows, dtype=torch.float16, device=dev),
+        "F": [torch.empty(max(1, L.k_full[g]), dtype=torch.int32, device=dev) for g in range(4)],
+        "A": [torch.empty(max(1, L.k_approx[g]), dtype=torch.int32, device=dev) for g in range(4)],
+    }
+    io = spax.LayerIO.make(h=to_dev(h), z=to_dev(z), x=to_dev(x), qkv=out["qkv"], o=out["o"],
+                           g=out["g"], u=out["u"], a=out["a"], down=out["down"],
+                           full_idx=out["F"], approx_idx=out["A"])
+    return io, out
+
+
+def _run_layer(L, h, z, x, ws=None, copy_stream=None):
+    import torch
+    spax = _spax()
+    if ws is None:
+        ws = torch.zeros(spax.layer_workspace_bytes(L), dtype=torch.uint8, device="cuda:0")
+    io, out = _io(L, h, z, x)
+    spax.layer_step(L, io, ws, copy_stream=copy_stream)
+    torch.cuda.synchronize()
+    res = {k: to_host(out[k]) for k in ("qkv", "o", "g", "u", "a", "down")}
+    res["lists"] = [(to_host(out["F"][g])[:L.k_full[g]], to_host(out["A"][g])[:L.k_approx[g]])
+                    for g in range(4)]
+    return res, ws
+
+
+def _check_layer(res, w: LayerWeights, ks, h, z, x, ff, af, label, rows_per=None):
+    """Stage-wise parity: each group is compared with the oracle fed the same
+    inputs the GPU group saw (down is fed the GPU's a)."""
+    def stores(Wt, rows=None):
+        sub = Wt if rows is None else np.ascontiguousarray(Wt[:, rows])
+        return O.ColumnStore(ff, sub), O.ColumnStore(af, sub)
+
+    L0 = O.plan_tiers(h, *ks["qkv"])
+    assert all(np.array_equal(a, b) for a, b in zip(res["lists"][0], L0)), f"{label}: qkv lists"
+    Wqkv = np.concatenate([w.q, w.k, w.v], axis=1)
+    rows = sample_groups(Wqkv.shape[1], 8, 1) if rows_per else None
+    check_product(res["qkv"], h, *L0, *stores(Wqkv, rows), f"{label} qkv", rows=rows)
+
+    L1 = O.plan_tiers(z, *ks["o"])
+    assert all(np.array_equal(a, b) for a, b in zip(res["lists"][1], L1)), f"{label}: o lists"
+    rows = sample_groups(w.o.shape[1], 8, 2) if rows_per else None
+    check_product(res["o"], z, *L1, *stores(w.o, rows), f"{label} o", rows=rows)
+
+    L2 = O.plan_tiers(x, *ks["ffn"])
+    assert all(np.array_equal(a, b) for a, b in zip(res["lists"][2], L2)), f"{label}: ffn lists"
+    rows = sample_groups(w.inter, 8, 3) if rows_per else None
+    check_product(res["g"], x, *L2, *stores(w.gate, rows), f"{label} gate", rows=rows)
+    check_product(res["u"], x, *L2, *stores(w.up, rows), f"{label} up", rows=rows)
+    # a is formed from the GPU's own fp16 g and u
+    a_want = O.swiglu_fp16(res["g"], res["u"]).astype(np.float64)
+    a_got = res["a"].astype(np.float64)
+    scale = np.abs(a_want).max()
+    assert np.abs(a_got - a_want).max() <= 2e-3 * scale, f"{label}: a"
+    assert np.all(np.abs(a_got - a_want) <= 2.0 ** -10 * np.abs(a_want) + 2.0 ** -24), \
+        f"{label}: a off by more than one fp16 ulp"
+
+    L3 = O.plan_tiers(res["a"], *ks["down"])
+    assert all(np.array_equal(a, b) for a, b in zip(res["lists"][3], L3)), f"{label}: down lists"
+    rows = sample_groups(w.hidden, 8, 4) if rows_per else None
+    check_product(res["down"], res["a"], *L3, *stores(w.down, rows), f"{label} down", rows=rows)
+
+
+def _ks(hidden, inter, split):
+    return {"qkv": WL.tier_counts(hidden, split), "o": WL.tier_counts(hidden, split),
+            "ffn": WL.tier_counts(hidden, split), "down": WL.tier_counts(inter, split)}
+
+
+@pytest.mark.parametrize("ff,af", [("fp16", "int4"), ("int4", "int2"), ("fp16", "int2")])
+def test_layer_small(ff, af):
+    hidden, inter = 512, 1408          # ragged tiles: 1408 = 2*512 + 384; gate/up 2816 rows
+    w = LayerWeights(810, 0, hidden, inter, 0.02)
+    ks = _ks(hidden, inter, WL.TierSplit(40, 30, 30))
+    L = _build_layer(w, ff, af, 0, ks)
+    for tok in range(3):
+        h = WL.laplace_fp16(810, 0, "h", tok, hidden)
+        z = WL.laplace_fp16(810, 0, "z", tok, hidden)
+        x = WL.laplace_fp16(810, 0, "x", tok, hidden)
+        res, _ = _run_layer(L, h, z, x)
+        _check_layer(res, w, ks, h, z, x, ff, af, f"small {ff}/{af} token {tok}")
+    log(f"layer small {ff}/{af} ok")
+
+
+def test_layer_7b_shapes():
+    w = LayerWeights(4, 0, 4096, 11008, 0.02)
+    ks = _ks(4096, 11008, WL.CONFIGS[4].splits[0])
+    L = _build_layer(w, "fp16", "int4", 0, ks)
+    for tok in (0, 1):
+        h = WL.laplace_fp16(4, 0, "h", tok, 4096)
+        z = WL.laplace_fp16(4, 0, "z", tok, 4096)
+        x = WL.laplace_fp16(4, 0, "x", tok, 4096)
+        res, _ = _run_layer(L, h, z, x)
+        _check_layer(res, w, ks, h, z, x, "fp16", "int4", f"7B layer token {tok}", rows_per=True)
+        log(f"7B layer token {tok} ok")
+
+
+@pytest.mark.parametrize("ff,af", [("fp16", "int4"), ("int4", "int2")])
+def test_host_pinned_bitwise_equals_device(ff, af):
+    import torch
+    hidden, inter = 1024, 2816
+    w = LayerWeights(811, 0, hidden, inter, 0.02)
+    ks = _ks(hidden, inter, WL.TierSplit(50, 25, 25))
+    Ld = _build_layer(w, ff, af, 0, ks)
+    Lh = _build_layer(w, ff, af, 1, ks)
+    cs = torch.cuda.Stream()
+    ws_d = ws_h = None
+    for tok in range(3):
+        h = WL.laplace_fp16(811, 0, "h", tok, hidden)
+        z = WL.laplace_fp16(811, 0, "z", tok, hidden)
+        x = WL.laplace_fp16(811, 0, "x", tok, hidden)
+        rd, ws_d = _run_layer(Ld, h, z, x, ws_d)
+        rh, ws_h = _run_layer(Lh, h, z, x, ws_h, copy_stream=cs)
+        for k in ("qkv", "o", "g", "u", "a", "down"):
+            assert np.array_equal(rd[k].view(np.uint16), rh[k].view(np.uint16)), (k, tok)
+        for g in range(4):
+            for i in range(2):
+                assert np.array_equal(rd["lists"][g][i], rh["lists"][g][i])
+        if tok == 0:
+            _check_layer(rh, w, ks, h, z, x, ff, af, f"host {ff}/{af}")
+    log(f"host-pinned {ff}/{af} == device bitwise")
