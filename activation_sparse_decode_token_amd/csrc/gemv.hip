@@ -135,10 +135,12 @@ __device__ __forceinline__ void run_tier(float (&acc)[8], float& corr,
                                          const uint16_t* __restrict__ scales, int64_t sstride,
                                          const int32_t* __restrict__ idx,
                                          const uint16_t* __restrict__ x, int p_lo, int p_hi,
-                                         int row0, int lane) {
+                                         int row0, int lane, int ld_lane) {
+  // lane: this lane's slot in the 64-wide batches of indices / activations;
+  // ld_lane: the lane whose rows it loads (lane 0 past the last row)
   using T = Tier<FMT>;
   constexpr int U = T::U;
-  const int sc_off = (row0 >> 7) + (lane >> 4);
+  const int sc_off = (row0 >> 7) + (ld_lane >> 4);
   int nxt = 0;
   if (p_lo < p_hi && lane < p_hi - p_lo) nxt = idx[p_lo + lane];
   for (int kb = p_lo; kb < p_hi; kb += 64) {
@@ -157,7 +159,7 @@ __device__ __forceinline__ void run_tier(float (&acc)[8], float& corr,
       for (int u = 0; u < U; ++u) {
         const int col = STAGED ? (kb + c + u) : __builtin_amdgcn_readlane(my_idx, c + u);
         const uint8_t* cp = base + (int64_t)col * stride;
-        v[u] = T::load(cp, row0, lane);
+        v[u] = T::load(cp, row0, ld_lane);
         if constexpr (FMT != kFp16)
           sv[u] = scales[(int64_t)col * sstride + sc_off];
         else
@@ -172,7 +174,7 @@ __device__ __forceinline__ void run_tier(float (&acc)[8], float& corr,
     for (; c < cnt; ++c) {
       const int col = STAGED ? (kb + c) : __builtin_amdgcn_readlane(my_idx, c);
       const uint8_t* cp = base + (int64_t)col * stride;
-      const typename T::V v = T::load(cp, row0, lane);
+      const typename T::V v = T::load(cp, row0, ld_lane);
       uint32_t sv = 0u;
       if constexpr (FMT != kFp16) sv = scales[(int64_t)col * sstride + sc_off];
       const float xs = h2f((uint32_t)__builtin_amdgcn_readlane((int)my_xb, c));
@@ -247,7 +249,7 @@ __global__ __launch_bounds__(kGemvThreads) void gemv_kernel(GemvArgs a) {
     const int len = hi - lo;
     const int wlo = lo + (len * wave) / kWaves, whi = lo + (len * (wave + 1)) / kWaves;
     run_tier<FF, STAGED>(acc, corr, a.full_base, a.full_stride, a.full_scales, a.full_sstride,
-                         a.full_idx, a.x, wlo, whi, row0, ld_lane);
+                         a.full_idx, a.x, wlo, whi, row0, lane, ld_lane);
   }
   if constexpr (AF != kNone) {
     const int lo = (int)(max<int64_t>(e0, a.k_full) - a.k_full);
@@ -255,7 +257,7 @@ __global__ __launch_bounds__(kGemvThreads) void gemv_kernel(GemvArgs a) {
     const int len = hi - lo;
     const int wlo = lo + (len * wave) / kWaves, whi = lo + (len * (wave + 1)) / kWaves;
     run_tier<AF, STAGED>(acc, corr, a.approx_base, a.approx_stride, a.approx_scales,
-                         a.approx_sstride, a.approx_idx, a.x, wlo, whi, row0, ld_lane);
+                         a.approx_sstride, a.approx_idx, a.x, wlo, whi, row0, lane, ld_lane);
   }
   if constexpr (FF == kInt4 || AF != kNone) {
 #pragma unroll

@@ -65,6 +65,10 @@ CASES = [
     (3072, 2000, "fp16", "int4", 0, 2000),    # all approx
     (3072, 2000, "fp16", "int2", 0, 0),       # all skipped -> zeros
     (512, 7, "fp16", "int4", 3, 4),
+    # more than 16 columns per wave on a ragged last tile (one split / capped splits)
+    (1152, 777, "int4", "none", 100, 0),
+    (1152, 777, "fp16", "int2", 0, 400),
+    (640, 6000, "fp16", "none", 6000, 0),
 ]
 
 
