@@ -74,11 +74,19 @@ struct ProductPlan {
   int64_t wf = 0, wa = 0;
 };
 
-// Number of column splits: about two workgroups per compute unit, at least
-// 16 KB of weights per workgroup, a multiple of 8 (one XCD per split group).
+#ifndef SPAX_TARGET_BLOCKS
+#define SPAX_TARGET_BLOCKS 256
+#endif
+#ifndef SPAX_MIN_SPLIT_BYTES
+#define SPAX_MIN_SPLIT_BYTES 32768
+#endif
+
+// Number of column splits: about one 8-wave workgroup per compute unit, at
+// least SPAX_MIN_SPLIT_BYTES of weights per workgroup, a multiple of 8 (one
+// XCD per split group).
 ProductPlan plan_product(const spax_matrix* W, int32_t kf, int32_t ka) {
-  constexpr int64_t kTargetBlocks = 512;
-  constexpr int64_t kMinSplitBytes = 16384;
+  constexpr int64_t kTargetBlocks = SPAX_TARGET_BLOCKS;
+  constexpr int64_t kMinSplitBytes = SPAX_MIN_SPLIT_BYTES;
   ProductPlan p;
   p.tiles = (W->rows + kTileRows - 1) / kTileRows;
   p.wf = tile_bytes(W->full_fmt);
@@ -92,6 +100,30 @@ ProductPlan plan_product(const spax_matrix* W, int32_t kf, int32_t ka) {
   if (s >= 8) s = s / 8 * 8;
   p.splits = (int32_t)std::max<int64_t>(1, s);
   return p;
+}
+
+// Largest number of list positions one split holds.
+int64_t max_piece(const ProductPlan& p, int32_t kf, int32_t ka) {
+  int64_t m = 0;
+  for (int s = 0; s < p.splits; ++s)
+    m = std::max(m, split_start(s + 1, p.splits, kf, ka, p.wf, p.wa) -
+                        split_start(s, p.splits, kf, ka, p.wf, p.wa));
+  return m;
+}
+
+// Plan of the fused rank + product: more splits while a piece would not fit
+// the workgroup's LDS list. Returns false when no split count fits.
+bool plan_fused(const spax_matrix* W, int32_t kf, int32_t ka, ProductPlan* out) {
+  if (W->cols > kRankMaxN || W->residency != SPAX_RES_DEVICE) return false;
+  ProductPlan p = plan_product(W, kf, ka);
+  while (max_piece(p, kf, ka) > kListCap) {
+    if (p.splits >= kMaxSplits || p.splits >= (int64_t)kf + ka) return false;
+    int64_t s = std::min<int64_t>({(int64_t)p.splits * 2, kMaxSplits, (int64_t)kf + ka});
+    if (s >= 8) s = s / 8 * 8;
+    p.splits = (int32_t)s;
+  }
+  *out = p;
+  return true;
 }
 
 size_t counters_bytes(const spax_matrix* W) {
@@ -141,10 +173,14 @@ hipError_t events_for_current_device(EventSet** out) {
   return hipSuccess;
 }
 
+// Enqueue one tiered product. mode kListRank ranks x inside the product and
+// writes the lists to out_f / out_a; the other modes read fidx / aidx.
 int run_product(const spax_matrix* W, const uint16_t* x, const int32_t* fidx, int32_t kf,
                 const int32_t* aidx, int32_t ka, int32_t epi, uint16_t* y, uint16_t* ga,
-                uint16_t* gg, uint16_t* gu, void* ws, hipStream_t s, hipStream_t cs) {
-  const ProductPlan p = plan_product(W, kf, ka);
+                uint16_t* gg, uint16_t* gu, void* ws, hipStream_t s, hipStream_t cs,
+                const ProductPlan* fused = nullptr, int32_t* out_f = nullptr,
+                int32_t* out_a = nullptr) {
+  const ProductPlan p = fused ? *fused : plan_product(W, kf, ka);
   uint8_t* wsb = static_cast<uint8_t*>(ws);
   GemvArgs a{};
   a.rows = W->rows;
@@ -152,11 +188,14 @@ int run_product(const spax_matrix* W, const uint16_t* x, const int32_t* fidx, in
   a.n_splits = p.splits;
   a.k_full = kf;
   a.k_approx = ka;
+  a.n = W->cols;
   a.w_full = p.wf;
   a.w_approx = p.wa;
   a.x = x;
   a.full_idx = fidx;
   a.approx_idx = aidx;
+  a.out_full_idx = out_f;
+  a.out_approx_idx = out_a;
   a.counters = reinterpret_cast<uint32_t*>(wsb);
   a.partials = reinterpret_cast<float*>(wsb + counters_bytes(W));
   a.y = y;
@@ -177,7 +216,8 @@ int run_product(const spax_matrix* W, const uint16_t* x, const int32_t* fidx, in
     a.approx_scales = W->approx_scales;
     a.split_lo = 0;
     a.splits_here = p.splits;
-    const hipError_t e = launch_gemv(a, W->full_fmt, W->approx_fmt, false, epi, s);
+    const hipError_t e =
+        launch_gemv(a, W->full_fmt, W->approx_fmt, fused ? kListRank : kListGlobal, epi, s);
     return e == hipSuccess ? SPAX_OK : hip_fail(e);
   }
 
@@ -233,7 +273,7 @@ int run_product(const spax_matrix* W, const uint16_t* x, const int32_t* fidx, in
     if ((e = hipStreamWaitEvent(s, ev->chunk[k], 0)) != hipSuccess) return hip_fail(e);
     a.split_lo = s_lo;
     a.splits_here = s_hi - s_lo;
-    if ((e = launch_gemv(a, W->full_fmt, W->approx_fmt, true, epi, s)) != hipSuccess)
+    if ((e = launch_gemv(a, W->full_fmt, W->approx_fmt, kListStaged, epi, s)) != hipSuccess)
       return hip_fail(e);
   }
   return SPAX_OK;
@@ -344,18 +384,25 @@ int spax_layer_step(const spax_layer* L, const spax_layer_io* io, void* ws, size
   }
   for (int g = 0; g < 4; ++g) {
     if (G[g].cols <= 0) continue;
-    hipError_t e = launch_plan(inputs[g], G[g].cols, L->k_full[g], L->k_approx[g],
-                               io->full_idx[g], io->approx_idx[g], compute_stream);
-    if (e != hipSuccess) return hip_fail(e);
+    const int32_t kf = L->k_full[g], ka = L->k_approx[g];
+    uint16_t* y = g == SPAX_GROUP_GATE_UP ? nullptr : outputs[g];
+    uint16_t* ga = g == SPAX_GROUP_GATE_UP ? io->a : nullptr;
+    uint16_t* gg = g == SPAX_GROUP_GATE_UP ? io->g : nullptr;
+    uint16_t* gu = g == SPAX_GROUP_GATE_UP ? io->u : nullptr;
+    const int32_t epi = g == SPAX_GROUP_GATE_UP ? kEpiGlu : kEpiPlain;
+    ProductPlan fp;
     int st;
-    if (g == SPAX_GROUP_GATE_UP)
-      st = run_product(&G[g], inputs[g], io->full_idx[g], L->k_full[g], io->approx_idx[g],
-                       L->k_approx[g], kEpiGlu, nullptr, io->a, io->g, io->u, ws,
-                       compute_stream, copy_stream);
-    else
-      st = run_product(&G[g], inputs[g], io->full_idx[g], L->k_full[g], io->approx_idx[g],
-                       L->k_approx[g], kEpiPlain, outputs[g], nullptr, nullptr, nullptr, ws,
-                       compute_stream, copy_stream);
+    if (plan_fused(&G[g], kf, ka, &fp)) {
+      // device-resident weights: selection fused into the product
+      st = run_product(&G[g], inputs[g], nullptr, kf, nullptr, ka, epi, y, ga, gg, gu, ws,
+                       compute_stream, copy_stream, &fp, io->full_idx[g], io->approx_idx[g]);
+    } else {
+      hipError_t e = launch_plan(inputs[g], G[g].cols, kf, ka, io->full_idx[g],
+                                 io->approx_idx[g], compute_stream);
+      if (e != hipSuccess) return hip_fail(e);
+      st = run_product(&G[g], inputs[g], io->full_idx[g], kf, io->approx_idx[g], ka, epi, y, ga,
+                       gg, gu, ws, compute_stream, copy_stream);
+    }
     if (st) return st;
   }
   return SPAX_OK;

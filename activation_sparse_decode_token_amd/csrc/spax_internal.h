@@ -10,15 +10,25 @@ namespace spax {
 // Rows of one workgroup tile of the tiered product: 64 lanes x 8 rows.
 constexpr int kTileRows = 512;
 // Waves per workgroup of the tiered product.
-constexpr int kWaves = 4;
+constexpr int kWaves = 8;
 constexpr int kGemvThreads = kWaves * 64;
 // Upper bound on column splits of one product (size of the fp32 partials).
 constexpr int kMaxSplits = 64;
 // Rows per quantisation group.
 constexpr int kGroup = 128;
+// List positions one workgroup of the fused rank + product keeps in LDS.
+constexpr int kListCap = 2048;
+// Largest input length the fused rank + product handles (64 per thread).
+constexpr int kRankMaxN = kGemvThreads * 64;
 
 enum Fmt : int32_t { kNone = 0, kFp16 = 1, kInt4 = 2, kInt2 = 3 };
 enum Epi : int32_t { kEpiPlain = 0, kEpiGlu = 1 };
+// Where the tiered product takes its tier lists from.
+enum ListMode : int32_t {
+  kListGlobal = 0,  // index lists in device memory
+  kListStaged = 1,  // selected columns staged in list order
+  kListRank = 2,    // every workgroup ranks x itself (fused selection)
+};
 
 // Arguments of one launch of the tiered product.
 struct GemvArgs {
@@ -28,6 +38,7 @@ struct GemvArgs {
   int32_t split_lo;              // first split handled by this launch
   int32_t splits_here;           // splits handled by this launch
   int32_t k_full, k_approx;
+  int32_t n;                     // input length (cols)
   // Per column-tile byte weights used to balance the splits.
   int64_t w_full, w_approx;
   // Full tier: fp16 columns or int4 codes; column c at full_base + c * full_stride.
@@ -43,6 +54,8 @@ struct GemvArgs {
   const uint16_t* x;
   const int32_t* full_idx;
   const int32_t* approx_idx;
+  int32_t* out_full_idx;         // kListRank: lists written by tile-0 groups
+  int32_t* out_approx_idx;
   float* partials;               // [n_splits][rows]
   uint32_t* counters;            // [n_tiles]
   uint16_t* y;                   // plain: fp16[rows]
@@ -71,7 +84,7 @@ hipError_t launch_plan(const uint16_t* x, int32_t n, int32_t k_full, int32_t k_a
                        int32_t* full_idx, int32_t* approx_idx, hipStream_t s);
 
 hipError_t launch_gemv(const GemvArgs& a, int32_t full_fmt, int32_t approx_fmt,
-                       bool staged, int32_t epi, hipStream_t s);
+                       int32_t mode, int32_t epi, hipStream_t s);
 
 hipError_t launch_copy(const CopyArgs& a, hipStream_t s);
 

@@ -13,6 +13,7 @@ GROUP = 128
 # 2e-3, norm-wise (|y - r|_inf / |r|_inf).
 REL_TOL = 2e-3
 U24 = 2.0 ** -24
+FP16_MIN_NORMAL = 2.0 ** -14
 
 
 def log(msg: str) -> None:
@@ -93,7 +94,11 @@ def check_product(y16: np.ndarray, x, F, A, full, approx, label: str = "",
         assert np.all(y == 0), f"{label}: expected zeros"
         return 0.0
     err = np.abs(y - r).max() / rmax
-    assert err <= REL_TOL, f"{label}: norm-wise error {err:.3e} > {REL_TOL}"
+    # Below the smallest normal fp16 (2^-14) the output grid is an absolute
+    # 2^-24, so a relative gate cannot hold for any rounding; there the
+    # elementwise bound below is the gate.
+    if rmax >= FP16_MIN_NORMAL:
+        assert err <= REL_TOL, f"{label}: norm-wise error {err:.3e} > {REL_TOL}"
     m = len(F) + len(A) + 80
     gamma = m * U24 / (1 - m * U24)
     S = abs_sum(x, F, A, full, approx)
