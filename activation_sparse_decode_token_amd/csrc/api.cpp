@@ -71,7 +71,6 @@ int validate_matrix(const spax_matrix* W) {
 struct ProductPlan {
   int32_t tiles = 1;
   int32_t splits = 1;
-  int64_t wf = 0, wa = 0;
 };
 
 #ifndef SPAX_TARGET_BLOCKS
@@ -89,9 +88,7 @@ ProductPlan plan_product(const spax_matrix* W, int32_t kf, int32_t ka) {
   constexpr int64_t kMinSplitBytes = SPAX_MIN_SPLIT_BYTES;
   ProductPlan p;
   p.tiles = (W->rows + kTileRows - 1) / kTileRows;
-  p.wf = tile_bytes(W->full_fmt);
-  p.wa = tile_bytes(W->approx_fmt);
-  const int64_t total = kf * p.wf + ka * p.wa;
+  const int64_t total = kf * tile_bytes(W->full_fmt) + ka * tile_bytes(W->approx_fmt);
   if (total == 0) return p;
   int64_t s = (kTargetBlocks + p.tiles - 1) / p.tiles;
   s = std::min<int64_t>(s, std::max<int64_t>(1, total / kMinSplitBytes));
@@ -106,8 +103,8 @@ ProductPlan plan_product(const spax_matrix* W, int32_t kf, int32_t ka) {
 int64_t max_piece(const ProductPlan& p, int32_t kf, int32_t ka) {
   int64_t m = 0;
   for (int s = 0; s < p.splits; ++s)
-    m = std::max(m, split_start(s + 1, p.splits, kf, ka, p.wf, p.wa) -
-                        split_start(s, p.splits, kf, ka, p.wf, p.wa));
+    m = std::max<int64_t>(m, split_pos(s + 1, p.splits, kf) - split_pos(s, p.splits, kf) +
+                                 split_pos(s + 1, p.splits, ka) - split_pos(s, p.splits, ka));
   return m;
 }
 
@@ -189,8 +186,6 @@ int run_product(const spax_matrix* W, const uint16_t* x, const int32_t* fidx, in
   a.k_full = kf;
   a.k_approx = ka;
   a.n = W->cols;
-  a.w_full = p.wf;
-  a.w_approx = p.wa;
   a.x = x;
   a.full_idx = fidx;
   a.approx_idx = aidx;
@@ -266,8 +261,10 @@ int run_product(const spax_matrix* W, const uint16_t* x, const int32_t* fidx, in
   for (int k = 0; k < chunks; ++k) {
     const int s_lo = (int)((int64_t)p.splits * k / chunks);
     const int s_hi = (int)((int64_t)p.splits * (k + 1) / chunks);
-    c.e_lo = split_start(s_lo, p.splits, kf, ka, p.wf, p.wa);
-    c.e_hi = split_start(s_hi, p.splits, kf, ka, p.wf, p.wa);
+    c.f_lo = split_pos(s_lo, p.splits, kf);
+    c.f_hi = split_pos(s_hi, p.splits, kf);
+    c.a_lo = split_pos(s_lo, p.splits, ka);
+    c.a_hi = split_pos(s_hi, p.splits, ka);
     if ((e = launch_copy(c, cs)) != hipSuccess) return hip_fail(e);
     if ((e = hipEventRecord(ev->chunk[k], cs)) != hipSuccess) return hip_fail(e);
     if ((e = hipStreamWaitEvent(s, ev->chunk[k], 0)) != hipSuccess) return hip_fail(e);

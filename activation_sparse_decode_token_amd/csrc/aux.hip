@@ -42,15 +42,18 @@ __global__ __launch_bounds__(kCopyThreads) void copy_kernel(CopyArgs a) {
   const int lane = threadIdx.x & 63;
   const int64_t gw = (int64_t)blockIdx.x * (kCopyThreads / 64) + (threadIdx.x >> 6);
   const int64_t nw = (int64_t)gridDim.x * (kCopyThreads / 64);
-  for (int64_t e = a.e_lo + gw; e < a.e_hi; e += nw) {
-    if (e < a.k_full) {
-      const int64_t col = a.full_idx[e];
-      copy_bytes(a.full_dst + e * a.full_bytes, a.full_src + col * a.full_bytes, a.full_bytes,
+  const int64_t nf = a.f_hi - a.f_lo;
+  const int64_t total = nf + (a.a_hi - a.a_lo);
+  for (int64_t e = gw; e < total; e += nw) {
+    if (e < nf) {
+      const int64_t p = a.f_lo + e;
+      const int64_t col = a.full_idx[p];
+      copy_bytes(a.full_dst + p * a.full_bytes, a.full_src + col * a.full_bytes, a.full_bytes,
                  lane);
       for (int i = lane; i < a.fscale_n; i += 64)
-        a.fscale_dst[e * a.fscale_n + i] = a.fscale_src[col * a.fscale_n + i];
+        a.fscale_dst[p * a.fscale_n + i] = a.fscale_src[col * a.fscale_n + i];
     } else {
-      const int64_t p = e - a.k_full;
+      const int64_t p = a.a_lo + (e - nf);
       const int64_t col = a.approx_idx[p];
       copy_bytes(a.approx_dst + p * a.approx_bytes, a.approx_src + col * a.approx_bytes,
                  a.approx_bytes, lane);
@@ -127,7 +130,7 @@ __global__ void clear_kernel(uint32_t* __restrict__ p, int64_t n) {
 }  // namespace
 
 hipError_t launch_copy(const CopyArgs& a, hipStream_t s) {
-  const int64_t cols = a.e_hi - a.e_lo;
+  const int64_t cols = (int64_t)(a.f_hi - a.f_lo) + (a.a_hi - a.a_lo);
   if (cols <= 0) return hipSuccess;
   const int64_t waves = (kCopyThreads / 64);
   int64_t blocks = (cols + waves - 1) / waves;

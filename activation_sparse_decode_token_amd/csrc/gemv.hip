@@ -72,7 +72,7 @@ struct Tier<kFp16> {
   static __device__ __forceinline__ V load(const uint8_t* col, int row0, int lane) {
     return *reinterpret_cast<const uint4*>(col + 2 * (size_t)(row0 + 8 * lane));
   }
-  static __device__ __forceinline__ void fma(float (&acc)[8], float&, V v, float xs, uint32_t) {
+  static __device__ __forceinline__ void fma(float (&acc)[8], float&, V v, float xs, float) {
     acc[0] = fmaf(h2f(v.x & 0xFFFFu), xs, acc[0]);
     acc[1] = fmaf(h2f(v.x >> 16), xs, acc[1]);
     acc[2] = fmaf(h2f(v.y & 0xFFFFu), xs, acc[2]);
@@ -94,8 +94,8 @@ struct Tier<kInt4> {
   // Rows 2b and 2b+1 sit in the low and high nibble of byte b, as
   // two's-complement q; flipping each nibble's sign bit gives u = q + 8.
   static __device__ __forceinline__ void fma(float (&acc)[8], float& corr, V v, float xs,
-                                             uint32_t scale) {
-    const float c = xs * h2f(scale);  // exact: product of two fp16 values
+                                             float scale) {
+    const float c = xs * scale;  // exact: product of two fp16 values
     corr = fmaf(8.0f, c, corr);
     v ^= 0x88888888u;
     const uint32_t lo = v & 0x0F0F0F0Fu;
@@ -121,8 +121,8 @@ struct Tier<kInt2> {
   // Row 4b + r sits in bits 2r..2r+1 of byte b; masking leaves u * 4^r, so
   // the factor is scaled by 4^-r (exact).
   static __device__ __forceinline__ void fma(float (&acc)[8], float& corr, V v, float xs,
-                                             uint32_t scale) {
-    const float c = xs * h2f(scale);
+                                             float scale) {
+    const float c = xs * scale;
     corr = fmaf(1.5f, c, corr);
     const uint32_t m0 = v & 0x0303u, m1 = v & 0x0C0Cu, m2 = v & 0x3030u, m3 = v & 0xC0C0u;
     const float c1 = c * 0.25f, c2 = c * 0.0625f, c3 = c * 0.015625f;
@@ -137,75 +137,152 @@ struct Tier<kInt2> {
   }
 };
 
-// Stream list positions [p_lo, p_hi) of one tier for this wave's rows.
-//   kListGlobal: idx = global index list, x = global fp16 activations;
-//   kListStaged: idx = global index list (for x only), column = position;
-//   kListRank:   lidx / lx = this workgroup's list piece in LDS (index and
-//                fp32 activation per position).
+// Per-lane metadata of one 64-column batch of a tier: lane l holds the
+// column index and activation of batch position l and, for code tiers, the
+// tile's four group scales of that column (groups 0,1 in sc01, 2,3 in sc23).
+struct Meta {
+  int idx;
+  uint32_t xb;  // fp16 bits (global modes) or fp32 bits (rank mode)
+  uint32_t sc01, sc23;
+};
+
 template <int FMT, int MODE>
-__device__ __forceinline__ void run_tier(float (&acc)[8], float& corr,
-                                         const uint8_t* __restrict__ base, int64_t stride,
-                                         const uint16_t* __restrict__ scales, int64_t sstride,
-                                         const int32_t* __restrict__ idx,
-                                         const uint16_t* __restrict__ x, const int32_t* lidx,
-                                         const float* lx, int p_lo, int p_hi, int row0, int lane,
-                                         int ld_lane) {
-  // lane: this lane's slot in the 64-wide batches of indices / activations;
-  // ld_lane: the lane whose rows it loads (lane 0 past the last row)
-  using T = Tier<FMT>;
-  constexpr int U = T::U;
-  const int sc_off = (row0 >> 7) + (ld_lane >> 4);
-  int nxt = 0;
-  if constexpr (MODE != kListRank) {
-    if (p_lo < p_hi && lane < p_hi - p_lo) nxt = idx[p_lo + lane];
+__device__ __forceinline__ Meta load_meta(const uint16_t* __restrict__ scales, int64_t sstride,
+                                          const int32_t* __restrict__ idx,
+                                          const uint16_t* __restrict__ x, const int32_t* lidx,
+                                          const float* lx, int p, int cnt, int row0, int ngrp,
+                                          int lane) {
+  Meta m{0, 0u, 0u, 0u};
+  if (cnt <= 0) return m;
+  // lanes past the batch repeat its first position (in range, never used)
+  const int q = p + (lane < cnt ? lane : 0);
+  if constexpr (MODE == kListRank) {
+    m.idx = lidx[q];
+    m.xb = __float_as_uint(lx[q]);
+  } else {
+    m.idx = idx[q];
+    m.xb = x[m.idx];
   }
-  for (int kb = p_lo; kb < p_hi; kb += 64) {
-    const int cnt = min(64, p_hi - kb);
-    int my_idx;
-    uint32_t my_xb;  // fp16 bits (global modes) or fp32 bits (rank mode)
-    if constexpr (MODE == kListRank) {
-      const int q = lane < cnt ? kb + lane : kb;
-      my_idx = lidx[q];
-      my_xb = __float_as_uint(lx[q]);
-    } else {
-      my_idx = nxt;
-      // prefetch the next batch of indices before streaming this one
-      if (kb + 64 < p_hi && lane < p_hi - kb - 64) nxt = idx[kb + 64 + lane];
-      // raw fp16 bits; converted where used so that this gather overlaps the
-      // weight loads (lanes >= cnt hold an in-range stale index, never read)
-      my_xb = x[my_idx];
-    }
-    auto xval = [&](int c) -> float {
-      const uint32_t b = (uint32_t)__builtin_amdgcn_readlane((int)my_xb, c);
-      if constexpr (MODE == kListRank) return __uint_as_float(b);
-      else return h2f(b);
-    };
-    int c = 0;
-    for (; c + U <= cnt; c += U) {
-      typename T::V v[U];
-      uint32_t sv[U];
+  if constexpr (FMT == kInt4 || FMT == kInt2) {
+    const int64_t col = MODE == kListStaged ? (int64_t)q : (int64_t)m.idx;
+    const uint16_t* sp = scales + col * sstride + (row0 >> 7);
+    const uint32_t g0 = sp[0];
+    const uint32_t g1 = ngrp > 1 ? sp[1] : 0u;
+    const uint32_t g2 = ngrp > 2 ? sp[2] : 0u;
+    const uint32_t g3 = ngrp > 3 ? sp[3] : 0u;
+    m.sc01 = g0 | (g1 << 16);
+    m.sc23 = g2 | (g3 << 16);
+  }
+  return m;
+}
+
+template <int MODE>
+__device__ __forceinline__ float meta_x(const Meta& m, int c) {
+  const uint32_t b = (uint32_t)__builtin_amdgcn_readlane((int)m.xb, c);
+  if constexpr (MODE == kListRank) return __uint_as_float(b);
+  else return h2f(b);
+}
+
+// This lane's group scale of batch column c (hi_pair: groups 2,3; sh: 0 or 16).
+__device__ __forceinline__ float meta_scale(const Meta& m, int c, bool hi_pair, uint32_t sh) {
+  const uint32_t a01 = (uint32_t)__builtin_amdgcn_readlane((int)m.sc01, c);
+  const uint32_t a23 = (uint32_t)__builtin_amdgcn_readlane((int)m.sc23, c);
+  return h2f(((hi_pair ? a23 : a01) >> sh) & 0xFFFFu);
+}
+
+template <int MODE>
+__device__ __forceinline__ int meta_col(const Meta& m, int p, int c) {
+  return MODE == kListStaged ? p + c : __builtin_amdgcn_readlane(m.idx, c);
+}
+
+// Multiply-add U loaded columns of one tier; slots u >= n were loaded from
+// a valid column and are added with a zero activation.
+template <typename T, int MODE>
+__device__ __forceinline__ void consume(float (&acc)[8], float& corr,
+                                        const typename T::V (&v)[T::U], const Meta& m, int c0,
+                                        int n, bool hi_pair, uint32_t sh, bool code) {
 #pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const int col = MODE == kListStaged ? (kb + c + u)
-                                            : __builtin_amdgcn_readlane(my_idx, c + u);
-        const uint8_t* cp = base + (int64_t)col * stride;
-        v[u] = T::load(cp, row0, ld_lane);
-        if constexpr (FMT != kFp16)
-          sv[u] = scales[(int64_t)col * sstride + sc_off];
-        else
-          sv[u] = 0u;
+  for (int u = 0; u < T::U; ++u) {
+    const int c = c0 + (u < n ? u : 0);
+    const float xs = u < n ? meta_x<MODE>(m, c) : 0.0f;
+    const float sc = code ? meta_scale(m, c, hi_pair, sh) : 0.0f;
+    T::fma(acc, corr, v[u], xs, sc);
+  }
+}
+
+// Stream this wave's full-tier list positions [f_lo, f_hi) and approx-tier
+// positions [a_lo, a_hi) for its rows. Each round issues the loads of up to
+// UF full columns and UA code columns before any of them is consumed, so a
+// wave keeps both tiers' bytes in flight together; the last, partial round
+// of a batch issues only the loads it needs (wave-uniform guards).
+//   kListGlobal: idx lists and x in device memory;
+//   kListStaged: columns staged in list order (column = position);
+//   kListRank:   lidx / lx = this workgroup's list piece in LDS.
+template <int FF, int AF, int MODE>
+__device__ __forceinline__ void stream_tiers(float (&acc)[8], float& corr, const GemvArgs& a,
+                                             const int32_t* lidx, const float* lx, int f_lo,
+                                             int f_hi, int a_lo, int a_hi, int row0, int lane,
+                                             int ld_lane) {
+  using TF = Tier<FF>;
+  using TA = Tier<AF == kNone ? kInt4 : AF>;
+  constexpr int UF = TF::U;
+  constexpr int UA = AF == kNone ? 0 : TA::U;
+  const int grp = ld_lane >> 4;  // this lane's group in the tile
+  const bool hi_pair = grp >= 2;
+  const uint32_t sh = 16u * (uint32_t)(grp & 1);
+  const int ngrp = min(4, (a.rows - row0 + kGroup - 1) / kGroup);
+  if constexpr (AF == kNone) a_hi = a_lo;
+  // rank mode: the approx part of the piece follows the full part in LDS
+  int pf = f_lo, pa = a_lo;
+  while (pf < f_hi || pa < a_hi) {
+    const int nbf = min(64, f_hi - pf), nba = min(64, a_hi - pa);
+    const Meta mf = load_meta<FF, MODE>(a.full_scales, a.full_sstride, a.full_idx, a.x, lidx, lx,
+                                        pf, nbf, row0, ngrp, lane);
+    Meta ma{0, 0u, 0u, 0u};
+    if constexpr (AF != kNone)
+      ma = load_meta<AF, MODE>(a.approx_scales, a.approx_sstride, a.approx_idx, a.x, lidx, lx,
+                               pa, nba, row0, ngrp, lane);
+    for (int cf = 0, ca = 0; cf < nbf || ca < nba; cf += UF, ca += UA) {
+      // Slots past the batch reload the round's first column and add it
+      // times zero, so every load of a round is issued unconditionally.
+      const int nf = min(UF, nbf - cf), na = min(UA, nba - ca);
+      if (nf > 0) {
+        typename TF::V vf[UF];
+#pragma unroll
+        for (int u = 0; u < UF; ++u) {
+          const int c = cf + (u < nf ? u : 0);
+          vf[u] = TF::load(a.full_base + (int64_t)meta_col<MODE>(mf, pf, c) * a.full_stride, row0,
+                           ld_lane);
+        }
+        if constexpr (AF != kNone) {
+          if (na > 0) {
+            typename TA::V va[UA > 0 ? UA : 1];
+#pragma unroll
+            for (int u = 0; u < UA; ++u) {
+              const int c = ca + (u < na ? u : 0);
+              va[u] = TA::load(
+                  a.approx_base + (int64_t)meta_col<MODE>(ma, pa, c) * a.approx_stride, row0,
+                  ld_lane);
+            }
+            consume<TF, MODE>(acc, corr, vf, mf, cf, nf, hi_pair, sh, FF != kFp16);
+            consume<TA, MODE>(acc, corr, va, ma, ca, na, hi_pair, sh, true);
+            continue;
+          }
+        }
+        consume<TF, MODE>(acc, corr, vf, mf, cf, nf, hi_pair, sh, FF != kFp16);
+      } else if constexpr (AF != kNone) {
+        typename TA::V va[UA > 0 ? UA : 1];
+#pragma unroll
+        for (int u = 0; u < UA; ++u) {
+          const int c = ca + (u < na ? u : 0);
+          va[u] = TA::load(a.approx_base + (int64_t)meta_col<MODE>(ma, pa, c) * a.approx_stride,
+                           row0, ld_lane);
+        }
+        consume<TA, MODE>(acc, corr, va, ma, ca, na, hi_pair, sh, true);
       }
-#pragma unroll
-      for (int u = 0; u < U; ++u) T::fma(acc, corr, v[u], xval(c + u), sv[u]);
     }
-    for (; c < cnt; ++c) {
-      const int col = MODE == kListStaged ? (kb + c) : __builtin_amdgcn_readlane(my_idx, c);
-      const uint8_t* cp = base + (int64_t)col * stride;
-      const typename T::V v = T::load(cp, row0, ld_lane);
-      uint32_t sv = 0u;
-      if constexpr (FMT != kFp16) sv = scales[(int64_t)col * sstride + sc_off];
-      T::fma(acc, corr, v, xval(c), sv);
-    }
+    pf += max(nbf, 0);
+    pa += max(nba, 0);
   }
 }
 
@@ -249,25 +326,36 @@ struct RankShared {
   int32_t sel[8];
 };
 
-__device__ __forceinline__ uint32_t wave_excl_suffix(uint32_t v, int lane) {
-  uint32_t incl = v;
-#pragma unroll
-  for (int d = 1; d < 64; d <<= 1) {
-    const uint32_t t = __shfl_down(incl, d, 64);
-    if (lane + d < 64) incl += t;
-  }
-  return incl - v;
+// Inclusive prefix sum over the 64 lanes of a wave with DPP row shifts and
+// row broadcasts (lanes whose source is outside the row add 0).
+__device__ __forceinline__ uint32_t wave_incl_scan(uint32_t v) {
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x111, 0xf, 0xf, false);  // row_shr:1
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x112, 0xf, 0xf, false);  // row_shr:2
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x114, 0xf, 0xf, false);  // row_shr:4
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x118, 0xf, 0xf, false);  // row_shr:8
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x142, 0xa, 0xf, false);  // row_bcast:15
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x143, 0xc, 0xf, false);  // row_bcast:31
+  return v;
+}
+
+// Sum of v over the lanes above this one.
+__device__ __forceinline__ uint32_t wave_excl_suffix(uint32_t v) {
+  const uint32_t incl = wave_incl_scan(v);
+  const uint32_t total = (uint32_t)__builtin_amdgcn_readlane((int)incl, 63);
+  return total - incl;
 }
 
 __device__ __forceinline__ uint32_t rawbits(const uint32_t* xr, int i) {
   return (xr[i >> 1] >> (16 * (i & 1))) & 0xFFFFu;
 }
 
-// Ranks x and places this workgroup's list positions [e0, e1) in LDS.
-// Returns the number of full-tier positions in the piece.
+// Ranks x and places this workgroup's list positions in LDS: full-tier
+// positions [f0, f1) at slots [0, f1 - f0), approx-tier positions [a0, a1)
+// after them.
 template <int E>
-__device__ __forceinline__ int rank_piece(const GemvArgs& a, RankShared& rs, int32_t* lidx,
-                                          float* lx, int64_t e0, int64_t e1, bool write_lists) {
+__device__ __forceinline__ void rank_piece(const GemvArgs& a, RankShared& rs, int32_t* lidx,
+                                           float* lx, int f0, int f1, int a0, int a1,
+                                           bool write_lists) {
   const int t = threadIdx.x;
   const int lane = t & 63;
   const int wave = t >> 6;
@@ -323,7 +411,7 @@ __device__ __forceinline__ int rank_piece(const GemvArgs& a, RankShared& rs, int
     uint32_t c[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) c[j] = rs.hist[0][4 * lane + j];
-    uint32_t above = wave_excl_suffix(c[0] + c[1] + c[2] + c[3], lane);
+    uint32_t above = wave_excl_suffix(c[0] + c[1] + c[2] + c[3]);
 #pragma unroll
     for (int j = 3; j >= 0; --j) {
       if (K1 > 0 && above < K1 && K1 <= above + c[j]) {
@@ -358,7 +446,7 @@ __device__ __forceinline__ int rank_piece(const GemvArgs& a, RankShared& rs, int
       const uint32_t K = r == 0 ? K1 : K2;
       if (b < 0) continue;
       const uint32_t c0 = rs.sub[r][2 * lane], c1 = rs.sub[r][2 * lane + 1];
-      uint32_t above = (uint32_t)rs.sel[1 + 2 * r] + wave_excl_suffix(c0 + c1, lane);
+      uint32_t above = (uint32_t)rs.sel[1 + 2 * r] + wave_excl_suffix(c0 + c1);
       if (above < K && K <= above + c1) {
         rs.sel[4 + 2 * r] = (b << 7) | (2 * lane + 1);
         rs.sel[5 + 2 * r] = (int32_t)(K - above);
@@ -385,15 +473,9 @@ __device__ __forceinline__ int rank_piece(const GemvArgs& a, RankShared& rs, int
     c[2] += k > t2;
     c[3] += k == t2;
   }
-  uint32_t in[4] = {c[0], c[1], c[2], c[3]};
+  uint32_t in[4];
 #pragma unroll
-  for (int d = 1; d < 64; d <<= 1) {
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const uint32_t v = __shfl_up(in[j], d, 64);
-      if (lane >= d) in[j] += v;
-    }
-  }
+  for (int j = 0; j < 4; ++j) in[j] = wave_incl_scan(c[j]);
   if (lane == 63) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) rs.scan[j][wave] = in[j];
@@ -406,7 +488,6 @@ __device__ __forceinline__ int rank_piece(const GemvArgs& a, RankShared& rs, int
     g2 += rs.scan[2][w];
     e2r += rs.scan[3][w];
   }
-  const int kf = a.k_full;
 #pragma unroll
   for (int i = 0; i < E; ++i) {
     if (i >= nv) continue;
@@ -414,13 +495,15 @@ __device__ __forceinline__ int rank_piece(const GemvArgs& a, RankShared& rs, int
     const bool in_f = k > t1 || (k == t1 && e1r < q1);
     const bool in_fa = k > t2 || (k == t2 && e2r < q2);
     if (in_fa) {
-      const int64_t fpos = g1 + min(e1r, q1);          // F entries before this one
-      const int64_t apos = g2 + min(e2r, q2) - fpos;   // A entries before this one
-      const int64_t v = in_f ? fpos : kf + apos;
+      const int fpos = (int)(g1 + min(e1r, q1));          // F entries before this one
+      const int apos = (int)(g2 + min(e2r, q2)) - fpos;   // A entries before this one
       const int j = base + i;
-      if (v >= e0 && v < e1) {
-        lidx[v - e0] = j;
-        lx[v - e0] = h2f(rawbits(xr, i));
+      int slot = -1;
+      if (in_f && fpos >= f0 && fpos < f1) slot = fpos - f0;
+      if (!in_f && apos >= a0 && apos < a1) slot = (f1 - f0) + (apos - a0);
+      if (slot >= 0) {
+        lidx[slot] = j;
+        lx[slot] = h2f(rawbits(xr, i));
         if (write_lists) {
           if (in_f) a.out_full_idx[fpos] = j;
           else a.out_approx_idx[apos] = j;
@@ -433,7 +516,6 @@ __device__ __forceinline__ int rank_piece(const GemvArgs& a, RankShared& rs, int
     e2r += k == t2;
   }
   __syncthreads();
-  return (int)(min<int64_t>(e1, kf) - min<int64_t>(e0, kf));
 }
 
 // Gate / up pair: r1 is a gate row, r1 + 128 the matching up row.
@@ -473,8 +555,10 @@ __global__ __launch_bounds__(kGemvThreads) void gemv_kernel(GemvArgs a) {
   // their sums are never stored.
   const int ld_lane = row0 + 8 * lane < a.rows ? lane : 0;
 
-  const int64_t e0 = split_start(split, a.n_splits, a.k_full, a.k_approx, a.w_full, a.w_approx);
-  const int64_t e1 = split_start(split + 1, a.n_splits, a.k_full, a.k_approx, a.w_full, a.w_approx);
+  const int f0 = split_pos(split, a.n_splits, a.k_full);
+  const int f1 = split_pos(split + 1, a.n_splits, a.k_full);
+  const int a0 = split_pos(split, a.n_splits, a.k_approx);
+  const int a1 = split_pos(split + 1, a.n_splits, a.k_approx);
 
   float acc[8];
 #pragma unroll
@@ -483,29 +567,23 @@ __global__ __launch_bounds__(kGemvThreads) void gemv_kernel(GemvArgs a) {
 
   int f_lo, f_hi, a_lo, a_hi;  // tier ranges in the list (or in the LDS piece)
   if constexpr (MODE == kListRank) {
-    const int nf = rank_piece<E>(a, sm.rank, lidx, lx, e0, e1, tile == 0);
+    // the piece holds F positions [f0, f1) then A positions [a0, a1)
+    rank_piece<E>(a, sm.rank, lidx, lx, f0, f1, a0, a1, tile == 0);
     f_lo = 0;
-    f_hi = nf;
-    a_lo = nf;
-    a_hi = (int)(e1 - e0);
+    f_hi = f1 - f0;
+    a_lo = f1 - f0;
+    a_hi = f1 - f0 + a1 - a0;
   } else {
-    f_lo = (int)min<int64_t>(e0, a.k_full);
-    f_hi = (int)min<int64_t>(e1, a.k_full);
-    a_lo = (int)(max<int64_t>(e0, a.k_full) - a.k_full);
-    a_hi = (int)(max<int64_t>(e1, a.k_full) - a.k_full);
+    f_lo = f0;
+    f_hi = f1;
+    a_lo = a0;
+    a_hi = a1;
   }
   {
-    const int len = f_hi - f_lo;
-    const int wlo = f_lo + (len * wave) / kWaves, whi = f_lo + (len * (wave + 1)) / kWaves;
-    run_tier<FF, MODE>(acc, corr, a.full_base, a.full_stride, a.full_scales, a.full_sstride,
-                       a.full_idx, a.x, lidx, lx, wlo, whi, row0, lane, ld_lane);
-  }
-  if constexpr (AF != kNone) {
-    const int len = a_hi - a_lo;
-    const int wlo = a_lo + (len * wave) / kWaves, whi = a_lo + (len * (wave + 1)) / kWaves;
-    run_tier<AF, MODE>(acc, corr, a.approx_base, a.approx_stride, a.approx_scales,
-                       a.approx_sstride, a.approx_idx, a.x, lidx, lx, wlo, whi, row0, lane,
-                       ld_lane);
+    const int lf = f_hi - f_lo, la = a_hi - a_lo;
+    stream_tiers<FF, AF, MODE>(acc, corr, a, lidx, lx, f_lo + (lf * wave) / kWaves,
+                               f_lo + (lf * (wave + 1)) / kWaves, a_lo + (la * wave) / kWaves,
+                               a_lo + (la * (wave + 1)) / kWaves, row0, lane, ld_lane);
   }
   if constexpr (FF == kInt4 || AF != kNone) {
 #pragma unroll

@@ -39,8 +39,6 @@ struct GemvArgs {
   int32_t splits_here;           // splits handled by this launch
   int32_t k_full, k_approx;
   int32_t n;                     // input length (cols)
-  // Per column-tile byte weights used to balance the splits.
-  int64_t w_full, w_approx;
   // Full tier: fp16 columns or int4 codes; column c at full_base + c * full_stride.
   const uint8_t* full_base;
   int64_t full_stride;
@@ -67,7 +65,8 @@ struct GemvArgs {
 // Selected-column copy from host-resident storage into device staging.
 struct CopyArgs {
   int32_t k_full, k_approx;
-  int64_t e_lo, e_hi;            // virtual-list elements [e_lo, e_hi) to copy
+  int32_t f_lo, f_hi;            // full-tier list positions [f_lo, f_hi) to copy
+  int32_t a_lo, a_hi;            // approx-tier list positions [a_lo, a_hi) to copy
   const int32_t* full_idx;
   const int32_t* approx_idx;
   // sources (host pinned, device addressable)
@@ -93,17 +92,12 @@ hipError_t launch_pack(const uint16_t* w, int32_t rows, int32_t cols, int32_t fm
 
 hipError_t launch_clear(void* ws, size_t bytes, hipStream_t s);
 
-// First element of split s when the virtual list [full..., approx...] is cut
-// into n_splits pieces of (nearly) equal bytes.
-__host__ __device__ inline int64_t split_start(int64_t s, int64_t n_splits, int64_t kf,
-                                               int64_t ka, int64_t wf, int64_t wa) {
-  const int64_t ftot = kf * wf;
-  const int64_t tot = ftot + ka * wa;
-  if (s <= 0) return 0;
-  if (s >= n_splits) return kf + ka;
-  const int64_t B = (tot * s) / n_splits;
-  if (B <= ftot) return wf > 0 ? (B + wf - 1) / wf : 0;
-  return kf + (wa > 0 ? (B - ftot + wa - 1) / wa : ka);
+// List positions of split s of n_splits: every split takes the same share
+// of each tier, [k * s / n_splits, k * (s + 1) / n_splits), so every
+// workgroup gets the same mix of full columns (bytes) and code columns
+// (bytes plus dequantisation arithmetic).
+__host__ __device__ inline int32_t split_pos(int64_t s, int64_t n_splits, int64_t k) {
+  return (int32_t)(k * s / n_splits);
 }
 
 }  // namespace spax

@@ -5,9 +5,10 @@ fp16 weights ~ N(0, 0.02), column-major) with an int4 group-128 compressed
 copy, tiers skip / approx / full = 40 / 30 / 30 % of the 4096 inputs, batch 1,
 32 decode tokens of fresh Laplace(0, 1) activations per step.
 
-One step = the whole per-token path for 32 tokens:
-    rank h -> tier lists -> tiered product of q, k, v (stacked, one launch)
+One step = the whole per-token path for 32 tokens, through spax_layer_step:
+    rank h -> tier lists -> tiered product of q, k, v (rows stacked)
     rank z -> tier lists -> tiered product of o
+(each group is one fused launch: the ranking runs inside the product).
 Token t reads weight set t (32 distinct sets = 32 decoder layers' attention
 weights, 5.4 GB), so a set is read again only after the other 31 have
 streamed through, as in decoding a 32-layer model: weights come from HBM,
@@ -21,7 +22,9 @@ synchronisations. Inputs are resident in HBM before timing starts.
 Printed: ONE JSON line with the throughput (effective weight GB/s on the
 algorithmic bytes), microseconds per tiered projection, the roofline of the
 tiered product kernel (event-timed per launch on the launch stream) and the
-CPU oracle timed on a bounded sample of the same workload.
+CPU oracle timed on a bounded sample of the same workload. The per-launch
+duration of the product kernel comes from graph replays of one group's 32
+launches back to back, timed with events on the launch stream.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--eager]
                     [--no-cpu-baseline] [--calib-copy]
@@ -45,6 +48,38 @@ HIDDEN = 4096
 TOKENS = 32
 SETS = 32
 CONFIG_ID = 2
+
+
+PMC_SUMMARY = os.path.join(ROOT, "profiles", "gemv_kernel_7b_attention_pmc.txt")
+KERNEL_SOURCES = ("gemv.hip", "api.cpp", "spax_internal.h")
+
+
+def kernel_source_hash() -> str:
+    import hashlib
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "activation_sparse_decode_token_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def measured_traffic():
+    """HBM bytes per launch of the product kernel from the committed counter
+    summary (FETCH_SIZE and WRITE_SIZE, scaled by a plain copy's reading),
+    or None when the kernel sources changed since the counters were taken."""
+    try:
+        text = open(PMC_SUMMARY).read()
+    except OSError:
+        return None
+    vals = {}
+    for line in text.splitlines():
+        if line.startswith("traffic_bytes_per_launch:"):
+            vals["traffic"] = float(line.split(":", 1)[1])
+        elif line.startswith("kernel sources sha256"):
+            vals["sha"] = line.rsplit(":", 1)[1].strip()
+    if vals.get("sha") != kernel_source_hash() or "traffic" not in vals:
+        return None
+    return int(vals["traffic"])
 
 
 def log(msg: str) -> None:
@@ -133,22 +168,41 @@ class Workload:
             spax.layer_step(self.layers[t % self.sets], self.io[t], self.ws, self.ws_bytes,
                             compute_stream=stream)
 
-    def timed_launches(self, stream):
-        """The same launches one at a time, each bracketed by HIP events on
-        its stream; returns [(start, end, group)]."""
-        import torch
+    def launches(self, group: int):
+        """The product launches of one group (0: q,k,v; 1: o) for every
+        token, enqueued back to back -- one fused launch each."""
         spax = self.spax
-        ev = []
-        for t in range(TOKENS):
-            s = t % self.sets
-            for gi, L in enumerate((self.qkv_only[s], self.o_only[s])):
-                e0 = torch.cuda.Event(enable_timing=True)
-                e1 = torch.cuda.Event(enable_timing=True)
-                e0.record(stream)
-                spax.layer_step(L, self.io[t], self.ws, self.ws_bytes, compute_stream=stream)
-                e1.record(stream)
-                ev.append((e0, e1, gi))
-        return ev
+        layers = self.qkv_only if group == 0 else self.o_only
+
+        def run(stream):
+            for t in range(TOKENS):
+                spax.layer_step(layers[t % self.sets], self.io[t], self.ws, self.ws_bytes,
+                                compute_stream=stream)
+        return run
+
+
+def graph_launch_time(run, stream, launches: int, reps: int = 5) -> float:
+    """Average duration (s) of one launch: `run` (launches kernels back to
+    back) is captured in a HIP graph, replayed `reps` times between two
+    events on the launch stream."""
+    import torch
+    with torch.cuda.stream(stream):
+        run(stream)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=stream):
+            run(stream)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            g.replay()
+        e1.record(stream)
+        torch.cuda.synchronize()
+    return e0.elapsed_time(e1) * 1e-3 / (reps * launches)
 
 
 def gpu_run(args):
@@ -199,25 +253,19 @@ def gpu_run(args):
         ms_event = ev0.elapsed_time(ev1)
     log(f"timed {args.steps} steps: wall {wall * 1e3:.2f} ms, events {ms_event:.2f} ms")
 
-    # Per-launch duration of the tiered product, event-timed on its stream.
-    ev = []
-    with torch.cuda.stream(stream):
-        for _ in range(3):
-            ev += wl.timed_launches(stream)
-        torch.cuda.synchronize()
+    # Per-launch duration of the product kernel, event-timed on its stream:
+    # each group's launches back to back in a graph (host launch cost is
+    # not on the GPU timeline).
     qkv_b, o_b = wl.gemv_bytes()
-    dur = {0: [], 1: []}
-    for e0, e1, gi in ev:
-        dur[gi].append(e0.elapsed_time(e1) * 1e-3)       # seconds
-    n_launch = len(dur[0]) + len(dur[1])
-    tot_s = sum(dur[0]) + sum(dur[1])
-    tot_b = qkv_b * len(dur[0]) + o_b * len(dur[1])
-    avg_us = tot_s / n_launch * 1e6
-    achieved = tot_b / tot_s / 1e9
-    log(f"tiered product: {n_launch} launches, avg {avg_us:.2f} us "
-        f"(qkv {sum(dur[0]) / len(dur[0]) * 1e6:.2f} us, o {sum(dur[1]) / len(dur[1]) * 1e6:.2f} us)"
-        f", {achieved:.0f} GB/s")
-
+    if graph is not None:
+        t_qkv = graph_launch_time(wl.launches(0), stream, TOKENS)
+        t_o = graph_launch_time(wl.launches(1), stream, TOKENS)
+        avg_us = (t_qkv + t_o) / 2 * 1e6
+        achieved = (qkv_b + o_b) / (t_qkv + t_o) / 1e9
+        log(f"product kernel: qkv {t_qkv * 1e6:.2f} us, o {t_o * 1e6:.2f} us per launch, "
+            f"{achieved:.0f} GB/s on algorithmic bytes")
+    else:
+        t_qkv = t_o = avg_us = achieved = None
     if args.calib_copy:
         a = torch.empty(256 << 20, dtype=torch.uint8, device="cuda:0")
         b = torch.empty_like(a)
@@ -234,15 +282,17 @@ def gpu_run(args):
         "wall_step": wall / args.steps,
         "step_bytes": step_b,
         "projections": TOKENS * 4,
-        "roofline": {
+        "roofline": None if achieved is None else {
             "bound": "hbm",
             "achieved": round(achieved, 1),
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
-            "traffic": None,
-            "kernel": "gemv_kernel, fused tier selection + tiered gather-GEMV (fp16 full, int4 g128 approx)",
+            "traffic": measured_traffic(),
+            "kernel": "gemv_kernel: fused tier selection + tiered gather-GEMV "
+                      "(fp16 full, int4 g128 approx)",
             "avg_launch_us": round(avg_us, 3),
+            "launch_us": {"qkv": round(t_qkv * 1e6, 3), "o": round(t_o * 1e6, 3)},
             "bytes_per_launch": {"qkv": qkv_b, "o": o_b},
         },
         "kf": wl.kf, "ka": wl.ka,
