@@ -80,9 +80,9 @@ struct ProductPlan {
 #define SPAX_MIN_SPLIT_BYTES 32768
 #endif
 
-// Number of column splits: about one 8-wave workgroup per compute unit, at
-// least SPAX_MIN_SPLIT_BYTES of weights per workgroup, a multiple of 8 (one
-// XCD per split group).
+// Number of column splits: at most one 8-wave workgroup per compute unit
+// (tiles x splits <= SPAX_TARGET_BLOCKS, so the grid runs in one pass), at
+// least SPAX_MIN_SPLIT_BYTES of weights per workgroup.
 ProductPlan plan_product(const spax_matrix* W, int32_t kf, int32_t ka) {
   constexpr int64_t kTargetBlocks = SPAX_TARGET_BLOCKS;
   constexpr int64_t kMinSplitBytes = SPAX_MIN_SPLIT_BYTES;
@@ -90,11 +90,10 @@ ProductPlan plan_product(const spax_matrix* W, int32_t kf, int32_t ka) {
   p.tiles = (W->rows + kTileRows - 1) / kTileRows;
   const int64_t total = kf * tile_bytes(W->full_fmt) + ka * tile_bytes(W->approx_fmt);
   if (total == 0) return p;
-  int64_t s = (kTargetBlocks + p.tiles - 1) / p.tiles;
+  int64_t s = std::max<int64_t>(1, kTargetBlocks / p.tiles);
   s = std::min<int64_t>(s, std::max<int64_t>(1, total / kMinSplitBytes));
   s = std::min<int64_t>(s, kMaxSplits);
   s = std::min<int64_t>(s, (int64_t)kf + ka);
-  if (s >= 8) s = s / 8 * 8;
   p.splits = (int32_t)std::max<int64_t>(1, s);
   return p;
 }
@@ -115,9 +114,7 @@ bool plan_fused(const spax_matrix* W, int32_t kf, int32_t ka, ProductPlan* out) 
   ProductPlan p = plan_product(W, kf, ka);
   while (max_piece(p, kf, ka) > kListCap) {
     if (p.splits >= kMaxSplits || p.splits >= (int64_t)kf + ka) return false;
-    int64_t s = std::min<int64_t>({(int64_t)p.splits * 2, kMaxSplits, (int64_t)kf + ka});
-    if (s >= 8) s = s / 8 * 8;
-    p.splits = (int32_t)s;
+    p.splits = (int32_t)std::min<int64_t>({(int64_t)p.splits * 2, kMaxSplits, (int64_t)kf + ka});
   }
   *out = p;
   return true;

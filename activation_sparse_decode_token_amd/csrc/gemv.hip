@@ -62,6 +62,18 @@ __device__ __forceinline__ float b2f(uint32_t v, int byte) {
   return (float)((v >> (8 * byte)) & 0xFFu);
 }
 
+// Buffer resource of one column: a wave-uniform base in scalar registers
+// (pinned with readfirstlane so no lane offset is folded into it). Loads
+// through it take one shared 32-bit lane offset instead of a 64-bit address
+// per lane and load. Dword 3 selects 32-bit raw access on gfx9-family parts.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t column_rsrc(const uint8_t* p) {
+  const uint64_t v = reinterpret_cast<uint64_t>(p);
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)v);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(v >> 32));
+  void* base = reinterpret_cast<void*>(((uint64_t)hi << 32) | lo);
+  return __builtin_amdgcn_make_buffer_rsrc(base, (short)0, 0x7FFFFFFF, 0x00020000);
+}
+
 template <int FMT>
 struct Tier;
 
@@ -69,8 +81,12 @@ template <>
 struct Tier<kFp16> {
   using V = uint4;
   static constexpr int U = 8;
-  static __device__ __forceinline__ V load(const uint8_t* col, int row0, int lane) {
-    return *reinterpret_cast<const uint4*>(col + 2 * (size_t)(row0 + 8 * lane));
+  // byte offset of lane l's 8 rows in a column
+  static __device__ __forceinline__ uint32_t offset(int row0, int lane) {
+    return 2u * (uint32_t)(row0 + 8 * lane);
+  }
+  static __device__ __forceinline__ V load(__amdgpu_buffer_rsrc_t col, uint32_t off) {
+    return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(col, off, 0, 0));
   }
   static __device__ __forceinline__ void fma(float (&acc)[8], float&, V v, float xs, float) {
     acc[0] = fmaf(h2f(v.x & 0xFFFFu), xs, acc[0]);
@@ -88,8 +104,11 @@ template <>
 struct Tier<kInt4> {
   using V = uint32_t;
   static constexpr int U = 16;
-  static __device__ __forceinline__ V load(const uint8_t* col, int row0, int lane) {
-    return *reinterpret_cast<const uint32_t*>(col + (size_t)(row0 + 8 * lane) / 2);
+  static __device__ __forceinline__ uint32_t offset(int row0, int lane) {
+    return (uint32_t)(row0 + 8 * lane) / 2u;
+  }
+  static __device__ __forceinline__ V load(__amdgpu_buffer_rsrc_t col, uint32_t off) {
+    return __builtin_amdgcn_raw_buffer_load_b32(col, off, 0, 0);
   }
   // Rows 2b and 2b+1 sit in the low and high nibble of byte b, as
   // two's-complement q; flipping each nibble's sign bit gives u = q + 8.
@@ -115,8 +134,11 @@ template <>
 struct Tier<kInt2> {
   using V = uint32_t;
   static constexpr int U = 16;
-  static __device__ __forceinline__ V load(const uint8_t* col, int row0, int lane) {
-    return *reinterpret_cast<const uint16_t*>(col + (size_t)(row0 + 8 * lane) / 4);
+  static __device__ __forceinline__ uint32_t offset(int row0, int lane) {
+    return (uint32_t)(row0 + 8 * lane) / 4u;
+  }
+  static __device__ __forceinline__ V load(__amdgpu_buffer_rsrc_t col, uint32_t off) {
+    return __builtin_amdgcn_raw_buffer_load_b16(col, off, 0, 0);
   }
   // Row 4b + r sits in bits 2r..2r+1 of byte b; masking leaves u * 4^r, so
   // the factor is scaled by 4^-r (exact).
@@ -143,7 +165,8 @@ struct Tier<kInt2> {
 struct Meta {
   int idx;
   uint32_t xb;  // fp16 bits (global modes) or fp32 bits (rank mode)
-  uint32_t sc01, sc23;
+  uint32_t g[4];  // raw scales as loaded (code tiers)
+  uint32_t sc01, sc23;  // packed by pack_scales once the round's loads are issued
 };
 
 template <int FMT, int MODE>
@@ -152,7 +175,7 @@ __device__ __forceinline__ Meta load_meta(const uint16_t* __restrict__ scales, i
                                           const uint16_t* __restrict__ x, const int32_t* lidx,
                                           const float* lx, int p, int cnt, int row0, int ngrp,
                                           int lane) {
-  Meta m{0, 0u, 0u, 0u};
+  Meta m{0, 0u, {0u, 0u, 0u, 0u}, 0u, 0u};
   if (cnt <= 0) return m;
   // lanes past the batch repeat its first position (in range, never used)
   const int q = p + (lane < cnt ? lane : 0);
@@ -164,16 +187,27 @@ __device__ __forceinline__ Meta load_meta(const uint16_t* __restrict__ scales, i
     m.xb = x[m.idx];
   }
   if constexpr (FMT == kInt4 || FMT == kInt2) {
+    // a ragged last tile has fewer groups: their slots repeat its last group
+    // (never used, since lanes past the last row take group 0's rows), so
+    // the four loads are unconditional and issue back to back
     const int64_t col = MODE == kListStaged ? (int64_t)q : (int64_t)m.idx;
     const uint16_t* sp = scales + col * sstride + (row0 >> 7);
-    const uint32_t g0 = sp[0];
-    const uint32_t g1 = ngrp > 1 ? sp[1] : 0u;
-    const uint32_t g2 = ngrp > 2 ? sp[2] : 0u;
-    const uint32_t g3 = ngrp > 3 ? sp[3] : 0u;
-    m.sc01 = g0 | (g1 << 16);
-    m.sc23 = g2 | (g3 << 16);
+    const int gl = ngrp - 1;
+    m.g[0] = sp[0];
+    m.g[1] = sp[min(1, gl)];
+    m.g[2] = sp[min(2, gl)];
+    m.g[3] = sp[min(3, gl)];
   }
   return m;
+}
+
+__device__ __forceinline__ void pack_scales(Meta& m) {
+  // The empty volatile asm makes the raw scales opaque, so the packing (which
+  // waits for the scale loads) is not hoisted out of the round loop ahead of
+  // the round's weight loads.
+  asm volatile("" : "+v"(m.g[0]), "+v"(m.g[1]), "+v"(m.g[2]), "+v"(m.g[3]));
+  m.sc01 = m.g[0] | (m.g[1] << 16);
+  m.sc23 = m.g[2] | (m.g[3] << 16);
 }
 
 template <int MODE>
@@ -197,24 +231,24 @@ __device__ __forceinline__ int meta_col(const Meta& m, int p, int c) {
 
 // Multiply-add U loaded columns of one tier; slots u >= n were loaded from
 // a valid column and are added with a zero activation.
-template <typename T, int MODE>
-__device__ __forceinline__ void consume(float (&acc)[8], float& corr,
-                                        const typename T::V (&v)[T::U], const Meta& m, int c0,
-                                        int n, bool hi_pair, uint32_t sh, bool code) {
+template <typename T, int U, int MODE, bool CODE>
+__device__ __forceinline__ void consume(float (&acc)[8], float& corr, const typename T::V (&v)[U],
+                                        const Meta& m, int c0, int n, bool hi_pair, uint32_t sh) {
 #pragma unroll
-  for (int u = 0; u < T::U; ++u) {
+  for (int u = 0; u < U; ++u) {
     const int c = c0 + (u < n ? u : 0);
     const float xs = u < n ? meta_x<MODE>(m, c) : 0.0f;
-    const float sc = code ? meta_scale(m, c, hi_pair, sh) : 0.0f;
+    const float sc = CODE ? meta_scale(m, c, hi_pair, sh) : 0.0f;
     T::fma(acc, corr, v[u], xs, sc);
   }
 }
 
 // Stream this wave's full-tier list positions [f_lo, f_hi) and approx-tier
-// positions [a_lo, a_hi) for its rows. Each round issues the loads of up to
-// UF full columns and UA code columns before any of them is consumed, so a
-// wave keeps both tiers' bytes in flight together; the last, partial round
-// of a batch issues only the loads it needs (wave-uniform guards).
+// positions [a_lo, a_hi) for its rows. Each round issues the loads of UF
+// full columns and UA code columns before any of them is consumed, so a wave
+// keeps both tiers' bytes in flight together. Slots past a tier's share
+// reload a valid column and add it times zero, which keeps every load
+// unconditional: the compiler then issues a round's loads back to back.
 //   kListGlobal: idx lists and x in device memory;
 //   kListStaged: columns staged in list order (column = position);
 //   kListRank:   lidx / lx = this workgroup's list piece in LDS.
@@ -225,64 +259,90 @@ __device__ __forceinline__ void stream_tiers(float (&acc)[8], float& corr, const
                                              int ld_lane) {
   using TF = Tier<FF>;
   using TA = Tier<AF == kNone ? kInt4 : AF>;
+  constexpr bool kHasA = AF != kNone;
   constexpr int UF = TF::U;
-  constexpr int UA = AF == kNone ? 0 : TA::U;
+  // equal rounds for equal column counts when the full tier is fp16
+  constexpr int UA = FF == kFp16 ? 8 : TA::U;
   const int grp = ld_lane >> 4;  // this lane's group in the tile
   const bool hi_pair = grp >= 2;
   const uint32_t sh = 16u * (uint32_t)(grp & 1);
   const int ngrp = min(4, (a.rows - row0 + kGroup - 1) / kGroup);
-  if constexpr (AF == kNone) a_hi = a_lo;
-  // rank mode: the approx part of the piece follows the full part in LDS
+  // column bases are wave-uniform (buffer resources in scalar registers);
+  // the lane's part of the address is one 32-bit offset per tier
+  const uint32_t off_f = TF::offset(row0, ld_lane);
+  const uint32_t off_a = TA::offset(row0, ld_lane);
+  if constexpr (!kHasA) a_hi = a_lo;
   int pf = f_lo, pa = a_lo;
   while (pf < f_hi || pa < a_hi) {
-    const int nbf = min(64, f_hi - pf), nba = min(64, a_hi - pa);
-    const Meta mf = load_meta<FF, MODE>(a.full_scales, a.full_sstride, a.full_idx, a.x, lidx, lx,
-                                        pf, nbf, row0, ngrp, lane);
-    Meta ma{0, 0u, 0u, 0u};
-    if constexpr (AF != kNone)
+    const int nbf = max(0, min(64, f_hi - pf)), nba = max(0, min(64, a_hi - pa));
+    Meta mf = load_meta<FF, MODE>(a.full_scales, a.full_sstride, a.full_idx, a.x, lidx, lx, pf,
+                                  nbf, row0, ngrp, lane);
+    Meta ma{0, 0u, {0u, 0u, 0u, 0u}, 0u, 0u};
+    if constexpr (kHasA)
       ma = load_meta<AF, MODE>(a.approx_scales, a.approx_sstride, a.approx_idx, a.x, lidx, lx,
                                pa, nba, row0, ngrp, lane);
-    for (int cf = 0, ca = 0; cf < nbf || ca < nba; cf += UF, ca += UA) {
-      // Slots past the batch reload the round's first column and add it
-      // times zero, so every load of a round is issued unconditionally.
+    const int rounds = max((nbf + UF - 1) / UF, kHasA ? (nba + UA - 1) / UA : 0);
+    // Double-buffered rounds: the loads of round r + 1 are issued before
+    // round r is consumed, so a wave always has a round in flight. Each step
+    // issues and consumes in one straight-line block, so the wait before the
+    // consumption counts only the loads issued just before it.
+    typename TF::V vf0[UF], vf1[UF];
+    typename TA::V va0[kHasA ? UA : 1], va1[kHasA ? UA : 1];
+    auto issue = [&](int r, typename TF::V (&vf)[UF], typename TA::V (&va)[kHasA ? UA : 1]) {
+      const int cf = r * UF, ca = r * UA;
       const int nf = min(UF, nbf - cf), na = min(UA, nba - ca);
-      if (nf > 0) {
-        typename TF::V vf[UF];
 #pragma unroll
-        for (int u = 0; u < UF; ++u) {
-          const int c = cf + (u < nf ? u : 0);
-          vf[u] = TF::load(a.full_base + (int64_t)meta_col<MODE>(mf, pf, c) * a.full_stride, row0,
-                           ld_lane);
-        }
-        if constexpr (AF != kNone) {
-          if (na > 0) {
-            typename TA::V va[UA > 0 ? UA : 1];
-#pragma unroll
-            for (int u = 0; u < UA; ++u) {
-              const int c = ca + (u < na ? u : 0);
-              va[u] = TA::load(
-                  a.approx_base + (int64_t)meta_col<MODE>(ma, pa, c) * a.approx_stride, row0,
-                  ld_lane);
-            }
-            consume<TF, MODE>(acc, corr, vf, mf, cf, nf, hi_pair, sh, FF != kFp16);
-            consume<TA, MODE>(acc, corr, va, ma, ca, na, hi_pair, sh, true);
-            continue;
-          }
-        }
-        consume<TF, MODE>(acc, corr, vf, mf, cf, nf, hi_pair, sh, FF != kFp16);
-      } else if constexpr (AF != kNone) {
-        typename TA::V va[UA > 0 ? UA : 1];
+      for (int u = 0; u < UF; ++u) {
+        // an exhausted tier reloads a valid column of its batch
+        const int c = min(cf + (u < nf ? u : 0), 63);
+        vf[u] = TF::load(
+            column_rsrc(a.full_base + (int64_t)meta_col<MODE>(mf, pf, c) * a.full_stride), off_f);
+      }
+      if constexpr (kHasA) {
 #pragma unroll
         for (int u = 0; u < UA; ++u) {
-          const int c = ca + (u < na ? u : 0);
-          va[u] = TA::load(a.approx_base + (int64_t)meta_col<MODE>(ma, pa, c) * a.approx_stride,
-                           row0, ld_lane);
+          const int c = min(ca + (u < na ? u : 0), 63);
+          va[u] = TA::load(
+              column_rsrc(a.approx_base + (int64_t)meta_col<MODE>(ma, pa, c) * a.approx_stride),
+              off_a);
         }
-        consume<TA, MODE>(acc, corr, va, ma, ca, na, hi_pair, sh, true);
+      }
+      // keep the scale packing (which waits for the scale loads) behind the
+      // weight loads so the two round trips overlap
+      __builtin_amdgcn_sched_barrier(0);
+    };
+    auto use = [&](int r, const typename TF::V (&vf)[UF],
+                   const typename TA::V (&va)[kHasA ? UA : 1]) {
+      const int cf = r * UF, ca = r * UA;
+      const int nf = min(UF, nbf - cf), na = min(UA, nba - ca);
+      if constexpr (FF != kFp16) pack_scales(mf);
+      if constexpr (kHasA) pack_scales(ma);
+      consume<TF, UF, MODE, FF != kFp16>(acc, corr, vf, mf, cf, nf, hi_pair, sh);
+      if constexpr (kHasA) consume<TA, UA, MODE, true>(acc, corr, va, ma, ca, na, hi_pair, sh);
+    };
+    if (rounds > 0) {
+      issue(0, vf0, va0);
+      for (int r = 0;;) {
+        if (r + 1 < rounds) {
+          issue(r + 1, vf1, va1);
+          use(r, vf0, va0);
+        } else {
+          use(r, vf0, va0);
+          break;
+        }
+        ++r;
+        if (r + 1 < rounds) {
+          issue(r + 1, vf0, va0);
+          use(r, vf1, va1);
+        } else {
+          use(r, vf1, va1);
+          break;
+        }
+        ++r;
       }
     }
-    pf += max(nbf, 0);
-    pa += max(nba, 0);
+    pf += nbf;
+    pa += nba;
   }
 }
 
@@ -309,7 +369,7 @@ __device__ __forceinline__ void map_block(int b, int n_tiles, int splits_here, i
 // plan kernel: order key = fp16 magnitude bits, larger first, lower index
 // first among equal keys; the k_full first are F, the next k_approx are A.
 // Thread t owns entries [t*E, t*E+E).
-//   1. 256-bin histogram of key bits 14..7 (per-wave LDS histograms);
+//   1. 256-bin histogram of key bits 14..7 (LDS atomics);
 //   2. suffix counts give the bins holding rank k_full and k_full + k_approx;
 //   3. 128-bin histograms inside those bins give the boundary keys t1, t2
 //      and the number of entries equal to each that are kept (q1, q2);
@@ -320,10 +380,10 @@ __device__ __forceinline__ void map_block(int b, int n_tiles, int splits_here, i
 constexpr uint32_t kAboveAll = 0x8000u;  // boundary key when a tier is empty
 
 struct RankShared {
-  uint32_t hist[kWaves][256];
+  uint32_t hist[257];  // bin 256 absorbs the padding past n
   uint32_t sub[2][128];
   uint32_t scan[4][kWaves];
-  int32_t sel[8];
+  int32_t sel[8];  // b1, entries above b1, b2, entries above b2, t1, q1, t2, q2
 };
 
 // Inclusive prefix sum over the 64 lanes of a wave with DPP row shifts and
@@ -343,6 +403,21 @@ __device__ __forceinline__ uint32_t wave_excl_suffix(uint32_t v) {
   const uint32_t incl = wave_incl_scan(v);
   const uint32_t total = (uint32_t)__builtin_amdgcn_readlane((int)incl, 63);
   return total - incl;
+}
+
+// The one lane with sel >= 0 (if any) broadcasts (sel, val) to the wave;
+// otherwise out_sel = -1, out_val = 0.
+__device__ __forceinline__ void wave_pick(int sel, uint32_t val, int& out_sel,
+                                          uint32_t& out_val) {
+  const uint64_t m = __ballot(sel >= 0);
+  if (m == 0) {
+    out_sel = -1;
+    out_val = 0u;
+  } else {
+    const int src = (int)__builtin_ctzll(m);
+    out_sel = __builtin_amdgcn_readlane(sel, src);
+    out_val = (uint32_t)__builtin_amdgcn_readlane((int)val, src);
+  }
 }
 
 __device__ __forceinline__ uint32_t rawbits(const uint32_t* xr, int i) {
@@ -385,45 +460,43 @@ __device__ __forceinline__ void rank_piece(const GemvArgs& a, RankShared& rs, in
   }
   const int nv = max(0, min(E, n - base));  // valid entries of this thread
 
-  for (int i = t; i < kWaves * 256; i += kGemvThreads) (&rs.hist[0][0])[i] = 0u;
-  if (t < 256) (&rs.sub[0][0])[t] = 0u;
-  if (t == 0) {
-    rs.sel[0] = -1; rs.sel[1] = 0; rs.sel[2] = -1; rs.sel[3] = 0;
-    rs.sel[4] = (int32_t)kAboveAll; rs.sel[5] = 0; rs.sel[6] = (int32_t)kAboveAll; rs.sel[7] = 0;
+  if (t < 256) {
+    rs.hist[t] = 0u;
+    (&rs.sub[0][0])[t] = 0u;
   }
+  if (t == 256) rs.hist[256] = 0u;
   __syncthreads();
 
   // 1. top-level histogram
 #pragma unroll
   for (int i = 0; i < E; ++i)
-    if (i < nv) atomicAdd(&rs.hist[wave][(rawbits(xr, i) & 0x7FFFu) >> 7], 1u);
-  __syncthreads();
-  if (t < 256) {
-    uint32_t s = 0;
-#pragma unroll
-    for (int w = 0; w < kWaves; ++w) s += rs.hist[w][t];
-    rs.hist[0][t] = s;  // only this thread reads column t
-  }
+    atomicAdd(&rs.hist[i < nv ? (rawbits(xr, i) & 0x7FFFu) >> 7 : 256u], 1u);
   __syncthreads();
 
-  // 2. bins holding rank K1 and rank K2 (1-based, from the largest key)
+  // 2. bins holding rank K1 and rank K2 (1-based, from the largest key),
+  // found by wave 0 (the other waves wait at the barrier, leaving it the
+  // whole SIMD)
   if (wave == 0) {
     uint32_t c[4];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) c[j] = rs.hist[0][4 * lane + j];
+    for (int j = 0; j < 4; ++j) c[j] = rs.hist[4 * lane + j];
     uint32_t above = wave_excl_suffix(c[0] + c[1] + c[2] + c[3]);
+    int s1 = -1, s2 = -1;
+    uint32_t x1 = 0u, x2 = 0u;
 #pragma unroll
     for (int j = 3; j >= 0; --j) {
-      if (K1 > 0 && above < K1 && K1 <= above + c[j]) {
-        rs.sel[0] = 4 * lane + j;
-        rs.sel[1] = (int32_t)above;
-      }
-      if (K2 > 0 && above < K2 && K2 <= above + c[j]) {
-        rs.sel[2] = 4 * lane + j;
-        rs.sel[3] = (int32_t)above;
-      }
+      if (K1 > 0 && above < K1 && K1 <= above + c[j]) { s1 = 4 * lane + j; x1 = above; }
+      if (K2 > 0 && above < K2 && K2 <= above + c[j]) { s2 = 4 * lane + j; x2 = above; }
       above += c[j];
     }
+    int b, ab;
+    uint32_t v;
+    wave_pick(s1, x1, b, v);
+    ab = (int)v;
+    if (lane == 0) { rs.sel[0] = b; rs.sel[1] = ab; }
+    wave_pick(s2, x2, b, v);
+    ab = (int)v;
+    if (lane == 0) { rs.sel[2] = b; rs.sel[3] = ab; }
   }
   __syncthreads();
 
@@ -432,46 +505,51 @@ __device__ __forceinline__ void rank_piece(const GemvArgs& a, RankShared& rs, in
   const int b2 = rs.sel[2];
 #pragma unroll
   for (int i = 0; i < E; ++i) {
-    if (i >= nv) continue;
     const uint32_t k = rawbits(xr, i) & 0x7FFFu;
-    const int hb = (int)(k >> 7);
+    const int hb = i < nv ? (int)(k >> 7) : 256;
     if (hb == b1) atomicAdd(&rs.sub[0][k & 127u], 1u);
     if (hb == b2) atomicAdd(&rs.sub[1][k & 127u], 1u);
   }
   __syncthreads();
+  // boundary keys t (kAboveAll when the tier is empty) and quotas q: the
+  // number of entries equal to t that are kept; found by wave 0
   if (wave == 0) {
 #pragma unroll
     for (int r = 0; r < 2; ++r) {
       const int b = r == 0 ? b1 : b2;
       const uint32_t K = r == 0 ? K1 : K2;
-      if (b < 0) continue;
-      const uint32_t c0 = rs.sub[r][2 * lane], c1 = rs.sub[r][2 * lane + 1];
-      uint32_t above = (uint32_t)rs.sel[1 + 2 * r] + wave_excl_suffix(c0 + c1);
-      if (above < K && K <= above + c1) {
-        rs.sel[4 + 2 * r] = (b << 7) | (2 * lane + 1);
-        rs.sel[5 + 2 * r] = (int32_t)(K - above);
+      int key = (int)kAboveAll;
+      uint32_t quota = 0u;
+      if (b >= 0) {  // wave-uniform
+        const uint32_t c0 = rs.sub[r][2 * lane], c1 = rs.sub[r][2 * lane + 1];
+        uint32_t above = (uint32_t)rs.sel[1 + 2 * r] + wave_excl_suffix(c0 + c1);
+        int sk = -1;
+        uint32_t sq = 0u;
+        if (above < K && K <= above + c1) { sk = (b << 7) | (2 * lane + 1); sq = K - above; }
+        above += c1;
+        if (above < K && K <= above + c0) { sk = (b << 7) | (2 * lane); sq = K - above; }
+        wave_pick(sk, sq, key, quota);
       }
-      above += c1;
-      if (above < K && K <= above + c0) {
-        rs.sel[4 + 2 * r] = (b << 7) | (2 * lane);
-        rs.sel[5 + 2 * r] = (int32_t)(K - above);
+      if (lane == 0) {
+        rs.sel[4 + 2 * r] = key;
+        rs.sel[5 + 2 * r] = (int32_t)quota;
       }
     }
   }
   __syncthreads();
-
-  // 4. positions
   const uint32_t t1 = (uint32_t)rs.sel[4], q1 = (uint32_t)rs.sel[5];
   const uint32_t t2 = (uint32_t)rs.sel[6], q2 = (uint32_t)rs.sel[7];
+
+  // 4. positions
   uint32_t c[4] = {0u, 0u, 0u, 0u};
 #pragma unroll
   for (int i = 0; i < E; ++i) {
-    if (i >= nv) continue;
     const uint32_t k = rawbits(xr, i) & 0x7FFFu;
-    c[0] += k > t1;
-    c[1] += k == t1;
-    c[2] += k > t2;
-    c[3] += k == t2;
+    const bool ok = i < nv;
+    c[0] += ok && k > t1;
+    c[1] += ok && k == t1;
+    c[2] += ok && k > t2;
+    c[3] += ok && k == t2;
   }
   uint32_t in[4];
 #pragma unroll
@@ -481,39 +559,50 @@ __device__ __forceinline__ void rank_piece(const GemvArgs& a, RankShared& rs, in
     for (int j = 0; j < 4; ++j) rs.scan[j][wave] = in[j];
   }
   __syncthreads();
-  uint32_t g1 = in[0] - c[0], e1r = in[1] - c[1], g2 = in[2] - c[2], e2r = in[3] - c[3];
-  for (int w = 0; w < wave; ++w) {
-    g1 += rs.scan[0][w];
-    e1r += rs.scan[1][w];
-    g2 += rs.scan[2][w];
-    e2r += rs.scan[3][w];
-  }
+  // totals of the waves before this one: lanes 0..7 hold the wave totals,
+  // a lane scan gives their prefixes, lane `wave` holds this wave's
+  uint32_t pre[4];
 #pragma unroll
-  for (int i = 0; i < E; ++i) {
-    if (i >= nv) continue;
-    const uint32_t k = rawbits(xr, i) & 0x7FFFu;
-    const bool in_f = k > t1 || (k == t1 && e1r < q1);
-    const bool in_fa = k > t2 || (k == t2 && e2r < q2);
-    if (in_fa) {
-      const int fpos = (int)(g1 + min(e1r, q1));          // F entries before this one
-      const int apos = (int)(g2 + min(e2r, q2)) - fpos;   // A entries before this one
-      const int j = base + i;
-      int slot = -1;
-      if (in_f && fpos >= f0 && fpos < f1) slot = fpos - f0;
-      if (!in_f && apos >= a0 && apos < a1) slot = (f1 - f0) + (apos - a0);
-      if (slot >= 0) {
-        lidx[slot] = j;
-        lx[slot] = h2f(rawbits(xr, i));
-        if (write_lists) {
-          if (in_f) a.out_full_idx[fpos] = j;
-          else a.out_approx_idx[apos] = j;
+  for (int j = 0; j < 4; ++j) {
+    const uint32_t wt = lane < kWaves ? rs.scan[j][lane] : 0u;
+    pre[j] = (uint32_t)__builtin_amdgcn_readlane((int)(wave_incl_scan(wt) - wt), wave);
+  }
+  uint32_t g1 = pre[0] + in[0] - c[0], e1r = pre[1] + in[1] - c[1];
+  uint32_t g2 = pre[2] + in[2] - c[2], e2r = pre[3] + in[3] - c[3];
+  // This thread's F positions [fs, fe) and A positions [as, ae); only
+  // threads whose positions meet the piece place entries.
+  const int fs = (int)(g1 + min(e1r, q1));
+  const int fe = (int)(g1 + c[0] + min(e1r + c[1], q1));
+  const int as = (int)(g2 + min(e2r, q2)) - fs;
+  const int ae = (int)(g2 + c[2] + min(e2r + c[3], q2)) - fe;
+  if ((fs < f1 && fe > f0) || (as < a1 && ae > a0)) {
+#pragma unroll
+    for (int i = 0; i < E; ++i) {
+      if (i >= nv) continue;
+      const uint32_t k = rawbits(xr, i) & 0x7FFFu;
+      const bool in_f = k > t1 || (k == t1 && e1r < q1);
+      const bool in_fa = k > t2 || (k == t2 && e2r < q2);
+      if (in_fa) {
+        const int fpos = (int)(g1 + min(e1r, q1));          // F entries before this one
+        const int apos = (int)(g2 + min(e2r, q2)) - fpos;   // A entries before this one
+        const int j = base + i;
+        int slot = -1;
+        if (in_f && fpos >= f0 && fpos < f1) slot = fpos - f0;
+        if (!in_f && apos >= a0 && apos < a1) slot = (f1 - f0) + (apos - a0);
+        if (slot >= 0) {
+          lidx[slot] = j;
+          lx[slot] = h2f(rawbits(xr, i));
+          if (write_lists) {
+            if (in_f) a.out_full_idx[fpos] = j;
+            else a.out_approx_idx[apos] = j;
+          }
         }
       }
+      g1 += k > t1;
+      e1r += k == t1;
+      g2 += k > t2;
+      e2r += k == t2;
     }
-    g1 += k > t1;
-    e1r += k == t1;
-    g2 += k > t2;
-    e2r += k == t2;
   }
   __syncthreads();
 }
@@ -625,19 +714,18 @@ __global__ __launch_bounds__(kGemvThreads) void gemv_kernel(GemvArgs a) {
     }
     __syncthreads();
     if (!last_flag) return;
-    // partials are added in split order, 16 loads in flight
+    // partials are added in split order; the loads of up to 32 splits are
+    // issued together (clamped to valid addresses, unused ones not added)
     p = 0.0f;
-    const bool ok = r < a.rows;
-    for (int s0 = 0; s0 < a.n_splits; s0 += 16) {
-      float v[16];
+    const int64_t rr = min(r, a.rows - 1);
+    for (int s0 = 0; s0 < a.n_splits; s0 += 32) {
+      float v[32];
 #pragma unroll
-      for (int u = 0; u < 16; ++u)
-        v[u] = (ok && s0 + u < a.n_splits)
-                   ? __hip_atomic_load(&part[(s0 + u) * rows + r], __ATOMIC_RELAXED,
-                                       __HIP_MEMORY_SCOPE_AGENT)
-                   : 0.0f;
+      for (int u = 0; u < 32; ++u)
+        v[u] = __hip_atomic_load(&part[(int64_t)min(s0 + u, a.n_splits - 1) * rows + rr],
+                                 __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 #pragma unroll
-      for (int u = 0; u < 16; ++u)
+      for (int u = 0; u < 32; ++u)
         if (s0 + u < a.n_splits) p += v[u];
     }
   }
