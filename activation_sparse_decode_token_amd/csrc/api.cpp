@@ -59,6 +59,10 @@ int validate_matrix(const spax_matrix* W) {
   if (W->layout != SPAX_LAYOUT_PLAIN && W->layout != SPAX_LAYOUT_GLU_INTERLEAVED)
     return SPAX_EINVAL;
   if (W->layout == SPAX_LAYOUT_GLU_INTERLEAVED && W->rows % (2 * kGroup)) return SPAX_EINVAL;
+  // the product addresses each tier with 32-bit offsets
+  if (col_bytes(W->full_fmt, W->rows) * W->cols >= (int64_t(1) << 31) ||
+      col_bytes(W->approx_fmt, W->rows) * W->cols >= (int64_t(1) << 31))
+    return SPAX_EINVAL;
   if (!W->full_data) return SPAX_ENULL;
   if (W->full_fmt == kInt4 && !W->full_scales) return SPAX_ENULL;
   if (W->approx_fmt != kNone && (!W->approx_codes || !W->approx_scales)) return SPAX_ENULL;
@@ -200,6 +204,11 @@ int run_product(const spax_matrix* W, const uint16_t* x, const int32_t* fidx, in
   a.full_sstride = fsn;
   a.approx_stride = ab;
   a.approx_sstride = asn;
+  // bytes the product may read from each tier (the staging holds the
+  // selected columns in list order)
+  const bool staged = W->residency == SPAX_RES_HOST_PINNED;
+  a.full_bytes = (uint32_t)(fb * (staged ? kf : W->cols));
+  a.approx_bytes = (uint32_t)(ab * (staged ? ka : W->cols));
 
   if (W->residency == SPAX_RES_DEVICE) {
     a.full_base = static_cast<const uint8_t*>(W->full_data);

@@ -62,20 +62,27 @@ __device__ __forceinline__ float b2f(uint32_t v, int byte) {
   return (float)((v >> (8 * byte)) & 0xFFu);
 }
 
-// Buffer resource of one column: a wave-uniform base in scalar registers
-// (pinned with readfirstlane so no lane offset is folded into it). Loads
-// through it take one shared 32-bit lane offset instead of a 64-bit address
-// per lane and load. Dword 3 selects 32-bit raw access on gfx9-family parts.
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t column_rsrc(const uint8_t* p) {
-  const uint64_t v = reinterpret_cast<uint64_t>(p);
-  const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)v);
-  const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(v >> 32));
-  void* base = reinterpret_cast<void*>(((uint64_t)hi << 32) | lo);
-  return __builtin_amdgcn_make_buffer_rsrc(base, (short)0, 0x7FFFFFFF, 0x00020000);
+// Buffer resource of one tier of a matrix: a scalar base and size. A
+// column's load adds the column offset as the 32-bit scalar soffset and the
+// lane's part as one shared 32-bit vector offset, so each load costs one
+// scalar register instead of a 64-bit address per lane. Reads past the tier
+// return 0 instead of touching memory. Dword 3 selects 32-bit raw access on
+// gfx9-family parts. Tier sizes are below 2^31 bytes (checked on the host).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t tier_rsrc(const uint8_t* p, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(p), (short)0, (int)bytes,
+                                           0x00020000);
 }
 
 template <int FMT>
 struct Tier;
+
+// Opaque to the optimiser: keeps the byte-wise code extraction below from
+// being folded into per-value bit-field extracts, so each value is one
+// v_cvt_f32_ubyteN.
+__device__ __forceinline__ uint32_t opaque(uint32_t v) {
+  asm volatile("" : "+v"(v));
+  return v;
+}
 
 template <>
 struct Tier<kFp16> {
@@ -85,18 +92,19 @@ struct Tier<kFp16> {
   static __device__ __forceinline__ uint32_t offset(int row0, int lane) {
     return 2u * (uint32_t)(row0 + 8 * lane);
   }
-  static __device__ __forceinline__ V load(__amdgpu_buffer_rsrc_t col, uint32_t off) {
-    return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(col, off, 0, 0));
+  static __device__ __forceinline__ V load(__amdgpu_buffer_rsrc_t t, uint32_t off, uint32_t col) {
+    return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(t, off, col, 0));
   }
-  static __device__ __forceinline__ void fma(float (&acc)[8], float&, V v, float xs, float) {
-    acc[0] = fmaf(h2f(v.x & 0xFFFFu), xs, acc[0]);
-    acc[1] = fmaf(h2f(v.x >> 16), xs, acc[1]);
-    acc[2] = fmaf(h2f(v.y & 0xFFFFu), xs, acc[2]);
-    acc[3] = fmaf(h2f(v.y >> 16), xs, acc[3]);
-    acc[4] = fmaf(h2f(v.z & 0xFFFFu), xs, acc[4]);
-    acc[5] = fmaf(h2f(v.z >> 16), xs, acc[5]);
-    acc[6] = fmaf(h2f(v.w & 0xFFFFu), xs, acc[6]);
-    acc[7] = fmaf(h2f(v.w >> 16), xs, acc[7]);
+  // f = x_j
+  static __device__ __forceinline__ void fma(float (&acc)[8], float&, V v, float f) {
+    acc[0] = fmaf(h2f(v.x & 0xFFFFu), f, acc[0]);
+    acc[1] = fmaf(h2f(v.x >> 16), f, acc[1]);
+    acc[2] = fmaf(h2f(v.y & 0xFFFFu), f, acc[2]);
+    acc[3] = fmaf(h2f(v.y >> 16), f, acc[3]);
+    acc[4] = fmaf(h2f(v.z & 0xFFFFu), f, acc[4]);
+    acc[5] = fmaf(h2f(v.z >> 16), f, acc[5]);
+    acc[6] = fmaf(h2f(v.w & 0xFFFFu), f, acc[6]);
+    acc[7] = fmaf(h2f(v.w >> 16), f, acc[7]);
   }
 };
 
@@ -107,26 +115,26 @@ struct Tier<kInt4> {
   static __device__ __forceinline__ uint32_t offset(int row0, int lane) {
     return (uint32_t)(row0 + 8 * lane) / 2u;
   }
-  static __device__ __forceinline__ V load(__amdgpu_buffer_rsrc_t col, uint32_t off) {
-    return __builtin_amdgcn_raw_buffer_load_b32(col, off, 0, 0);
+  static __device__ __forceinline__ V load(__amdgpu_buffer_rsrc_t t, uint32_t off, uint32_t col) {
+    return __builtin_amdgcn_raw_buffer_load_b32(t, off, col, 0);
   }
   // Rows 2b and 2b+1 sit in the low and high nibble of byte b, as
   // two's-complement q; flipping each nibble's sign bit gives u = q + 8.
-  static __device__ __forceinline__ void fma(float (&acc)[8], float& corr, V v, float xs,
-                                             float scale) {
-    const float c = xs * scale;  // exact: product of two fp16 values
-    corr = fmaf(8.0f, c, corr);
+  // f = x_j * s_{j,g} (exact: a product of two fp16 values); the offset 8 f
+  // is taken off through corr.
+  static __device__ __forceinline__ void fma(float (&acc)[8], float& corr, V v, float f) {
+    corr = fmaf(8.0f, f, corr);
     v ^= 0x88888888u;
-    const uint32_t lo = v & 0x0F0F0F0Fu;
-    const uint32_t hi = (v >> 4) & 0x0F0F0F0Fu;
-    acc[0] = fmaf(c, b2f(lo, 0), acc[0]);
-    acc[1] = fmaf(c, b2f(hi, 0), acc[1]);
-    acc[2] = fmaf(c, b2f(lo, 1), acc[2]);
-    acc[3] = fmaf(c, b2f(hi, 1), acc[3]);
-    acc[4] = fmaf(c, b2f(lo, 2), acc[4]);
-    acc[5] = fmaf(c, b2f(hi, 2), acc[5]);
-    acc[6] = fmaf(c, b2f(lo, 3), acc[6]);
-    acc[7] = fmaf(c, b2f(hi, 3), acc[7]);
+    const uint32_t lo = opaque(v & 0x0F0F0F0Fu);
+    const uint32_t hi = opaque((v >> 4) & 0x0F0F0F0Fu);
+    acc[0] = fmaf(f, b2f(lo, 0), acc[0]);
+    acc[1] = fmaf(f, b2f(hi, 0), acc[1]);
+    acc[2] = fmaf(f, b2f(lo, 1), acc[2]);
+    acc[3] = fmaf(f, b2f(hi, 1), acc[3]);
+    acc[4] = fmaf(f, b2f(lo, 2), acc[4]);
+    acc[5] = fmaf(f, b2f(hi, 2), acc[5]);
+    acc[6] = fmaf(f, b2f(lo, 3), acc[6]);
+    acc[7] = fmaf(f, b2f(hi, 3), acc[7]);
   }
 };
 
@@ -137,212 +145,141 @@ struct Tier<kInt2> {
   static __device__ __forceinline__ uint32_t offset(int row0, int lane) {
     return (uint32_t)(row0 + 8 * lane) / 4u;
   }
-  static __device__ __forceinline__ V load(__amdgpu_buffer_rsrc_t col, uint32_t off) {
-    return __builtin_amdgcn_raw_buffer_load_b16(col, off, 0, 0);
+  static __device__ __forceinline__ V load(__amdgpu_buffer_rsrc_t t, uint32_t off, uint32_t col) {
+    return __builtin_amdgcn_raw_buffer_load_b16(t, off, col, 0);
   }
-  // Row 4b + r sits in bits 2r..2r+1 of byte b; masking leaves u * 4^r, so
-  // the factor is scaled by 4^-r (exact).
-  static __device__ __forceinline__ void fma(float (&acc)[8], float& corr, V v, float xs,
-                                             float scale) {
-    const float c = xs * scale;
-    corr = fmaf(1.5f, c, corr);
-    const uint32_t m0 = v & 0x0303u, m1 = v & 0x0C0Cu, m2 = v & 0x3030u, m3 = v & 0xC0C0u;
-    const float c1 = c * 0.25f, c2 = c * 0.0625f, c3 = c * 0.015625f;
-    acc[0] = fmaf(c, b2f(m0, 0), acc[0]);
-    acc[4] = fmaf(c, b2f(m0, 1), acc[4]);
-    acc[1] = fmaf(c1, b2f(m1, 0), acc[1]);
-    acc[5] = fmaf(c1, b2f(m1, 1), acc[5]);
-    acc[2] = fmaf(c2, b2f(m2, 0), acc[2]);
-    acc[6] = fmaf(c2, b2f(m2, 1), acc[6]);
-    acc[3] = fmaf(c3, b2f(m3, 0), acc[3]);
-    acc[7] = fmaf(c3, b2f(m3, 1), acc[7]);
+  // Row 4b + r sits in bits 2r..2r+1 of byte b (two bytes per lane); each
+  // 2-bit field is moved to the bottom of its byte and converted. The
+  // offset 1.5 f is taken off through corr.
+  static __device__ __forceinline__ void fma(float (&acc)[8], float& corr, V v, float f) {
+    corr = fmaf(1.5f, f, corr);
+    const uint32_t m0 = opaque(v & 0x0303u);
+    const uint32_t m1 = opaque((v >> 2) & 0x0303u);
+    const uint32_t m2 = opaque((v >> 4) & 0x0303u);
+    const uint32_t m3 = opaque((v >> 6) & 0x0303u);
+    acc[0] = fmaf(f, b2f(m0, 0), acc[0]);
+    acc[4] = fmaf(f, b2f(m0, 1), acc[4]);
+    acc[1] = fmaf(f, b2f(m1, 0), acc[1]);
+    acc[5] = fmaf(f, b2f(m1, 1), acc[5]);
+    acc[2] = fmaf(f, b2f(m2, 0), acc[2]);
+    acc[6] = fmaf(f, b2f(m2, 1), acc[6]);
+    acc[3] = fmaf(f, b2f(m3, 0), acc[3]);
+    acc[7] = fmaf(f, b2f(m3, 1), acc[7]);
   }
 };
 
-// Per-lane metadata of one 64-column batch of a tier: lane l holds the
-// column index and activation of batch position l and, for code tiers, the
-// tile's four group scales of that column (groups 0,1 in sc01, 2,3 in sc23).
-struct Meta {
-  int idx;
-  uint32_t xb;  // fp16 bits (global modes) or fp32 bits (rank mode)
-  uint32_t g[4];  // raw scales as loaded (code tiers)
-  uint32_t sc01, sc23;  // packed by pack_scales once the round's loads are issued
+// Metadata of one wave's current 64-column batch of one tier, in LDS: the
+// column (stored index, or staging position) and the factor each lane
+// multiplies that column by -- x_j for fp16 columns, x_j * s_{j,g} for code
+// columns, one per 128-row group g of the tile.
+struct WaveMeta {
+  int32_t col[64];
+  float fac[64][4];
 };
 
+// Fill the batch's metadata: lane l takes batch position p + l.
+//   kListGlobal: idx = global index list, x = global fp16 activations;
+//   kListStaged: column = list position (staging), x via the index list;
+//   kListRank:   lidx / lx = this workgroup's list piece in LDS.
 template <int FMT, int MODE>
-__device__ __forceinline__ Meta load_meta(const uint16_t* __restrict__ scales, int64_t sstride,
-                                          const int32_t* __restrict__ idx,
+__device__ __forceinline__ void fill_meta(WaveMeta& wm, const uint16_t* __restrict__ scales,
+                                          int64_t sstride, const int32_t* __restrict__ idx,
                                           const uint16_t* __restrict__ x, const int32_t* lidx,
                                           const float* lx, int p, int cnt, int row0, int ngrp,
                                           int lane) {
-  Meta m{0, 0u, {0u, 0u, 0u, 0u}, 0u, 0u};
-  if (cnt <= 0) return m;
-  // lanes past the batch repeat its first position (in range, never used)
-  const int q = p + (lane < cnt ? lane : 0);
-  if constexpr (MODE == kListRank) {
-    m.idx = lidx[q];
-    m.xb = __float_as_uint(lx[q]);
-  } else {
-    m.idx = idx[q];
-    m.xb = x[m.idx];
-  }
-  if constexpr (FMT == kInt4 || FMT == kInt2) {
-    // a ragged last tile has fewer groups: their slots repeat its last group
-    // (never used, since lanes past the last row take group 0's rows), so
-    // the four loads are unconditional and issue back to back
-    const int64_t col = MODE == kListStaged ? (int64_t)q : (int64_t)m.idx;
-    const uint16_t* sp = scales + col * sstride + (row0 >> 7);
-    const int gl = ngrp - 1;
-    m.g[0] = sp[0];
-    m.g[1] = sp[min(1, gl)];
-    m.g[2] = sp[min(2, gl)];
-    m.g[3] = sp[min(3, gl)];
-  }
-  return m;
-}
-
-__device__ __forceinline__ void pack_scales(Meta& m) {
-  // The empty volatile asm makes the raw scales opaque, so the packing (which
-  // waits for the scale loads) is not hoisted out of the round loop ahead of
-  // the round's weight loads.
-  asm volatile("" : "+v"(m.g[0]), "+v"(m.g[1]), "+v"(m.g[2]), "+v"(m.g[3]));
-  m.sc01 = m.g[0] | (m.g[1] << 16);
-  m.sc23 = m.g[2] | (m.g[3] << 16);
-}
-
-template <int MODE>
-__device__ __forceinline__ float meta_x(const Meta& m, int c) {
-  const uint32_t b = (uint32_t)__builtin_amdgcn_readlane((int)m.xb, c);
-  if constexpr (MODE == kListRank) return __uint_as_float(b);
-  else return h2f(b);
-}
-
-// This lane's group scale of batch column c (hi_pair: groups 2,3; sh: 0 or 16).
-__device__ __forceinline__ float meta_scale(const Meta& m, int c, bool hi_pair, uint32_t sh) {
-  const uint32_t a01 = (uint32_t)__builtin_amdgcn_readlane((int)m.sc01, c);
-  const uint32_t a23 = (uint32_t)__builtin_amdgcn_readlane((int)m.sc23, c);
-  return h2f(((hi_pair ? a23 : a01) >> sh) & 0xFFFFu);
-}
-
-template <int MODE>
-__device__ __forceinline__ int meta_col(const Meta& m, int p, int c) {
-  return MODE == kListStaged ? p + c : __builtin_amdgcn_readlane(m.idx, c);
-}
-
-// Multiply-add U loaded columns of one tier; slots u >= n were loaded from
-// a valid column and are added with a zero activation.
-template <typename T, int U, int MODE, bool CODE>
-__device__ __forceinline__ void consume(float (&acc)[8], float& corr, const typename T::V (&v)[U],
-                                        const Meta& m, int c0, int n, bool hi_pair, uint32_t sh) {
-#pragma unroll
-  for (int u = 0; u < U; ++u) {
-    const int c = c0 + (u < n ? u : 0);
-    const float xs = u < n ? meta_x<MODE>(m, c) : 0.0f;
-    const float sc = CODE ? meta_scale(m, c, hi_pair, sh) : 0.0f;
-    T::fma(acc, corr, v[u], xs, sc);
-  }
-}
-
-// Stream this wave's full-tier list positions [f_lo, f_hi) and approx-tier
-// positions [a_lo, a_hi) for its rows. Each round issues the loads of UF
-// full columns and UA code columns before any of them is consumed, so a wave
-// keeps both tiers' bytes in flight together. Slots past a tier's share
-// reload a valid column and add it times zero, which keeps every load
-// unconditional: the compiler then issues a round's loads back to back.
-//   kListGlobal: idx lists and x in device memory;
-//   kListStaged: columns staged in list order (column = position);
-//   kListRank:   lidx / lx = this workgroup's list piece in LDS.
-template <int FF, int AF, int MODE>
-__device__ __forceinline__ void stream_tiers(float (&acc)[8], float& corr, const GemvArgs& a,
-                                             const int32_t* lidx, const float* lx, int f_lo,
-                                             int f_hi, int a_lo, int a_hi, int row0, int lane,
-                                             int ld_lane) {
-  using TF = Tier<FF>;
-  using TA = Tier<AF == kNone ? kInt4 : AF>;
-  constexpr bool kHasA = AF != kNone;
-  constexpr int UF = TF::U;
-  // equal rounds for equal column counts when the full tier is fp16
-  constexpr int UA = FF == kFp16 ? 8 : TA::U;
-  const int grp = ld_lane >> 4;  // this lane's group in the tile
-  const bool hi_pair = grp >= 2;
-  const uint32_t sh = 16u * (uint32_t)(grp & 1);
-  const int ngrp = min(4, (a.rows - row0 + kGroup - 1) / kGroup);
-  // column bases are wave-uniform (buffer resources in scalar registers);
-  // the lane's part of the address is one 32-bit offset per tier
-  const uint32_t off_f = TF::offset(row0, ld_lane);
-  const uint32_t off_a = TA::offset(row0, ld_lane);
-  if constexpr (!kHasA) a_hi = a_lo;
-  int pf = f_lo, pa = a_lo;
-  while (pf < f_hi || pa < a_hi) {
-    const int nbf = max(0, min(64, f_hi - pf)), nba = max(0, min(64, a_hi - pa));
-    Meta mf = load_meta<FF, MODE>(a.full_scales, a.full_sstride, a.full_idx, a.x, lidx, lx, pf,
-                                  nbf, row0, ngrp, lane);
-    Meta ma{0, 0u, {0u, 0u, 0u, 0u}, 0u, 0u};
-    if constexpr (kHasA)
-      ma = load_meta<AF, MODE>(a.approx_scales, a.approx_sstride, a.approx_idx, a.x, lidx, lx,
-                               pa, nba, row0, ngrp, lane);
-    const int rounds = max((nbf + UF - 1) / UF, kHasA ? (nba + UA - 1) / UA : 0);
-    // Double-buffered rounds: the loads of round r + 1 are issued before
-    // round r is consumed, so a wave always has a round in flight. Each step
-    // issues and consumes in one straight-line block, so the wait before the
-    // consumption counts only the loads issued just before it.
-    typename TF::V vf0[UF], vf1[UF];
-    typename TA::V va0[kHasA ? UA : 1], va1[kHasA ? UA : 1];
-    auto issue = [&](int r, typename TF::V (&vf)[UF], typename TA::V (&va)[kHasA ? UA : 1]) {
-      const int cf = r * UF, ca = r * UA;
-      const int nf = min(UF, nbf - cf), na = min(UA, nba - ca);
-#pragma unroll
-      for (int u = 0; u < UF; ++u) {
-        // an exhausted tier reloads a valid column of its batch
-        const int c = min(cf + (u < nf ? u : 0), 63);
-        vf[u] = TF::load(
-            column_rsrc(a.full_base + (int64_t)meta_col<MODE>(mf, pf, c) * a.full_stride), off_f);
-      }
-      if constexpr (kHasA) {
-#pragma unroll
-        for (int u = 0; u < UA; ++u) {
-          const int c = min(ca + (u < na ? u : 0), 63);
-          va[u] = TA::load(
-              column_rsrc(a.approx_base + (int64_t)meta_col<MODE>(ma, pa, c) * a.approx_stride),
-              off_a);
-        }
-      }
-      // keep the scale packing (which waits for the scale loads) behind the
-      // weight loads so the two round trips overlap
-      __builtin_amdgcn_sched_barrier(0);
-    };
-    auto use = [&](int r, const typename TF::V (&vf)[UF],
-                   const typename TA::V (&va)[kHasA ? UA : 1]) {
-      const int cf = r * UF, ca = r * UA;
-      const int nf = min(UF, nbf - cf), na = min(UA, nba - ca);
-      if constexpr (FF != kFp16) pack_scales(mf);
-      if constexpr (kHasA) pack_scales(ma);
-      consume<TF, UF, MODE, FF != kFp16>(acc, corr, vf, mf, cf, nf, hi_pair, sh);
-      if constexpr (kHasA) consume<TA, UA, MODE, true>(acc, corr, va, ma, ca, na, hi_pair, sh);
-    };
-    if (rounds > 0) {
-      issue(0, vf0, va0);
-      for (int r = 0;;) {
-        if (r + 1 < rounds) {
-          issue(r + 1, vf1, va1);
-          use(r, vf0, va0);
-        } else {
-          use(r, vf0, va0);
-          break;
-        }
-        ++r;
-        if (r + 1 < rounds) {
-          issue(r + 1, vf0, va0);
-          use(r, vf1, va1);
-        } else {
-          use(r, vf1, va1);
-          break;
-        }
-        ++r;
-      }
+  if (lane < cnt) {
+    const int q = p + lane;
+    int j;
+    float xv;
+    if constexpr (MODE == kListRank) {
+      j = lidx[q];
+      xv = lx[q];
+    } else {
+      j = idx[q];
+      xv = h2f(x[j]);
     }
-    pf += nbf;
-    pa += nba;
+    const int col = MODE == kListStaged ? q : j;
+    wm.col[lane] = col;
+    if constexpr (FMT == kFp16) {
+      wm.fac[lane][0] = xv;
+    } else {
+      // a ragged last tile has fewer groups; their slots are never read
+      // (lanes past the last row take group 0's rows)
+      const uint16_t* sp = scales + (int64_t)col * sstride + (row0 >> 7);
+      const int gl = ngrp - 1;
+#pragma unroll
+      for (int g = 0; g < 4; ++g) wm.fac[lane][g] = xv * h2f(sp[min(g, gl)]);
+    }
+  }
+  // the batch's slots are read by every lane of this wave below
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// Stream this wave's list positions [p_lo, p_hi) of one tier for its rows.
+// Rounds of U columns are double-buffered: the loads of round r + 1 are
+// issued before round r is consumed, so a wave always has a round in flight.
+// Each step issues and consumes in one straight-line block (the wait before
+// the consumption counts only the loads issued just before it). Slots past
+// the batch reload its last column and add it times zero, which keeps every
+// load unconditional.
+template <int FMT, int MODE>
+__device__ __forceinline__ void stream_tier(float (&acc)[8], float& corr, WaveMeta& wm,
+                                            const uint8_t* base, int64_t stride, uint32_t bytes,
+                                            const uint16_t* scales, int64_t sstride,
+                                            const int32_t* idx, const uint16_t* x,
+                                            const int32_t* lidx, const float* lx, int p_lo,
+                                            int p_hi, int row0, int rows, int lane,
+                                            int ld_lane) {
+  using T = Tier<FMT>;
+  constexpr int U = T::U;
+  constexpr bool kCode = FMT != kFp16;
+  const int gsel = kCode ? (ld_lane >> 4) : 0;  // this lane's group in the tile
+  const int ngrp = min(4, (rows - row0 + kGroup - 1) / kGroup);
+  const uint32_t off = T::offset(row0, ld_lane);
+  const __amdgpu_buffer_rsrc_t rs = tier_rsrc(base, bytes);
+  const uint32_t cstride = (uint32_t)stride;
+  for (int pb = p_lo; pb < p_hi; pb += 64) {
+    const int cnt = min(64, p_hi - pb);
+    fill_meta<FMT, MODE>(wm, scales, sstride, idx, x, lidx, lx, pb, cnt, row0, ngrp, lane);
+    const int rounds = (cnt + U - 1) / U;
+    typename T::V v0[U], v1[U];
+    auto issue = [&](int r, typename T::V (&v)[U]) {
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int c = min(r * U + u, cnt - 1);
+        const uint32_t col = (uint32_t)__builtin_amdgcn_readfirstlane(wm.col[c]);
+        v[u] = T::load(rs, off, col * cstride);
+      }
+    };
+    auto use = [&](int r, const typename T::V (&v)[U]) {
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int c = r * U + u;
+        const float f = c < cnt ? wm.fac[c][gsel] : 0.0f;
+        T::fma(acc, corr, v[u], f);
+      }
+    };
+    issue(0, v0);
+    for (int r = 0;;) {
+      if (r + 1 < rounds) {
+        issue(r + 1, v1);
+        use(r, v0);
+      } else {
+        use(r, v0);
+        break;
+      }
+      ++r;
+      if (r + 1 < rounds) {
+        issue(r + 1, v0);
+        use(r, v1);
+      } else {
+        use(r, v1);
+        break;
+      }
+      ++r;
+    }
   }
 }
 
@@ -631,6 +568,7 @@ __global__ __launch_bounds__(kGemvThreads) void gemv_kernel(GemvArgs a) {
   __shared__ Scratch sm;
   __shared__ int32_t lidx[MODE == kListRank ? kListCap : 1];
   __shared__ float lx[MODE == kListRank ? kListCap : 1];
+  __shared__ WaveMeta wmeta[kWaves];
   __shared__ uint32_t last_flag;
 
   const int t = threadIdx.x;
@@ -669,10 +607,17 @@ __global__ __launch_bounds__(kGemvThreads) void gemv_kernel(GemvArgs a) {
     a_hi = a1;
   }
   {
+    WaveMeta& wm = wmeta[wave];
     const int lf = f_hi - f_lo, la = a_hi - a_lo;
-    stream_tiers<FF, AF, MODE>(acc, corr, a, lidx, lx, f_lo + (lf * wave) / kWaves,
-                               f_lo + (lf * (wave + 1)) / kWaves, a_lo + (la * wave) / kWaves,
-                               a_lo + (la * (wave + 1)) / kWaves, row0, lane, ld_lane);
+    stream_tier<FF, MODE>(acc, corr, wm, a.full_base, a.full_stride, a.full_bytes,
+                          a.full_scales, a.full_sstride, a.full_idx, a.x, lidx, lx,
+                          f_lo + (lf * wave) / kWaves, f_lo + (lf * (wave + 1)) / kWaves, row0,
+                          a.rows, lane, ld_lane);
+    if constexpr (AF != kNone)
+      stream_tier<AF, MODE>(acc, corr, wm, a.approx_base, a.approx_stride, a.approx_bytes,
+                            a.approx_scales, a.approx_sstride, a.approx_idx, a.x, lidx, lx,
+                            a_lo + (la * wave) / kWaves, a_lo + (la * (wave + 1)) / kWaves, row0,
+                            a.rows, lane, ld_lane);
   }
   if constexpr (FF == kInt4 || AF != kNone) {
 #pragma unroll

@@ -42,6 +42,8 @@ struct GemvArgs {
   // Full tier: fp16 columns or int4 codes; column c at full_base + c * full_stride.
   const uint8_t* full_base;
   int64_t full_stride;
+  uint32_t full_bytes;           // bytes of the full tier (< 2^31)
+  uint32_t approx_bytes;         // bytes of the approx codes (< 2^31)
   const uint16_t* full_scales;   // int4 full only; column c at + c * full_sstride
   int64_t full_sstride;          // elements
   // Approx tier codes and scales.

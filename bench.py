@@ -1,9 +1,10 @@
 """Benchmark of the three-tier activation-sparse decode path on one MI355X.
 
-Workload: 7B-shaped attention projections (q, k, v, o, each 4096 x 4096,
-fp16 weights ~ N(0, 0.02), column-major) with an int4 group-128 compressed
-copy, tiers skip / approx / full = 40 / 30 / 30 % of the 4096 inputs, batch 1,
-32 decode tokens of fresh Laplace(0, 1) activations per step.
+Headline workload (no --config): 7B-shaped attention projections (q, k, v, o,
+each 4096 x 4096, fp16 weights ~ N(0, 0.02), column-major) with an int4
+group-128 compressed copy, tiers skip / approx / full = 40 / 30 / 30 % of the
+4096 inputs, batch 1, 32 decode tokens of fresh Laplace(0, 1) activations per
+step.
 
 One step = the whole per-token path for 32 tokens, through spax_layer_step:
     rank h -> tier lists -> tiered product of q, k, v (rows stacked)
@@ -21,17 +22,27 @@ synchronisations. Inputs are resident in HBM before timing starts.
 
 Printed: ONE JSON line with the throughput (effective weight GB/s on the
 algorithmic bytes), microseconds per tiered projection, the roofline of the
-tiered product kernel (event-timed per launch on the launch stream) and the
-CPU oracle timed on a bounded sample of the same workload. The per-launch
-duration of the product kernel comes from graph replays of one group's 32
-launches back to back, timed with events on the launch stream.
+product kernel and the CPU oracle timed on a bounded sample of the same
+workload. The per-launch duration of the product kernel comes from graph
+replays of one group's 32 launches back to back, timed with events on the
+launch stream.
+
+Other workloads (one JSON line each, same keys; no roofline / CPU legs):
+    --config 1   single 1024 x 1024 layer, 50/25/25
+    --config 3   7B SwiGLU FFN (gate/up 11008x4096, down 4096x11008), skip
+                 30 / 50 / 70 %, approx 20 % (three lines)
+    --config 4   32-layer 7B projection stream, 50/25/25, weights in HBM;
+                 with --host the weights sit in pinned host memory and only
+                 the selected columns cross the host link
+    --config 5   70B-shaped FFN, int4 full tier, int2 approx, 50/30/20
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--eager]
-                    [--no-cpu-baseline] [--calib-copy]
+                    [--no-cpu-baseline] [--calib-copy] [--config N] [--host]
 """
 from __future__ import annotations
 
 import argparse
+import dataclasses
 import json
 import os
 import sys
@@ -44,10 +55,7 @@ if ROOT not in sys.path:
 METRIC = ("µs per tiered projection & effective weight GB/s (% of HBM peak), "
           "batch-1 decode")
 HBM_PEAK_GBS = 8000.0
-HIDDEN = 4096
-TOKENS = 32
-SETS = 32
-CONFIG_ID = 2
+PCIE5_X16_GBS = 64.0
 
 
 PMC_SUMMARY = os.path.join(ROOT, "profiles", "gemv_kernel_7b_attention_pmc.txt")
@@ -86,97 +94,200 @@ def log(msg: str) -> None:
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
-def parse():
-    p = argparse.ArgumentParser(description=__doc__.split("\n")[0])
-    p.add_argument("--gpus", type=int, default=1)
-    p.add_argument("--steps", type=int, default=50)
-    p.add_argument("--warmup", type=int, default=5)
-    p.add_argument("--sets", type=int, default=SETS,
-                   help="distinct weight sets rotated over the tokens (default 32)")
-    p.add_argument("--eager", action="store_true",
-                   help="launch every kernel from Python instead of replaying a graph")
-    p.add_argument("--no-cpu-baseline", action="store_true")
-    p.add_argument("--calib-copy", action="store_true",
-                   help="also run one plain 256 MiB device copy (counter calibration)")
-    return p.parse_args()
+# ---------------------------------------------------------------- workloads
+
+@dataclasses.dataclass
+class Spec:
+    """One benchmark workload: which groups a layer has, their shapes and
+    formats, the tier split, how many distinct weight sets rotate, and how
+    many (token, layer) layer-steps one step runs."""
+    config: int
+    name: str
+    hidden: int
+    inter: int                 # 0: no FFN groups
+    attn: bool                 # q,k,v + o groups
+    o_only: bool = False       # a single plain projection (the o slot)
+    full_fmt: str = "fp16"
+    approx_fmt: str = "int4"
+    split: tuple = (50, 25, 25)    # skip / approx / full %
+    std: float = 0.02
+    sets: int = 32
+    tokens: int = 32
+    layers_per_token: int = 1  # distinct sets each token walks through
+    host: bool = False
+
+    def describe(self) -> str:
+        s, a, f = self.split
+        return (f"{self.name}: skip/approx/full {s}/{a}/{f} %, {self.full_fmt} full + "
+                f"{self.approx_fmt} g128 approx, W ~N(0,{self.std}) column-major, "
+                f"x ~Laplace(0,1) fp16, batch 1, {self.tokens} tokens x "
+                f"{self.layers_per_token} layer(s) per step over {self.sets} weight sets"
+                + (", weights in pinned host memory" if self.host else ""))
+
+
+def headline_spec() -> Spec:
+    return Spec(2, "7B-shaped attention projections q,k,v,o 4096x4096", 4096, 0, True,
+                split=(40, 30, 30))
+
+
+def specs_for(config: int, host: bool):
+    if config == 1:
+        return [Spec(1, "single linear layer 1024x1024", 1024, 0, False, o_only=True)]
+    if config == 2:
+        return [headline_spec()]
+    if config == 3:
+        return [Spec(3, f"7B-shaped SwiGLU FFN gate/up 11008x4096, down 4096x11008", 4096, 11008,
+                     False, split=(s, 20, 80 - s), sets=16) for s in (30, 50, 70)]
+    if config == 4:
+        if host:
+            return [Spec(4, "32-layer 7B projection stream (4 attn + 3 FFN per layer)", 4096,
+                         11008, True, sets=32, tokens=1, layers_per_token=32, host=True)]
+        return [Spec(4, "32-layer 7B projection stream (4 attn + 3 FFN per layer)", 4096, 11008,
+                     True, sets=32, tokens=4, layers_per_token=32)]
+    if config == 5:
+        return [Spec(5, "70B-shaped FFN gate/up 28672x8192, down 8192x28672", 8192, 28672, False,
+                     full_fmt="int4", approx_fmt="int2", split=(50, 30, 20), std=0.015,
+                     sets=8, tokens=16)]
+    raise SystemExit(f"unknown --config {config}")
+
+
+FMT = {"fp16": 1, "int4": 2, "int2": 3}
 
 
 class Workload:
-    """Device-resident weights, inputs, outputs and lists of one step."""
+    """Device-resident (or pinned-host) weights, inputs, outputs and lists."""
 
-    def __init__(self, sets: int):
+    def __init__(self, spec: Spec):
         import torch
 
         import activation_sparse_decode_token_amd as spax
         import workloads as WL
-        from activation_sparse_decode_token_amd.layouts import build_matrix
+        from activation_sparse_decode_token_amd.layouts import (build_matrix, glu_interleave,
+                                                                stack_rows)
 
-        self.spax = spax
+        self.spax, self.spec = spax, spec
         dev = torch.device("cuda:0")
-        split = WL.CONFIGS[CONFIG_ID].splits[0]
-        self.kf, self.ka = WL.tier_counts(HIDDEN, split)
-        self.sets = sets
-        ks = ([self.kf, self.kf, 0, 0], [self.ka, self.ka, 0, 0])
-        self.layers, self.qkv_only, self.o_only = [], [], []
-        for s in range(sets):
-            q, k, v, o = (WL.weights_fp16_torch(CONFIG_ID, s, m, HIDDEN, HIDDEN, 0.02, dev)
-                          for m in ("q", "k", "v", "o"))
-            stacked = torch.cat([q, k, v], dim=1).contiguous()     # [n, 3*4096]
-            del q, k, v
-            Wqkv = build_matrix(stacked, spax.FMT_FP16, spax.FMT_INT4_G128)
-            Wo = build_matrix(o, spax.FMT_FP16, spax.FMT_INT4_G128)
-            del stacked, o
-            # the attention groups of one decoder layer: rank h -> q, k, v;
-            # rank z -> o (SpAx page, section 5.2 step 1 groups)
-            self.layers.append(spax.Layer.make([Wqkv, Wo, None, None], *ks))
-            self.qkv_only.append(spax.Layer.make([Wqkv, None, None, None], *ks))
-            self.o_only.append(spax.Layer.make([None, Wo, None, None], *ks))
-        torch.cuda.synchronize()
+        H, I = spec.hidden, spec.inter
+        sk, ap, fu = spec.split
+        split = WL.TierSplit(sk, ap, fu)
+        res = spax.RES_HOST_PINNED if spec.host else spax.RES_DEVICE
+        ff, af = FMT[spec.full_fmt], FMT[spec.approx_fmt]
+
+        def gen(s, m, rows, cols):
+            return WL.weights_fp16_torch(spec.config, s, m, rows, cols, spec.std, dev)
+
+        # tier counts per group: QKV, O, GATE_UP, DOWN
+        kq = WL.tier_counts(H, split)
+        kd = WL.tier_counts(I, split) if I else (0, 0)
+        self.k = {0: kq, 1: kq, 2: kq, 3: kd}
+        self.present = [spec.attn, spec.attn or spec.o_only, I > 0, I > 0]
+        kf = [self.k[g][0] if self.present[g] else 0 for g in range(4)]
+        ka = [self.k[g][1] if self.present[g] else 0 for g in range(4)]
+        self.layers, self.single = [], {g: [] for g in range(4)}
+        self.shapes = {}
+        for s in range(spec.sets):
+            mats = [None] * 4
+            if spec.attn:
+                q, k_, v = (gen(s, m, H, H) for m in ("q", "k", "v"))
+                st = stack_rows([q, k_, v])
+                del q, k_, v
+                mats[0] = build_matrix(st, ff, af, residency=res)
+                del st
+            if spec.attn or spec.o_only:
+                o = gen(s, "o" if spec.attn else "w", H, H)
+                mats[1] = build_matrix(o, ff, af, residency=res)
+                del o
+            if I:
+                g_, u_ = gen(s, "gate", I, H), gen(s, "up", I, H)
+                gu = glu_interleave(g_, u_)
+                del g_, u_
+                mats[2] = build_matrix(gu, ff, af, layout=spax.LAYOUT_GLU_INTERLEAVED,
+                                       residency=res)
+                del gu
+                d = gen(s, "down", H, I)
+                mats[3] = build_matrix(d, ff, af, residency=res)
+                del d
+            torch.cuda.synchronize()
+            self.layers.append(spax.Layer.make(mats, kf, ka))
+            for g in range(4):
+                if mats[g] is not None:
+                    only = [None] * 4
+                    only[g] = mats[g]
+                    self.single[g].append(spax.Layer.make(only, kf, ka))
+                    self.shapes[g] = (mats[g].rows, mats[g].cols)
+            if s % 8 == 7 or s == spec.sets - 1:
+                log(f"  {s + 1}/{spec.sets} weight sets built")
         f16, i32 = torch.float16, torch.int32
+        # one input / output slot per (token, layer) layer-step
+        self.slots = spec.tokens * spec.layers_per_token
         self.io = []
-        for t in range(TOKENS):
-            h = WL.laplace_fp16_torch(CONFIG_ID, 0, "h", t, HIDDEN, dev)
-            z = WL.laplace_fp16_torch(CONFIG_ID, 0, "z", t, HIDDEN, dev)
-            F = [torch.empty(self.kf, dtype=i32, device=dev) for _ in range(2)]
-            A = [torch.empty(self.ka, dtype=i32, device=dev) for _ in range(2)]
-            self.io.append(spax.LayerIO.make(
-                h=h, z=z, qkv=torch.empty(3 * HIDDEN, dtype=f16, device=dev),
-                o=torch.empty(HIDDEN, dtype=f16, device=dev),
-                full_idx=(F[0], F[1], None, None), approx_idx=(A[0], A[1], None, None)))
+        for i in range(self.slots):
+            t, l = divmod(i, spec.layers_per_token)
+            vec = lambda nm: WL.laplace_fp16_torch(spec.config, l, nm, t, H, dev)
+            F = [torch.empty(max(1, kf[g]), dtype=i32, device=dev) for g in range(4)]
+            A = [torch.empty(max(1, ka[g]), dtype=i32, device=dev) for g in range(4)]
+            kw = dict(full_idx=tuple(F), approx_idx=tuple(A))
+            if spec.attn:
+                kw.update(h=vec("h"), qkv=torch.empty(3 * H, dtype=f16, device=dev))
+            if spec.attn or spec.o_only:
+                kw.update(z=vec("z"), o=torch.empty(H, dtype=f16, device=dev))
+            if I:
+                kw.update(x=vec("x"), a=torch.empty(I, dtype=f16, device=dev),
+                          down=torch.empty(H, dtype=f16, device=dev))
+            self.io.append(spax.LayerIO.make(**kw))
         wsb = spax.layer_workspace_bytes(self.layers[0])
         self.ws = torch.zeros(wsb, dtype=torch.uint8, device=dev)
         self.ws_bytes = wsb
+        self.copy_stream = torch.cuda.Stream() if spec.host else None
         torch.cuda.synchronize()
 
     # bytes the method must move (selected columns, codes and scales, x,
     # index lists, y) -- see workloads.accounting
-    def gemv_bytes(self):
+    def group_bytes(self, g: int) -> int:
         from workloads.accounting import gemv_algorithmic_bytes
-        qkv = gemv_algorithmic_bytes(3 * HIDDEN, HIDDEN, self.kf, self.ka, "fp16", "int4")
-        o = gemv_algorithmic_bytes(HIDDEN, HIDDEN, self.kf, self.ka, "fp16", "int4")
-        return qkv, o
+        rows, cols = self.shapes[g]
+        kf, ka = self.k[g]
+        b = gemv_algorithmic_bytes(rows, cols, kf, ka, self.spec.full_fmt, self.spec.approx_fmt)
+        if g == 2:          # gate/up writes a = silu(g) * u: half the stored rows
+            b -= rows
+        return b
 
-    def step_bytes(self):
-        qkv, o = self.gemv_bytes()
-        return TOKENS * (qkv + o)
+    def layer_bytes(self) -> int:
+        return sum(self.group_bytes(g) for g in range(4) if self.present[g])
+
+    def step_bytes(self) -> int:
+        return self.slots * self.layer_bytes()
+
+    def projections_per_layer(self) -> int:
+        p = 0
+        if self.spec.attn:
+            p += 4
+        elif self.spec.o_only:
+            p += 1
+        if self.spec.inter:
+            p += 3
+        return p
+
+    def layer_of(self, i: int):
+        t, l = divmod(i, self.spec.layers_per_token)
+        return self.layers[(t * self.spec.layers_per_token + l) % self.spec.sets]
 
     def step(self, stream=None):
-        """Enqueue one step: every token runs the attention groups of the
-        layer whose weights it reads (one fused launch per group)."""
+        """Enqueue one step: every (token, layer) slot runs the layer's groups
+        (one fused launch per group with device-resident weights)."""
         spax = self.spax
-        for t in range(TOKENS):
-            spax.layer_step(self.layers[t % self.sets], self.io[t], self.ws, self.ws_bytes,
-                            compute_stream=stream)
+        for i in range(self.slots):
+            spax.layer_step(self.layer_of(i), self.io[i], self.ws, self.ws_bytes,
+                            compute_stream=stream, copy_stream=self.copy_stream)
 
     def launches(self, group: int):
-        """The product launches of one group (0: q,k,v; 1: o) for every
-        token, enqueued back to back -- one fused launch each."""
+        """The product launches of one group for every slot, back to back."""
         spax = self.spax
-        layers = self.qkv_only if group == 0 else self.o_only
+        layers = self.single[group]
 
         def run(stream):
-            for t in range(TOKENS):
-                spax.layer_step(layers[t % self.sets], self.io[t], self.ws, self.ws_bytes,
+            for i in range(self.slots):
+                spax.layer_step(layers[i % len(layers)], self.io[i], self.ws, self.ws_bytes,
                                 compute_stream=stream)
         return run
 
@@ -205,25 +316,17 @@ def graph_launch_time(run, stream, launches: int, reps: int = 5) -> float:
     return e0.elapsed_time(e1) * 1e-3 / (reps * launches)
 
 
-def gpu_run(args):
+def time_steps(wl: Workload, steps: int, warmup: int, eager: bool):
+    """Warm up, then time exactly `steps` steps between synchronisations.
+    Returns (seconds per step by events, seconds per step by wall clock,
+    mode, stream)."""
     import torch
-
-    import activation_sparse_decode_token_amd as spax
-    spax.lib()  # fails loudly when the HIP library is missing
-    if not torch.cuda.is_available():
-        raise SystemExit("bench.py needs a GPU (torch.cuda.is_available() is False)")
-    log(f"device {torch.cuda.get_device_name(0)}; building {args.sets} weight sets")
-    t0 = time.perf_counter()
-    wl = Workload(args.sets)
-    log(f"weights ready in {time.perf_counter() - t0:.1f} s; "
-        f"k_full={wl.kf} k_approx={wl.ka}")
-
     stream = torch.cuda.Stream()
     graph = None
     with torch.cuda.stream(stream):
         wl.step(stream)                      # eager warm pass (also loads code objects)
         torch.cuda.synchronize()
-        if not args.eager:
+        if not eager:
             graph = torch.cuda.CUDAGraph()
             with torch.cuda.graph(graph, stream=stream):
                 wl.step(stream)
@@ -236,76 +339,47 @@ def gpu_run(args):
             wl.step(stream)
 
     with torch.cuda.stream(stream):
-        for _ in range(args.warmup):
+        for _ in range(warmup):
             run_once()
         torch.cuda.synchronize()
-        log(f"warmup done ({args.warmup} steps, {'eager' if graph is None else 'graph'})")
+        log(f"warmup done ({warmup} steps, {'eager' if graph is None else 'graph'})")
         ev0 = torch.cuda.Event(enable_timing=True)
         ev1 = torch.cuda.Event(enable_timing=True)
         torch.cuda.synchronize()
         w0 = time.perf_counter()
         ev0.record(stream)
-        for _ in range(args.steps):
+        for _ in range(steps):
             run_once()
         ev1.record(stream)
         torch.cuda.synchronize()
         wall = time.perf_counter() - w0
         ms_event = ev0.elapsed_time(ev1)
-    log(f"timed {args.steps} steps: wall {wall * 1e3:.2f} ms, events {ms_event:.2f} ms")
+    log(f"timed {steps} steps: wall {wall * 1e3:.2f} ms, events {ms_event:.2f} ms")
+    return ms_event * 1e-3 / steps, wall / steps, ("graph" if graph is not None else "eager"), stream
 
-    # Per-launch duration of the product kernel, event-timed on its stream:
-    # each group's launches back to back in a graph (host launch cost is
-    # not on the GPU timeline).
-    qkv_b, o_b = wl.gemv_bytes()
-    if graph is not None:
-        t_qkv = graph_launch_time(wl.launches(0), stream, TOKENS)
-        t_o = graph_launch_time(wl.launches(1), stream, TOKENS)
-        avg_us = (t_qkv + t_o) / 2 * 1e6
-        achieved = (qkv_b + o_b) / (t_qkv + t_o) / 1e9
-        log(f"product kernel: qkv {t_qkv * 1e6:.2f} us, o {t_o * 1e6:.2f} us per launch, "
-            f"{achieved:.0f} GB/s on algorithmic bytes")
-    else:
-        t_qkv = t_o = avg_us = achieved = None
-    if args.calib_copy:
-        a = torch.empty(256 << 20, dtype=torch.uint8, device="cuda:0")
-        b = torch.empty_like(a)
-        a.fill_(1)
-        torch.cuda.synchronize()
-        b.copy_(a)
-        torch.cuda.synchronize()
-        log("calibration copy: 268435456 bytes read, 268435456 bytes written")
 
-    sec_step = ms_event * 1e-3 / args.steps
-    step_b = wl.step_bytes()
-    return {
-        "sec_step": sec_step,
-        "wall_step": wall / args.steps,
-        "step_bytes": step_b,
-        "projections": TOKENS * 4,
-        "roofline": None if achieved is None else {
-            "bound": "hbm",
-            "achieved": round(achieved, 1),
-            "peak": HBM_PEAK_GBS,
-            "unit": "GB/s",
-            "frac": round(achieved / HBM_PEAK_GBS, 4),
-            "traffic": measured_traffic(),
-            "kernel": "gemv_kernel: fused tier selection + tiered gather-GEMV "
-                      "(fp16 full, int4 g128 approx)",
-            "avg_launch_us": round(avg_us, 3),
-            "launch_us": {"qkv": round(t_qkv * 1e6, 3), "o": round(t_o * 1e6, 3)},
-            "bytes_per_launch": {"qkv": qkv_b, "o": o_b},
-        },
-        "kf": wl.kf, "ka": wl.ka,
-        "mode": "graph" if graph is not None else "eager",
-    }
+def host_link_peak_gbs() -> float:
+    """Pinned host -> device copy rate of one large contiguous buffer."""
+    import torch
+    n = 1 << 30
+    h = torch.empty(n, dtype=torch.uint8, pin_memory=True)
+    d = torch.empty(n, dtype=torch.uint8, device="cuda:0")
+    d.copy_(h, non_blocking=True)
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(3):
+        d.copy_(h, non_blocking=True)
+    e1.record()
+    torch.cuda.synchronize()
+    return 3 * n / (e0.elapsed_time(e1) * 1e-3) / 1e9
 
 
 def cpu_baseline(kf: int, ka: int, budget_s: float = 15.0):
-    """The CPU oracle on a bounded sample of the same workload: weight set 0,
-    tokens 0, 1, ... each ranking h and z and forming q, k, v and o, until
+    """The CPU oracle on a bounded sample of the headline workload: weight set
+    0, tokens 0, 1, ... each ranking h and z and forming q, k, v and o, until
     about `budget_s` seconds of timed work are done."""
-    import numpy as np
-
     import oracle as O
     import workloads as WL
     from workloads.accounting import gemv_algorithmic_bytes
@@ -314,15 +388,16 @@ def cpu_baseline(kf: int, ka: int, budget_s: float = 15.0):
         threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
     except Exception:  # pragma: no cover - threadpoolctl missing
         threads = 1
+    H, cfg = 4096, 2
     mats = {}
     for m in ("q", "k", "v", "o"):
-        Wt = WL.weights_fp16(CONFIG_ID, 0, m, HIDDEN, HIDDEN, 0.02)
+        Wt = WL.weights_fp16(cfg, 0, m, H, H, 0.02)
         mats[m] = (O.ColumnStore("fp16", Wt), O.ColumnStore("int4", Wt))
-    per_proj = gemv_algorithmic_bytes(HIDDEN, HIDDEN, kf, ka, "fp16", "int4")
+    per_proj = gemv_algorithmic_bytes(H, H, kf, ka, "fp16", "int4")
     done, t_acc, tok = 0, 0.0, 0
-    while t_acc < budget_s and tok < TOKENS:
-        h = WL.laplace_fp16(CONFIG_ID, 0, "h", tok, HIDDEN)
-        z = WL.laplace_fp16(CONFIG_ID, 0, "z", tok, HIDDEN)
+    while t_acc < budget_s and tok < 32:
+        h = WL.laplace_fp16(cfg, 0, "h", tok, H)
+        z = WL.laplace_fp16(cfg, 0, "z", tok, H)
         t0 = time.perf_counter()
         Fh, Ah = O.plan_tiers(h, kf, ka)
         for m in ("q", "k", "v"):
@@ -340,19 +415,10 @@ def cpu_baseline(kf: int, ka: int, budget_s: float = 15.0):
             "host_cores": os.cpu_count()}
 
 
-def main():
-    args = parse()
-    if args.gpus != 1:
-        print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "
-              "(the path has no multi-GPU mode)", file=sys.stderr)
-        sys.exit(2)
-    r = gpu_run(args)
-    base = None
-    if not args.no_cpu_baseline:
-        log("timing the CPU oracle on a bounded sample")
-        base = cpu_baseline(r["kf"], r["ka"])
-    gbs = r["step_bytes"] / r["sec_step"] / 1e9
-    us_proj = r["sec_step"] / r["projections"] * 1e6
+def result_line(spec: Spec, wl: Workload, args, sec_step: float, mode: str, extra=None):
+    step_b = wl.step_bytes()
+    gbs = step_b / sec_step / 1e9
+    n_proj = wl.slots * wl.projections_per_layer()
     line = {
         "metric": METRIC,
         "value": round(gbs, 1),
@@ -360,29 +426,149 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(r["sec_step"] * 1e3, 4),
+        "ms_per_step": round(sec_step * 1e3, 4),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "fp32",
         "data": "synthetic",
-        "us_per_projection": round(us_proj, 3),
+        "us_per_projection": round(sec_step / n_proj * 1e6, 3),
         "frac_hbm_peak": round(gbs / HBM_PEAK_GBS, 4),
         "config": {
-            "workload": ("7B-shaped attention projections q,k,v,o 4096x4096, fp16 W ~N(0,0.02) "
-                         "column-major, int4 group-128 approx copy, skip/approx/full 40/30/30 %, "
-                         "x ~Laplace(0,1) fp16, batch 1, 32 tokens per step over 32 weight sets"),
-            "tokens_per_step": TOKENS,
-            "weight_sets": args.sets,
-            "k_full": r["kf"], "k_approx": r["ka"],
-            "algorithmic_bytes_per_step": r["step_bytes"],
-            "launch": r["mode"],
+            "workload": spec.describe(),
+            "tokens_per_step": spec.tokens,
+            "layers_per_token": spec.layers_per_token,
+            "weight_sets": spec.sets,
+            "k_full_approx": {g: list(wl.k[g]) for g in range(4) if wl.present[g]},
+            "algorithmic_bytes_per_step": step_b,
+            "launch": mode,
             "parallelism": "single GPU",
         },
-        "roofline": r["roofline"],
-        "cpu_baseline": base,
     }
-    print(json.dumps(line), flush=True)
+    if extra:
+        line.update(extra)
+    return line
+
+
+def run_headline(args):
+    import torch
+
+    import activation_sparse_decode_token_amd as spax
+    spax.lib()  # fails loudly when the HIP library is missing
+    if not torch.cuda.is_available():
+        raise SystemExit("bench.py needs a GPU (torch.cuda.is_available() is False)")
+    spec = headline_spec()
+    spec.sets = args.sets
+    log(f"device {torch.cuda.get_device_name(0)}; building {spec.sets} weight sets")
+    t0 = time.perf_counter()
+    wl = Workload(spec)
+    log(f"weights ready in {time.perf_counter() - t0:.1f} s; k_full={wl.k[0][0]} "
+        f"k_approx={wl.k[0][1]}")
+    sec_step, _, mode, stream = time_steps(wl, args.steps, args.warmup, args.eager)
+
+    # Per-launch duration of the product kernel, event-timed on its stream:
+    # each group's launches back to back in a graph (host launch cost is not
+    # on the GPU timeline).
+    qkv_b, o_b = wl.group_bytes(0), wl.group_bytes(1)
+    roof = None
+    if mode == "graph":
+        t_qkv = graph_launch_time(wl.launches(0), stream, wl.slots)
+        t_o = graph_launch_time(wl.launches(1), stream, wl.slots)
+        achieved = (qkv_b + o_b) / (t_qkv + t_o) / 1e9
+        log(f"product kernel: qkv {t_qkv * 1e6:.2f} us, o {t_o * 1e6:.2f} us per launch, "
+            f"{achieved:.0f} GB/s on algorithmic bytes")
+        roof = {
+            "bound": "hbm",
+            "achieved": round(achieved, 1),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": measured_traffic(),
+            "kernel": "gemv_kernel: fused tier selection + tiered gather-GEMV "
+                      "(fp16 full, int4 g128 approx)",
+            "avg_launch_us": round((t_qkv + t_o) / 2 * 1e6, 3),
+            "launch_us": {"qkv": round(t_qkv * 1e6, 3), "o": round(t_o * 1e6, 3)},
+            "bytes_per_launch": {"qkv": qkv_b, "o": o_b},
+        }
+    if args.calib_copy:
+        a = torch.empty(256 << 20, dtype=torch.uint8, device="cuda:0")
+        b = torch.empty_like(a)
+        a.fill_(1)
+        torch.cuda.synchronize()
+        b.copy_(a)
+        torch.cuda.synchronize()
+        log("calibration copy: 268435456 bytes read, 268435456 bytes written")
+    base = None
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle on a bounded sample")
+        base = cpu_baseline(*wl.k[0])
+    return result_line(spec, wl, args, sec_step, mode, {"roofline": roof, "cpu_baseline": base})
+
+
+def run_config(args):
+    import torch
+
+    import activation_sparse_decode_token_amd as spax
+    spax.lib()
+    if not torch.cuda.is_available():
+        raise SystemExit("bench.py needs a GPU (torch.cuda.is_available() is False)")
+    lines = []
+    for spec in specs_for(args.config, args.host):
+        log(f"config {spec.config}: {spec.describe()}")
+        t0 = time.perf_counter()
+        wl = Workload(spec)
+        log(f"weights ready in {time.perf_counter() - t0:.1f} s")
+        eager = args.eager or spec.host
+        sec_step, _, mode, _ = time_steps(wl, args.steps, args.warmup, eager)
+        extra = {}
+        if spec.host:
+            peak = host_link_peak_gbs()
+            link = wl.step_bytes() / sec_step / 1e9
+            extra["host_link"] = {
+                "achieved": round(link, 2), "unit": "GB/s",
+                "copy_peak_measured": round(peak, 2), "nominal_pcie5_x16": PCIE5_X16_GBS,
+                "frac_of_measured_peak": round(link / peak, 4),
+                "note": "selected columns and scales copied from pinned host memory each "
+                        "step, overlapped with the product; bytes = algorithmic bytes",
+            }
+            log(f"host link: {link:.1f} GB/s effective, plain pinned copy {peak:.1f} GB/s")
+        line = result_line(spec, wl, args, sec_step, mode, extra)
+        print(json.dumps(line), flush=True)
+        lines.append(line)
+        del wl
+        torch.cuda.empty_cache()
+    return lines
+
+
+def parse():
+    p = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=50)
+    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--sets", type=int, default=32,
+                   help="distinct weight sets rotated over the tokens (headline; default 32)")
+    p.add_argument("--eager", action="store_true",
+                   help="launch every kernel from Python instead of replaying a graph")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--calib-copy", action="store_true",
+                   help="also run one plain 256 MiB device copy (counter calibration)")
+    p.add_argument("--config", type=int, default=None,
+                   help="run another benchmark workload (1, 3, 4, 5) instead of the headline")
+    p.add_argument("--host", action="store_true",
+                   help="with --config 4: weights in pinned host memory")
+    return p.parse_args()
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "
+              "(the path has no multi-GPU mode)", file=sys.stderr)
+        sys.exit(2)
+    if args.config is not None and args.config != 2:
+        run_config(args)
+        return
+    print(json.dumps(run_headline(args)), flush=True)
 
 
 if __name__ == "__main__":
