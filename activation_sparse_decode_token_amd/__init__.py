@@ -26,6 +26,8 @@ FMT_NONE, FMT_FP16, FMT_INT4_G128, FMT_INT2_G128 = 0, 1, 2, 3
 RES_DEVICE, RES_HOST_PINNED = 0, 1
 LAYOUT_PLAIN, LAYOUT_GLU_INTERLEAVED = 0, 1
 GROUP_QKV, GROUP_O, GROUP_GATE_UP, GROUP_DOWN = 0, 1, 2, 3
+KERNEL_AUTO, KERNEL_SPLIT, KERNEL_ROWS_ONLY = 0, 1, 2
+MAX_ROWS = 1 << 20
 
 STATUS = {0: "SPAX_OK", -1: "SPAX_EINVAL", -2: "SPAX_ENULL", -3: "SPAX_EALIGN",
           -4: "SPAX_EFORMAT", -5: "SPAX_EWORKSPACE", -6: "SPAX_ESTREAM", -7: "SPAX_EHIP"}
@@ -35,6 +37,7 @@ EXPORTS = (
     "spax_plan_tiers", "spax_gemv_workspace_bytes", "spax_tiered_gemv",
     "spax_layer_workspace_bytes", "spax_layer_step", "spax_pack_g128",
     "spax_workspace_clear", "spax_status_string", "spax_last_error", "spax_version",
+    "spax_set_kernel_choice",
 )
 
 library_path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libspax.so")
@@ -56,6 +59,9 @@ def lib() -> ctypes.CDLL:
     """Load libspax.so (raises if it has not been built)."""
     global _lib
     if _lib is None:
+        # torch first: the library then binds to the HIP runtime torch has
+        # loaded, so both share one runtime (devices, streams, allocations)
+        import torch  # noqa: F401
         if not os.path.exists(library_path):
             raise ImportError(
                 f"{library_path} is missing; build it with "
@@ -176,12 +182,19 @@ def _declare(L: ctypes.CDLL) -> None:
     L.spax_last_error.restype = ctypes.c_char_p
     L.spax_version.argtypes = []
     L.spax_version.restype = ctypes.c_int
+    L.spax_set_kernel_choice.argtypes = [i32]
+    L.spax_set_kernel_choice.restype = ctypes.c_int
 
 
 # ---------------------------------------------------------------- entry points
 
 def version() -> int:
     return lib().spax_version()
+
+
+def set_kernel_choice(choice: int) -> None:
+    """spax_set_kernel_choice: product kernel of layer_step (KERNEL_*)."""
+    _check(lib().spax_set_kernel_choice(int(choice)), "spax_set_kernel_choice")
 
 
 def status_string(status: int) -> str:

@@ -13,7 +13,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libspax.so")
 
-SOURCES = ["plan.hip", "gemv.hip", "aux.hip", "api.cpp"]
+SOURCES = ["plan.hip", "gemv.hip", "rows.hip", "aux.hip", "api.cpp"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
@@ -25,17 +25,30 @@ FLAGS = [
 ]
 
 
-def build(verbose: bool = False) -> str:
-    srcs = [os.path.join(CSRC, s) for s in SOURCES]
-    tmp = LIB + ".tmp"
-    cmd = [HIPCC, *FLAGS, "-I", os.path.join(ROOT, "include"), "-I", CSRC, *srcs, "-o", tmp]
+def _run(cmd, verbose):
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         sys.stderr.write(res.stdout + res.stderr)
         raise RuntimeError("hipcc failed building libspax.so")
-    os.replace(tmp, LIB)
+
+
+def build(verbose: bool = False) -> str:
+    """Compile every source to an object (in parallel), then link."""
+    import concurrent.futures
+    import tempfile
+    inc = ["-I", os.path.join(ROOT, "include"), "-I", CSRC]
+    with tempfile.TemporaryDirectory(prefix="spax_build_") as tmpdir:
+        objs = [os.path.join(tmpdir, s + ".o") for s in SOURCES]
+        cmds = [[HIPCC, *FLAGS, *inc, "-c", os.path.join(CSRC, s), "-o", o]
+                for s, o in zip(SOURCES, objs)]
+        workers = max(1, min(len(cmds), os.cpu_count() or 1, 8))
+        with concurrent.futures.ThreadPoolExecutor(workers) as ex:
+            list(ex.map(lambda c: _run(c, verbose), cmds))
+        tmp = LIB + ".tmp"
+        _run([HIPCC, *FLAGS, *objs, "-o", tmp], verbose)
+        os.replace(tmp, LIB)
     return LIB
 
 

@@ -5,6 +5,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <atomic>
 #include <cstdint>
 #include <string>
 
@@ -50,7 +51,8 @@ int64_t tile_bytes(int32_t fmt) {
 
 int validate_matrix(const spax_matrix* W) {
   if (!W) return SPAX_ENULL;
-  if (W->rows <= 0 || W->cols <= 0 || W->rows % kGroup) return SPAX_EINVAL;
+  if (W->rows <= 0 || W->cols <= 0 || W->rows % kGroup || W->rows > kMaxRows)
+    return SPAX_EINVAL;
   if (W->full_fmt != kFp16 && W->full_fmt != kInt4) return SPAX_EFORMAT;
   if (W->approx_fmt != kNone && W->approx_fmt != kInt4 && W->approx_fmt != kInt2)
     return SPAX_EFORMAT;
@@ -124,9 +126,33 @@ bool plan_fused(const spax_matrix* W, int32_t kf, int32_t ka, ProductPlan* out) 
   return true;
 }
 
-size_t counters_bytes(const spax_matrix* W) {
-  return align256(sizeof(uint32_t) * ((W->rows + kTileRows - 1) / kTileRows));
+// Row-sliced product (fused selection, whole rows per workgroup): 16-row
+// chunks dealt to at most SPAX_TARGET_BLOCKS workgroups, at most kRowsMaxM
+// each. Needs fp16 full-tier columns in device memory and both tier lists in
+// the workgroup's LDS.
+struct RowPlan {
+  int32_t chunks = 0;
+  int32_t m = 0;
+  int32_t grid = 0;
+};
+
+bool plan_rows(const spax_matrix* W, int32_t kf, int32_t ka, int32_t epi, RowPlan* out) {
+  if (W->residency != SPAX_RES_DEVICE || W->full_fmt != kFp16) return false;
+  if (W->cols > kRowsMaxN || (int64_t)kf + ka > kRowListCap) return false;
+  const int64_t rows_per_chunk = epi == kEpiGlu ? 2 * kChunkRows : kChunkRows;
+  const int64_t chunks = W->rows / rows_per_chunk;
+  const int64_t m = (chunks + SPAX_TARGET_BLOCKS - 1) / SPAX_TARGET_BLOCKS;
+  if (m < 1 || m > kRowsMaxM) return false;
+  out->chunks = (int32_t)chunks;
+  out->m = (int32_t)m;
+  out->grid = (int32_t)((chunks + m - 1) / m);
+  return true;
 }
+
+// Kernel choice of spax_layer_step (SPAX_KERNEL_*), process-wide.
+std::atomic<int32_t> g_kernel_choice{SPAX_KERNEL_AUTO};
+
+size_t counters_bytes(const spax_matrix*) { return align256(kCounterRegionBytes); }
 size_t partials_bytes(const spax_matrix* W) {
   return align256(sizeof(float) * (size_t)kMaxSplits * W->rows);
 }
@@ -282,6 +308,37 @@ int run_product(const spax_matrix* W, const uint16_t* x, const int32_t* fidx, in
   return SPAX_OK;
 }
 
+// Enqueue the row-sliced product with fused selection; the lists are
+// written to out_f / out_a.
+int run_rows(const spax_matrix* W, const uint16_t* x, int32_t kf, int32_t ka, int32_t epi,
+             uint16_t* y, uint16_t* ga, uint16_t* gg, uint16_t* gu, hipStream_t s,
+             const RowPlan& rp, int32_t* out_f, int32_t* out_a) {
+  GemvArgs a{};
+  a.rows = W->rows;
+  a.k_full = kf;
+  a.k_approx = ka;
+  a.n = W->cols;
+  a.x = x;
+  a.out_full_idx = out_f;
+  a.out_approx_idx = out_a;
+  a.y = y;
+  a.glu_a = ga;
+  a.glu_g = gg;
+  a.glu_u = gu;
+  a.full_base = static_cast<const uint8_t*>(W->full_data);
+  a.full_stride = col_bytes(W->full_fmt, W->rows);
+  a.full_bytes = (uint32_t)(a.full_stride * W->cols);
+  a.approx_base = W->approx_codes;
+  a.approx_stride = col_bytes(W->approx_fmt, W->rows);
+  a.approx_bytes = (uint32_t)(a.approx_stride * W->cols);
+  a.approx_scales = W->approx_scales;
+  a.approx_sstride = col_scales(W->approx_fmt, W->rows);
+  a.n_chunks = rp.chunks;
+  a.grid = rp.grid;
+  const hipError_t e = launch_rows(a, W->approx_fmt, epi, rp.m, s);
+  return e == hipSuccess ? SPAX_OK : hip_fail(e);
+}
+
 int check_counts(int32_t n, int32_t kf, int32_t ka) {
   if (kf < 0 || ka < 0 || (int64_t)kf + ka > n) return SPAX_EINVAL;
   return SPAX_OK;
@@ -306,6 +363,13 @@ int validate_product(const spax_matrix* W, const uint16_t* x, const int32_t* fid
 extern "C" {
 
 int spax_version(void) { return 100; }
+
+int spax_set_kernel_choice(int32_t choice) {
+  if (choice != SPAX_KERNEL_AUTO && choice != SPAX_KERNEL_SPLIT && choice != SPAX_KERNEL_ROWS_ONLY)
+    return SPAX_EINVAL;
+  g_kernel_choice.store(choice, std::memory_order_relaxed);
+  return SPAX_OK;
+}
 
 const char* spax_status_string(int status) {
   switch (status) {
@@ -394,12 +458,19 @@ int spax_layer_step(const spax_layer* L, const spax_layer_io* io, void* ws, size
     uint16_t* gu = g == SPAX_GROUP_GATE_UP ? io->u : nullptr;
     const int32_t epi = g == SPAX_GROUP_GATE_UP ? kEpiGlu : kEpiPlain;
     ProductPlan fp;
+    RowPlan rp;
     int st;
-    if (plan_fused(&G[g], kf, ka, &fp)) {
+    const int32_t choice = g_kernel_choice.load(std::memory_order_relaxed);
+    if (choice != SPAX_KERNEL_SPLIT && plan_rows(&G[g], kf, ka, epi, &rp)) {
+      // few rows per column split: whole rows per workgroup
+      st = run_rows(&G[g], inputs[g], kf, ka, epi, y, ga, gg, gu, compute_stream, rp,
+                    io->full_idx[g], io->approx_idx[g]);
+    } else if (choice != SPAX_KERNEL_ROWS_ONLY && plan_fused(&G[g], kf, ka, &fp)) {
       // device-resident weights: selection fused into the product
       st = run_product(&G[g], inputs[g], nullptr, kf, nullptr, ka, epi, y, ga, gg, gu, ws,
                        compute_stream, copy_stream, &fp, io->full_idx[g], io->approx_idx[g]);
     } else {
+      if (choice == SPAX_KERNEL_ROWS_ONLY) return SPAX_EINVAL;
       hipError_t e = launch_plan(inputs[g], G[g].cols, kf, ka, io->full_idx[g],
                                  io->approx_idx[g], compute_stream);
       if (e != hipSuccess) return hip_fail(e);

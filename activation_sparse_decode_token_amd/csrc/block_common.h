@@ -1,0 +1,395 @@
+// Device helpers shared by the tiered-product kernels: fp16 bit helpers,
+// buffer resources, and the in-workgroup tier selection (SpAx page, section
+// 5, Figure 2 step 3: rank x by |x_j|, the largest k_full go to the full
+// tier, the next k_approx to the approx tier).
+#pragma once
+
+#include <hip/hip_fp16.h>
+#include <hip/hip_runtime.h>
+
+#include "spax_internal.h"
+
+namespace spax {
+namespace {
+
+__device__ __forceinline__ float h2f(uint32_t bits) {
+  return __half2float(__ushort_as_half((unsigned short)bits));
+}
+__device__ __forceinline__ uint16_t f2h(float v) {
+  return __half_as_ushort(__float2half_rn(v));
+}
+__device__ __forceinline__ float b2f(uint32_t v, int byte) {
+  return (float)((v >> (8 * byte)) & 0xFFu);
+}
+
+// Buffer resource of one tier of a matrix: a scalar base and size. A
+// column's load adds the column offset as the 32-bit scalar soffset and the
+// lane's part as one shared 32-bit vector offset, so each load costs one
+// scalar register instead of a 64-bit address per lane. Reads past the tier
+// return 0 instead of touching memory. Dword 3 selects 32-bit raw access on
+// gfx9-family parts. Tier sizes are below 2^31 bytes (checked on the host).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t tier_rsrc(const uint8_t* p, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(p), (short)0, (int)bytes,
+                                           0x00020000);
+}
+
+// Opaque to the optimiser: keeps the byte-wise code extraction below from
+// being folded into per-value bit-field extracts, so each value is one
+// v_cvt_f32_ubyteN.
+__device__ __forceinline__ uint32_t opaque(uint32_t v) {
+  asm volatile("" : "+v"(v));
+  return v;
+}
+
+// Per-format load and multiply-add of one lane's 8 consecutive rows of one
+// column: fp16 values (16 bytes), int4 codes (4 bytes) or int2 codes
+// (2 bytes). offset(row0, lane) is the byte offset, within a column, of
+// row row0 + 8 * lane.
+template <int FMT>
+struct Tier;
+
+template <>
+struct Tier<kFp16> {
+  using V = uint4;
+  static constexpr int U = 8;
+  // byte offset of lane l's 8 rows in a column
+  static __device__ __forceinline__ uint32_t offset(int row0, int lane) {
+    return 2u * (uint32_t)(row0 + 8 * lane);
+  }
+  static __device__ __forceinline__ V load(__amdgpu_buffer_rsrc_t t, uint32_t off, uint32_t col) {
+    return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(t, off, col, 0));
+  }
+  // f = x_j
+  static __device__ __forceinline__ void fma(float (&acc)[8], float&, V v, float f) {
+    acc[0] = fmaf(h2f(v.x & 0xFFFFu), f, acc[0]);
+    acc[1] = fmaf(h2f(v.x >> 16), f, acc[1]);
+    acc[2] = fmaf(h2f(v.y & 0xFFFFu), f, acc[2]);
+    acc[3] = fmaf(h2f(v.y >> 16), f, acc[3]);
+    acc[4] = fmaf(h2f(v.z & 0xFFFFu), f, acc[4]);
+    acc[5] = fmaf(h2f(v.z >> 16), f, acc[5]);
+    acc[6] = fmaf(h2f(v.w & 0xFFFFu), f, acc[6]);
+    acc[7] = fmaf(h2f(v.w >> 16), f, acc[7]);
+  }
+};
+
+template <>
+struct Tier<kInt4> {
+  using V = uint32_t;
+  static constexpr int U = 16;
+  static __device__ __forceinline__ uint32_t offset(int row0, int lane) {
+    return (uint32_t)(row0 + 8 * lane) / 2u;
+  }
+  static __device__ __forceinline__ V load(__amdgpu_buffer_rsrc_t t, uint32_t off, uint32_t col) {
+    return __builtin_amdgcn_raw_buffer_load_b32(t, off, col, 0);
+  }
+  // Rows 2b and 2b+1 sit in the low and high nibble of byte b, as
+  // two's-complement q; flipping each nibble's sign bit gives u = q + 8.
+  // f = x_j * s_{j,g} (exact: a product of two fp16 values); the offset 8 f
+  // is taken off through corr.
+  static __device__ __forceinline__ void fma(float (&acc)[8], float& corr, V v, float f) {
+    corr = fmaf(8.0f, f, corr);
+    v ^= 0x88888888u;
+    const uint32_t lo = opaque(v & 0x0F0F0F0Fu);
+    const uint32_t hi = opaque((v >> 4) & 0x0F0F0F0Fu);
+    acc[0] = fmaf(f, b2f(lo, 0), acc[0]);
+    acc[1] = fmaf(f, b2f(hi, 0), acc[1]);
+    acc[2] = fmaf(f, b2f(lo, 1), acc[2]);
+    acc[3] = fmaf(f, b2f(hi, 1), acc[3]);
+    acc[4] = fmaf(f, b2f(lo, 2), acc[4]);
+    acc[5] = fmaf(f, b2f(hi, 2), acc[5]);
+    acc[6] = fmaf(f, b2f(lo, 3), acc[6]);
+    acc[7] = fmaf(f, b2f(hi, 3), acc[7]);
+  }
+};
+
+template <>
+struct Tier<kInt2> {
+  using V = uint32_t;
+  static constexpr int U = 16;
+  static __device__ __forceinline__ uint32_t offset(int row0, int lane) {
+    return (uint32_t)(row0 + 8 * lane) / 4u;
+  }
+  static __device__ __forceinline__ V load(__amdgpu_buffer_rsrc_t t, uint32_t off, uint32_t col) {
+    return __builtin_amdgcn_raw_buffer_load_b16(t, off, col, 0);
+  }
+  // Row 4b + r sits in bits 2r..2r+1 of byte b (two bytes per lane); each
+  // 2-bit field is moved to the bottom of its byte and converted. The
+  // offset 1.5 f is taken off through corr.
+  static __device__ __forceinline__ void fma(float (&acc)[8], float& corr, V v, float f) {
+    corr = fmaf(1.5f, f, corr);
+    const uint32_t m0 = opaque(v & 0x0303u);
+    const uint32_t m1 = opaque((v >> 2) & 0x0303u);
+    const uint32_t m2 = opaque((v >> 4) & 0x0303u);
+    const uint32_t m3 = opaque((v >> 6) & 0x0303u);
+    acc[0] = fmaf(f, b2f(m0, 0), acc[0]);
+    acc[4] = fmaf(f, b2f(m0, 1), acc[4]);
+    acc[1] = fmaf(f, b2f(m1, 0), acc[1]);
+    acc[5] = fmaf(f, b2f(m1, 1), acc[5]);
+    acc[2] = fmaf(f, b2f(m2, 0), acc[2]);
+    acc[6] = fmaf(f, b2f(m2, 1), acc[6]);
+    acc[3] = fmaf(f, b2f(m3, 0), acc[3]);
+    acc[7] = fmaf(f, b2f(m3, 1), acc[7]);
+  }
+};
+
+// ---------------------------------------------------------------------------
+// In-workgroup tier selection (kListRank). Same definition as the stand-alone
+// plan kernel: order key = fp16 magnitude bits, larger first, lower index
+// first among equal keys; the k_full first are F, the next k_approx are A.
+// Thread t owns entries [t*E, t*E+E).
+//   1. 256-bin histogram of key bits 14..7 (LDS atomics);
+//   2. suffix counts give the bins holding rank k_full and k_full + k_approx;
+//   3. 128-bin histograms inside those bins give the boundary keys t1, t2
+//      and the number of entries equal to each that are kept (q1, q2);
+//   4. one block scan of (#key > t1, #key == t1, #key > t2, #key == t2) gives
+//      every entry its position: #F before entry i is
+//      gt1(i) + min(eq1(i), q1), #(F or A) before it gt2(i) + min(eq2(i), q2).
+// ---------------------------------------------------------------------------
+constexpr uint32_t kAboveAll = 0x8000u;  // boundary key when a tier is empty
+
+struct RankShared {
+  uint32_t hist[257];  // bin 256 absorbs the padding past n
+  uint32_t sub[2][128];
+  uint32_t scan[4][kWaves];
+  int32_t sel[8];  // b1, entries above b1, b2, entries above b2, t1, q1, t2, q2
+};
+
+// Inclusive prefix sum over the 64 lanes of a wave with DPP row shifts and
+// row broadcasts (lanes whose source is outside the row add 0).
+__device__ __forceinline__ uint32_t wave_incl_scan(uint32_t v) {
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x111, 0xf, 0xf, false);  // row_shr:1
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x112, 0xf, 0xf, false);  // row_shr:2
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x114, 0xf, 0xf, false);  // row_shr:4
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x118, 0xf, 0xf, false);  // row_shr:8
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x142, 0xa, 0xf, false);  // row_bcast:15
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x143, 0xc, 0xf, false);  // row_bcast:31
+  return v;
+}
+
+// Sum of v over the lanes above this one.
+__device__ __forceinline__ uint32_t wave_excl_suffix(uint32_t v) {
+  const uint32_t incl = wave_incl_scan(v);
+  const uint32_t total = (uint32_t)__builtin_amdgcn_readlane((int)incl, 63);
+  return total - incl;
+}
+
+// The one lane with sel >= 0 (if any) broadcasts (sel, val) to the wave;
+// otherwise out_sel = -1, out_val = 0.
+__device__ __forceinline__ void wave_pick(int sel, uint32_t val, int& out_sel,
+                                          uint32_t& out_val) {
+  const uint64_t m = __ballot(sel >= 0);
+  if (m == 0) {
+    out_sel = -1;
+    out_val = 0u;
+  } else {
+    const int src = (int)__builtin_ctzll(m);
+    out_sel = __builtin_amdgcn_readlane(sel, src);
+    out_val = (uint32_t)__builtin_amdgcn_readlane((int)val, src);
+  }
+}
+
+__device__ __forceinline__ uint32_t rawbits(const uint32_t* xr, int i) {
+  return (xr[i >> 1] >> (16 * (i & 1))) & 0xFFFFu;
+}
+
+// Ranks x and places this workgroup's list positions in LDS: full-tier
+// positions [f0, f1) at slots [0, f1 - f0), approx-tier positions [a0, a1)
+// after them.
+template <int E>
+__device__ __forceinline__ void rank_piece(const GemvArgs& a, RankShared& rs, int32_t* lidx,
+                                           float* lx, int f0, int f1, int a0, int a1,
+                                           bool write_lists) {
+  const int t = threadIdx.x;
+  const int lane = t & 63;
+  const int wave = t >> 6;
+  const int n = a.n;
+  const int base = t * E;
+  const uint32_t K1 = (uint32_t)a.k_full;
+  const uint32_t K2 = (uint32_t)(a.k_full + a.k_approx);
+
+  // raw fp16 bits, two per register
+  uint32_t xr[E / 2];
+#pragma unroll
+  for (int i = 0; i < E; i += 8) {
+    if (base + i + 7 < n) {
+      const uint4 v = *reinterpret_cast<const uint4*>(a.x + base + i);
+      xr[i / 2 + 0] = v.x;
+      xr[i / 2 + 1] = v.y;
+      xr[i / 2 + 2] = v.z;
+      xr[i / 2 + 3] = v.w;
+    } else {
+#pragma unroll
+      for (int j = 0; j < 8; j += 2) {
+        const uint32_t lo = base + i + j < n ? a.x[base + i + j] : 0u;
+        const uint32_t hi = base + i + j + 1 < n ? a.x[base + i + j + 1] : 0u;
+        xr[(i + j) / 2] = lo | (hi << 16);
+      }
+    }
+  }
+  const int nv = max(0, min(E, n - base));  // valid entries of this thread
+
+  if (t < 256) {
+    rs.hist[t] = 0u;
+    (&rs.sub[0][0])[t] = 0u;
+  }
+  if (t == 256) rs.hist[256] = 0u;
+  __syncthreads();
+
+  // 1. top-level histogram
+#pragma unroll
+  for (int i = 0; i < E; ++i)
+    atomicAdd(&rs.hist[i < nv ? (rawbits(xr, i) & 0x7FFFu) >> 7 : 256u], 1u);
+  __syncthreads();
+
+  // 2. bins holding rank K1 and rank K2 (1-based, from the largest key),
+  // found by wave 0 (the other waves wait at the barrier, leaving it the
+  // whole SIMD)
+  if (wave == 0) {
+    uint32_t c[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) c[j] = rs.hist[4 * lane + j];
+    uint32_t above = wave_excl_suffix(c[0] + c[1] + c[2] + c[3]);
+    int s1 = -1, s2 = -1;
+    uint32_t x1 = 0u, x2 = 0u;
+#pragma unroll
+    for (int j = 3; j >= 0; --j) {
+      if (K1 > 0 && above < K1 && K1 <= above + c[j]) { s1 = 4 * lane + j; x1 = above; }
+      if (K2 > 0 && above < K2 && K2 <= above + c[j]) { s2 = 4 * lane + j; x2 = above; }
+      above += c[j];
+    }
+    int b, ab;
+    uint32_t v;
+    wave_pick(s1, x1, b, v);
+    ab = (int)v;
+    if (lane == 0) { rs.sel[0] = b; rs.sel[1] = ab; }
+    wave_pick(s2, x2, b, v);
+    ab = (int)v;
+    if (lane == 0) { rs.sel[2] = b; rs.sel[3] = ab; }
+  }
+  __syncthreads();
+
+  // 3. low-level histograms inside the two boundary bins
+  const int b1 = rs.sel[0];
+  const int b2 = rs.sel[2];
+#pragma unroll
+  for (int i = 0; i < E; ++i) {
+    const uint32_t k = rawbits(xr, i) & 0x7FFFu;
+    const int hb = i < nv ? (int)(k >> 7) : 256;
+    if (hb == b1) atomicAdd(&rs.sub[0][k & 127u], 1u);
+    if (hb == b2) atomicAdd(&rs.sub[1][k & 127u], 1u);
+  }
+  __syncthreads();
+  // boundary keys t (kAboveAll when the tier is empty) and quotas q: the
+  // number of entries equal to t that are kept; found by wave 0
+  if (wave == 0) {
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+      const int b = r == 0 ? b1 : b2;
+      const uint32_t K = r == 0 ? K1 : K2;
+      int key = (int)kAboveAll;
+      uint32_t quota = 0u;
+      if (b >= 0) {  // wave-uniform
+        const uint32_t c0 = rs.sub[r][2 * lane], c1 = rs.sub[r][2 * lane + 1];
+        uint32_t above = (uint32_t)rs.sel[1 + 2 * r] + wave_excl_suffix(c0 + c1);
+        int sk = -1;
+        uint32_t sq = 0u;
+        if (above < K && K <= above + c1) { sk = (b << 7) | (2 * lane + 1); sq = K - above; }
+        above += c1;
+        if (above < K && K <= above + c0) { sk = (b << 7) | (2 * lane); sq = K - above; }
+        wave_pick(sk, sq, key, quota);
+      }
+      if (lane == 0) {
+        rs.sel[4 + 2 * r] = key;
+        rs.sel[5 + 2 * r] = (int32_t)quota;
+      }
+    }
+  }
+  __syncthreads();
+  const uint32_t t1 = (uint32_t)rs.sel[4], q1 = (uint32_t)rs.sel[5];
+  const uint32_t t2 = (uint32_t)rs.sel[6], q2 = (uint32_t)rs.sel[7];
+
+  // 4. positions
+  uint32_t c[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+  for (int i = 0; i < E; ++i) {
+    const uint32_t k = rawbits(xr, i) & 0x7FFFu;
+    const bool ok = i < nv;
+    c[0] += ok && k > t1;
+    c[1] += ok && k == t1;
+    c[2] += ok && k > t2;
+    c[3] += ok && k == t2;
+  }
+  uint32_t in[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) in[j] = wave_incl_scan(c[j]);
+  if (lane == 63) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) rs.scan[j][wave] = in[j];
+  }
+  __syncthreads();
+  // totals of the waves before this one: lanes 0..7 hold the wave totals,
+  // a lane scan gives their prefixes, lane `wave` holds this wave's
+  const int wv = __builtin_amdgcn_readfirstlane(wave);
+  uint32_t pre[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const uint32_t wt = lane < kWaves ? rs.scan[j][lane] : 0u;
+    pre[j] = (uint32_t)__builtin_amdgcn_readlane((int)(wave_incl_scan(wt) - wt), wv);
+  }
+  uint32_t g1 = pre[0] + in[0] - c[0], e1r = pre[1] + in[1] - c[1];
+  uint32_t g2 = pre[2] + in[2] - c[2], e2r = pre[3] + in[3] - c[3];
+  // This thread's F positions [fs, fe) and A positions [as, ae); only
+  // threads whose positions meet the piece place entries. Entries past n
+  // (key 0, after every real entry) are never placed: a boundary key 0
+  // has its quota used up by the real zeros before them.
+  const int fs = (int)(g1 + min(e1r, q1));
+  const int fe = (int)(g1 + c[0] + min(e1r + c[1], q1));
+  const int as = (int)(g2 + min(e2r, q2)) - fs;
+  const int ae = (int)(g2 + c[2] + min(e2r + c[3], q2)) - fe;
+  if ((fs < f1 && fe > f0) || (as < a1 && ae > a0)) {
+    const int nf = f1 - f0;
+#pragma unroll
+    for (int i = 0; i < E; ++i) {
+      const uint32_t k = rawbits(xr, i) & 0x7FFFu;
+      const bool gt1 = k > t1, eq1 = k == t1, gt2 = k > t2, eq2 = k == t2;
+      const bool in_f = gt1 || (eq1 && e1r < q1);
+      const bool in_fa = gt2 || (eq2 && e2r < q2);
+      const int fpos = (int)(g1 + min(e1r, q1));          // F entries before this one
+      const int apos = (int)(g2 + min(e2r, q2)) - fpos;   // A entries before this one
+      const bool put_f = in_f && fpos >= f0 && fpos < f1;
+      const bool put_a = in_fa && !in_f && apos >= a0 && apos < a1;
+      const int slot = put_f ? fpos - f0 : nf + (apos - a0);
+      if (put_f || put_a) {
+        lidx[slot] = base + i;
+        lx[slot] = h2f(rawbits(xr, i));
+      }
+      g1 += gt1;
+      e1r += eq1;
+      g2 += gt2;
+      e2r += eq2;
+    }
+  }
+  __syncthreads();
+  // the caller's lists: this piece, copied out of LDS
+  if (write_lists) {
+    const int nf = f1 - f0;
+    for (int q = t; q < nf; q += kGemvThreads) a.out_full_idx[f0 + q] = lidx[q];
+    for (int q = t; q < a1 - a0; q += kGemvThreads) a.out_approx_idx[a0 + q] = lidx[nf + q];
+  }
+}
+
+// Gate / up pair: r1 is a gate row, r1 + 128 the matching up row.
+__device__ __forceinline__ void store_glu(const GemvArgs& a, int r1, float v1, float v2) {
+  if (r1 < a.rows) {
+    const int gi = (r1 >> 8) * 128 + (r1 & 127);
+    const uint16_t gb = f2h(v1), ub = f2h(v2);
+    const float g = h2f(gb), u = h2f(ub);
+    const float sg = g / (1.0f + expf(-g));
+    a.glu_a[gi] = f2h(sg * u);
+    if (a.glu_g) a.glu_g[gi] = gb;
+    if (a.glu_u) a.glu_u[gi] = ub;
+  }
+}
+
+}  // namespace
+}  // namespace spax

@@ -14,12 +14,27 @@ constexpr int kWaves = 8;
 constexpr int kGemvThreads = kWaves * 64;
 // Upper bound on column splits of one product (size of the fp32 partials).
 constexpr int kMaxSplits = 64;
+// Arrival counters per row tile: one total and one per group of 8 splits.
+constexpr int kCountersPerTile = 1 + kMaxSplits / 8;
+// Largest matrix height and its row tiles. The counters of every matrix
+// occupy one fixed region at the start of the workspace, so matrices of
+// different heights can share a workspace without their partial sums
+// landing on each other's counters.
+constexpr int kMaxRows = 1 << 20;
+constexpr int kMaxTiles = kMaxRows / kTileRows;
+constexpr size_t kCounterRegionBytes = sizeof(uint32_t) * kCountersPerTile * kMaxTiles;
 // Rows per quantisation group.
 constexpr int kGroup = 128;
 // List positions one workgroup of the fused rank + product keeps in LDS.
 constexpr int kListCap = 2048;
 // Largest input length the fused rank + product handles (64 per thread).
 constexpr int kRankMaxN = kGemvThreads * 64;
+// Row-sliced product: rows per chunk, chunks per workgroup, list capacity
+// (both tiers, in LDS) and largest input length.
+constexpr int kChunkRows = 16;
+constexpr int kRowsMaxM = 3;
+constexpr int kRowListCap = 8192;
+constexpr int kRowsMaxN = kGemvThreads * 32;
 
 enum Fmt : int32_t { kNone = 0, kFp16 = 1, kInt4 = 2, kInt2 = 3 };
 enum Epi : int32_t { kEpiPlain = 0, kEpiGlu = 1 };
@@ -57,11 +72,14 @@ struct GemvArgs {
   int32_t* out_full_idx;         // kListRank: lists written by tile-0 groups
   int32_t* out_approx_idx;
   float* partials;               // [n_splits][rows]
-  uint32_t* counters;            // [n_tiles]
+  uint32_t* counters;            // [n_tiles][kCountersPerTile]
   uint16_t* y;                   // plain: fp16[rows]
   uint16_t* glu_a;               // glu: fp16[rows/2]
   uint16_t* glu_g;               // optional
   uint16_t* glu_u;               // optional
+  // row-sliced product only
+  int32_t n_chunks;              // 16-row chunks (GLU: chunks of gate rows)
+  int32_t grid;                  // workgroups; workgroup b takes chunks b, b + grid, ...
 };
 
 // Selected-column copy from host-resident storage into device staging.
@@ -86,6 +104,11 @@ hipError_t launch_plan(const uint16_t* x, int32_t n, int32_t k_full, int32_t k_a
 
 hipError_t launch_gemv(const GemvArgs& a, int32_t full_fmt, int32_t approx_fmt,
                        int32_t mode, int32_t epi, hipStream_t s);
+
+// Row-sliced product with fused selection: full tier fp16, up to m chunks
+// per workgroup.
+hipError_t launch_rows(const GemvArgs& a, int32_t approx_fmt, int32_t epi, int32_t m,
+                       hipStream_t s);
 
 hipError_t launch_copy(const CopyArgs& a, hipStream_t s);
 

@@ -59,7 +59,7 @@ PCIE5_X16_GBS = 64.0
 
 
 PMC_SUMMARY = os.path.join(ROOT, "profiles", "gemv_kernel_7b_attention_pmc.txt")
-KERNEL_SOURCES = ("gemv.hip", "api.cpp", "spax_internal.h")
+KERNEL_SOURCES = ("gemv.hip", "block_common.h", "api.cpp", "spax_internal.h")
 
 
 def kernel_source_hash() -> str:
@@ -556,6 +556,8 @@ def parse():
                    help="run another benchmark workload (1, 3, 4, 5) instead of the headline")
     p.add_argument("--host", action="store_true",
                    help="with --config 4: weights in pinned host memory")
+    p.add_argument("--kernel", choices=("auto", "split"), default="auto",
+                   help="product kernel of the layer step (default: the library's choice)")
     return p.parse_args()
 
 
@@ -565,6 +567,9 @@ def main():
         print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "
               "(the path has no multi-GPU mode)", file=sys.stderr)
         sys.exit(2)
+    if args.kernel != "auto":
+        import activation_sparse_decode_token_amd as spax
+        spax.set_kernel_choice(spax.KERNEL_SPLIT)
     if args.config is not None and args.config != 2:
         run_config(args)
         return

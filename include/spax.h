@@ -23,7 +23,8 @@
  *             with scales s and s/2); row 4i+r in bits 2r..2r+1 of byte i.
  *       codes: [cols][rows/2] (int4) or [cols][rows/4] (int2) bytes;
  *       scales: [cols][rows/128] fp16.
- *   - rows must be a multiple of 128 for every format.
+ *   - rows must be a multiple of 128 for every format and at most
+ *     SPAX_MAX_ROWS.
  *   - Every device pointer must be 16-byte aligned.
  *   - The caller owns every buffer. Calls validate their arguments on the
  *     host, enqueue kernels on the given stream(s) and return; results are
@@ -48,6 +49,8 @@ extern "C" {
 #define SPAX_ENULL      -2  /* a required pointer is null                      */
 #define SPAX_EALIGN     -3  /* a device pointer is not 16-byte aligned         */
 #define SPAX_EFORMAT    -4  /* unknown format or unsupported combination       */
+/* Largest matrix height (rows) the product accepts. */
+#define SPAX_MAX_ROWS 1048576
 #define SPAX_EWORKSPACE -5  /* workspace smaller than the *_workspace_bytes()  */
 #define SPAX_ESTREAM    -6  /* host-resident matrix but no copy stream given   */
 #define SPAX_EHIP       -7  /* the HIP runtime reported an error; see
@@ -126,8 +129,11 @@ size_t spax_gemv_workspace_bytes(const spax_matrix* W);
  *              GLU-interleaved layout this is the interleaved order).
  *   ws         device workspace of spax_gemv_workspace_bytes(W) bytes. It
  *              must be all zero before its first use (spax_workspace_clear);
- *              every call leaves its counters at zero again. Calls that share
- *              a workspace must be ordered on one stream.
+ *              every call leaves its counters at zero again. The counters
+ *              sit at a fixed place at the start of every workspace, so one
+ *              workspace (sized for the largest matrix) may serve any mix of
+ *              matrices and calls. Calls that share a workspace must be
+ *              ordered on one stream.
  *   stream     compute stream. copy_stream: required when W is
  *              SPAX_RES_HOST_PINNED (only the selected columns are copied to
  *              device staging inside ws, in chunks overlapped with the
@@ -187,6 +193,26 @@ size_t spax_layer_workspace_bytes(const spax_layer* L);
 int spax_layer_step(const spax_layer* L, const spax_layer_io* io,
                     void* ws, size_t ws_bytes,
                     hipStream_t compute_stream, hipStream_t copy_stream);
+
+/* spax_set_kernel_choice -- which product kernel spax_layer_step uses for a
+ * group whose weights are device-resident (process-wide; set it before
+ * concurrent calls, not during them):
+ *   SPAX_KERNEL_AUTO       row-sliced kernel (every workgroup ranks the
+ *                          input and computes whole rows) where it applies
+ *                          -- fp16 full tier, at most 3 16-row chunks per
+ *                          workgroup, both lists within 8192 entries, input
+ *                          length <= 16384 -- else the split-column kernel
+ *                          with fused ranking, else ranking kernel + product;
+ *   SPAX_KERNEL_SPLIT      never the row-sliced kernel;
+ *   SPAX_KERNEL_ROWS_ONLY  only the row-sliced kernel; a group it cannot
+ *                          take fails with SPAX_EINVAL.
+ * All choices compute the same selection and products within the same
+ * error bound; results of different kernels differ in fp32 summation order.
+ * Errors: SPAX_EINVAL for an unknown value.                                 */
+#define SPAX_KERNEL_AUTO      0
+#define SPAX_KERNEL_SPLIT     1
+#define SPAX_KERNEL_ROWS_ONLY 2
+int spax_set_kernel_choice(int32_t choice);
 
 /* ---- offline helpers ---------------------------------------------------- */
 /* spax_pack_g128 -- encode the compressed copy of a matrix (SpAx page

@@ -18,3 +18,13 @@ def pytest_configure(config):
 @pytest.fixture(scope="session")
 def golden_dir():
     return GOLDEN
+
+
+@pytest.fixture(params=["auto", "split"])
+def kernel_choice(request):
+    """Runs a GPU test once with the default product-kernel choice of
+    spax_layer_step and once with the split-column kernel forced."""
+    import activation_sparse_decode_token_amd as spax
+    spax.set_kernel_choice({"auto": spax.KERNEL_AUTO, "split": spax.KERNEL_SPLIT}[request.param])
+    yield request.param
+    spax.set_kernel_choice(spax.KERNEL_AUTO)

@@ -48,8 +48,8 @@ def _matrix(rows=4096, cols=4096, ff=spax.FMT_FP16, af=spax.FMT_INT4_G128,
 def test_workspace_sizes():
     W = _matrix()
     ws = spax.gemv_workspace_bytes(W)
-    # counters (8 tiles, padded) + 64 splits of fp32 partials
-    assert ws == 256 + 64 * 4096 * 4
+    # fixed counter region (2048 tiles x 9 counters) + 64 splits of fp32 partials
+    assert ws == 2048 * 9 * 4 + 64 * 4096 * 4
     Wh = _matrix(res=spax.RES_HOST_PINNED)
     assert spax.gemv_workspace_bytes(Wh) >= ws + 4096 * 2 * 4096
     bad = _matrix(rows=100)
@@ -68,6 +68,7 @@ def test_gemv_validation_errors():
     assert _gemv(W, kf=-1) == -1
     assert _gemv(W, kf=3000, ka=2000) == -1
     assert _gemv(_matrix(rows=200)) == -1
+    assert _gemv(_matrix(rows=spax.MAX_ROWS + 128)) == -1
     assert _gemv(_matrix(af=spax.FMT_NONE), ka=5) == -1
     assert _gemv(W, x=None) == -2
     assert _gemv(W, fidx=None) == -2

@@ -80,8 +80,8 @@ CASES = [
 
 
 @pytest.mark.parametrize("R,n,ff,af,kf,ka", CASES)
-def test_fused_vs_oracle(R, n, ff, af, kf, ka):
-    log(f"fused R={R} n={n} {ff}/{af} kf={kf} ka={ka}")
+def test_fused_vs_oracle(R, n, ff, af, kf, ka, kernel_choice):
+    log(f"fused ({kernel_choice}) R={R} n={n} {ff}/{af} kf={kf} ka={ka}")
     Wt = WL.weights_fp16(820, R, "w", R, n, 0.02)
     x = WL.laplace_fp16(820, R, "x", n % 1000, n)
     err = _check(Wt, x, ff, af, kf, ka, f"R={R} n={n} {ff}/{af} kf={kf} ka={ka}")
@@ -89,7 +89,7 @@ def test_fused_vs_oracle(R, n, ff, af, kf, ka):
 
 
 @pytest.mark.parametrize("n", [300, 4096, 11008])
-def test_fused_ties(n):
+def test_fused_ties(n, kernel_choice):
     rs = np.random.default_rng(31 + n)
     Wt = WL.weights_fp16(821, 0, "w", 512, n, 0.02)
     cases = {
@@ -102,3 +102,21 @@ def test_fused_ties(n):
         for kf, ka in [(n // 4, n // 4), (n // 2, 0), (1, n - 1), (n // 3, n // 2)]:
             log(f"fused ties {name} n={n} kf={kf} ka={ka}")
             _check(Wt, x, "fp16", "int4", kf, ka, f"{name} n={n} kf={kf} ka={ka}")
+
+
+def test_rows_only_rejects_int4_full():
+    """SPAX_KERNEL_ROWS_ONLY fails cleanly (SPAX_EINVAL, nothing enqueued) for
+    a group the row-sliced kernel cannot take (int4 full tier)."""
+    import activation_sparse_decode_token_amd as spax
+    Wt = WL.weights_fp16(822, 0, "w", 256, 300, 0.02)
+    x = WL.laplace_fp16(822, 0, "x", 0, 300)
+    spax.set_kernel_choice(spax.KERNEL_ROWS_ONLY)
+    try:
+        with pytest.raises(spax.SpaxError) as ei:
+            _one_group(Wt, x, "int4", "int2", 30, 60)
+        assert ei.value.status == -1
+        y, F, A, _ = _one_group(Wt, x, "fp16", "int2", 30, 60)
+        oF, oA = O.plan_tiers(x, 30, 60)
+        assert np.array_equal(F, oF) and np.array_equal(A, oA)
+    finally:
+        spax.set_kernel_choice(spax.KERNEL_AUTO)

@@ -153,3 +153,25 @@ def test_full_size_70b_ffn():
     c = WL.CONFIGS[5]
     _full_size_case(5, 28672, 8192, "int4", "int2", c.splits[0], 0.015, 1, "70B gate")
     _full_size_case(5, 8192, 28672, "int4", "int2", c.splits[0], 0.015, 1, "70B down")
+
+
+def test_workspace_shared_by_heights():
+    """One workspace serves a tall matrix (80 row tiles, many splits) and a
+    short one in turn: their partial sums and arrival counters must never
+    overlap, whatever the heights."""
+    import torch
+    spax = _spax()
+    tall = WL.weights_fp16(830, 0, "w", 40960, 256, 0.02)
+    short = WL.weights_fp16(830, 1, "w", 512, 2048, 0.02)
+    Wt = _device_matrix(tall, "fp16", "int4")
+    Ws = _device_matrix(short, "fp16", "int4")
+    ws = torch.zeros(max(spax.gemv_workspace_bytes(Wt), spax.gemv_workspace_bytes(Ws)),
+                     dtype=torch.uint8, device="cuda:0")
+    for rep in range(3):
+        for Wd, Wh, n, label in ((Wt, tall, 256, "tall"), (Ws, short, 2048, "short")):
+            x = WL.laplace_fp16(830, rep, "x", n, n)
+            F, A = O.plan_tiers(x, n // 4, n // 4)
+            y, ws = _run(Wd, x, F, A, ws)
+            check_product(y, x, F, A, O.ColumnStore("fp16", Wh), O.ColumnStore("int4", Wh),
+                          f"{label} rep {rep}")
+    log("shared workspace ok")

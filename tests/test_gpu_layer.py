@@ -124,7 +124,7 @@ def _ks(hidden, inter, split):
 
 
 @pytest.mark.parametrize("ff,af", [("fp16", "int4"), ("int4", "int2"), ("fp16", "int2")])
-def test_layer_small(ff, af):
+def test_layer_small(ff, af, kernel_choice):
     hidden, inter = 512, 1408          # ragged tiles: 1408 = 2*512 + 384; gate/up 2816 rows
     w = LayerWeights(810, 0, hidden, inter, 0.02)
     ks = _ks(hidden, inter, WL.TierSplit(40, 30, 30))
@@ -138,7 +138,7 @@ def test_layer_small(ff, af):
     log(f"layer small {ff}/{af} ok")
 
 
-def test_layer_7b_shapes():
+def test_layer_7b_shapes(kernel_choice):
     w = LayerWeights(4, 0, 4096, 11008, 0.02)
     ks = _ks(4096, 11008, WL.CONFIGS[4].splits[0])
     L = _build_layer(w, "fp16", "int4", 0, ks)
@@ -159,6 +159,17 @@ def test_host_pinned_bitwise_equals_device(ff, af):
     ks = _ks(hidden, inter, WL.TierSplit(50, 25, 25))
     Ld = _build_layer(w, ff, af, 0, ks)
     Lh = _build_layer(w, ff, af, 1, ks)
+    # the host-resident mode runs the split-column kernel; with the same
+    # kernel on device-resident weights the results are bitwise equal
+    _spax().set_kernel_choice(_spax().KERNEL_SPLIT)
+    try:
+        _host_vs_device(w, ks, Ld, Lh, ff, af, hidden)
+    finally:
+        _spax().set_kernel_choice(_spax().KERNEL_AUTO)
+
+
+def _host_vs_device(w, ks, Ld, Lh, ff, af, hidden):
+    import torch
     cs = torch.cuda.Stream()
     ws_d = ws_h = None
     for tok in range(3):
