@@ -26,7 +26,7 @@ FMT_NONE, FMT_FP16, FMT_INT4_G128, FMT_INT2_G128 = 0, 1, 2, 3
 RES_DEVICE, RES_HOST_PINNED = 0, 1
 LAYOUT_PLAIN, LAYOUT_GLU_INTERLEAVED = 0, 1
 GROUP_QKV, GROUP_O, GROUP_GATE_UP, GROUP_DOWN = 0, 1, 2, 3
-KERNEL_AUTO, KERNEL_SPLIT, KERNEL_ROWS_ONLY = 0, 1, 2
+KERNEL_AUTO, KERNEL_SEPARATE = 0, 1
 MAX_ROWS = 1 << 20
 
 STATUS = {0: "SPAX_OK", -1: "SPAX_EINVAL", -2: "SPAX_ENULL", -3: "SPAX_EALIGN",
@@ -193,7 +193,7 @@ def version() -> int:
 
 
 def set_kernel_choice(choice: int) -> None:
-    """spax_set_kernel_choice: product kernel of layer_step (KERNEL_*)."""
+    """spax_set_kernel_choice: fused or separate selection in layer_step (KERNEL_*)."""
     _check(lib().spax_set_kernel_choice(int(choice)), "spax_set_kernel_choice")
 
 

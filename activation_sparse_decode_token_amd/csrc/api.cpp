@@ -126,29 +126,6 @@ bool plan_fused(const spax_matrix* W, int32_t kf, int32_t ka, ProductPlan* out) 
   return true;
 }
 
-// Row-sliced product (fused selection, whole rows per workgroup): 16-row
-// chunks dealt to at most SPAX_TARGET_BLOCKS workgroups, at most kRowsMaxM
-// each. Needs fp16 full-tier columns in device memory and both tier lists in
-// the workgroup's LDS.
-struct RowPlan {
-  int32_t chunks = 0;
-  int32_t m = 0;
-  int32_t grid = 0;
-};
-
-bool plan_rows(const spax_matrix* W, int32_t kf, int32_t ka, int32_t epi, RowPlan* out) {
-  if (W->residency != SPAX_RES_DEVICE || W->full_fmt != kFp16) return false;
-  if (W->cols > kRowsMaxN || (int64_t)kf + ka > kRowListCap) return false;
-  const int64_t rows_per_chunk = epi == kEpiGlu ? 2 * kChunkRows : kChunkRows;
-  const int64_t chunks = W->rows / rows_per_chunk;
-  const int64_t m = (chunks + SPAX_TARGET_BLOCKS - 1) / SPAX_TARGET_BLOCKS;
-  if (m < 1 || m > kRowsMaxM) return false;
-  out->chunks = (int32_t)chunks;
-  out->m = (int32_t)m;
-  out->grid = (int32_t)((chunks + m - 1) / m);
-  return true;
-}
-
 // Kernel choice of spax_layer_step (SPAX_KERNEL_*), process-wide.
 std::atomic<int32_t> g_kernel_choice{SPAX_KERNEL_AUTO};
 
@@ -308,37 +285,6 @@ int run_product(const spax_matrix* W, const uint16_t* x, const int32_t* fidx, in
   return SPAX_OK;
 }
 
-// Enqueue the row-sliced product with fused selection; the lists are
-// written to out_f / out_a.
-int run_rows(const spax_matrix* W, const uint16_t* x, int32_t kf, int32_t ka, int32_t epi,
-             uint16_t* y, uint16_t* ga, uint16_t* gg, uint16_t* gu, hipStream_t s,
-             const RowPlan& rp, int32_t* out_f, int32_t* out_a) {
-  GemvArgs a{};
-  a.rows = W->rows;
-  a.k_full = kf;
-  a.k_approx = ka;
-  a.n = W->cols;
-  a.x = x;
-  a.out_full_idx = out_f;
-  a.out_approx_idx = out_a;
-  a.y = y;
-  a.glu_a = ga;
-  a.glu_g = gg;
-  a.glu_u = gu;
-  a.full_base = static_cast<const uint8_t*>(W->full_data);
-  a.full_stride = col_bytes(W->full_fmt, W->rows);
-  a.full_bytes = (uint32_t)(a.full_stride * W->cols);
-  a.approx_base = W->approx_codes;
-  a.approx_stride = col_bytes(W->approx_fmt, W->rows);
-  a.approx_bytes = (uint32_t)(a.approx_stride * W->cols);
-  a.approx_scales = W->approx_scales;
-  a.approx_sstride = col_scales(W->approx_fmt, W->rows);
-  a.n_chunks = rp.chunks;
-  a.grid = rp.grid;
-  const hipError_t e = launch_rows(a, W->approx_fmt, epi, rp.m, s);
-  return e == hipSuccess ? SPAX_OK : hip_fail(e);
-}
-
 int check_counts(int32_t n, int32_t kf, int32_t ka) {
   if (kf < 0 || ka < 0 || (int64_t)kf + ka > n) return SPAX_EINVAL;
   return SPAX_OK;
@@ -365,8 +311,7 @@ extern "C" {
 int spax_version(void) { return 100; }
 
 int spax_set_kernel_choice(int32_t choice) {
-  if (choice != SPAX_KERNEL_AUTO && choice != SPAX_KERNEL_SPLIT && choice != SPAX_KERNEL_ROWS_ONLY)
-    return SPAX_EINVAL;
+  if (choice != SPAX_KERNEL_AUTO && choice != SPAX_KERNEL_SEPARATE) return SPAX_EINVAL;
   g_kernel_choice.store(choice, std::memory_order_relaxed);
   return SPAX_OK;
 }
@@ -428,13 +373,11 @@ int spax_layer_step(const spax_layer* L, const spax_layer_io* io, void* ws, size
                     hipStream_t compute_stream, hipStream_t copy_stream) {
   if (!L || !io) return SPAX_ENULL;
   const spax_matrix* G = L->group;
-  const bool ffn = G[SPAX_GROUP_GATE_UP].cols > 0;
-  if (ffn != (G[SPAX_GROUP_DOWN].cols > 0)) return SPAX_EINVAL;
-  if (ffn) {
-    if (G[SPAX_GROUP_GATE_UP].layout != SPAX_LAYOUT_GLU_INTERLEAVED) return SPAX_EINVAL;
-    if (G[SPAX_GROUP_DOWN].cols != G[SPAX_GROUP_GATE_UP].rows / 2) return SPAX_EINVAL;
-    if (G[SPAX_GROUP_DOWN].layout != SPAX_LAYOUT_PLAIN) return SPAX_EINVAL;
-  }
+  const bool has_gu = G[SPAX_GROUP_GATE_UP].cols > 0, has_dn = G[SPAX_GROUP_DOWN].cols > 0;
+  if (has_gu && G[SPAX_GROUP_GATE_UP].layout != SPAX_LAYOUT_GLU_INTERLEAVED) return SPAX_EINVAL;
+  if (has_dn && G[SPAX_GROUP_DOWN].layout != SPAX_LAYOUT_PLAIN) return SPAX_EINVAL;
+  if (has_gu && has_dn && G[SPAX_GROUP_DOWN].cols != G[SPAX_GROUP_GATE_UP].rows / 2)
+    return SPAX_EINVAL;
   const uint16_t* inputs[4] = {io->h, io->z, io->x, io->a};
   uint16_t* outputs[4] = {io->qkv, io->o, io->a, io->down};
   if (ws_bytes < spax_layer_workspace_bytes(L)) return SPAX_EWORKSPACE;
@@ -458,19 +401,13 @@ int spax_layer_step(const spax_layer* L, const spax_layer_io* io, void* ws, size
     uint16_t* gu = g == SPAX_GROUP_GATE_UP ? io->u : nullptr;
     const int32_t epi = g == SPAX_GROUP_GATE_UP ? kEpiGlu : kEpiPlain;
     ProductPlan fp;
-    RowPlan rp;
     int st;
     const int32_t choice = g_kernel_choice.load(std::memory_order_relaxed);
-    if (choice != SPAX_KERNEL_SPLIT && plan_rows(&G[g], kf, ka, epi, &rp)) {
-      // few rows per column split: whole rows per workgroup
-      st = run_rows(&G[g], inputs[g], kf, ka, epi, y, ga, gg, gu, compute_stream, rp,
-                    io->full_idx[g], io->approx_idx[g]);
-    } else if (choice != SPAX_KERNEL_ROWS_ONLY && plan_fused(&G[g], kf, ka, &fp)) {
+    if (choice == SPAX_KERNEL_AUTO && plan_fused(&G[g], kf, ka, &fp)) {
       // device-resident weights: selection fused into the product
       st = run_product(&G[g], inputs[g], nullptr, kf, nullptr, ka, epi, y, ga, gg, gu, ws,
                        compute_stream, copy_stream, &fp, io->full_idx[g], io->approx_idx[g]);
     } else {
-      if (choice == SPAX_KERNEL_ROWS_ONLY) return SPAX_EINVAL;
       hipError_t e = launch_plan(inputs[g], G[g].cols, kf, ka, io->full_idx[g],
                                  io->approx_idx[g], compute_stream);
       if (e != hipSuccess) return hip_fail(e);

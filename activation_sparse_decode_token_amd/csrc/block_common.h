@@ -51,7 +51,8 @@ struct Tier;
 template <>
 struct Tier<kFp16> {
   using V = uint4;
-  static constexpr int U = 8;
+  // columns per round (a round's loads stay in registers, double-buffered)
+  static constexpr int U = kWaves > 8 ? 4 : 8;
   // byte offset of lane l's 8 rows in a column
   static __device__ __forceinline__ uint32_t offset(int row0, int lane) {
     return 2u * (uint32_t)(row0 + 8 * lane);
@@ -188,6 +189,24 @@ __device__ __forceinline__ void wave_pick(int sel, uint32_t val, int& out_sel,
   }
 }
 
+// Adds E per-entry bins (-1: not counted) to an LDS histogram, one entry
+// per thread at a time. When the whole wave holds the same bin, one lane
+// adds 64 at once: skewed inputs (many equal magnitudes, e.g. exact zeros)
+// then do not serialise 64 atomics on one LDS address.
+template <int E>
+__device__ __forceinline__ void hist_add(uint32_t* hist, const int (&bin)[E]) {
+#pragma unroll
+  for (int i = 0; i < E; ++i) {
+    const int b = bin[i];
+    const int b0 = __builtin_amdgcn_readfirstlane(b);
+    if (__ballot(b == b0) == ~0ull) {  // wave-uniform
+      if (b0 >= 0 && (threadIdx.x & 63) == 0) atomicAdd(&hist[b0], 64u);
+    } else if (b >= 0) {
+      atomicAdd(&hist[b], 1u);
+    }
+  }
+}
+
 __device__ __forceinline__ uint32_t rawbits(const uint32_t* xr, int i) {
   return (xr[i >> 1] >> (16 * (i & 1))) & 0xFFFFu;
 }
@@ -207,19 +226,28 @@ __device__ __forceinline__ void rank_piece(const GemvArgs& a, RankShared& rs, in
   const uint32_t K1 = (uint32_t)a.k_full;
   const uint32_t K2 = (uint32_t)(a.k_full + a.k_approx);
 
-  // raw fp16 bits, two per register
+  // raw fp16 bits, two per register; loads of 8 entries (16 bytes), or of
+  // 4 (8 bytes) when a thread owns only 4
+  static_assert(E % 4 == 0, "entries per thread");
+  constexpr int kLoad = E >= 8 ? 8 : 4;
   uint32_t xr[E / 2];
 #pragma unroll
-  for (int i = 0; i < E; i += 8) {
-    if (base + i + 7 < n) {
-      const uint4 v = *reinterpret_cast<const uint4*>(a.x + base + i);
-      xr[i / 2 + 0] = v.x;
-      xr[i / 2 + 1] = v.y;
-      xr[i / 2 + 2] = v.z;
-      xr[i / 2 + 3] = v.w;
+  for (int i = 0; i < E; i += kLoad) {
+    if (base + i + kLoad - 1 < n) {
+      if constexpr (kLoad == 8) {
+        const uint4 v = *reinterpret_cast<const uint4*>(a.x + base + i);
+        xr[i / 2 + 0] = v.x;
+        xr[i / 2 + 1] = v.y;
+        xr[i / 2 + 2] = v.z;
+        xr[i / 2 + 3] = v.w;
+      } else {
+        const uint2 v = *reinterpret_cast<const uint2*>(a.x + base + i);
+        xr[i / 2 + 0] = v.x;
+        xr[i / 2 + 1] = v.y;
+      }
     } else {
 #pragma unroll
-      for (int j = 0; j < 8; j += 2) {
+      for (int j = 0; j < kLoad; j += 2) {
         const uint32_t lo = base + i + j < n ? a.x[base + i + j] : 0u;
         const uint32_t hi = base + i + j + 1 < n ? a.x[base + i + j + 1] : 0u;
         xr[(i + j) / 2] = lo | (hi << 16);
@@ -236,9 +264,12 @@ __device__ __forceinline__ void rank_piece(const GemvArgs& a, RankShared& rs, in
   __syncthreads();
 
   // 1. top-level histogram
+  {
+    int bin[E];
 #pragma unroll
-  for (int i = 0; i < E; ++i)
-    atomicAdd(&rs.hist[i < nv ? (rawbits(xr, i) & 0x7FFFu) >> 7 : 256u], 1u);
+    for (int i = 0; i < E; ++i) bin[i] = i < nv ? (int)((rawbits(xr, i) & 0x7FFFu) >> 7) : 256;
+    hist_add<E>(rs.hist, bin);
+  }
   __syncthreads();
 
   // 2. bins holding rank K1 and rank K2 (1-based, from the largest key),
@@ -271,12 +302,17 @@ __device__ __forceinline__ void rank_piece(const GemvArgs& a, RankShared& rs, in
   // 3. low-level histograms inside the two boundary bins
   const int b1 = rs.sel[0];
   const int b2 = rs.sel[2];
+  {
+    int s1[E], s2[E];
 #pragma unroll
-  for (int i = 0; i < E; ++i) {
-    const uint32_t k = rawbits(xr, i) & 0x7FFFu;
-    const int hb = i < nv ? (int)(k >> 7) : 256;
-    if (hb == b1) atomicAdd(&rs.sub[0][k & 127u], 1u);
-    if (hb == b2) atomicAdd(&rs.sub[1][k & 127u], 1u);
+    for (int i = 0; i < E; ++i) {
+      const uint32_t k = rawbits(xr, i) & 0x7FFFu;
+      const int hb = i < nv ? (int)(k >> 7) : 256;
+      s1[i] = hb == b1 ? (int)(k & 127u) : -1;
+      s2[i] = hb == b2 ? (int)(k & 127u) : -1;
+    }
+    hist_add<E>(rs.sub[0], s1);
+    hist_add<E>(rs.sub[1], s2);
   }
   __syncthreads();
   // boundary keys t (kAboveAll when the tier is empty) and quotas q: the

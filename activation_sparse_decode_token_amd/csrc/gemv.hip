@@ -302,10 +302,13 @@ __global__ __launch_bounds__(kGemvThreads) void gemv_kernel(GemvArgs a) {
   dst[1] = make_float4(acc[4], acc[5], acc[6], acc[7]);
   __syncthreads();
 
-  // thread t owns row t of the tile from here on
+  // thread t < kTileRows owns row t of the tile from here on
+  const bool owner = t < kTileRows;
   float p = 0.0f;
+  if (owner) {
 #pragma unroll
-  for (int w = 0; w < kWaves; ++w) p += sm.red[w][t];
+    for (int w = 0; w < kWaves; ++w) p += sm.red[w][t];
+  }
   const int r = row0 + t;
 
   if (a.n_splits > 1) {
@@ -316,7 +319,7 @@ __global__ __launch_bounds__(kGemvThreads) void gemv_kernel(GemvArgs a) {
     // to complete before the counter increment orders them for every XCD.
     float* part = a.partials;
     const int64_t rows = a.rows;
-    if (r < a.rows)
+    if (owner && r < a.rows)
       __hip_atomic_store(&part[split * rows + r], p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     __atomic_signal_fence(__ATOMIC_SEQ_CST);
     __builtin_amdgcn_s_waitcnt(0);  // this lane's stores are complete
@@ -350,24 +353,26 @@ __global__ __launch_bounds__(kGemvThreads) void gemv_kernel(GemvArgs a) {
     // partials are added in split order; the loads of up to 32 splits are
     // issued together (clamped to valid addresses, unused ones not added)
     p = 0.0f;
-    const int64_t rr = min(r, a.rows - 1);
-    for (int s0 = 0; s0 < a.n_splits; s0 += 32) {
-      float v[32];
+    if (owner) {
+      const int64_t rr = min(r, a.rows - 1);
+      for (int s0 = 0; s0 < a.n_splits; s0 += 32) {
+        float v[32];
 #pragma unroll
-      for (int u = 0; u < 32; ++u)
-        v[u] = __hip_atomic_load(&part[(int64_t)min(s0 + u, a.n_splits - 1) * rows + rr],
-                                 __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        for (int u = 0; u < 32; ++u)
+          v[u] = __hip_atomic_load(&part[(int64_t)min(s0 + u, a.n_splits - 1) * rows + rr],
+                                   __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 #pragma unroll
-      for (int u = 0; u < 32; ++u)
-        if (s0 + u < a.n_splits) p += v[u];
+        for (int u = 0; u < 32; ++u)
+          if (s0 + u < a.n_splits) p += v[u];
+      }
     }
   }
 
   if constexpr (EPI == kEpiPlain) {
-    if (r < a.rows) a.y[r] = f2h(p);
+    if (owner && r < a.rows) a.y[r] = f2h(p);
   } else {
     __syncthreads();
-    sm.red[0][t] = p;
+    if (owner) sm.red[0][t] = p;
     __syncthreads();
     if (t < kTileRows / 2) {
       const int i1 = (t >> 7) * 256 + (t & 127);
@@ -390,6 +395,7 @@ template <int FF, int AF>
 hipError_t launch_mode(const GemvArgs& a, int32_t mode, int32_t epi, hipStream_t s) {
   if (mode == kListStaged) return launch_epi<FF, AF, kListStaged, 0>(a, epi, s);
   if (mode == kListGlobal) return launch_epi<FF, AF, kListGlobal, 0>(a, epi, s);
+  if (a.n <= kGemvThreads * 4) return launch_epi<FF, AF, kListRank, 4>(a, epi, s);
   if (a.n <= kGemvThreads * 8) return launch_epi<FF, AF, kListRank, 8>(a, epi, s);
   if (a.n <= kGemvThreads * 16) return launch_epi<FF, AF, kListRank, 16>(a, epi, s);
   if (a.n <= kGemvThreads * 32) return launch_epi<FF, AF, kListRank, 32>(a, epi, s);

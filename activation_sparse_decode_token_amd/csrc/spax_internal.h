@@ -10,7 +10,10 @@ namespace spax {
 // Rows of one workgroup tile of the tiered product: 64 lanes x 8 rows.
 constexpr int kTileRows = 512;
 // Waves per workgroup of the tiered product.
-constexpr int kWaves = 8;
+#ifndef SPAX_WAVES
+#define SPAX_WAVES 16
+#endif
+constexpr int kWaves = SPAX_WAVES;
 constexpr int kGemvThreads = kWaves * 64;
 // Upper bound on column splits of one product (size of the fp32 partials).
 constexpr int kMaxSplits = 64;
@@ -29,12 +32,6 @@ constexpr int kGroup = 128;
 constexpr int kListCap = 2048;
 // Largest input length the fused rank + product handles (64 per thread).
 constexpr int kRankMaxN = kGemvThreads * 64;
-// Row-sliced product: rows per chunk, chunks per workgroup, list capacity
-// (both tiers, in LDS) and largest input length.
-constexpr int kChunkRows = 16;
-constexpr int kRowsMaxM = 3;
-constexpr int kRowListCap = 8192;
-constexpr int kRowsMaxN = kGemvThreads * 32;
 
 enum Fmt : int32_t { kNone = 0, kFp16 = 1, kInt4 = 2, kInt2 = 3 };
 enum Epi : int32_t { kEpiPlain = 0, kEpiGlu = 1 };
@@ -77,9 +74,6 @@ struct GemvArgs {
   uint16_t* glu_a;               // glu: fp16[rows/2]
   uint16_t* glu_g;               // optional
   uint16_t* glu_u;               // optional
-  // row-sliced product only
-  int32_t n_chunks;              // 16-row chunks (GLU: chunks of gate rows)
-  int32_t grid;                  // workgroups; workgroup b takes chunks b, b + grid, ...
 };
 
 // Selected-column copy from host-resident storage into device staging.
@@ -104,11 +98,6 @@ hipError_t launch_plan(const uint16_t* x, int32_t n, int32_t k_full, int32_t k_a
 
 hipError_t launch_gemv(const GemvArgs& a, int32_t full_fmt, int32_t approx_fmt,
                        int32_t mode, int32_t epi, hipStream_t s);
-
-// Row-sliced product with fused selection: full tier fp16, up to m chunks
-// per workgroup.
-hipError_t launch_rows(const GemvArgs& a, int32_t approx_fmt, int32_t epi, int32_t m,
-                       hipStream_t s);
 
 hipError_t launch_copy(const CopyArgs& a, hipStream_t s);
 

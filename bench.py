@@ -556,8 +556,8 @@ def parse():
                    help="run another benchmark workload (1, 3, 4, 5) instead of the headline")
     p.add_argument("--host", action="store_true",
                    help="with --config 4: weights in pinned host memory")
-    p.add_argument("--kernel", choices=("auto", "split"), default="auto",
-                   help="product kernel of the layer step (default: the library's choice)")
+    p.add_argument("--select", choices=("fused", "separate"), default="fused",
+                   help="tier selection inside the product (default) or a separate kernel")
     return p.parse_args()
 
 
@@ -567,9 +567,9 @@ def main():
         print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "
               "(the path has no multi-GPU mode)", file=sys.stderr)
         sys.exit(2)
-    if args.kernel != "auto":
+    if args.select != "fused":
         import activation_sparse_decode_token_amd as spax
-        spax.set_kernel_choice(spax.KERNEL_SPLIT)
+        spax.set_kernel_choice(spax.KERNEL_SEPARATE)
     if args.config is not None and args.config != 2:
         run_config(args)
         return

@@ -157,8 +157,9 @@ int spax_tiered_gemv(const spax_matrix* W, const uint16_t* x,
 /* The seven matrices of a layer in the four groups that share a ranking
  * (section 2; section 5.2 step 1; section 5.3 Figure 4). A group whose
  * matrix has cols == 0 is absent and skipped. GATE_UP must use
- * SPAX_LAYOUT_GLU_INTERLEAVED and DOWN must have cols == GATE_UP.rows / 2;
- * GATE_UP and DOWN are present together or not at all. */
+ * SPAX_LAYOUT_GLU_INTERLEAVED; with both present, DOWN must have
+ * cols == GATE_UP.rows / 2 and reads the a that GATE_UP writes. DOWN alone
+ * reads a caller-provided a (io->a). */
 typedef struct spax_layer {
   spax_matrix group[4];
   int32_t k_full[4];
@@ -194,24 +195,19 @@ int spax_layer_step(const spax_layer* L, const spax_layer_io* io,
                     void* ws, size_t ws_bytes,
                     hipStream_t compute_stream, hipStream_t copy_stream);
 
-/* spax_set_kernel_choice -- which product kernel spax_layer_step uses for a
- * group whose weights are device-resident (process-wide; set it before
- * concurrent calls, not during them):
- *   SPAX_KERNEL_AUTO       row-sliced kernel (every workgroup ranks the
- *                          input and computes whole rows) where it applies
- *                          -- fp16 full tier, at most 3 16-row chunks per
- *                          workgroup, both lists within 8192 entries, input
- *                          length <= 16384 -- else the split-column kernel
- *                          with fused ranking, else ranking kernel + product;
- *   SPAX_KERNEL_SPLIT      never the row-sliced kernel;
- *   SPAX_KERNEL_ROWS_ONLY  only the row-sliced kernel; a group it cannot
- *                          take fails with SPAX_EINVAL.
- * All choices compute the same selection and products within the same
- * error bound; results of different kernels differ in fp32 summation order.
+/* spax_set_kernel_choice -- how spax_layer_step runs a group whose weights
+ * are device-resident (process-wide; set it before concurrent calls, not
+ * during them):
+ *   SPAX_KERNEL_AUTO      the tiered product ranks the input itself (every
+ *                         workgroup selects the tiers in LDS) where the input
+ *                         length and list pieces allow, else as below;
+ *   SPAX_KERNEL_SEPARATE  always the stand-alone selection kernel, then the
+ *                         tiered product reading the lists from memory.
+ * Both compute the same lists; the products agree within the error bound of
+ * spax_tiered_gemv (bitwise when both cut the lists into the same splits).
  * Errors: SPAX_EINVAL for an unknown value.                                 */
-#define SPAX_KERNEL_AUTO      0
-#define SPAX_KERNEL_SPLIT     1
-#define SPAX_KERNEL_ROWS_ONLY 2
+#define SPAX_KERNEL_AUTO     0
+#define SPAX_KERNEL_SEPARATE 1
 int spax_set_kernel_choice(int32_t choice);
 
 /* ---- offline helpers ---------------------------------------------------- */

@@ -20,11 +20,13 @@ def golden_dir():
     return GOLDEN
 
 
-@pytest.fixture(params=["auto", "split"])
+@pytest.fixture(params=["fused", "separate"])
 def kernel_choice(request):
-    """Runs a GPU test once with the default product-kernel choice of
-    spax_layer_step and once with the split-column kernel forced."""
+    """Runs a GPU test once with the selection fused into the product (the
+    default of spax_layer_step) and once with the stand-alone selection
+    kernel followed by the list-reading product."""
     import activation_sparse_decode_token_amd as spax
-    spax.set_kernel_choice({"auto": spax.KERNEL_AUTO, "split": spax.KERNEL_SPLIT}[request.param])
+    spax.set_kernel_choice({"fused": spax.KERNEL_AUTO,
+                            "separate": spax.KERNEL_SEPARATE}[request.param])
     yield request.param
     spax.set_kernel_choice(spax.KERNEL_AUTO)

@@ -100,8 +100,15 @@ def test_layer_and_helper_validation_errors():
     io = spax.LayerIO.make(h=P, z=P, x=P, qkv=P, o=P, a=P, down=P, full_idx=(P,) * 4,
                            approx_idx=(P,) * 4)
     f = spax.lib().spax_layer_step
-    # gate/up without down
+    # gate/up alone needs its output a
     L = spax.Layer.make([W, None, gu, None], [1] * 4, [1] * 4)
+    io_no_a = spax.LayerIO.make(h=P, z=P, x=P, qkv=P, o=P, a=None, down=P, full_idx=(P,) * 4,
+                                approx_idx=(P,) * 4)
+    assert f(ctypes.byref(L), ctypes.byref(io_no_a), P2, 1 << 30, None, None) == -2
+    # down needs the plain layout
+    L = spax.Layer.make([None, None, None, _matrix(rows=4096, cols=11008,
+                                                   layout=spax.LAYOUT_GLU_INTERLEAVED)],
+                        [1] * 4, [1] * 4)
     assert f(ctypes.byref(L), ctypes.byref(io), P2, 1 << 30, None, None) == -1
     # down width must match the gate/up intermediate size
     L = spax.Layer.make([None, None, gu, _matrix(rows=4096, cols=4096)], [1] * 4, [1] * 4)

@@ -103,20 +103,3 @@ def test_fused_ties(n, kernel_choice):
             log(f"fused ties {name} n={n} kf={kf} ka={ka}")
             _check(Wt, x, "fp16", "int4", kf, ka, f"{name} n={n} kf={kf} ka={ka}")
 
-
-def test_rows_only_rejects_int4_full():
-    """SPAX_KERNEL_ROWS_ONLY fails cleanly (SPAX_EINVAL, nothing enqueued) for
-    a group the row-sliced kernel cannot take (int4 full tier)."""
-    import activation_sparse_decode_token_amd as spax
-    Wt = WL.weights_fp16(822, 0, "w", 256, 300, 0.02)
-    x = WL.laplace_fp16(822, 0, "x", 0, 300)
-    spax.set_kernel_choice(spax.KERNEL_ROWS_ONLY)
-    try:
-        with pytest.raises(spax.SpaxError) as ei:
-            _one_group(Wt, x, "int4", "int2", 30, 60)
-        assert ei.value.status == -1
-        y, F, A, _ = _one_group(Wt, x, "fp16", "int2", 30, 60)
-        oF, oA = O.plan_tiers(x, 30, 60)
-        assert np.array_equal(F, oF) and np.array_equal(A, oA)
-    finally:
-        spax.set_kernel_choice(spax.KERNEL_AUTO)

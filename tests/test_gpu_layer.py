@@ -159,13 +159,7 @@ def test_host_pinned_bitwise_equals_device(ff, af):
     ks = _ks(hidden, inter, WL.TierSplit(50, 25, 25))
     Ld = _build_layer(w, ff, af, 0, ks)
     Lh = _build_layer(w, ff, af, 1, ks)
-    # the host-resident mode runs the split-column kernel; with the same
-    # kernel on device-resident weights the results are bitwise equal
-    _spax().set_kernel_choice(_spax().KERNEL_SPLIT)
-    try:
-        _host_vs_device(w, ks, Ld, Lh, ff, af, hidden)
-    finally:
-        _spax().set_kernel_choice(_spax().KERNEL_AUTO)
+    _host_vs_device(w, ks, Ld, Lh, ff, af, hidden)
 
 
 def _host_vs_device(w, ks, Ld, Lh, ff, af, hidden):
