@@ -142,16 +142,17 @@ struct Tier<kInt2> {
 //   2. suffix counts give the bins holding rank k_full and k_full + k_approx;
 //   3. 128-bin histograms inside those bins give the boundary keys t1, t2
 //      and the number of entries equal to each that are kept (q1, q2);
-//   4. one block scan of (#key > t1, #key == t1, #key > t2, #key == t2) gives
-//      every entry its position: #F before entry i is
-//      gt1(i) + min(eq1(i), q1), #(F or A) before it gt2(i) + min(eq2(i), q2).
+//   4. one block scan of (#key > t1, #key == t1, #key > t2, #key == t2),
+//      packed two counts per register, gives every entry its position: #F
+//      before entry i is gt1(i) + min(eq1(i), q1), #(F or A) before it
+//      gt2(i) + min(eq2(i), q2).
 // ---------------------------------------------------------------------------
 constexpr uint32_t kAboveAll = 0x8000u;  // boundary key when a tier is empty
 
 struct RankShared {
   uint32_t hist[257];  // bin 256 absorbs the padding past n
   uint32_t sub[2][128];
-  uint32_t scan[4][kWaves];
+  uint32_t scan[2][kWaves];  // packed count pairs, per wave
   int32_t sel[8];  // b1, entries above b1, b2, entries above b2, t1, q1, t2, q2
 };
 
@@ -164,6 +165,15 @@ __device__ __forceinline__ uint32_t wave_incl_scan(uint32_t v) {
   v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x118, 0xf, 0xf, false);  // row_shr:8
   v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x142, 0xa, 0xf, false);  // row_bcast:15
   v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x143, 0xc, 0xf, false);  // row_bcast:31
+  return v;
+}
+
+// Inclusive prefix sum within each 16-lane row (row shifts only).
+__device__ __forceinline__ uint32_t row16_incl_scan(uint32_t v) {
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x111, 0xf, 0xf, false);  // row_shr:1
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x112, 0xf, 0xf, false);  // row_shr:2
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x114, 0xf, 0xf, false);  // row_shr:4
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x118, 0xf, 0xf, false);  // row_shr:8
   return v;
 }
 
@@ -355,25 +365,26 @@ __device__ __forceinline__ void rank_piece(const GemvArgs& a, RankShared& rs, in
     c[2] += ok && k > t2;
     c[3] += ok && k == t2;
   }
-  uint32_t in[4];
-#pragma unroll
-  for (int j = 0; j < 4; ++j) in[j] = wave_incl_scan(c[j]);
+  // Scans run on the counts packed two per register: every partial sum
+  // below is under 2^16 (at most 64 * E per wave, 15 waves before any
+  // wave), and the packed sums subtract exactly.
+  static_assert(kWaves <= 16, "wave totals fit one 16-lane row");
+  const uint32_t p01 = c[0] | (c[1] << 16), p23 = c[2] | (c[3] << 16);
+  const uint32_t i01 = wave_incl_scan(p01), i23 = wave_incl_scan(p23);
   if (lane == 63) {
-#pragma unroll
-    for (int j = 0; j < 4; ++j) rs.scan[j][wave] = in[j];
+    rs.scan[0][wave] = i01;
+    rs.scan[1][wave] = i23;
   }
   __syncthreads();
-  // totals of the waves before this one: lanes 0..7 hold the wave totals,
-  // a lane scan gives their prefixes, lane `wave` holds this wave's
+  // totals of the waves before this one: lane 16 h + w holds wave w's total
+  // of pair h; a scan within each 16-lane row gives the prefixes
   const int wv = __builtin_amdgcn_readfirstlane(wave);
-  uint32_t pre[4];
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const uint32_t wt = lane < kWaves ? rs.scan[j][lane] : 0u;
-    pre[j] = (uint32_t)__builtin_amdgcn_readlane((int)(wave_incl_scan(wt) - wt), wv);
-  }
-  uint32_t g1 = pre[0] + in[0] - c[0], e1r = pre[1] + in[1] - c[1];
-  uint32_t g2 = pre[2] + in[2] - c[2], e2r = pre[3] + in[3] - c[3];
+  const uint32_t wt = (lane >> 4) < 2 && (lane & 15) < kWaves ? rs.scan[lane >> 4][lane & 15] : 0u;
+  const uint32_t wex = row16_incl_scan(wt) - wt;
+  const uint32_t ex01 = (uint32_t)__builtin_amdgcn_readlane((int)wex, wv) + i01 - p01;
+  const uint32_t ex23 = (uint32_t)__builtin_amdgcn_readlane((int)wex, 16 + wv) + i23 - p23;
+  uint32_t g1 = ex01 & 0xFFFFu, e1r = ex01 >> 16;
+  uint32_t g2 = ex23 & 0xFFFFu, e2r = ex23 >> 16;
   // This thread's F positions [fs, fe) and A positions [as, ae); only
   // threads whose positions meet the piece place entries. Entries past n
   // (key 0, after every real entry) are never placed: a boundary key 0
