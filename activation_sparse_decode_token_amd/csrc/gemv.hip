@@ -208,19 +208,21 @@ struct TierStream {
 
 // Block -> (split, tile): groups of 8 consecutive splits are interleaved so
 // that block b and split (b mod 8) coincide on the XCD that runs block b.
-__device__ __forceinline__ void map_block(int b, int n_tiles, int splits_here, int& s_loc,
-                                          int& tile) {
-  const int groups = splits_here >> 3;
-  const int fb = groups * 8 * n_tiles;
+// (unsigned 32-bit arithmetic: the divisions are short on the scalar unit)
+__device__ __forceinline__ void map_block(uint32_t b, uint32_t n_tiles, uint32_t splits_here,
+                                          int& s_loc, int& tile) {
+  const uint32_t groups = splits_here >> 3;
+  const uint32_t fb = groups * 8u * n_tiles;
   if (b < fb) {
-    const int g = b / (8 * n_tiles);
-    const int r = b - g * 8 * n_tiles;
-    s_loc = g * 8 + (r & 7);
-    tile = r >> 3;
+    const uint32_t g = b / (8u * n_tiles);
+    const uint32_t r = b - g * 8u * n_tiles;
+    s_loc = (int)(g * 8u + (r & 7u));
+    tile = (int)(r >> 3);
   } else {
-    const int r = b - fb;
-    s_loc = groups * 8 + r / n_tiles;
-    tile = r % n_tiles;
+    const uint32_t r = b - fb;
+    const uint32_t q = r / n_tiles;
+    s_loc = (int)(groups * 8u + q);
+    tile = (int)(r - q * n_tiles);
   }
 }
 

@@ -109,8 +109,10 @@ hipError_t launch_clear(void* ws, size_t bytes, hipStream_t s);
 // List positions of split s of n_splits: every split takes the same share
 // of each tier, [k * s / n_splits, k * (s + 1) / n_splits), so every
 // workgroup gets the same mix of full columns (bytes) and code columns
-// (bytes plus dequantisation arithmetic).
-__host__ __device__ inline int32_t split_pos(int64_t s, int64_t n_splits, int64_t k) {
+// (bytes plus dequantisation arithmetic). 32-bit arithmetic: k * n_splits
+// stays below 2^32 (k <= columns, which are below 2^26 since a tier holds
+// under 2^31 bytes of at least 32-byte columns, and n_splits <= 64).
+__host__ __device__ inline int32_t split_pos(uint32_t s, uint32_t n_splits, uint32_t k) {
   return (int32_t)(k * s / n_splits);
 }
 
