@@ -203,11 +203,11 @@ __device__ __forceinline__ void wave_pick(int sel, uint32_t val, int& out_sel,
 // per thread at a time. When the whole wave holds the same bin, one lane
 // adds 64 at once: skewed inputs (many equal magnitudes, e.g. exact zeros)
 // then do not serialise 64 atomics on one LDS address.
-template <int E>
-__device__ __forceinline__ void hist_add(uint32_t* hist, const int (&bin)[E]) {
+template <int E, class BinOf>
+__device__ __forceinline__ void hist_add(uint32_t* hist, BinOf bin_of) {
 #pragma unroll
   for (int i = 0; i < E; ++i) {
-    const int b = bin[i];
+    const int b = bin_of(i);
     const int b0 = __builtin_amdgcn_readfirstlane(b);
     if (__ballot(b == b0) == ~0ull) {  // wave-uniform
       if (b0 >= 0 && (threadIdx.x & 63) == 0) atomicAdd(&hist[b0], 64u);
@@ -274,12 +274,9 @@ __device__ __forceinline__ void rank_piece(const GemvArgs& a, RankShared& rs, in
   __syncthreads();
 
   // 1. top-level histogram
-  {
-    int bin[E];
-#pragma unroll
-    for (int i = 0; i < E; ++i) bin[i] = i < nv ? (int)((rawbits(xr, i) & 0x7FFFu) >> 7) : 256;
-    hist_add<E>(rs.hist, bin);
-  }
+  hist_add<E>(rs.hist, [&](int i) {
+    return i < nv ? (int)((rawbits(xr, i) & 0x7FFFu) >> 7) : 256;
+  });
   __syncthreads();
 
   // 2. bins holding rank K1 and rank K2 (1-based, from the largest key),
@@ -312,18 +309,13 @@ __device__ __forceinline__ void rank_piece(const GemvArgs& a, RankShared& rs, in
   // 3. low-level histograms inside the two boundary bins
   const int b1 = rs.sel[0];
   const int b2 = rs.sel[2];
-  {
-    int s1[E], s2[E];
-#pragma unroll
-    for (int i = 0; i < E; ++i) {
-      const uint32_t k = rawbits(xr, i) & 0x7FFFu;
-      const int hb = i < nv ? (int)(k >> 7) : 256;
-      s1[i] = hb == b1 ? (int)(k & 127u) : -1;
-      s2[i] = hb == b2 ? (int)(k & 127u) : -1;
-    }
-    hist_add<E>(rs.sub[0], s1);
-    hist_add<E>(rs.sub[1], s2);
-  }
+  auto sub_bin = [&](int i, int b) {
+    const uint32_t k = rawbits(xr, i) & 0x7FFFu;
+    const int hb = i < nv ? (int)(k >> 7) : 256;
+    return hb == b ? (int)(k & 127u) : -1;
+  };
+  hist_add<E>(rs.sub[0], [&](int i) { return sub_bin(i, b1); });
+  hist_add<E>(rs.sub[1], [&](int i) { return sub_bin(i, b2); });
   __syncthreads();
   // boundary keys t (kAboveAll when the tier is empty) and quotas q: the
   // number of entries equal to t that are kept; found by wave 0

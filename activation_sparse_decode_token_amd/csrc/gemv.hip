@@ -55,13 +55,9 @@
 namespace spax {
 namespace {
 
-// Metadata of one wave's current 64-column batch of one tier, in LDS: the
-// column (stored index, or staging position) and the factor each lane
-// multiplies that column by -- x_j for fp16 columns, x_j * s_{j,g} for code
-// columns, one per 128-row group g of the tile. Slots past the batch hold a
-// factor of 0.
+// Factors of one wave's current 64-column batch of a code tier, in LDS:
+// x_j * s_{j,g} for each 128-row group g of the tile (0 past the batch).
 struct WaveMeta {
-  int32_t col[64];
   float fac[64][4];
 };
 
@@ -72,16 +68,22 @@ __device__ __forceinline__ void wave_sync() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
+__device__ __forceinline__ float readlane_f(float v, int l) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), l));
+}
+
 // One wave's stream over list positions [p_lo, p_hi) of one tier, for its
 // rows of the tile. Batches of 64 columns: lane l fetches position p + l
 // (kListGlobal: index list and activations in device memory; kListStaged:
 // staging position, activation via the index list; kListRank: the
-// workgroup's piece in LDS) and publishes it in the wave's LDS metadata.
+// workgroup's piece in LDS) and keeps the column and activation in
+// registers; each column's index (and an fp16 column's activation) reaches
+// the wave with readlane. Code tiers form x_j * s_{j,g} per lane and group
+// in LDS, since each lane needs the factor of its own 128-row group.
 // Rounds of U columns are double-buffered: the loads of round r + 1 are
 // issued before round r is consumed, so a wave always has a round in
-// flight; each step issues and consumes in one straight-line block. Slots
-// past the batch reload its last column and add it times zero, which keeps
-// every load unconditional.
+// flight. Slots past the batch reload its last column and are not added,
+// which keeps every load unconditional.
 // begin() issues the first round early -- before the other tier is
 // streamed -- so the two tiers' first loads share one memory latency. The
 // code loads of a batch are issued before its scales have arrived; the
@@ -105,8 +107,9 @@ struct TierStream {
   const float* lx;
   int p_lo, p_hi;
   V v0[U];
+  int mycol;       // this lane's column of the pending batch
+  float xv;        // this lane's activation of the pending batch (0 past it)
   uint32_t sc[4];  // this lane's raw fp16 scales of the pending batch (codes)
-  float xv;        // this lane's activation of the pending batch
 
   __device__ __forceinline__ TierStream(WaveMeta& wm_, const uint8_t* base, int64_t stride,
                                         uint32_t bytes, const uint16_t* scales_, int64_t sstride_,
@@ -119,10 +122,11 @@ struct TierStream {
         scales(scales_), sstride(sstride_), idx(idx_), x(x_), lidx(lidx_), lx(lx_),
         p_lo(p_lo_), p_hi(p_hi_) {}
 
-  // Columns of the batch at pb to LDS; this lane's activation and (codes)
-  // raw scales to registers, without waiting for the scales.
+  // This lane's column and activation of the batch at pb, and (codes) its
+  // raw scales, without waiting for the scales.
   __device__ __forceinline__ void fill_cols(int pb, int cnt) {
     xv = 0.0f;
+    mycol = 0;
     if (lane < cnt) {
       const int q = pb + lane;
       int j;
@@ -133,19 +137,26 @@ struct TierStream {
         j = idx[q];
         xv = h2f(x[j]);
       }
-      const int col = MODE == kListStaged ? q : j;
-      wm.col[lane] = col;
+      mycol = MODE == kListStaged ? q : j;
       if constexpr (kCode) {
-        // a ragged last tile has fewer groups; their slots are never read
-        // (lanes past the last row take group 0's rows)
-        const uint16_t* sp = scales + (int64_t)col * sstride + (row0 >> 7);
-        const int gl = ngrp - 1;
+        const uint16_t* sp = scales + (int64_t)mycol * sstride + (row0 >> 7);
+        if (ngrp == 4 && (sstride & 3) == 0) {
+          // the tile's 4 group scales in one 8-byte load (aligned: row0 is
+          // a multiple of 512 and a column's scales start 8-byte aligned)
+          const uint2 v = *reinterpret_cast<const uint2*>(sp);
+          sc[0] = v.x & 0xFFFFu;
+          sc[1] = v.x >> 16;
+          sc[2] = v.y & 0xFFFFu;
+          sc[3] = v.y >> 16;
+        } else {
+          // a ragged last tile has fewer groups; their slots are never read
+          // (lanes past the last row take group 0's rows)
+          const int gl = ngrp - 1;
 #pragma unroll
-        for (int g = 0; g < 4; ++g) sc[g] = sp[min(g, gl)];
+          for (int g = 0; g < 4; ++g) sc[g] = sp[min(g, gl)];
+        }
       }
     }
-    if constexpr (!kCode) wm.fac[lane][0] = xv;
-    wave_sync();
   }
   // Code factors x_j * s_{j,g} of the pending batch (0 past the batch).
   __device__ __forceinline__ void fill_facs(int cnt) {
@@ -157,13 +168,23 @@ struct TierStream {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int c = min(r * U + u, cnt - 1);
-      const uint32_t col = (uint32_t)__builtin_amdgcn_readfirstlane(wm.col[c]);
+      const uint32_t col = (uint32_t)__builtin_amdgcn_readlane(mycol, c);
       v[u] = T::load(rs, off, col * cstride);
     }
   }
-  __device__ __forceinline__ void use(float (&acc)[8], float& corr, int r, const V (&v)[U]) {
+  __device__ __forceinline__ void use(float (&acc)[8], float& corr, int r, int cnt,
+                                      const V (&v)[U]) {
+    if ((r + 1) * U <= cnt) {  // a full round (wave-uniform)
 #pragma unroll
-    for (int u = 0; u < U; ++u) T::fma(acc, corr, v[u], wm.fac[r * U + u][gsel]);
+      for (int u = 0; u < U; ++u)
+        T::fma(acc, corr, v[u], kCode ? wm.fac[r * U + u][gsel] : readlane_f(xv, r * U + u));
+    } else {  // the batch's last, partial round: only its columns are added
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int c = r * U + u;
+        if (c < cnt) T::fma(acc, corr, v[u], kCode ? wm.fac[c][gsel] : readlane_f(xv, c));
+      }
+    }
   }
 
   __device__ __forceinline__ void begin() {
@@ -187,17 +208,17 @@ struct TierStream {
       for (int r = 0;;) {
         if (r + 1 < rounds) {
           issue(r + 1, cnt, v1);
-          use(acc, corr, r, v0);
+          use(acc, corr, r, cnt, v0);
         } else {
-          use(acc, corr, r, v0);
+          use(acc, corr, r, cnt, v0);
           break;
         }
         ++r;
         if (r + 1 < rounds) {
           issue(r + 1, cnt, v0);
-          use(acc, corr, r, v1);
+          use(acc, corr, r, cnt, v1);
         } else {
-          use(acc, corr, r, v1);
+          use(acc, corr, r, cnt, v1);
           break;
         }
         ++r;
