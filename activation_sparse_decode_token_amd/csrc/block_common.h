@@ -33,14 +33,6 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t tier_rsrc(const uint8_t* p, ui
                                            0x00020000);
 }
 
-// Opaque to the optimiser: keeps the byte-wise code extraction below from
-// being folded into per-value bit-field extracts, so each value is one
-// v_cvt_f32_ubyteN.
-__device__ __forceinline__ uint32_t opaque(uint32_t v) {
-  asm volatile("" : "+v"(v));
-  return v;
-}
-
 // Per-format load and multiply-add of one lane's 8 consecutive rows of one
 // column: fp16 values (16 bytes), int4 codes (4 bytes) or int2 codes
 // (2 bytes). offset(row0, lane) is the byte offset, within a column, of
@@ -60,8 +52,10 @@ struct Tier<kFp16> {
   static __device__ __forceinline__ V load(__amdgpu_buffer_rsrc_t t, uint32_t off, uint32_t col) {
     return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(t, off, col, 0));
   }
+  static constexpr float kScale = 1.0f;
+  static constexpr uint32_t kMask = 0u;
   // f = x_j
-  static __device__ __forceinline__ void fma(float (&acc)[8], float&, V v, float f) {
+  static __device__ __forceinline__ void fma(float (&acc)[8], float&, V v, float f, uint32_t) {
     acc[0] = fmaf(h2f(v.x & 0xFFFFu), f, acc[0]);
     acc[1] = fmaf(h2f(v.x >> 16), f, acc[1]);
     acc[2] = fmaf(h2f(v.y & 0xFFFFu), f, acc[2]);
@@ -73,63 +67,83 @@ struct Tier<kFp16> {
   }
 };
 
+// Code tiers: each code u is turned into the fp16 value 1 + u / 2^b (b the
+// code width; the code fills the top mantissa bits under the exponent of
+// 1.0), two rows per 32-bit word, and multiplied in by fp16 x fp32 FMAs
+// (v_fma_mix_f32) -- no int-to-float conversions. The factor f passed in is
+// 2^b x_j s_{j,g} (kScale; exact), so each FMA adds x_j s (2^b + u); the
+// running sum corr takes back x_j s (2^b + the code offset) per column.
 template <>
 struct Tier<kInt4> {
   using V = uint32_t;
-  static constexpr int U = 16;
+  static constexpr int U = 8;
+  static constexpr float kScale = 16.0f;  // 2^4
+  static constexpr uint32_t kMask = 0x03C003C0u;  // bits 6..9 of both halves
   static __device__ __forceinline__ uint32_t offset(int row0, int lane) {
     return (uint32_t)(row0 + 8 * lane) / 2u;
   }
   static __device__ __forceinline__ V load(__amdgpu_buffer_rsrc_t t, uint32_t off, uint32_t col) {
     return __builtin_amdgcn_raw_buffer_load_b32(t, off, col, 0);
   }
-  // Rows 2b and 2b+1 sit in the low and high nibble of byte b, as
-  // two's-complement q; flipping each nibble's sign bit gives u = q + 8.
-  // f = x_j * s_{j,g} (exact: a product of two fp16 values); the offset 8 f
-  // is taken off through corr.
-  static __device__ __forceinline__ void fma(float (&acc)[8], float& corr, V v, float f) {
-    corr = fmaf(8.0f, f, corr);
+  // Row k sits in nibble k (bits 4k..4k+3) as two's-complement q; flipping
+  // each nibble's sign bit gives u = q + 8. Rows k and k+4 land in bits
+  // 6..9 of the two halves with one shift: fp16 1 + u/16.
+  // Adds x s (16 + u); corr takes back x s (16 + 8) = 1.5 f. kM is kMask
+  // held in a VGPR, so each pair is one shift and one v_and_or_b32.
+  static __device__ __forceinline__ void fma(float (&acc)[8], float& corr, V v, float f,
+                                             uint32_t kM) {
+    corr = fmaf(1.5f, f, corr);
     v ^= 0x88888888u;
-    const uint32_t lo = opaque(v & 0x0F0F0F0Fu);
-    const uint32_t hi = opaque((v >> 4) & 0x0F0F0F0Fu);
-    acc[0] = fmaf(f, b2f(lo, 0), acc[0]);
-    acc[1] = fmaf(f, b2f(hi, 0), acc[1]);
-    acc[2] = fmaf(f, b2f(lo, 1), acc[2]);
-    acc[3] = fmaf(f, b2f(hi, 1), acc[3]);
-    acc[4] = fmaf(f, b2f(lo, 2), acc[4]);
-    acc[5] = fmaf(f, b2f(hi, 2), acc[5]);
-    acc[6] = fmaf(f, b2f(lo, 3), acc[6]);
-    acc[7] = fmaf(f, b2f(hi, 3), acc[7]);
+    constexpr uint32_t kOne = 0x3C003C00u;
+    const uint32_t p0 = ((v << 6) & kM) | kOne;  // rows 0, 4
+    const uint32_t p1 = ((v << 2) & kM) | kOne;  // rows 1, 5
+    const uint32_t p2 = ((v >> 2) & kM) | kOne;  // rows 2, 6
+    const uint32_t p3 = ((v >> 6) & kM) | kOne;  // rows 3, 7
+    acc[0] = fmaf(h2f(p0 & 0xFFFFu), f, acc[0]);
+    acc[4] = fmaf(h2f(p0 >> 16), f, acc[4]);
+    acc[1] = fmaf(h2f(p1 & 0xFFFFu), f, acc[1]);
+    acc[5] = fmaf(h2f(p1 >> 16), f, acc[5]);
+    acc[2] = fmaf(h2f(p2 & 0xFFFFu), f, acc[2]);
+    acc[6] = fmaf(h2f(p2 >> 16), f, acc[6]);
+    acc[3] = fmaf(h2f(p3 & 0xFFFFu), f, acc[3]);
+    acc[7] = fmaf(h2f(p3 >> 16), f, acc[7]);
   }
 };
 
 template <>
 struct Tier<kInt2> {
   using V = uint32_t;
-  static constexpr int U = 16;
+  static constexpr int U = 8;
+  static constexpr float kScale = 4.0f;  // 2^2
+  static constexpr uint32_t kMask = 0x03000300u;  // bits 8..9 of both halves
   static __device__ __forceinline__ uint32_t offset(int row0, int lane) {
     return (uint32_t)(row0 + 8 * lane) / 4u;
   }
   static __device__ __forceinline__ V load(__amdgpu_buffer_rsrc_t t, uint32_t off, uint32_t col) {
     return __builtin_amdgcn_raw_buffer_load_b16(t, off, col, 0);
   }
-  // Row 4b + r sits in bits 2r..2r+1 of byte b (two bytes per lane); each
-  // 2-bit field is moved to the bottom of its byte and converted. The
-  // offset 1.5 f is taken off through corr.
-  static __device__ __forceinline__ void fma(float (&acc)[8], float& corr, V v, float f) {
-    corr = fmaf(1.5f, f, corr);
-    const uint32_t m0 = opaque(v & 0x0303u);
-    const uint32_t m1 = opaque((v >> 2) & 0x0303u);
-    const uint32_t m2 = opaque((v >> 4) & 0x0303u);
-    const uint32_t m3 = opaque((v >> 6) & 0x0303u);
-    acc[0] = fmaf(f, b2f(m0, 0), acc[0]);
-    acc[4] = fmaf(f, b2f(m0, 1), acc[4]);
-    acc[1] = fmaf(f, b2f(m1, 0), acc[1]);
-    acc[5] = fmaf(f, b2f(m1, 1), acc[5]);
-    acc[2] = fmaf(f, b2f(m2, 0), acc[2]);
-    acc[6] = fmaf(f, b2f(m2, 1), acc[6]);
-    acc[3] = fmaf(f, b2f(m3, 0), acc[3]);
-    acc[7] = fmaf(f, b2f(m3, 1), acc[7]);
+  // Row 4b + r sits in bits 2r..2r+1 of byte b (two bytes per lane). The
+  // second byte moves to bits 16..23; then rows r and 4 + r land in bits
+  // 8..9 of the two halves with one shift: fp16 1 + u/4.
+  // Adds x s (4 + u); corr takes back x s (4 + 1.5) = 1.375 f. kM is kMask
+  // held in a VGPR, so each pair is one shift and one v_and_or_b32.
+  static __device__ __forceinline__ void fma(float (&acc)[8], float& corr, V v, float f,
+                                             uint32_t kM) {
+    corr = fmaf(1.375f, f, corr);
+    const uint32_t w = (v & 0xFFu) | ((v & 0xFF00u) << 8);
+    constexpr uint32_t kOne = 0x3C003C00u;
+    const uint32_t p0 = ((w << 8) & kM) | kOne;  // rows 0, 4
+    const uint32_t p1 = ((w << 6) & kM) | kOne;  // rows 1, 5
+    const uint32_t p2 = ((w << 4) & kM) | kOne;  // rows 2, 6
+    const uint32_t p3 = ((w << 2) & kM) | kOne;  // rows 3, 7
+    acc[0] = fmaf(h2f(p0 & 0xFFFFu), f, acc[0]);
+    acc[4] = fmaf(h2f(p0 >> 16), f, acc[4]);
+    acc[1] = fmaf(h2f(p1 & 0xFFFFu), f, acc[1]);
+    acc[5] = fmaf(h2f(p1 >> 16), f, acc[5]);
+    acc[2] = fmaf(h2f(p2 & 0xFFFFu), f, acc[2]);
+    acc[6] = fmaf(h2f(p2 >> 16), f, acc[6]);
+    acc[3] = fmaf(h2f(p3 & 0xFFFFu), f, acc[3]);
+    acc[7] = fmaf(h2f(p3 >> 16), f, acc[7]);
   }
 };
 

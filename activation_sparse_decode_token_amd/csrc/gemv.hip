@@ -30,9 +30,11 @@
 //                    same boundaries, so no list crosses global memory before
 //                    the product; the tile-0 workgroups also write the lists
 //                    out for the caller.
-//   * Code tiers fold x_j * s_{j,g} into one fp32 factor per column and lane
-//     and accumulate the unsigned code; the code offset (8 for int4, 1.5 for
-//     int2) is removed once at the end through a per-lane running sum.
+//   * Code tiers fold 2^b x_j s_{j,g} into one fp32 factor per column and
+//     lane, turn each code u into the fp16 value 1 + u / 2^b with bit
+//     operations and multiply it in with fp16 x fp32 FMAs; the constant part
+//     (2^b plus the code offset, 8 for int4, 1.5 for int2) is removed once at
+//     the end through a per-lane running sum.
 //   * The 8 wave partials are added in LDS in a fixed order. With one split
 //     the workgroup writes y; otherwise each workgroup stores its fp32 partial
 //     and the last workgroup of a tile (agent-scope counter) adds the n_splits
@@ -107,6 +109,7 @@ struct TierStream {
   const float* lx;
   int p_lo, p_hi;
   V v0[U];
+  uint32_t vmask;  // the tier's code mask, kept in a VGPR
   int mycol;       // this lane's column of the pending batch
   float xv;        // this lane's activation of the pending batch (0 past it)
   uint32_t sc[4];  // this lane's raw fp16 scales of the pending batch (codes)
@@ -120,7 +123,12 @@ struct TierStream {
         cstride((uint32_t)stride), gsel(kCode ? (ld_lane >> 4) : 0),
         ngrp(min(4, (rows - row0_ + kGroup - 1) / kGroup)), row0(row0_), lane(lane_),
         scales(scales_), sstride(sstride_), idx(idx_), x(x_), lidx(lidx_), lx(lx_),
-        p_lo(p_lo_), p_hi(p_hi_) {}
+        p_lo(p_lo_), p_hi(p_hi_) {
+    // opaque to the optimiser: the mask stays in a VGPR instead of becoming
+    // a literal (gfx9 VOP3 instructions take no literals)
+    vmask = T::kMask;
+    asm volatile("" : "+v"(vmask));
+  }
 
   // This lane's column and activation of the batch at pb, and (codes) its
   // raw scales, without waiting for the scales.
@@ -158,10 +166,10 @@ struct TierStream {
       }
     }
   }
-  // Code factors x_j * s_{j,g} of the pending batch (0 past the batch).
+  // Code factors 2^b x_j s_{j,g} of the pending batch (0 past the batch).
   __device__ __forceinline__ void fill_facs(int cnt) {
 #pragma unroll
-    for (int g = 0; g < 4; ++g) wm.fac[lane][g] = lane < cnt ? xv * h2f(sc[g]) : 0.0f;
+    for (int g = 0; g < 4; ++g) wm.fac[lane][g] = lane < cnt ? xv * h2f(sc[g]) * T::kScale : 0.0f;
     wave_sync();
   }
   __device__ __forceinline__ void issue(int r, int cnt, V (&v)[U]) {
@@ -177,12 +185,13 @@ struct TierStream {
     if ((r + 1) * U <= cnt) {  // a full round (wave-uniform)
 #pragma unroll
       for (int u = 0; u < U; ++u)
-        T::fma(acc, corr, v[u], kCode ? wm.fac[r * U + u][gsel] : readlane_f(xv, r * U + u));
+        T::fma(acc, corr, v[u], kCode ? wm.fac[r * U + u][gsel] : readlane_f(xv, r * U + u),
+               vmask);
     } else {  // the batch's last, partial round: only its columns are added
 #pragma unroll
       for (int u = 0; u < U; ++u) {
         const int c = r * U + u;
-        if (c < cnt) T::fma(acc, corr, v[u], kCode ? wm.fac[c][gsel] : readlane_f(xv, c));
+        if (c < cnt) T::fma(acc, corr, v[u], kCode ? wm.fac[c][gsel] : readlane_f(xv, c), vmask);
       }
     }
   }

@@ -43,8 +43,10 @@ def ulp16(v: np.ndarray) -> np.ndarray:
 
 def abs_sum(x, F, A, full: O.ColumnStore, approx) -> np.ndarray:
     """Per-row sum of the magnitudes the fp32 accumulation adds: |x_j W_ij|
-    for full fp16 columns, and |x_j s_jg| (u_ij + offset) for code columns
-    (the kernel sums c*u and c*offset separately)."""
+    for full fp16 columns. A code column with b-bit code u adds
+    x_j s_jg (2^b + u) per element (the code as fp16 1 + u / 2^b times the
+    factor 2^b x_j s_jg) and x_j s_jg (2^b + offset) once to the running sum
+    that is subtracted at the end (offset 8 for int4, 1.5 for int2)."""
     xf = np.asarray(x, dtype=np.float16).astype(np.float64)
     S = np.zeros(full.rows)
 
@@ -55,15 +57,15 @@ def abs_sum(x, F, A, full: O.ColumnStore, approx) -> np.ndarray:
             nib[:, 0::2] = c & 0xF
             nib[:, 1::2] = c >> 4
             u = (nib ^ 8).astype(np.float64)
-            off = 8.0
+            base, off = 16.0, 8.0
         else:
             c = store.codes[idx]
             u = np.empty((len(idx), store.rows), dtype=np.float64)
             for r in range(4):
                 u[:, r::4] = (c >> (2 * r)) & 3
-            off = 1.5
+            base, off = 4.0, 1.5
         s = np.repeat(store.scales[idx].astype(np.float64), GROUP, axis=1)
-        return np.abs(xf[idx])[:, None] * s * (u + off)
+        return np.abs(xf[idx])[:, None] * s * ((base + u) + (base + off))
 
     if len(F):
         if full.fmt == "fp16":
