@@ -401,10 +401,15 @@ __device__ __forceinline__ void rank_piece(const GemvArgs& a, RankShared& rs, in
   const int ae = (int)(g2 + c[2] + min(e2r + c[3], q2)) - fe;
   if ((fs < f1 && fe > f0) || (as < a1 && ae > a0)) {
     const int nf = f1 - f0;
+    // fresh copies of the boundary keys: the comparisons below are not
+    // shared with the counting above (sharing them kept 4E compare masks
+    // alive across the barrier, spilled from scalar registers)
+    uint32_t t1c = t1, t2c = t2;
+    asm volatile("" : "+v"(t1c), "+v"(t2c));
 #pragma unroll
     for (int i = 0; i < E; ++i) {
       const uint32_t k = rawbits(xr, i) & 0x7FFFu;
-      const bool gt1 = k > t1, eq1 = k == t1, gt2 = k > t2, eq2 = k == t2;
+      const bool gt1 = k > t1c, eq1 = k == t1c, gt2 = k > t2c, eq2 = k == t2c;
       const bool in_f = gt1 || (eq1 && e1r < q1);
       const bool in_fa = gt2 || (eq2 && e2r < q2);
       const int fpos = (int)(g1 + min(e1r, q1));          // F entries before this one
