@@ -13,7 +13,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libspax.so")
 
-SOURCES = ["plan.hip", "gemv.hip", "aux.hip", "api.cpp"]
+SOURCES = ["plan.hip", "select.hip", "gemv.hip", "aux.hip", "api.cpp"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 

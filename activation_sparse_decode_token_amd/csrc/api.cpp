@@ -113,10 +113,11 @@ int64_t max_piece(const ProductPlan& p, int32_t kf, int32_t ka) {
   return m;
 }
 
-// Plan of the fused rank + product: more splits while a piece would not fit
-// the workgroup's LDS list. Returns false when no split count fits.
-bool plan_fused(const spax_matrix* W, int32_t kf, int32_t ka, ProductPlan* out) {
-  if (W->cols > kRankMaxN || W->residency != SPAX_RES_DEVICE) return false;
+// Plan of a product whose workgroups keep their list piece in LDS (fused
+// rank, or placement from the sliced selection): more splits while a piece
+// would not fit. Returns false when no split count fits.
+bool plan_piece(const spax_matrix* W, int32_t kf, int32_t ka, ProductPlan* out) {
+  if (W->residency != SPAX_RES_DEVICE) return false;
   ProductPlan p = plan_product(W, kf, ka);
   while (max_piece(p, kf, ka) > kListCap) {
     if (p.splits >= kMaxSplits || p.splits >= (int64_t)kf + ka) return false;
@@ -130,6 +131,11 @@ bool plan_fused(const spax_matrix* W, int32_t kf, int32_t ka, ProductPlan* out) 
 std::atomic<int32_t> g_kernel_choice{SPAX_KERNEL_AUTO};
 
 size_t counters_bytes(const spax_matrix*) { return align256(kCounterRegionBytes); }
+// The sliced selection's region follows the counters, also at a fixed place.
+constexpr size_t kSelectBytes = (sizeof(SelectScratch) + 255) & ~size_t(255);
+SelectScratch* select_scratch(void* ws) {
+  return reinterpret_cast<SelectScratch*>(static_cast<uint8_t*>(ws) + align256(kCounterRegionBytes));
+}
 size_t partials_bytes(const spax_matrix* W) {
   return align256(sizeof(float) * (size_t)kMaxSplits * W->rows);
 }
@@ -141,7 +147,7 @@ size_t staging_bytes(const spax_matrix* W) {
   return align256((size_t)W->cols * std::max(per_full, per_apx)) + 4 * 256;
 }
 size_t gemv_ws(const spax_matrix* W) {
-  return counters_bytes(W) + partials_bytes(W) + staging_bytes(W);
+  return counters_bytes(W) + kSelectBytes + partials_bytes(W) + staging_bytes(W);
 }
 
 // Events for the host-resident copy pipeline, one set per thread and device.
@@ -179,9 +185,10 @@ hipError_t events_for_current_device(EventSet** out) {
 int run_product(const spax_matrix* W, const uint16_t* x, const int32_t* fidx, int32_t kf,
                 const int32_t* aidx, int32_t ka, int32_t epi, uint16_t* y, uint16_t* ga,
                 uint16_t* gg, uint16_t* gu, void* ws, hipStream_t s, hipStream_t cs,
-                const ProductPlan* fused = nullptr, int32_t* out_f = nullptr,
+                const ProductPlan* piece = nullptr, int32_t piece_mode = kListRank,
+                int32_t* out_f = nullptr,
                 int32_t* out_a = nullptr) {
-  const ProductPlan p = fused ? *fused : plan_product(W, kf, ka);
+  const ProductPlan p = piece ? *piece : plan_product(W, kf, ka);
   uint8_t* wsb = static_cast<uint8_t*>(ws);
   GemvArgs a{};
   a.rows = W->rows;
@@ -195,8 +202,10 @@ int run_product(const spax_matrix* W, const uint16_t* x, const int32_t* fidx, in
   a.approx_idx = aidx;
   a.out_full_idx = out_f;
   a.out_approx_idx = out_a;
+  a.sel = select_scratch(ws);
+  a.slices = (W->cols + kSliceEntries - 1) / kSliceEntries;
   a.counters = reinterpret_cast<uint32_t*>(wsb);
-  a.partials = reinterpret_cast<float*>(wsb + counters_bytes(W));
+  a.partials = reinterpret_cast<float*>(wsb + counters_bytes(W) + kSelectBytes);
   a.y = y;
   a.glu_a = ga;
   a.glu_g = gg;
@@ -221,13 +230,13 @@ int run_product(const spax_matrix* W, const uint16_t* x, const int32_t* fidx, in
     a.split_lo = 0;
     a.splits_here = p.splits;
     const hipError_t e =
-        launch_gemv(a, W->full_fmt, W->approx_fmt, fused ? kListRank : kListGlobal, epi, s);
+        launch_gemv(a, W->full_fmt, W->approx_fmt, piece ? piece_mode : kListGlobal, epi, s);
     return e == hipSuccess ? SPAX_OK : hip_fail(e);
   }
 
   // Host-resident: copy the selected columns into staging in chunks on the
   // copy stream; the product consumes each chunk's splits as it lands.
-  uint8_t* st = wsb + counters_bytes(W) + partials_bytes(W);
+  uint8_t* st = wsb + counters_bytes(W) + kSelectBytes + partials_bytes(W);
   size_t off = 0;
   uint8_t* full_dst = st + off;
   off = align256(off + (size_t)kf * fb);
@@ -403,10 +412,27 @@ int spax_layer_step(const spax_layer* L, const spax_layer_io* io, void* ws, size
     ProductPlan fp;
     int st;
     const int32_t choice = g_kernel_choice.load(std::memory_order_relaxed);
-    if (choice == SPAX_KERNEL_AUTO && plan_fused(&G[g], kf, ka, &fp)) {
+    if (choice == SPAX_KERNEL_AUTO && G[g].cols > kRankMaxN && plan_piece(&G[g], kf, ka, &fp)) {
+      // long input: the sliced selection finds the thresholds and slice
+      // counts; every product workgroup places its own piece from them
+      hipError_t e = launch_select(inputs[g], G[g].cols, kf, ka, nullptr, nullptr,
+                                   select_scratch(ws), compute_stream);
+      if (e != hipSuccess) return hip_fail(e);
+      st = run_product(&G[g], inputs[g], nullptr, kf, nullptr, ka, epi, y, ga, gg, gu, ws,
+                       compute_stream, copy_stream, &fp, kListSliced, io->full_idx[g],
+                       io->approx_idx[g]);
+    } else if (choice == SPAX_KERNEL_AUTO && G[g].cols > kRankMaxN) {
+      // long input, host-resident weights: lists in memory for the copy
+      hipError_t e = launch_select(inputs[g], G[g].cols, kf, ka, io->full_idx[g],
+                                   io->approx_idx[g], select_scratch(ws), compute_stream);
+      if (e != hipSuccess) return hip_fail(e);
+      st = run_product(&G[g], inputs[g], io->full_idx[g], kf, io->approx_idx[g], ka, epi, y, ga,
+                       gg, gu, ws, compute_stream, copy_stream);
+    } else if (choice == SPAX_KERNEL_AUTO && plan_piece(&G[g], kf, ka, &fp)) {
       // device-resident weights: selection fused into the product
       st = run_product(&G[g], inputs[g], nullptr, kf, nullptr, ka, epi, y, ga, gg, gu, ws,
-                       compute_stream, copy_stream, &fp, io->full_idx[g], io->approx_idx[g]);
+                       compute_stream, copy_stream, &fp, kListRank, io->full_idx[g],
+                       io->approx_idx[g]);
     } else {
       hipError_t e = launch_plan(inputs[g], G[g].cols, kf, ka, io->full_idx[g],
                                  io->approx_idx[g], compute_stream);

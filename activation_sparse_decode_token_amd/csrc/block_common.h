@@ -436,6 +436,107 @@ __device__ __forceinline__ void rank_piece(const GemvArgs& a, RankShared& rs, in
   }
 }
 
+// Places this workgroup's piece (full-tier positions [f0, f1) at LDS slots
+// [0, f1 - f0), approx-tier positions [a0, a1) after them) from the sliced
+// selection's thresholds and per-slice counts: only the slices whose
+// positions meet the piece are scanned, 4 entries per thread. The same
+// position rule as rank_piece.
+__device__ __forceinline__ void place_sliced(const GemvArgs& a, uint32_t (&scan_sm)[2][kWaves],
+                                             int32_t* lidx, float* lx, int f0, int f1, int a0,
+                                             int a1, bool write_lists) {
+  const SelectScratch* ws = a.sel;
+  const int t = threadIdx.x;
+  const int lane = t & 63;
+  const int wave = t >> 6;
+  const int wv = __builtin_amdgcn_readfirstlane(wave);
+  const int n = a.n;
+  const uint32_t t1 = (uint32_t)ws->sel[4], q1 = (uint32_t)ws->sel[5];
+  const uint32_t t2 = (uint32_t)ws->sel[6], q2 = (uint32_t)ws->sel[7];
+  const int nf = f1 - f0;
+  // counts of the slices before the current one
+  uint32_t G1 = 0u, E1 = 0u, G2 = 0u, E2 = 0u;
+  for (int s = 0; s < a.slices; ++s) {
+    const uint32_t c0 = ws->cnt[s][0], c1 = ws->cnt[s][1];
+    const uint32_t c2 = ws->cnt[s][2], c3 = ws->cnt[s][3];
+    const int fs = (int)(G1 + min(E1, q1)), fe = (int)(G1 + c0 + min(E1 + c1, q1));
+    const int as = (int)(G2 + min(E2, q2)) - fs, ae = (int)(G2 + c2 + min(E2 + c3, q2)) - fe;
+    if ((fs < f1 && fe > f0) || (as < a1 && ae > a0)) {  // wave-uniform
+      const int base = s * kSliceEntries + 4 * t;
+      uint32_t xr[2];
+      if (base + 3 < n) {
+        const uint2 v = *reinterpret_cast<const uint2*>(a.x + base);
+        xr[0] = v.x;
+        xr[1] = v.y;
+      } else {
+#pragma unroll
+        for (int j = 0; j < 4; j += 2) {
+          const uint32_t lo = base + j < n ? a.x[base + j] : 0u;
+          const uint32_t hi = base + j + 1 < n ? a.x[base + j + 1] : 0u;
+          xr[j / 2] = lo | (hi << 16);
+        }
+      }
+      const int nv = max(0, min(4, n - base));
+      uint32_t c[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const uint32_t k = rawbits(xr, i) & 0x7FFFu;
+        const bool ok = i < nv;
+        c[0] += ok && k > t1;
+        c[1] += ok && k == t1;
+        c[2] += ok && k > t2;
+        c[3] += ok && k == t2;
+      }
+      // in-slice prefixes, packed two counts per register (under 2^16)
+      const uint32_t p01 = c[0] | (c[1] << 16), p23 = c[2] | (c[3] << 16);
+      const uint32_t i01 = wave_incl_scan(p01), i23 = wave_incl_scan(p23);
+      if (lane == 63) {
+        scan_sm[0][wave] = i01;
+        scan_sm[1][wave] = i23;
+      }
+      __syncthreads();
+      const uint32_t wt =
+          (lane >> 4) < 2 && (lane & 15) < kWaves ? scan_sm[lane >> 4][lane & 15] : 0u;
+      const uint32_t wex = row16_incl_scan(wt) - wt;
+      const uint32_t ex01 = (uint32_t)__builtin_amdgcn_readlane((int)wex, wv) + i01 - p01;
+      const uint32_t ex23 = (uint32_t)__builtin_amdgcn_readlane((int)wex, 16 + wv) + i23 - p23;
+      uint32_t g1 = G1 + (ex01 & 0xFFFFu), e1r = E1 + (ex01 >> 16);
+      uint32_t g2 = G2 + (ex23 & 0xFFFFu), e2r = E2 + (ex23 >> 16);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const uint32_t k = rawbits(xr, i) & 0x7FFFu;
+        const bool ok = i < nv;
+        const bool gt1 = ok && k > t1, eq1 = ok && k == t1;
+        const bool gt2 = ok && k > t2, eq2 = ok && k == t2;
+        const bool in_f = gt1 || (eq1 && e1r < q1);
+        const bool in_fa = gt2 || (eq2 && e2r < q2);
+        const int fpos = (int)(g1 + min(e1r, q1));
+        const int apos = (int)(g2 + min(e2r, q2)) - fpos;
+        const bool put_f = in_f && fpos >= f0 && fpos < f1;
+        const bool put_a = in_fa && !in_f && apos >= a0 && apos < a1;
+        const int slot = put_f ? fpos - f0 : nf + (apos - a0);
+        if (put_f || put_a) {
+          lidx[slot] = base + i;
+          lx[slot] = h2f(rawbits(xr, i));
+        }
+        g1 += gt1;
+        e1r += eq1;
+        g2 += gt2;
+        e2r += eq2;
+      }
+      __syncthreads();  // scan_sm is reused by the next slice
+    }
+    G1 += c0;
+    E1 += c1;
+    G2 += c2;
+    E2 += c3;
+  }
+  __syncthreads();
+  if (write_lists) {
+    for (int q = t; q < nf; q += kGemvThreads) a.out_full_idx[f0 + q] = lidx[q];
+    for (int q = t; q < a1 - a0; q += kGemvThreads) a.out_approx_idx[a0 + q] = lidx[nf + q];
+  }
+}
+
 // Gate / up pair: r1 is a gate row, r1 + 128 the matching up row.
 __device__ __forceinline__ void store_glu(const GemvArgs& a, int r1, float v1, float v2) {
   if (r1 < a.rows) {

@@ -138,7 +138,7 @@ struct TierStream {
     if (lane < cnt) {
       const int q = pb + lane;
       int j;
-      if constexpr (MODE == kListRank) {
+      if constexpr (MODE == kListRank || MODE == kListSliced) {
         j = lidx[q];
         xv = lx[q];
       } else {
@@ -265,8 +265,9 @@ __global__ __launch_bounds__(kGemvThreads) void gemv_kernel(GemvArgs a) {
     float red[kWaves][kTileRows];
   };
   __shared__ Scratch sm;
-  __shared__ int32_t lidx[MODE == kListRank ? kListCap : 1];
-  __shared__ float lx[MODE == kListRank ? kListCap : 1];
+  constexpr bool kPiece = MODE == kListRank || MODE == kListSliced;  // list piece in LDS
+  __shared__ int32_t lidx[kPiece ? kListCap : 1];
+  __shared__ float lx[kPiece ? kListCap : 1];
   __shared__ WaveMeta wmeta[2][kWaves];  // per tier and wave
   __shared__ uint32_t last_flag;
 
@@ -292,9 +293,12 @@ __global__ __launch_bounds__(kGemvThreads) void gemv_kernel(GemvArgs a) {
   float corr = 0.0f;
 
   int f_lo, f_hi, a_lo, a_hi;  // tier ranges in the list (or in the LDS piece)
-  if constexpr (MODE == kListRank) {
+  if constexpr (kPiece) {
     // the piece holds F positions [f0, f1) then A positions [a0, a1)
-    rank_piece<E>(a, sm.rank, lidx, lx, f0, f1, a0, a1, tile == 0);
+    if constexpr (MODE == kListRank)
+      rank_piece<E>(a, sm.rank, lidx, lx, f0, f1, a0, a1, tile == 0);
+    else
+      place_sliced(a, sm.rank.scan, lidx, lx, f0, f1, a0, a1, tile == 0);
     f_lo = 0;
     f_hi = f1 - f0;
     a_lo = f1 - f0;
@@ -427,11 +431,11 @@ template <int FF, int AF>
 hipError_t launch_mode(const GemvArgs& a, int32_t mode, int32_t epi, hipStream_t s) {
   if (mode == kListStaged) return launch_epi<FF, AF, kListStaged, 0>(a, epi, s);
   if (mode == kListGlobal) return launch_epi<FF, AF, kListGlobal, 0>(a, epi, s);
+  if (mode == kListSliced) return launch_epi<FF, AF, kListSliced, 0>(a, epi, s);
+  static_assert(kRankMaxN == kGemvThreads * 16, "fused ranking at 4, 8 or 16 entries per thread");
   if (a.n <= kGemvThreads * 4) return launch_epi<FF, AF, kListRank, 4>(a, epi, s);
   if (a.n <= kGemvThreads * 8) return launch_epi<FF, AF, kListRank, 8>(a, epi, s);
   if (a.n <= kGemvThreads * 16) return launch_epi<FF, AF, kListRank, 16>(a, epi, s);
-  if (a.n <= kGemvThreads * 32) return launch_epi<FF, AF, kListRank, 32>(a, epi, s);
-  if (a.n <= kGemvThreads * 64) return launch_epi<FF, AF, kListRank, 64>(a, epi, s);
   return hipErrorInvalidValue;
 }
 

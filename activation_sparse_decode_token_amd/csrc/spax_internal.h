@@ -30,8 +30,14 @@ constexpr size_t kCounterRegionBytes = sizeof(uint32_t) * kCountersPerTile * kMa
 constexpr int kGroup = 128;
 // List positions one workgroup of the fused rank + product keeps in LDS.
 constexpr int kListCap = 2048;
-// Largest input length the fused rank + product handles (64 per thread).
-constexpr int kRankMaxN = kGemvThreads * 64;
+// Largest input length the fused rank + product handles (16 per thread);
+// longer inputs are ranked by the sliced selection kernels first (measured:
+// at n = 11008 the fused form is faster, at n = 28672 the sliced one).
+constexpr int kRankMaxN = kGemvThreads * 16;
+// Sliced selection: entries per slice (one workgroup, 4 per thread) and the
+// most slices (inputs up to 65536 entries).
+constexpr int kSliceEntries = kGemvThreads * 4;
+constexpr int kMaxSlices = 65536 / kSliceEntries;
 
 enum Fmt : int32_t { kNone = 0, kFp16 = 1, kInt4 = 2, kInt2 = 3 };
 enum Epi : int32_t { kEpiPlain = 0, kEpiGlu = 1 };
@@ -40,6 +46,8 @@ enum ListMode : int32_t {
   kListGlobal = 0,  // index lists in device memory
   kListStaged = 1,  // selected columns staged in list order
   kListRank = 2,    // every workgroup ranks x itself (fused selection)
+  kListSliced = 3,  // thresholds and slice counts from the sliced selection;
+                    // every workgroup places its piece from its slices
 };
 
 // Arguments of one launch of the tiered product.
@@ -74,6 +82,18 @@ struct GemvArgs {
   uint16_t* glu_a;               // glu: fp16[rows/2]
   uint16_t* glu_g;               // optional
   uint16_t* glu_u;               // optional
+  const struct SelectScratch* sel;  // kListSliced: thresholds and slice counts
+  int32_t slices;                // kListSliced: slices of x
+};
+
+// Workspace region of the sliced selection: per-slice histograms and counts,
+// and the selection results (b1, entries above b1, b2, entries above b2,
+// t1, q1, t2, q2). Every field is written before it is read in each call.
+struct SelectScratch {
+  uint32_t hist[kMaxSlices][256];
+  uint32_t sub[kMaxSlices][2][128];
+  uint32_t cnt[kMaxSlices][4];
+  int32_t sel[8];
 };
 
 // Selected-column copy from host-resident storage into device staging.
@@ -95,6 +115,12 @@ struct CopyArgs {
 
 hipError_t launch_plan(const uint16_t* x, int32_t n, int32_t k_full, int32_t k_approx,
                        int32_t* full_idx, int32_t* approx_idx, hipStream_t s);
+
+// Sliced selection of x (n <= 65536): thresholds and per-slice counts into
+// ws; with lists (full_idx non-null) also the ascending full / approx lists.
+hipError_t launch_select(const uint16_t* x, int32_t n, int32_t k_full, int32_t k_approx,
+                         int32_t* full_idx, int32_t* approx_idx, SelectScratch* ws,
+                         hipStream_t s);
 
 hipError_t launch_gemv(const GemvArgs& a, int32_t full_fmt, int32_t approx_fmt,
                        int32_t mode, int32_t epi, hipStream_t s);

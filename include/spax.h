@@ -130,10 +130,10 @@ size_t spax_gemv_workspace_bytes(const spax_matrix* W);
  *   ws         device workspace of spax_gemv_workspace_bytes(W) bytes. It
  *              must be all zero before its first use (spax_workspace_clear);
  *              every call leaves its counters at zero again. The counters
- *              sit at a fixed place at the start of every workspace, so one
- *              workspace (sized for the largest matrix) may serve any mix of
- *              matrices and calls. Calls that share a workspace must be
- *              ordered on one stream.
+ *              and the selection scratch sit at fixed places at the start of
+ *              every workspace, so one workspace (sized for the largest
+ *              matrix) may serve any mix of matrices and calls. Calls that
+ *              share a workspace must be ordered on one stream.
  *   stream     compute stream. copy_stream: required when W is
  *              SPAX_RES_HOST_PINNED (only the selected columns are copied to
  *              device staging inside ws, in chunks overlapped with the
@@ -198,9 +198,12 @@ int spax_layer_step(const spax_layer* L, const spax_layer_io* io,
 /* spax_set_kernel_choice -- how spax_layer_step runs a group whose weights
  * are device-resident (process-wide; set it before concurrent calls, not
  * during them):
- *   SPAX_KERNEL_AUTO      the tiered product ranks the input itself (every
- *                         workgroup selects the tiers in LDS) where the input
- *                         length and list pieces allow, else as below;
+ *   SPAX_KERNEL_AUTO      inputs up to 16384 long: the tiered product ranks
+ *                         the input itself (every workgroup selects the tiers
+ *                         in LDS) where the list pieces fit; longer inputs:
+ *                         the selection runs first as four short launches over
+ *                         4096-entry slices (workspace scratch), then the
+ *                         tiered product reads the lists; otherwise as below;
  *   SPAX_KERNEL_SEPARATE  always the stand-alone selection kernel, then the
  *                         tiered product reading the lists from memory.
  * Both compute the same lists; the products agree within the error bound of

@@ -48,8 +48,11 @@ def _matrix(rows=4096, cols=4096, ff=spax.FMT_FP16, af=spax.FMT_INT4_G128,
 def test_workspace_sizes():
     W = _matrix()
     ws = spax.gemv_workspace_bytes(W)
-    # fixed counter region (2048 tiles x 9 counters) + 64 splits of fp32 partials
-    assert ws == 2048 * 9 * 4 + 64 * 4096 * 4
+    # fixed counter region (2048 tiles x 9 counters), the sliced selection's
+    # region (16 slices of 256 + 256 + 4 counts, 8 results; 256-byte padded),
+    # 64 splits of fp32 partials
+    sel = (16 * (256 + 256 + 4) * 4 + 8 * 4 + 255) // 256 * 256
+    assert ws == 2048 * 9 * 4 + sel + 64 * 4096 * 4
     Wh = _matrix(res=spax.RES_HOST_PINNED)
     assert spax.gemv_workspace_bytes(Wh) >= ws + 4096 * 2 * 4096
     bad = _matrix(rows=100)

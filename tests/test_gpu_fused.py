@@ -73,8 +73,9 @@ CASES = [
     (1024, 11008, "fp16", "int4", 2752, 2752),
     (640, 16385, "fp16", "int2", 4000, 6000),
     (1024, 28672, "int4", "int2", 5734, 8602),
-    (512, 32768, "fp16", "int4", 9000, 9000),    # largest fused input
-    (512, 32769, "fp16", "int4", 9000, 9000),    # separate selection kernel
+    (512, 32768, "fp16", "int4", 9000, 9000),    # sliced selection, 8 slices
+    (512, 32769, "fp16", "int4", 9000, 9000),    # sliced selection, ragged last slice
+    (256, 65536, "fp16", "int2", 20000, 30000),  # longest input: 16 slices
     (128, 6000, "fp16", "none", 6000, 0),        # one tile, one split, long list
 ]
 
@@ -88,7 +89,8 @@ def test_fused_vs_oracle(R, n, ff, af, kf, ka, kernel_choice):
     log(f"  norm-wise error {err:.2e}")
 
 
-@pytest.mark.parametrize("n", [300, 4096, 11008])
+# 20000: past the fused ranking's limit, so the sliced selection's placement
+@pytest.mark.parametrize("n", [300, 4096, 11008, 20000])
 def test_fused_ties(n, kernel_choice):
     rs = np.random.default_rng(31 + n)
     Wt = WL.weights_fp16(821, 0, "w", 512, n, 0.02)
