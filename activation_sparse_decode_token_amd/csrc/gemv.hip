@@ -364,7 +364,8 @@ __global__ __launch_bounds__(kGemvThreads) void gemv_kernel(GemvArgs a) {
     if (t == 0) {
       // Two-level arrival count, so that at most 8 workgroups meet on one
       // counter: the last of each group of 8 splits counts its group in,
-      // the last group's last workgroup reduces. Each counter is reset by
+      // the last group's last workgroup reduces (with 8 splits or fewer the
+      // group's last workgroup reduces directly). Each counter is reset by
       // the workgroup that completes it.
       uint32_t* c = a.counters + tile * kCountersPerTile;
       const int g = split >> 3;
@@ -375,11 +376,15 @@ __global__ __launch_bounds__(kGemvThreads) void gemv_kernel(GemvArgs a) {
           __hip_atomic_fetch_add(&c[1 + g], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       if (old == gsize - 1) {
         __hip_atomic_store(&c[1 + g], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        const uint32_t old2 =
-            __hip_atomic_fetch_add(&c[0], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        if (old2 == ngroups - 1) {
-          __hip_atomic_store(&c[0], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (ngroups == 1) {  // one group: its last workgroup is the last
           last = 1u;
+        } else {
+          const uint32_t old2 =
+              __hip_atomic_fetch_add(&c[0], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          if (old2 == ngroups - 1) {
+            __hip_atomic_store(&c[0], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            last = 1u;
+          }
         }
       }
       last_flag = last;
