@@ -151,21 +151,46 @@ struct Tier<kInt2> {
 // In-workgroup tier selection (kListRank). Same definition as the stand-alone
 // plan kernel: order key = fp16 magnitude bits, larger first, lower index
 // first among equal keys; the k_full first are F, the next k_approx are A.
-// Thread t owns entries [t*E, t*E+E).
-//   1. 256-bin histogram of key bits 14..7 (LDS atomics);
+// The histogram steps run on the first kRankWaves waves only (the other
+// waves meet the barriers): they are issue-bound, a few instructions per
+// entry plus a fixed cost per wave and step, so fewer waves over more
+// entries each take less time per SIMD. The counting and placement steps
+// run on every wave over its own short chunk, since only the threads whose
+// positions meet the piece place entries, and a long per-thread loop there
+// would leave one wave with all the work. Entries past n read as key 0 and
+// are taken out of the counts of key 0 where the boundaries are found;
+// they are never placed.
+//   1. 256-bin histogram of key bits 14..7;
 //   2. suffix counts give the bins holding rank k_full and k_full + k_approx;
-//   3. 128-bin histograms inside those bins give the boundary keys t1, t2
-//      and the number of entries equal to each that are kept (q1, q2);
-//   4. one block scan of (#key > t1, #key == t1, #key > t2, #key == t2),
-//      packed two counts per register, gives every entry its position: #F
-//      before entry i is gt1(i) + min(eq1(i), q1), #(F or A) before it
-//      gt2(i) + min(eq2(i), q2).
+//   3. 128-bin histograms inside those two bins (one pass) give the boundary
+//      keys t1, t2 and the number of entries equal to each that are kept
+//      (q1, q2);
+//   4. one scan of (#key > t1, #key == t1, #key > t2, #key == t2) over the
+//      workgroup, packed two counts per register, gives every entry its
+//      position: #F before entry i is gt1(i) + min(eq1(i), q1), #(F or A)
+//      before it gt2(i) + min(eq2(i), q2).
+// Histograms keep kHistCopies interleaved copies of each bin (lane l adds
+// to copy l mod kHistCopies), so skewed inputs (many equal magnitudes, e.g.
+// exact zeros) put at most 64 / kHistCopies adds of one instruction on one
+// LDS address.
 // ---------------------------------------------------------------------------
 constexpr uint32_t kAboveAll = 0x8000u;  // boundary key when a tier is empty
+// Measured on the 7B attention launches: 8 ranking waves (two per SIMD)
+// beat 4 by 0.2-0.3 us per launch; the ranking waves then overlap each
+// other's LDS and barrier waits.
+constexpr int kRankWaves = 8;
+constexpr int kRankThreads = kRankWaves * 64;
+constexpr int kHistCopies = 4;
+static_assert(kRankWaves <= kWaves && kRankMaxN % (kRankThreads * 32) == 0,
+              "fused ranking entries per thread are multiples of 8");
 
 struct RankShared {
-  uint32_t hist[257];  // bin 256 absorbs the padding past n
-  uint32_t sub[2][128];
+  // bin b, copy c at word kHistCopies * b + c
+  uint32_t hist[256 * kHistCopies];
+  // sub-bins in the bin of rank k_full at [0, 128), in the bin of rank
+  // k_full + k_approx at [128, 256) (both at [0, 128) when the bins coincide)
+  uint32_t sub[256 * kHistCopies];
+  uint32_t spare[64];  // per-lane targets of the adds that count nothing
   uint32_t scan[2][kWaves];  // packed count pairs, per wave
   int32_t sel[8];  // b1, entries above b1, b2, entries above b2, t1, q1, t2, q2
 };
@@ -235,71 +260,102 @@ __device__ __forceinline__ uint32_t rawbits(const uint32_t* xr, int i) {
   return (xr[i >> 1] >> (16 * (i & 1))) & 0xFFFFu;
 }
 
+// Loads entries [base, base + C) of x as raw fp16 bits, two per register,
+// 0 past n: 16-byte loads, or 8-byte ones where C is not a multiple of 8
+// (x is 16-byte aligned and base a multiple of C).
+template <int C>
+__device__ __forceinline__ void load_chunk(const uint16_t* __restrict__ x, int n, int base,
+                                           uint32_t* r) {
+  static_assert(C % 4 == 0, "chunk of whole 8-byte words");
+  constexpr int L = C % 8 == 0 ? 8 : 4;
+#pragma unroll
+  for (int i = 0; i < C; i += L) {
+    if (base + i + L - 1 < n) {
+      if constexpr (L == 8) {
+        const uint4 v = *reinterpret_cast<const uint4*>(x + base + i);
+        r[i / 2 + 0] = v.x;
+        r[i / 2 + 1] = v.y;
+        r[i / 2 + 2] = v.z;
+        r[i / 2 + 3] = v.w;
+      } else {
+        const uint2 v = *reinterpret_cast<const uint2*>(x + base + i);
+        r[i / 2 + 0] = v.x;
+        r[i / 2 + 1] = v.y;
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < L; j += 2) {
+        const uint32_t lo = base + i + j < n ? x[base + i + j] : 0u;
+        const uint32_t hi = base + i + j + 1 < n ? x[base + i + j + 1] : 0u;
+        r[(i + j) / 2] = lo | (hi << 16);
+      }
+    }
+  }
+}
+
+// 15-bit key (fp16 magnitude pattern) of entry i of a packed chunk
+__device__ __forceinline__ uint32_t chunk_key(const uint32_t* r, int i) {
+  return (i & 1) ? (r[i >> 1] >> 16) & 0x7FFFu : r[i >> 1] & 0x7FFFu;
+}
+
 // Ranks x and places this workgroup's list positions in LDS: full-tier
 // positions [f0, f1) at slots [0, f1 - f0), approx-tier positions [a0, a1)
-// after them.
+// after them. Every thread owns the chunk [t*C, t*C + C) of x, C = E *
+// kRankThreads / kGemvThreads, for the counting and placement steps;
+// ranking thread t builds the histograms from the chunks of threads t,
+// t + kRankThreads, ... (E entries).
 template <int E>
 __device__ __forceinline__ void rank_piece(const GemvArgs& a, RankShared& rs, int32_t* lidx,
                                            float* lx, int f0, int f1, int a0, int a1,
                                            bool write_lists) {
+  constexpr int kChunks = kGemvThreads / kRankThreads;
+  constexpr int C = E / kChunks;
+  static_assert(E % kChunks == 0 && C % 4 == 0, "whole 8-byte words per chunk");
   const int t = threadIdx.x;
   const int lane = t & 63;
   const int wave = t >> 6;
+  const bool ranker = t < kRankThreads;  // wave-uniform
   const int n = a.n;
-  const int base = t * E;
+  const int base = t * C;
   const uint32_t K1 = (uint32_t)a.k_full;
   const uint32_t K2 = (uint32_t)(a.k_full + a.k_approx);
+  const uint32_t pad = (uint32_t)(kGemvThreads * C - n);  // entries past n
+  const uint32_t copy = (uint32_t)(lane & (kHistCopies - 1));
 
-  // raw fp16 bits, two per register; loads of 8 entries (16 bytes), or of
-  // 4 (8 bytes) when a thread owns only 4
-  static_assert(E % 4 == 0, "entries per thread");
-  constexpr int kLoad = E >= 8 ? 8 : 4;
-  uint32_t xr[E / 2];
+  uint32_t xp[C / 2];                   // this thread's chunk
+  uint32_t xq[(kChunks - 1) * C / 2];   // a ranking thread's other chunks
+  load_chunk<C>(a.x, n, base, xp);
+  if (ranker) {
 #pragma unroll
-  for (int i = 0; i < E; i += kLoad) {
-    if (base + i + kLoad - 1 < n) {
-      if constexpr (kLoad == 8) {
-        const uint4 v = *reinterpret_cast<const uint4*>(a.x + base + i);
-        xr[i / 2 + 0] = v.x;
-        xr[i / 2 + 1] = v.y;
-        xr[i / 2 + 2] = v.z;
-        xr[i / 2 + 3] = v.w;
-      } else {
-        const uint2 v = *reinterpret_cast<const uint2*>(a.x + base + i);
-        xr[i / 2 + 0] = v.x;
-        xr[i / 2 + 1] = v.y;
-      }
-    } else {
-#pragma unroll
-      for (int j = 0; j < kLoad; j += 2) {
-        const uint32_t lo = base + i + j < n ? a.x[base + i + j] : 0u;
-        const uint32_t hi = base + i + j + 1 < n ? a.x[base + i + j + 1] : 0u;
-        xr[(i + j) / 2] = lo | (hi << 16);
-      }
-    }
+    for (int c = 1; c < kChunks; ++c)
+      load_chunk<C>(a.x, n, (t + c * kRankThreads) * C, xq + (c - 1) * (C / 2));
   }
-  const int nv = max(0, min(E, n - base));  // valid entries of this thread
+  // key of a ranking thread's entry i of E
+  auto rkey = [&](int i) -> uint32_t { return i < C ? chunk_key(xp, i) : chunk_key(xq, i - C); };
 
-  if (t < 256) {
-    rs.hist[t] = 0u;
-    (&rs.sub[0][0])[t] = 0u;
-  }
-  if (t == 256) rs.hist[256] = 0u;
+  // both histograms cleared at once (2 words per thread)
+  static_assert(2 * 256 * kHistCopies == 2 * kGemvThreads, "one 8-byte clear per thread");
+  reinterpret_cast<uint2*>(rs.hist)[t] = make_uint2(0u, 0u);
   __syncthreads();
 
   // 1. top-level histogram
-  hist_add<E>(rs.hist, [&](int i) {
-    return i < nv ? (int)((rawbits(xr, i) & 0x7FFFu) >> 7) : 256;
-  });
+  if (ranker) {
+#pragma unroll
+    for (int i = 0; i < E; ++i) atomicAdd(&rs.hist[((rkey(i) >> 7) << 2) | copy], 1u);
+  }
   __syncthreads();
 
   // 2. bins holding rank K1 and rank K2 (1-based, from the largest key),
-  // found by wave 0 (the other waves wait at the barrier, leaving it the
-  // whole SIMD)
+  // found by wave 0; the padding is taken out of bin 0
   if (wave == 0) {
     uint32_t c[4];
+    const uint4* hp = reinterpret_cast<const uint4*>(rs.hist) + 4 * lane;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) c[j] = rs.hist[4 * lane + j];
+    for (int j = 0; j < 4; ++j) {
+      const uint4 v = hp[j];
+      c[j] = v.x + v.y + v.z + v.w;
+    }
+    if (lane == 0) c[0] -= pad;
     uint32_t above = wave_excl_suffix(c[0] + c[1] + c[2] + c[3]);
     int s1 = -1, s2 = -1;
     uint32_t x1 = 0u, x2 = 0u;
@@ -320,16 +376,22 @@ __device__ __forceinline__ void rank_piece(const GemvArgs& a, RankShared& rs, in
   }
   __syncthreads();
 
-  // 3. low-level histograms inside the two boundary bins
+  // 3. low-level histograms inside the two boundary bins, in one pass;
+  // other entries add to the lane's spare word
   const int b1 = rs.sel[0];
   const int b2 = rs.sel[2];
-  auto sub_bin = [&](int i, int b) {
-    const uint32_t k = rawbits(xr, i) & 0x7FFFu;
-    const int hb = i < nv ? (int)(k >> 7) : 256;
-    return hb == b ? (int)(k & 127u) : -1;
-  };
-  hist_add<E>(rs.sub[0], [&](int i) { return sub_bin(i, b1); });
-  hist_add<E>(rs.sub[1], [&](int i) { return sub_bin(i, b2); });
+  const int b2x = b2 == b1 ? -1 : b2;  // a shared bin is counted once
+  if (ranker) {
+#pragma unroll
+    for (int i = 0; i < E; ++i) {
+      const uint32_t k = rkey(i);
+      const int hb = (int)(k >> 7);
+      const uint32_t w = ((k & 127u) << 2) | copy;
+      uint32_t* p = hb == b1 ? &rs.sub[w]
+                             : (hb == b2x ? &rs.sub[128 * kHistCopies + w] : &rs.spare[lane]);
+      atomicAdd(p, 1u);
+    }
+  }
   __syncthreads();
   // boundary keys t (kAboveAll when the tier is empty) and quotas q: the
   // number of entries equal to t that are kept; found by wave 0
@@ -338,20 +400,25 @@ __device__ __forceinline__ void rank_piece(const GemvArgs& a, RankShared& rs, in
     for (int r = 0; r < 2; ++r) {
       const int b = r == 0 ? b1 : b2;
       const uint32_t K = r == 0 ? K1 : K2;
-      int key = (int)kAboveAll;
+      int key_t = (int)kAboveAll;
       uint32_t quota = 0u;
       if (b >= 0) {  // wave-uniform
-        const uint32_t c0 = rs.sub[r][2 * lane], c1 = rs.sub[r][2 * lane + 1];
+        const uint4* sp = reinterpret_cast<const uint4*>(
+                              rs.sub + (r == 1 && b2x >= 0 ? 128 * kHistCopies : 0)) +
+                          2 * lane;
+        const uint4 v0 = sp[0], v1 = sp[1];
+        uint32_t c0 = v0.x + v0.y + v0.z + v0.w, c1 = v1.x + v1.y + v1.z + v1.w;
+        if (b == 0 && lane == 0) c0 -= pad;  // the padding has key 0
         uint32_t above = (uint32_t)rs.sel[1 + 2 * r] + wave_excl_suffix(c0 + c1);
         int sk = -1;
         uint32_t sq = 0u;
         if (above < K && K <= above + c1) { sk = (b << 7) | (2 * lane + 1); sq = K - above; }
         above += c1;
         if (above < K && K <= above + c0) { sk = (b << 7) | (2 * lane); sq = K - above; }
-        wave_pick(sk, sq, key, quota);
+        wave_pick(sk, sq, key_t, quota);
       }
       if (lane == 0) {
-        rs.sel[4 + 2 * r] = key;
+        rs.sel[4 + 2 * r] = key_t;
         rs.sel[5 + 2 * r] = (int32_t)quota;
       }
     }
@@ -360,20 +427,22 @@ __device__ __forceinline__ void rank_piece(const GemvArgs& a, RankShared& rs, in
   const uint32_t t1 = (uint32_t)rs.sel[4], q1 = (uint32_t)rs.sel[5];
   const uint32_t t2 = (uint32_t)rs.sel[6], q2 = (uint32_t)rs.sel[7];
 
-  // 4. positions
+  // 4. positions, every thread over its chunk. The padding (key 0, after
+  // every real entry) may be counted as equal to a boundary key 0, but the
+  // quota of such a key is used up by the real zeros before it, so it is
+  // never placed.
   uint32_t c[4] = {0u, 0u, 0u, 0u};
 #pragma unroll
-  for (int i = 0; i < E; ++i) {
-    const uint32_t k = rawbits(xr, i) & 0x7FFFu;
-    const bool ok = i < nv;
-    c[0] += ok && k > t1;
-    c[1] += ok && k == t1;
-    c[2] += ok && k > t2;
-    c[3] += ok && k == t2;
+  for (int i = 0; i < C; ++i) {
+    const uint32_t k = chunk_key(xp, i);
+    c[0] += k > t1;
+    c[1] += k == t1;
+    c[2] += k > t2;
+    c[3] += k == t2;
   }
   // Scans run on the counts packed two per register: every partial sum
-  // below is under 2^16 (at most 64 * E per wave, 15 waves before any
-  // wave), and the packed sums subtract exactly.
+  // below is under 2^16 (at most kRankMaxN), and the packed sums subtract
+  // exactly.
   static_assert(kWaves <= 16, "wave totals fit one 16-lane row");
   const uint32_t p01 = c[0] | (c[1] << 16), p23 = c[2] | (c[3] << 16);
   const uint32_t i01 = wave_incl_scan(p01), i23 = wave_incl_scan(p23);
@@ -392,9 +461,7 @@ __device__ __forceinline__ void rank_piece(const GemvArgs& a, RankShared& rs, in
   uint32_t g1 = ex01 & 0xFFFFu, e1r = ex01 >> 16;
   uint32_t g2 = ex23 & 0xFFFFu, e2r = ex23 >> 16;
   // This thread's F positions [fs, fe) and A positions [as, ae); only
-  // threads whose positions meet the piece place entries. Entries past n
-  // (key 0, after every real entry) are never placed: a boundary key 0
-  // has its quota used up by the real zeros before them.
+  // threads whose positions meet the piece place entries.
   const int fs = (int)(g1 + min(e1r, q1));
   const int fe = (int)(g1 + c[0] + min(e1r + c[1], q1));
   const int as = (int)(g2 + min(e2r, q2)) - fs;
@@ -402,13 +469,13 @@ __device__ __forceinline__ void rank_piece(const GemvArgs& a, RankShared& rs, in
   if ((fs < f1 && fe > f0) || (as < a1 && ae > a0)) {
     const int nf = f1 - f0;
     // fresh copies of the boundary keys: the comparisons below are not
-    // shared with the counting above (sharing them kept 4E compare masks
-    // alive across the barrier, spilled from scalar registers)
+    // shared with the counting above (sharing them kept 4C compare masks
+    // alive across the barrier)
     uint32_t t1c = t1, t2c = t2;
     asm volatile("" : "+v"(t1c), "+v"(t2c));
 #pragma unroll
-    for (int i = 0; i < E; ++i) {
-      const uint32_t k = rawbits(xr, i) & 0x7FFFu;
+    for (int i = 0; i < C; ++i) {
+      const uint32_t k = chunk_key(xp, i);
       const bool gt1 = k > t1c, eq1 = k == t1c, gt2 = k > t2c, eq2 = k == t2c;
       const bool in_f = gt1 || (eq1 && e1r < q1);
       const bool in_fa = gt2 || (eq2 && e2r < q2);
@@ -419,7 +486,7 @@ __device__ __forceinline__ void rank_piece(const GemvArgs& a, RankShared& rs, in
       const int slot = put_f ? fpos - f0 : nf + (apos - a0);
       if (put_f || put_a) {
         lidx[slot] = base + i;
-        lx[slot] = h2f(rawbits(xr, i));
+        lx[slot] = h2f((i & 1) ? xp[i >> 1] >> 16 : xp[i >> 1] & 0xFFFFu);
       }
       g1 += gt1;
       e1r += eq1;

@@ -437,10 +437,13 @@ hipError_t launch_mode(const GemvArgs& a, int32_t mode, int32_t epi, hipStream_t
   if (mode == kListStaged) return launch_epi<FF, AF, kListStaged, 0>(a, epi, s);
   if (mode == kListGlobal) return launch_epi<FF, AF, kListGlobal, 0>(a, epi, s);
   if (mode == kListSliced) return launch_epi<FF, AF, kListSliced, 0>(a, epi, s);
-  static_assert(kRankMaxN == kGemvThreads * 16, "fused ranking at 4, 8 or 16 entries per thread");
-  if (a.n <= kGemvThreads * 4) return launch_epi<FF, AF, kListRank, 4>(a, epi, s);
-  if (a.n <= kGemvThreads * 8) return launch_epi<FF, AF, kListRank, 8>(a, epi, s);
-  if (a.n <= kGemvThreads * 16) return launch_epi<FF, AF, kListRank, 16>(a, epi, s);
+  // entries per ranking thread: a quarter, half, three quarters or all of
+  // kRankMaxN / kRankThreads, the smallest that covers n
+  constexpr int kE = kRankMaxN / kRankThreads;
+  if (a.n <= kRankMaxN / 4) return launch_epi<FF, AF, kListRank, kE / 4>(a, epi, s);
+  if (a.n <= kRankMaxN / 2) return launch_epi<FF, AF, kListRank, kE / 2>(a, epi, s);
+  if (a.n <= kRankMaxN / 4 * 3) return launch_epi<FF, AF, kListRank, kE / 4 * 3>(a, epi, s);
+  if (a.n <= kRankMaxN) return launch_epi<FF, AF, kListRank, kE>(a, epi, s);
   return hipErrorInvalidValue;
 }
 

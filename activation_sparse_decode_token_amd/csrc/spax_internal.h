@@ -30,7 +30,8 @@ constexpr size_t kCounterRegionBytes = sizeof(uint32_t) * kCountersPerTile * kMa
 constexpr int kGroup = 128;
 // List positions one workgroup of the fused rank + product keeps in LDS.
 constexpr int kListCap = 2048;
-// Largest input length the fused rank + product handles (16 per thread);
+// Largest input length the fused rank + product handles (64 per ranking
+// thread, 4 ranking waves);
 // longer inputs are ranked by the sliced selection kernels first (measured:
 // at n = 11008 the fused form is faster, at n = 28672 the sliced one).
 constexpr int kRankMaxN = kGemvThreads * 16;
