@@ -36,6 +36,7 @@ import numpy as np
 __all__ = [
     "magnitude_key", "plan_tiers", "fp16_round",
     "pack_int4_g128", "pack_int2_g128", "dequant_int4_g128", "dequant_int2_g128",
+    "pack_sign2", "dequant_sign2", "fp16_units",
     "ColumnStore", "tiered_product", "tiered_gemv_fp16",
     "silu", "swiglu_fp16", "layer_step", "GROUP_SIZE",
 ]
@@ -185,8 +186,77 @@ def dequant_int2_g128(codes: np.ndarray, scales: np.ndarray) -> np.ndarray:
     return (u.astype(np.float64) - 1.5) * s
 
 
+# --------------------------------------------------------------------------
+# The SpAx page's own scalar middle-tier code (section 5.1, Eq. 4): every
+# weight of column j is rebuilt as e1 s_{j,0} + e2 s_{j,1} with two sign
+# codes (e1, e2) in {-1, +1} and two scales per column; the codes are the
+# argmin of the squared error given the scales.
+# --------------------------------------------------------------------------
+
+def fp16_units(Wt: np.ndarray) -> np.ndarray:
+    """fp16 values as exact integers in units of 2^-24 (every finite fp16
+    value is a multiple of 2^-24 below 2^16, so |w| 2^24 < 2^40)."""
+    return (np.asarray(Wt, dtype=np.float16).astype(np.float64) * 2.0 ** 24).astype(np.int64)
+
+
+def _mean_to_fp16(total: np.ndarray, count: int) -> np.ndarray:
+    """fp16(total 2^-24 / count) for exact integer totals: one fp64 division
+    of the two (exact) operands, then one rounding to fp16."""
+    return fp16_round(total.astype(np.float64) / float(count) * 2.0 ** -24)
+
+
+def pack_sign2(Wt: np.ndarray) -> Tuple[np.ndarray, np.ndarray]:
+    """Two-scale 2-bit sign code of each column (SpAx page section 5.1, Eq. 4).
+
+    Scales (the page fits them Lloyd-Max style; the fitting text is lost, so
+    the reading here is the closed-form greedy fit, each scale the
+    least-squares optimum for its own sign code):
+        e1_i = +1 if w_i >= 0 else -1
+        s0 = fp16(mean_i |w_i|)
+        s1 = fp16(mean_i |w_i - e1_i s0|)
+    Codes: (e1, e2) = argmin over {-1, +1}^2 of (w_i - e1 s0 - e2 s1)^2 with
+    the stored (fp16) scales; among equal errors the smaller code u wins.
+    The 2-bit code is u = 2 [e1 = -1] + [e2 = -1]; row 4i + r is stored in
+    bits 2r..2r+1 of byte i of the column (the int2 packing).
+    All arithmetic is exact: weights and scales as integers in units of
+    2^-24, so sums and distances never round; the two means are rounded
+    once each (fp64 division, then fp16).
+
+    Wt: fp16 [n, R]. Returns codes uint8 [n, R/4] and scales fp16 [n, 2]
+    (s0, s1)."""
+    n, R = Wt.shape
+    if R % 4:
+        raise ValueError("rows must be a multiple of 4")
+    w = fp16_units(Wt)                                   # exact, signed
+    s0 = _mean_to_fp16(np.abs(w).sum(axis=1), R)
+    s0u = fp16_units(s0)[:, None]
+    e1 = np.where(w >= 0, 1, -1)
+    s1 = _mean_to_fp16(np.abs(w - e1 * s0u).sum(axis=1), R)
+    s1u = fp16_units(s1)[:, None]
+    # candidate levels in code order u = 0..3: (+,+), (+,-), (-,+), (-,-)
+    levels = [s0u + s1u, s0u - s1u, -s0u + s1u, -s0u - s1u]
+    dist = np.stack([np.abs(w - L) for L in levels])     # [4, n, R], exact
+    u = np.argmin(dist, axis=0).astype(np.int64)         # first minimum: smallest u
+    codes = (u[:, 0::4] | (u[:, 1::4] << 2) | (u[:, 2::4] << 4) | (u[:, 3::4] << 6))
+    scales = np.stack([s0, s1], axis=1).astype(np.float16)
+    return codes.astype(np.uint8), scales
+
+
+def dequant_sign2(codes: np.ndarray, scales: np.ndarray) -> np.ndarray:
+    """w_hat = e1 s0 + e2 s1 in fp64 (exact); returns [n, R]."""
+    n = codes.shape[0]
+    R = codes.shape[1] * 4
+    u = np.empty((n, R), dtype=np.int64)
+    for r in range(4):
+        u[:, r::4] = (codes >> (2 * r)) & 3
+    e1 = np.where(u & 2, -1.0, 1.0)
+    e2 = np.where(u & 1, -1.0, 1.0)
+    s = scales.astype(np.float64)
+    return e1 * s[:, 0:1] + e2 * s[:, 1:2]
+
+
 class ColumnStore:
-    """One tier's copy of a matrix: fp16 columns, or int4 / int2 codes.
+    """One tier's copy of a matrix: fp16 columns, or int4 / int2 / sign2 codes.
 
     columns(idx) returns the exact fp64 values of the selected columns as an
     array [len(idx), R] (SpAx page, Figure 2 step 5: the GPU rebuilds the
@@ -198,9 +268,10 @@ class ColumnStore:
         if fmt == "fp16":
             self.Wt = np.ascontiguousarray(Wt, dtype=np.float16)
             self.rows = self.Wt.shape[1]
-        elif fmt in ("int4", "int2"):
+        elif fmt in ("int4", "int2", "sign2"):
             if codes is None:
-                codes, scales = (pack_int4_g128 if fmt == "int4" else pack_int2_g128)(Wt)
+                codes, scales = {"int4": pack_int4_g128, "int2": pack_int2_g128,
+                                 "sign2": pack_sign2}[fmt](Wt)
             self.codes, self.scales = codes, scales
             self.rows = codes.shape[1] * (2 if fmt == "int4" else 4)
         else:
@@ -212,6 +283,8 @@ class ColumnStore:
             return self.Wt[idx].astype(np.float64)
         if self.fmt == "int4":
             return dequant_int4_g128(self.codes[idx], self.scales[idx])
+        if self.fmt == "sign2":
+            return dequant_sign2(self.codes[idx], self.scales[idx])
         return dequant_int2_g128(self.codes[idx], self.scales[idx])
 
 

@@ -307,6 +307,118 @@ def test_pack_on_grid_and_zero_groups():
     assert not np.any(O.dequant_int2_g128(c2, s2))
 
 
+# ---------------------------------------------------------------- two-scale sign code
+
+def _sign2_levels(s0: Fraction, s1: Fraction):
+    # code order u = 0..3: (+,+), (+,-), (-,+), (-,-)  (SpAx page section 5.1, Eq. 4)
+    return [s0 + s1, s0 - s1, -s0 + s1, -s0 - s1]
+
+
+def _sign2_brute(col: np.ndarray):
+    """Eq. 4 by exact rational arithmetic: greedy scales from exact means,
+    rounded by the rational fp16 rounding; each code the smallest u among
+    the exact minimisers of (w - a s0 - b s1)^2."""
+    w = [Fraction(float(v)) for v in col.astype(np.float64)]
+    R = len(w)
+    s0 = Fraction(_exact_fp16_rne(float(sum(abs(v) for v in w) / R)))
+    e1 = [1 if v >= 0 else -1 for v in w]
+    s1 = Fraction(_exact_fp16_rne(float(sum(abs(v - e * s0) for v, e in zip(w, e1)) / R)))
+    L = _sign2_levels(s0, s1)
+    u = []
+    for v in w:
+        d = [(v - lv) ** 2 for lv in L]
+        u.append(min(range(4), key=lambda k: (d[k], k)))
+    return s0, s1, u
+
+
+def test_sign2_golden(golden_dir):
+    g = _load(golden_dir, "sign2_pack_example.json")
+    col = np.tile(np.array(g["pattern"], dtype=np.float16), g["rows"] // 4)
+    codes, scales = O.pack_sign2(col[None, :])
+    assert float(scales[0, 0]) == g["expected_s0"] and float(scales[0, 1]) == g["expected_s1"]
+    assert np.all(codes[0] == g["expected_byte"])
+    what = O.dequant_sign2(codes, scales)[0]
+    assert list(what[:4]) == g["expected_what_pattern"]
+    u = [(int(codes[0, 0]) >> (2 * r)) & 3 for r in range(4)]
+    assert u == g["expected_u_pattern"]
+
+
+def test_sign2_matches_exact_rational_fit_and_argmin():
+    rs = np.random.default_rng(11)
+    cols = [WL.weights_fp16(93, 0, "w", 128, 3, 0.02)[c] for c in range(3)]
+    # coarse grids force exact ties between levels (midpoints)
+    cols.append((rs.integers(-8, 9, 128) * 0.125).astype(np.float16))
+    cols.append((rs.integers(-3, 4, 128) * 0.25).astype(np.float16))
+    # tiny (subnormal fp16) weights and a lone outlier
+    tiny = (rs.integers(-20, 21, 128) * 2.0 ** -24).astype(np.float16)
+    cols.append(tiny)
+    out = np.zeros(128, dtype=np.float16)
+    out[5] = 3.0
+    cols.append(out)
+    for col in cols:
+        codes, scales = O.pack_sign2(col[None, :])
+        s0, s1, u = _sign2_brute(col)
+        assert Fraction(float(scales[0, 0])) == s0 and Fraction(float(scales[0, 1])) == s1
+        got = [(int(codes[0, i // 4]) >> (2 * (i % 4))) & 3 for i in range(128)]
+        assert got == u
+        what = O.dequant_sign2(codes, scales)[0]
+        L = _sign2_levels(s0, s1)
+        assert [Fraction(float(v)) for v in what] == [L[k] for k in u]
+
+
+def test_sign2_closed_forms():
+    rs = np.random.default_rng(12)
+    # one magnitude: s0 = that magnitude, s1 = 0, exact reconstruction
+    c = (rs.choice([-1.0, 1.0], 256) * 0.375).astype(np.float16)
+    codes, scales = O.pack_sign2(c[None, :])
+    assert float(scales[0, 0]) == 0.375 and float(scales[0, 1]) == 0.0
+    assert np.array_equal(O.dequant_sign2(codes, scales)[0], c.astype(np.float64))
+    # two magnitudes a > b in equal numbers: s0 = (a + b) / 2, s1 = (a - b) / 2,
+    # and the four levels +-a, +-b reproduce every weight exactly
+    mags = np.repeat([0.75, 0.25], 128)
+    rs.shuffle(mags)
+    c = (rs.choice([-1.0, 1.0], 256) * mags).astype(np.float16)
+    codes, scales = O.pack_sign2(c[None, :])
+    assert float(scales[0, 0]) == 0.5 and float(scales[0, 1]) == 0.25
+    assert np.array_equal(O.dequant_sign2(codes, scales)[0], c.astype(np.float64))
+    # zero column: both scales 0, code 0, reconstruction 0
+    codes, scales = O.pack_sign2(np.zeros((2, 128), dtype=np.float16))
+    assert not np.any(codes) and not np.any(scales.astype(np.float64))
+    assert not np.any(O.dequant_sign2(codes, scales))
+    # negating a column flips every code's signs and keeps the scales
+    c = WL.weights_fp16(92, 0, "w", 256, 4, 0.02)
+    nz = c[:, :]
+    c1, s1 = O.pack_sign2(nz)
+    c2, s2 = O.pack_sign2(-nz)
+    assert np.array_equal(s1, s2)
+    w1 = O.dequant_sign2(c1, s1)
+    w2 = O.dequant_sign2(c2, s2)
+    # exact ties may resolve differently; the errors are equal everywhere
+    assert np.array_equal(np.abs(nz.astype(np.float64) - w1),
+                          np.abs(-nz.astype(np.float64) - w2))
+
+
+def test_sign2_error_bounds_and_layout():
+    Wt = WL.weights_fp16(91, 0, "w", 512, 64, 0.02)
+    codes, scales = O.pack_sign2(Wt)
+    n, R = Wt.shape
+    assert codes.shape == (n, R // 4) and codes.dtype == np.uint8
+    assert scales.shape == (n, 2) and scales.dtype == np.float16
+    w = Wt.astype(np.float64)
+    what = O.dequant_sign2(codes, scales)
+    s0 = scales[:, 0:1].astype(np.float64)
+    s1 = scales[:, 1:2].astype(np.float64)
+    # the argmin is never worse than the greedy sign pair, nor than the
+    # one-scale sign code alone
+    e1 = np.where(w >= 0, 1.0, -1.0)
+    e2 = np.where(w - e1 * s0 >= 0, 1.0, -1.0)
+    err = np.abs(w - what)
+    assert np.all(err <= np.abs(w - (e1 * s0 + e2 * s1)))
+    assert np.all(err <= np.abs(w - e1 * s0) + s1)
+    # and on N(0, 0.02) weights it removes most of the energy
+    assert (err ** 2).sum() < 0.15 * (w ** 2).sum()
+
+
 # ---------------------------------------------------------------- tiered product
 
 def _fsum_product(x, Wt, idx):
@@ -330,7 +442,7 @@ def test_all_full_equals_dense_product():
 def test_all_approx_equals_dense_product_of_reconstruction():
     Wt = WL.weights_fp16(97, 0, "w", 256, 30, 0.02)
     x = WL.laplace_fp16(97, 0, "x", 0, 30)
-    for fmt in ("int4", "int2"):
+    for fmt in ("int4", "int2", "sign2"):
         approx = O.ColumnStore(fmt, Wt)
         rec = approx.columns(np.arange(30))
         F, A = O.plan_tiers(x, 0, 30)
