@@ -13,16 +13,16 @@ from typing import Optional, Sequence
 
 __all__ = [
     "SpaxError", "lib", "library_path",
-    "FMT_NONE", "FMT_FP16", "FMT_INT4_G128", "FMT_INT2_G128",
+    "FMT_NONE", "FMT_FP16", "FMT_INT4_G128", "FMT_INT2_G128", "FMT_SIGN2",
     "RES_DEVICE", "RES_HOST_PINNED", "LAYOUT_PLAIN", "LAYOUT_GLU_INTERLEAVED",
     "GROUP_QKV", "GROUP_O", "GROUP_GATE_UP", "GROUP_DOWN",
     "Matrix", "Layer", "LayerIO",
     "plan_tiers", "tiered_gemv", "gemv_workspace_bytes", "layer_step",
-    "layer_workspace_bytes", "pack_g128", "workspace_clear", "version",
+    "layer_workspace_bytes", "pack_g128", "pack_sign2", "workspace_clear", "version",
     "status_string", "last_error", "EXPORTS",
 ]
 
-FMT_NONE, FMT_FP16, FMT_INT4_G128, FMT_INT2_G128 = 0, 1, 2, 3
+FMT_NONE, FMT_FP16, FMT_INT4_G128, FMT_INT2_G128, FMT_SIGN2 = 0, 1, 2, 3, 4
 RES_DEVICE, RES_HOST_PINNED = 0, 1
 LAYOUT_PLAIN, LAYOUT_GLU_INTERLEAVED = 0, 1
 GROUP_QKV, GROUP_O, GROUP_GATE_UP, GROUP_DOWN = 0, 1, 2, 3
@@ -35,7 +35,7 @@ STATUS = {0: "SPAX_OK", -1: "SPAX_EINVAL", -2: "SPAX_ENULL", -3: "SPAX_EALIGN",
 # Every entry point declared in include/spax.h.
 EXPORTS = (
     "spax_plan_tiers", "spax_gemv_workspace_bytes", "spax_tiered_gemv",
-    "spax_layer_workspace_bytes", "spax_layer_step", "spax_pack_g128",
+    "spax_layer_workspace_bytes", "spax_layer_step", "spax_pack_g128", "spax_pack_sign2",
     "spax_workspace_clear", "spax_status_string", "spax_last_error", "spax_version",
     "spax_set_kernel_choice",
 )
@@ -174,6 +174,8 @@ def _declare(L: ctypes.CDLL) -> None:
     L.spax_layer_step.restype = ctypes.c_int
     L.spax_pack_g128.argtypes = [vp, i32, i32, i32, vp, vp, vp]
     L.spax_pack_g128.restype = ctypes.c_int
+    L.spax_pack_sign2.argtypes = [vp, i32, i32, vp, vp, vp]
+    L.spax_pack_sign2.restype = ctypes.c_int
     L.spax_workspace_clear.argtypes = [vp, sz, vp]
     L.spax_workspace_clear.restype = ctypes.c_int
     L.spax_status_string.argtypes = [ctypes.c_int]
@@ -246,6 +248,13 @@ def pack_g128(w, rows, cols, fmt, codes, scales, stream=None) -> None:
     _check(lib().spax_pack_g128(_ptr(w), int(rows), int(cols), int(fmt), _ptr(codes),
                                 _ptr(scales), _stream(stream)),
            "spax_pack_g128")
+
+
+def pack_sign2(w, rows, cols, codes, scales, stream=None) -> None:
+    """spax_pack_sign2: two-scale 2-bit sign codes and fp16 (s0, s1) of w."""
+    _check(lib().spax_pack_sign2(_ptr(w), int(rows), int(cols), _ptr(codes), _ptr(scales),
+                                 _stream(stream)),
+           "spax_pack_sign2")
 
 
 def workspace_clear(ws, nbytes=None, stream=None) -> None:

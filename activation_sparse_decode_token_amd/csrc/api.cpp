@@ -32,11 +32,13 @@ int64_t col_bytes(int32_t fmt, int64_t rows) {
     case kFp16: return 2 * rows;
     case kInt4: return rows / 2;
     case kInt2: return rows / 4;
+    case kSign2: return rows / 4;
     default: return 0;
   }
 }
-// fp16 scales per stored column (0 for fp16 values).
+// fp16 scales per stored column (0 for fp16 values; 2 for the sign code).
 int64_t col_scales(int32_t fmt, int64_t rows) {
+  if (fmt == kSign2) return 2;
   return (fmt == kInt4 || fmt == kInt2) ? rows / kGroup : 0;
 }
 // Bytes one 512-row tile of a column costs, used to balance the splits.
@@ -45,6 +47,7 @@ int64_t tile_bytes(int32_t fmt) {
     case kFp16: return 2 * kTileRows;
     case kInt4: return kTileRows / 2 + 2 * (kTileRows / kGroup);
     case kInt2: return kTileRows / 4 + 2 * (kTileRows / kGroup);
+    case kSign2: return kTileRows / 4 + 4;
     default: return 0;
   }
 }
@@ -54,8 +57,10 @@ int validate_matrix(const spax_matrix* W) {
   if (W->rows <= 0 || W->cols <= 0 || W->rows % kGroup || W->rows > kMaxRows)
     return SPAX_EINVAL;
   if (W->full_fmt != kFp16 && W->full_fmt != kInt4) return SPAX_EFORMAT;
-  if (W->approx_fmt != kNone && W->approx_fmt != kInt4 && W->approx_fmt != kInt2)
+  if (W->approx_fmt != kNone && W->approx_fmt != kInt4 && W->approx_fmt != kInt2 &&
+      W->approx_fmt != kSign2)
     return SPAX_EFORMAT;
+  if (W->approx_fmt == kSign2 && W->full_fmt != kFp16) return SPAX_EFORMAT;
   if (W->residency != SPAX_RES_DEVICE && W->residency != SPAX_RES_HOST_PINNED)
     return SPAX_EINVAL;
   if (W->layout != SPAX_LAYOUT_PLAIN && W->layout != SPAX_LAYOUT_GLU_INTERLEAVED)
@@ -452,6 +457,15 @@ int spax_pack_g128(const uint16_t* w, int32_t rows, int32_t cols, int32_t fmt, u
   if (!w || !codes || !scales) return SPAX_ENULL;
   if (!aligned16(w) || !aligned16(codes) || !aligned16(scales)) return SPAX_EALIGN;
   const hipError_t e = launch_pack(w, rows, cols, fmt, codes, scales, stream);
+  return e == hipSuccess ? SPAX_OK : hip_fail(e);
+}
+
+int spax_pack_sign2(const uint16_t* w, int32_t rows, int32_t cols, uint8_t* codes,
+                    uint16_t* scales, hipStream_t stream) {
+  if (!w || !codes || !scales) return SPAX_ENULL;
+  if (rows <= 0 || cols <= 0 || rows % kGroup || rows > kMaxRows) return SPAX_EINVAL;
+  if (!aligned16(w) || !aligned16(codes) || !aligned16(scales)) return SPAX_EALIGN;
+  const hipError_t e = launch_pack_sign2(w, rows, cols, codes, scales, stream);
   return e == hipSuccess ? SPAX_OK : hip_fail(e);
 }
 

@@ -121,6 +121,111 @@ __global__ __launch_bounds__(256) void pack_kernel(const uint16_t* __restrict__ 
   }
 }
 
+// ---------------------------------------------------------------------------
+// Two-scale 2-bit sign packer (offline). SpAx page section 5.1, Eq. 4: a
+// weight is rebuilt as e1 s0 + e2 s1 with signs e1, e2 and two scales per
+// column; the codes minimise the squared error given the scales. Scales
+// (closed-form greedy fit): s0 = fp16(mean |w|), s1 = fp16(mean |w - e1 s0|)
+// with e1 = +1 iff w >= 0. Every fp16 value is an exact integer in units of
+// 2^-24 (below 2^40 in magnitude), so the sums and the distances are exact
+// 64-bit integers; each mean is one fp64 division rounded once to fp16.
+// One workgroup per column.
+// ---------------------------------------------------------------------------
+constexpr int kSign2Threads = 256;
+
+// fp16 bits -> signed value in units of 2^-24 (finite inputs)
+__device__ __forceinline__ int64_t h_units(uint32_t b) {
+  const uint32_t e = (b >> 10) & 31u, m = b & 1023u;
+  const int64_t mag = e == 0u ? (int64_t)m : (int64_t)(m | 1024u) << (e - 1u);
+  return (b & 0x8000u) ? -mag : mag;
+}
+
+// Round a finite v >= 0 to fp16, ties to even, in one step from the double
+// (the quantum of [2^E, 2^(E+1)) is 2^(E-10), 2^-24 below 2^-14; rint rounds
+// ties to even; both scalings are exact).
+__device__ __forceinline__ uint16_t f64_to_h_rne(double v) {
+  if (v == 0.0) return 0;
+  int e;
+  (void)frexp(v, &e);  // v in [2^(e-1), 2^e)
+  int E = e - 1;
+  if (E < -14) return (uint16_t)rint(ldexp(v, 24));  // 1024 is the smallest normal
+  uint32_t q = (uint32_t)rint(ldexp(v, 10 - E));      // in [1024, 2048]
+  if (q == 2048u) {
+    q = 1024u;
+    ++E;
+  }
+  if (E > 15) return 0x7C00;
+  return (uint16_t)(((uint32_t)(E + 15) << 10) | (q - 1024u));
+}
+
+// Sum of one int64 per thread over the workgroup (result on thread 0).
+__device__ __forceinline__ int64_t block_sum64(int64_t v, int64_t* part) {
+  const int t = threadIdx.x;
+  part[t] = v;
+  __syncthreads();
+  for (int w = kSign2Threads / 2; w > 0; w >>= 1) {
+    if (t < w) part[t] += part[t + w];
+    __syncthreads();
+  }
+  const int64_t r = part[0];
+  __syncthreads();
+  return r;
+}
+
+__global__ __launch_bounds__(kSign2Threads) void pack_sign2_kernel(
+    const uint16_t* __restrict__ w, int rows, uint8_t* __restrict__ codes,
+    uint16_t* __restrict__ scales) {
+  __shared__ int64_t part[kSign2Threads];
+  const int t = threadIdx.x;
+  const int64_t col = blockIdx.x;
+  const uint16_t* src = w + col * rows;
+  // s0: mean magnitude
+  int64_t acc = 0;
+  for (int i = t; i < rows; i += kSign2Threads) {
+    const int64_t v = h_units(src[i]);
+    acc += v < 0 ? -v : v;
+  }
+  const int64_t S0 = block_sum64(acc, part);
+  const uint16_t s0h = f64_to_h_rne(ldexp((double)S0 / (double)rows, -24));
+  const int64_t s0 = h_units(s0h);
+  // s1: mean magnitude of the residual of the first sign code
+  acc = 0;
+  for (int i = t; i < rows; i += kSign2Threads) {
+    const int64_t v = h_units(src[i]);
+    const int64_t r = v - (v >= 0 ? s0 : -s0);
+    acc += r < 0 ? -r : r;
+  }
+  const int64_t S1 = block_sum64(acc, part);
+  const uint16_t s1h = f64_to_h_rne(ldexp((double)S1 / (double)rows, -24));
+  const int64_t s1 = h_units(s1h);
+  if (t == 0) {
+    scales[2 * col] = s0h;
+    scales[2 * col + 1] = s1h;
+  }
+  // codes: levels in code order u = 0..3 are (+,+), (+,-), (-,+), (-,-);
+  // the first minimum (smallest u) wins
+  const int64_t L[4] = {s0 + s1, s0 - s1, -s0 + s1, -s0 - s1};
+  for (int b = t; b < rows / 4; b += kSign2Threads) {
+    uint32_t byte = 0;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int64_t v = h_units(src[4 * b + r]);
+      uint32_t best = 0;
+      int64_t bd = v - L[0] < 0 ? L[0] - v : v - L[0];
+#pragma unroll
+      for (uint32_t k = 1; k < 4; ++k) {
+        const int64_t d = v - L[k] < 0 ? L[k] - v : v - L[k];
+        if (d < bd) {
+          bd = d;
+          best = k;
+        }
+      }
+      byte |= best << (2 * r);
+    }
+    codes[col * (rows / 4) + b] = (uint8_t)byte;
+  }
+}
+
 __global__ void clear_kernel(uint32_t* __restrict__ p, int64_t n) {
   for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
        i += (int64_t)gridDim.x * blockDim.x)
@@ -146,6 +251,14 @@ hipError_t launch_pack(const uint16_t* w, int32_t rows, int32_t cols, int32_t fm
   const int64_t blocks = (items + 3) / 4;
   hipLaunchKernelGGL(pack_kernel, dim3((unsigned)blocks), dim3(256), 0, s, w, rows, cols, fmt,
                      codes, scales);
+  return hipGetLastError();
+}
+
+hipError_t launch_pack_sign2(const uint16_t* w, int32_t rows, int32_t cols, uint8_t* codes,
+                             uint16_t* scales, hipStream_t s) {
+  if (cols == 0) return hipSuccess;
+  hipLaunchKernelGGL(pack_sign2_kernel, dim3((unsigned)cols), dim3(kSign2Threads), 0, s, w,
+                     rows, codes, scales);
   return hipGetLastError();
 }
 

@@ -147,6 +147,41 @@ struct Tier<kInt2> {
   }
 };
 
+// The SpAx page's two-scale sign code (section 5.1, Eq. 4): weight i of
+// column j is e1 s_{j,0} + e2 s_{j,1}. Row 4b + r holds [e2 = -1] in bit 2r
+// and [e1 = -1] in bit 2r + 1 of byte b (two bytes per lane). The second
+// byte moves to bits 16..23; each sign bit of rows r and r + 4 is then
+// shifted into the sign bits (15 and 31) of a pair of fp16 1.0s, and the
+// resulting +-1 are multiplied in by fp16 x fp32 FMAs with the column's
+// factors fa = x_j s_{j,0} and fb = x_j s_{j,1}. Every added term is exactly
+// +-x_j s, with no offset to take back. kM is kMask held in a VGPR.
+template <>
+struct Tier<kSign2> {
+  using V = uint32_t;
+  static constexpr int U = 8;
+  static constexpr uint32_t kMask = 0x80008000u;  // sign bits of both halves
+  static __device__ __forceinline__ uint32_t offset(int row0, int lane) {
+    return (uint32_t)(row0 + 8 * lane) / 4u;
+  }
+  static __device__ __forceinline__ V load(__amdgpu_buffer_rsrc_t t, uint32_t off, uint32_t col) {
+    return __builtin_amdgcn_raw_buffer_load_b16(t, off, col, 0);
+  }
+  static __device__ __forceinline__ void fma2(float (&acc)[8], V v, float fa, float fb,
+                                              uint32_t kM) {
+    const uint32_t w = (v & 0xFFu) | ((v & 0xFF00u) << 8);
+    constexpr uint32_t kOne = 0x3C003C00u;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const uint32_t pa = ((w << (14 - 2 * r)) & kM) | kOne;  // e1 of rows r, r + 4
+      const uint32_t pb = ((w << (15 - 2 * r)) & kM) | kOne;  // e2 of rows r, r + 4
+      acc[r] = fmaf(h2f(pa & 0xFFFFu), fa, acc[r]);
+      acc[r] = fmaf(h2f(pb & 0xFFFFu), fb, acc[r]);
+      acc[r + 4] = fmaf(h2f(pa >> 16), fa, acc[r + 4]);
+      acc[r + 4] = fmaf(h2f(pb >> 16), fb, acc[r + 4]);
+    }
+  }
+};
+
 // ---------------------------------------------------------------------------
 // In-workgroup tier selection (kListRank). Same definition as the stand-alone
 // plan kernel: order key = fp16 magnitude bits, larger first, lower index

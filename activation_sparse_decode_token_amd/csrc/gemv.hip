@@ -95,7 +95,10 @@ struct TierStream {
   using T = Tier<FMT>;
   using V = typename T::V;
   static constexpr int U = T::U;
-  static constexpr bool kCode = FMT != kFp16;
+  // group-scaled integer codes: a factor per 128-row group, through LDS
+  static constexpr bool kCode = FMT == kInt4 || FMT == kInt2;
+  // two-scale sign code: two factors per column, lane-uniform (readlane)
+  static constexpr bool kTwo = FMT == kSign2;
 
   WaveMeta& wm;
   __amdgpu_buffer_rsrc_t rs;
@@ -112,6 +115,7 @@ struct TierStream {
   uint32_t vmask;  // the tier's code mask, kept in a VGPR
   int mycol;       // this lane's column of the pending batch
   float xv;        // this lane's activation of the pending batch (0 past it)
+  float xb;        // sign code: x_j s_{j,1} (xv then holds x_j s_{j,0})
   uint32_t sc[4];  // this lane's raw fp16 scales of the pending batch (codes)
 
   __device__ __forceinline__ TierStream(WaveMeta& wm_, const uint8_t* base, int64_t stride,
@@ -134,6 +138,7 @@ struct TierStream {
   // raw scales, without waiting for the scales.
   __device__ __forceinline__ void fill_cols(int pb, int cnt) {
     xv = 0.0f;
+    xb = 0.0f;
     mycol = 0;
     if (lane < cnt) {
       const int q = pb + lane;
@@ -146,6 +151,12 @@ struct TierStream {
         xv = h2f(x[j]);
       }
       mycol = MODE == kListStaged ? q : j;
+      if constexpr (kTwo) {
+        // the column's (s0, s1) in one 4-byte load
+        const uint32_t sv = *reinterpret_cast<const uint32_t*>(scales + (int64_t)mycol * 2);
+        xb = xv * h2f(sv >> 16);
+        xv = xv * h2f(sv & 0xFFFFu);
+      }
       if constexpr (kCode) {
         const uint16_t* sp = scales + (int64_t)mycol * sstride + (row0 >> 7);
         if (ngrp == 4 && (sstride & 3) == 0) {
@@ -180,18 +191,23 @@ struct TierStream {
       v[u] = T::load(rs, off, col * cstride);
     }
   }
+  // Adds batch column c (loaded as v) to the accumulators.
+  __device__ __forceinline__ void add(float (&acc)[8], float& corr, int c, const V& v) {
+    if constexpr (kTwo)
+      T::fma2(acc, v, readlane_f(xv, c), readlane_f(xb, c), vmask);
+    else
+      T::fma(acc, corr, v, kCode ? wm.fac[c][gsel] : readlane_f(xv, c), vmask);
+  }
   __device__ __forceinline__ void use(float (&acc)[8], float& corr, int r, int cnt,
                                       const V (&v)[U]) {
     if ((r + 1) * U <= cnt) {  // a full round (wave-uniform)
 #pragma unroll
-      for (int u = 0; u < U; ++u)
-        T::fma(acc, corr, v[u], kCode ? wm.fac[r * U + u][gsel] : readlane_f(xv, r * U + u),
-               vmask);
+      for (int u = 0; u < U; ++u) add(acc, corr, r * U + u, v[u]);
     } else {  // the batch's last, partial round: only its columns are added
 #pragma unroll
       for (int u = 0; u < U; ++u) {
         const int c = r * U + u;
-        if (c < cnt) T::fma(acc, corr, v[u], kCode ? wm.fac[c][gsel] : readlane_f(xv, c), vmask);
+        if (c < cnt) add(acc, corr, c, v[u]);
       }
     }
   }
@@ -455,6 +471,7 @@ hipError_t launch_gemv(const GemvArgs& a, int32_t full_fmt, int32_t approx_fmt, 
     if (approx_fmt == kNone) return launch_mode<kFp16, kNone>(a, mode, epi, s);
     if (approx_fmt == kInt4) return launch_mode<kFp16, kInt4>(a, mode, epi, s);
     if (approx_fmt == kInt2) return launch_mode<kFp16, kInt2>(a, mode, epi, s);
+    if (approx_fmt == kSign2) return launch_mode<kFp16, kSign2>(a, mode, epi, s);
   } else if (full_fmt == kInt4) {
     if (approx_fmt == kNone) return launch_mode<kInt4, kNone>(a, mode, epi, s);
     if (approx_fmt == kInt4) return launch_mode<kInt4, kInt4>(a, mode, epi, s);

@@ -40,7 +40,7 @@ constexpr int kRankMaxN = kGemvThreads * 16;
 constexpr int kSliceEntries = kGemvThreads * 4;
 constexpr int kMaxSlices = 65536 / kSliceEntries;
 
-enum Fmt : int32_t { kNone = 0, kFp16 = 1, kInt4 = 2, kInt2 = 3 };
+enum Fmt : int32_t { kNone = 0, kFp16 = 1, kInt4 = 2, kInt2 = 3, kSign2 = 4 };
 enum Epi : int32_t { kEpiPlain = 0, kEpiGlu = 1 };
 // Where the tiered product takes its tier lists from.
 enum ListMode : int32_t {
@@ -130,6 +130,9 @@ hipError_t launch_copy(const CopyArgs& a, hipStream_t s);
 
 hipError_t launch_pack(const uint16_t* w, int32_t rows, int32_t cols, int32_t fmt,
                        uint8_t* codes, uint16_t* scales, hipStream_t s);
+
+hipError_t launch_pack_sign2(const uint16_t* w, int32_t rows, int32_t cols, uint8_t* codes,
+                             uint16_t* scales, hipStream_t s);
 
 hipError_t launch_clear(void* ws, size_t bytes, hipStream_t s);
 

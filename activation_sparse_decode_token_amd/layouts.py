@@ -6,7 +6,8 @@ input are stored as one matrix so that the columns one activation entry
 indexes are adjacent (SpAx page, section 5.3, Figure 4):
   * q, k, v: rows stacked, column j = [q_j; k_j; v_j];
   * gate, up: rows interleaved in 128-row blocks (SPAX_LAYOUT_GLU_INTERLEAVED).
-The compressed copies are produced by the library's packer (spax_pack_g128).
+The compressed copies are produced by the library's packers (spax_pack_g128,
+spax_pack_sign2).
 These helpers only move data; nothing here is on the per-token path.
 """
 from __future__ import annotations
@@ -15,8 +16,9 @@ from typing import Optional, Sequence
 
 import torch
 
-from . import (FMT_FP16, FMT_INT2_G128, FMT_INT4_G128, FMT_NONE, LAYOUT_GLU_INTERLEAVED,
-               LAYOUT_PLAIN, RES_DEVICE, RES_HOST_PINNED, Matrix, pack_g128)
+from . import (FMT_FP16, FMT_INT2_G128, FMT_INT4_G128, FMT_NONE, FMT_SIGN2,
+               LAYOUT_GLU_INTERLEAVED, LAYOUT_PLAIN, RES_DEVICE, RES_HOST_PINNED, Matrix,
+               pack_g128, pack_sign2)
 
 GROUP = 128
 
@@ -46,6 +48,12 @@ def glu_deinterleave(stacked: torch.Tensor):
 def pack(w_cm: torch.Tensor, fmt: int, stream=None):
     """Codes and scales of a column-major fp16 device tensor [n, R]."""
     n, R = w_cm.shape
+    if fmt == FMT_SIGN2:
+        # two-scale sign code: 2 bits per weight, (s0, s1) per column
+        codes = torch.empty((n, R // 4), dtype=torch.uint8, device=w_cm.device)
+        scales = torch.empty((n, 2), dtype=torch.float16, device=w_cm.device)
+        pack_sign2(w_cm, R, n, codes, scales, stream)
+        return codes, scales
     per = {FMT_INT4_G128: 2, FMT_INT2_G128: 4}[fmt]
     codes = torch.empty((n, R // per), dtype=torch.uint8, device=w_cm.device)
     scales = torch.empty((n, R // GROUP), dtype=torch.float16, device=w_cm.device)
@@ -67,7 +75,9 @@ def build_matrix(w_cm: torch.Tensor, full_fmt: int = FMT_FP16,
     """A spax_matrix for a column-major fp16 device tensor [n, R].
 
     The full tier is w_cm itself (fp16) or its int4 code; the approx tier is
-    the int4 / int2 code of w_cm. With RES_HOST_PINNED every buffer is copied
+    the int4 / int2 group-128 code or the two-scale sign code of w_cm (the
+    sign code's two scales are fitted per stored column: with stacked
+    matrices, one pair per column of the stack). With RES_HOST_PINNED every buffer is copied
     to pinned host memory and the device copies are dropped."""
     n, R = w_cm.shape
     fs = None

@@ -61,6 +61,13 @@ extern "C" {
 #define SPAX_FMT_FP16       1  /* fp16 values, rows*2 bytes per column        */
 #define SPAX_FMT_INT4_G128  2  /* int4 codes + fp16 scale per 128 rows        */
 #define SPAX_FMT_INT2_G128  3  /* int2 codes + fp16 scale per 128 rows        */
+/* Two-scale 2-bit sign code of the middle tier (SpAx page section 5.1,
+ * Eq. 4): weight i of column j is rebuilt as e1 s_{j,0} + e2 s_{j,1} with
+ * signs (e1, e2) in {-1, +1} and two fp16 scales per stored column. Code u
+ * = 2 [e1 = -1] + [e2 = -1], rows/4 bytes per column packed like int2 (row
+ * 4i + r in bits 2r..2r+1 of byte i); scales [cols][2] = (s0, s1). Approx
+ * tier only, with an fp16 full tier. Produced by spax_pack_sign2. */
+#define SPAX_FMT_SIGN2      4
 
 #define SPAX_RES_DEVICE       0  /* weights in device memory (HBM)            */
 #define SPAX_RES_HOST_PINNED  1  /* weights in pinned host memory that the GPU
@@ -82,13 +89,14 @@ typedef struct spax_matrix {
   int32_t rows;            /* output length R (multiple of 128)            */
   int32_t cols;            /* input length n                                */
   int32_t full_fmt;        /* SPAX_FMT_FP16 or SPAX_FMT_INT4_G128           */
-  int32_t approx_fmt;      /* SPAX_FMT_NONE, _INT4_G128 or _INT2_G128       */
+  int32_t approx_fmt;      /* SPAX_FMT_NONE, _INT4_G128, _INT2_G128 or
+                              _SIGN2 (the last with an fp16 full tier)    */
   int32_t residency;       /* SPAX_RES_*                                    */
   int32_t layout;          /* SPAX_LAYOUT_*                                 */
   const void* full_data;   /* fp16 [cols][rows] or int4 codes [cols][rows/2] */
   const uint16_t* full_scales;   /* int4 full tier only: [cols][rows/128]   */
   const uint8_t* approx_codes;   /* approx codes, layout per approx_fmt     */
-  const uint16_t* approx_scales; /* [cols][rows/128]                        */
+  const uint16_t* approx_scales; /* [cols][rows/128]; SIGN2: [cols][2]      */
 } spax_matrix;
 
 /* ---- tier selection ----------------------------------------------------- */
@@ -224,6 +232,24 @@ int spax_set_kernel_choice(int32_t choice);
  *   Errors: SPAX_ENULL, SPAX_EINVAL, SPAX_EALIGN, SPAX_EFORMAT, SPAX_EHIP.  */
 int spax_pack_g128(const uint16_t* w, int32_t rows, int32_t cols, int32_t fmt,
                    uint8_t* codes, uint16_t* scales, hipStream_t stream);
+
+/* spax_pack_sign2 -- encode the two-scale 2-bit sign code of a matrix
+ * (SpAx page section 5.1, Eq. 4; offline, Figure 2 step 1). Per column j,
+ * with every weight taken exactly (units of 2^-24):
+ *   s0 = fp16(mean_i |w_i|)                 (the least-squares scale of the
+ *   s1 = fp16(mean_i |w_i - e1_i s0|)        sign code e1_i = +1 iff w_i >= 0,
+ *                                            then of the residual's sign)
+ *   (e1, e2) = argmin over {-1,+1}^2 of (w_i - e1 s0 - e2 s1)^2, the smaller
+ *   code u on equal errors.
+ * The sums are exact; each mean is one fp64 division rounded once to fp16
+ * (ties to even). The page fits its scales Lloyd-Max style; this closed
+ * form is the reading taken where its fitting text is not available.
+ *   w      device fp16 [cols][rows] (column-major), finite, rows % 128 == 0.
+ *   codes  device out, [cols][rows/4] bytes.
+ *   scales device out, fp16 [cols][2] = (s0, s1).
+ *   Errors: SPAX_ENULL, SPAX_EINVAL, SPAX_EALIGN, SPAX_EHIP.                */
+int spax_pack_sign2(const uint16_t* w, int32_t rows, int32_t cols, uint8_t* codes,
+                    uint16_t* scales, hipStream_t stream);
 
 /* spax_workspace_clear -- zero `bytes` bytes of ws with a kernel (no memset
  * node, so it may be captured in a graph). bytes % 4 == 0. */

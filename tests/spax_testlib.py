@@ -43,7 +43,8 @@ def ulp16(v: np.ndarray) -> np.ndarray:
 
 def abs_sum(x, F, A, full: O.ColumnStore, approx) -> np.ndarray:
     """Per-row sum of the magnitudes the fp32 accumulation adds: |x_j W_ij|
-    for full fp16 columns. A code column with b-bit code u adds
+    for full fp16 columns; |x_j| (s_{j,0} + s_{j,1}) for a two-scale sign
+    code column (its two terms). A code column with b-bit code u adds
     x_j s_jg (2^b + u) per element (the code as fp16 1 + u / 2^b times the
     factor 2^b x_j s_jg) and x_j s_jg (2^b + offset) once to the running sum
     that is subtracted at the end (offset 8 for int4, 1.5 for int2)."""
@@ -51,6 +52,10 @@ def abs_sum(x, F, A, full: O.ColumnStore, approx) -> np.ndarray:
     S = np.zeros(full.rows)
 
     def code_part(store, idx):
+        if store.fmt == "sign2":
+            # two exact terms per element: +-x_j s_{j,0} and +-x_j s_{j,1}
+            s = store.scales[idx].astype(np.float64)
+            return np.repeat((np.abs(xf[idx]) * (s[:, 0] + s[:, 1]))[:, None], store.rows, axis=1)
         if store.fmt == "int4":
             nib = np.empty((len(idx), store.rows), dtype=np.int64)
             c = store.codes[idx]
@@ -101,7 +106,10 @@ def check_product(y16: np.ndarray, x, F, A, full, approx, label: str = "",
     # elementwise bound below is the gate.
     if rmax >= FP16_MIN_NORMAL:
         assert err <= REL_TOL, f"{label}: norm-wise error {err:.3e} > {REL_TOL}"
-    m = len(F) + len(A) + 80
+    # terms summed per element: one per full or integer-code column, two per
+    # sign-code column, plus the split partials and the running offset sum
+    per_a = 2 if approx is not None and approx.fmt == "sign2" else 1
+    m = len(F) + per_a * len(A) + 80
     gamma = m * U24 / (1 - m * U24)
     S = abs_sum(x, F, A, full, approx)
     bound = gamma * S + 0.5 * ulp16(y) + 2.0 ** -25

@@ -57,6 +57,9 @@ def test_workspace_sizes():
     assert spax.gemv_workspace_bytes(Wh) >= ws + 4096 * 2 * 4096
     bad = _matrix(rows=100)
     assert spax.gemv_workspace_bytes(bad) == 0
+    # staging of the sign code: rows / 4 code bytes and 2 scales per column
+    Ws = _matrix(af=spax.FMT_SIGN2, res=spax.RES_HOST_PINNED)
+    assert spax.gemv_workspace_bytes(Ws) == spax.gemv_workspace_bytes(Wh)
     L = spax.Layer.make([W, _matrix(), None, None], [1, 1, 0, 0], [1, 1, 0, 0])
     assert spax.layer_workspace_bytes(L) == ws
 
@@ -79,6 +82,9 @@ def test_gemv_validation_errors():
     assert _gemv(W, x=P + 2) == -3
     assert _gemv(_matrix(ff=spax.FMT_INT2_G128)) == -4
     assert _gemv(_matrix(af=7)) == -4
+    # the sign code is an approx tier under an fp16 full tier only
+    assert _gemv(_matrix(ff=spax.FMT_INT4_G128, af=spax.FMT_SIGN2)) == -4
+    assert _gemv(_matrix(af=spax.FMT_SIGN2), ws_bytes=1024) == -5
     assert _gemv(W, ws_bytes=1024) == -5
     assert _gemv(_matrix(res=spax.RES_HOST_PINNED)) == -6
     assert _gemv(_matrix(layout=spax.LAYOUT_GLU_INTERLEAVED, rows=128 * 3)) == -1
@@ -129,6 +135,11 @@ def test_layer_and_helper_validation_errors():
     assert g(P, 4096, 16, spax.FMT_FP16, P, P, None) == -4
     assert g(P, 100, 16, spax.FMT_INT4_G128, P, P, None) == -1
     assert g(None, 128, 16, spax.FMT_INT2_G128, P, P, None) == -2
+    s2 = spax.lib().spax_pack_sign2
+    assert s2(P, 100, 16, P, P, None) == -1
+    assert s2(P, 128, 0, P, P, None) == -1
+    assert s2(None, 128, 16, P, P, None) == -2
+    assert s2(P, 128, 16, P + 4, P, None) == -3
     c = spax.lib().spax_workspace_clear
     assert c(P, 6, None) == -1
     assert c(None, 8, None) == -2

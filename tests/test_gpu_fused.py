@@ -15,7 +15,7 @@ from tests.spax_testlib import check_product, log, to_dev, to_host
 
 pytestmark = pytest.mark.gpu
 
-FMT = {"fp16": 1, "int4": 2, "int2": 3, "none": 0}
+FMT = {"fp16": 1, "int4": 2, "int2": 3, "sign2": 4, "none": 0}
 
 
 def _one_group(Wt, x, ff, af, kf, ka, ws=None):
@@ -77,6 +77,9 @@ CASES = [
     (512, 32769, "fp16", "int4", 9000, 9000),    # sliced selection, ragged last slice
     (256, 65536, "fp16", "int2", 20000, 30000),  # longest input: 16 slices
     (128, 6000, "fp16", "none", 6000, 0),        # one tile, one split, long list
+    (640, 300, "fp16", "sign2", 60, 90),         # two-scale sign code
+    (1024, 11008, "fp16", "sign2", 2752, 2752),
+    (512, 32769, "fp16", "sign2", 9000, 9000),   # sliced selection
 ]
 
 

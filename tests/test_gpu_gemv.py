@@ -8,7 +8,7 @@ from tests.spax_testlib import (check_product, log, sample_groups, to_dev, to_ho
 
 pytestmark = pytest.mark.gpu
 
-FMT = {"fp16": 1, "int4": 2, "int2": 3, "none": 0}
+FMT = {"fp16": 1, "int4": 2, "int2": 3, "sign2": 4, "none": 0}
 
 
 def _spax():
@@ -51,6 +51,26 @@ def test_pack_bit_exact(fmt, R, n):
     assert np.array_equal(to_host(scales).view(np.uint16), os_.view(np.uint16))
 
 
+@pytest.mark.parametrize("R,n", [(128, 3), (640, 77), (4096, 300)])
+def test_pack_sign2_bit_exact(R, n):
+    """The two-scale sign packer against the oracle's: codes and both scales."""
+    import torch
+    from activation_sparse_decode_token_amd.layouts import pack
+    rs = np.random.default_rng(R + n)
+    Wt = WL.weights_fp16(804, 0, "w", R, n, 0.02)
+    Wt[0] = 0                                                        # zero column
+    Wt[1] = (rs.choice([-1.0, 1.0], R) * 0.375).astype(np.float16)   # one magnitude
+    Wt[2] = (rs.integers(-8, 9, R) * 0.125).astype(np.float16)       # coarse grid: ties
+    Wt[3 % n] = (rs.integers(-20, 21, R) * 2.0 ** -24).astype(np.float16)  # subnormal
+    if n > 4:
+        Wt[4, 5] = np.float16(7.0)                                   # an outlier
+    codes, scales = pack(to_dev(Wt), FMT["sign2"])
+    torch.cuda.synchronize()
+    oc, os_ = O.pack_sign2(Wt)
+    assert np.array_equal(to_host(scales).view(np.uint16), os_.view(np.uint16))
+    assert np.array_equal(to_host(codes), oc)
+
+
 CASES = [
     # R, n, full fmt, approx fmt, k_full, k_approx
     (128, 64, "fp16", "int4", 10, 20),
@@ -69,6 +89,11 @@ CASES = [
     (1152, 777, "int4", "none", 100, 0),
     (1152, 777, "fp16", "int2", 0, 400),
     (640, 6000, "fp16", "none", 6000, 0),
+    # the two-scale sign code as the approx tier
+    (640, 300, "fp16", "sign2", 60, 90),
+    (1536, 1000, "fp16", "sign2", 300, 300),
+    (3072, 2000, "fp16", "sign2", 0, 2000),   # all approx
+    (512, 7, "fp16", "sign2", 3, 4),
 ]
 
 
@@ -125,7 +150,14 @@ def _full_size_case(cfg, R, n, ff, af, split, std, tokens, label, stacked=None):
     rows = sample_groups(R, 12, cfg * 7 + R)
     sub = np.ascontiguousarray(Wt[:, rows])
     full = O.ColumnStore(ff, sub)
-    approx = O.ColumnStore(af, sub) if af != "none" else None
+    if af == "sign2":
+        # the sign code's scales are fitted over whole columns: pack all rows,
+        # keep the codes of the sampled ones
+        codes, scales = O.pack_sign2(Wt)
+        approx = O.ColumnStore("sign2", codes=np.ascontiguousarray(codes[:, rows[0::4] // 4]),
+                               scales=scales)
+    else:
+        approx = O.ColumnStore(af, sub) if af != "none" else None
     for tok in range(tokens):
         x = WL.laplace_fp16(cfg, 0, "x", tok, n)
         F, A = O.plan_tiers(x, kf, ka)
@@ -140,6 +172,13 @@ def test_full_size_7b_attention():
     _full_size_case(2, 4096, 4096, "fp16", "int4", c.splits[0], 0.02, 2, "7B o-proj")
     _full_size_case(2, 12288, 4096, "fp16", "int4", c.splits[0], 0.02, 2, "7B qkv stacked",
                     stacked=("q", "k", "v"))
+
+
+def test_full_size_7b_attention_sign2():
+    c = WL.CONFIGS[2]
+    _full_size_case(2, 4096, 4096, "fp16", "sign2", c.splits[0], 0.02, 1, "7B o-proj sign2")
+    _full_size_case(2, 12288, 4096, "fp16", "sign2", c.splits[0], 0.02, 1,
+                    "7B qkv stacked sign2", stacked=("q", "k", "v"))
 
 
 @pytest.mark.parametrize("si", [0, 1, 2])

@@ -33,7 +33,7 @@ def _build_layer(w: LayerWeights, ff, af, residency, ks):
     spax = _spax()
     from activation_sparse_decode_token_amd.layouts import build_matrix, glu_interleave, stack_rows
     F = {"fp16": 1, "int4": 2}[ff]
-    A = {"int4": 2, "int2": 3}[af]
+    A = {"int4": 2, "int2": 3, "sign2": 4}[af]
     qkv = build_matrix(stack_rows([to_dev(w.q), to_dev(w.k), to_dev(w.v)]), F, A,
                        residency=residency)
     o = build_matrix(to_dev(w.o), F, A, residency=residency)
@@ -84,9 +84,33 @@ def _run_layer(L, h, z, x, ws=None, copy_stream=None):
 def _check_layer(res, w: LayerWeights, ks, h, z, x, ff, af, label, rows_per=None):
     """Stage-wise parity: each group is compared with the oracle fed the same
     inputs the GPU group saw (down is fed the GPU's a)."""
-    def stores(Wt, rows=None):
+    packed = {}
+
+    def stores(Wt, rows=None, stored=None, smap=None):
+        """Oracle stores of the rows `rows` of Wt. The sign code fits its two
+        scales per stored column, so its codes come from the stored matrix
+        (stacked q/k/v, interleaved gate/up): smap gives the stored row of
+        every row of Wt."""
         sub = Wt if rows is None else np.ascontiguousarray(Wt[:, rows])
-        return O.ColumnStore(ff, sub), O.ColumnStore(af, sub)
+        if af != "sign2":
+            return O.ColumnStore(ff, sub), O.ColumnStore(af, sub)
+        if stored is None:
+            stored, smap = Wt, np.arange(Wt.shape[1])
+        key = id(stored)
+        if key not in packed:
+            packed[key] = O.pack_sign2(stored)
+        codes, scales = packed[key]
+        r = smap if rows is None else smap[rows]
+        return (O.ColumnStore(ff, sub),
+                O.ColumnStore("sign2", codes=np.ascontiguousarray(codes[:, r[0::4] // 4]),
+                              scales=scales))
+
+    # stored rows of gate and up rows in the interleaved gate/up matrix
+    i = np.arange(w.inter)
+    gmap = (i // 128) * 256 + i % 128
+    Wgu = np.empty((w.gate.shape[0], 2 * w.inter), dtype=np.float16)
+    Wgu[:, gmap] = w.gate
+    Wgu[:, gmap + 128] = w.up
 
     L0 = O.plan_tiers(h, *ks["qkv"])
     assert all(np.array_equal(a, b) for a, b in zip(res["lists"][0], L0)), f"{label}: qkv lists"
@@ -102,8 +126,9 @@ def _check_layer(res, w: LayerWeights, ks, h, z, x, ff, af, label, rows_per=None
     L2 = O.plan_tiers(x, *ks["ffn"])
     assert all(np.array_equal(a, b) for a, b in zip(res["lists"][2], L2)), f"{label}: ffn lists"
     rows = sample_groups(w.inter, 8, 3) if rows_per else None
-    check_product(res["g"], x, *L2, *stores(w.gate, rows), f"{label} gate", rows=rows)
-    check_product(res["u"], x, *L2, *stores(w.up, rows), f"{label} up", rows=rows)
+    check_product(res["g"], x, *L2, *stores(w.gate, rows, Wgu, gmap), f"{label} gate", rows=rows)
+    check_product(res["u"], x, *L2, *stores(w.up, rows, Wgu, gmap + 128), f"{label} up",
+                  rows=rows)
     # a is formed from the GPU's own fp16 g and u
     a_want = O.swiglu_fp16(res["g"], res["u"]).astype(np.float64)
     a_got = res["a"].astype(np.float64)
@@ -123,7 +148,8 @@ def _ks(hidden, inter, split):
             "ffn": WL.tier_counts(hidden, split), "down": WL.tier_counts(inter, split)}
 
 
-@pytest.mark.parametrize("ff,af", [("fp16", "int4"), ("int4", "int2"), ("fp16", "int2")])
+@pytest.mark.parametrize("ff,af", [("fp16", "int4"), ("int4", "int2"), ("fp16", "int2"),
+                                   ("fp16", "sign2")])
 def test_layer_small(ff, af, kernel_choice):
     hidden, inter = 512, 1408          # ragged tiles: 1408 = 2*512 + 384; gate/up 2816 rows
     w = LayerWeights(810, 0, hidden, inter, 0.02)
@@ -151,7 +177,7 @@ def test_layer_7b_shapes(kernel_choice):
         log(f"7B layer token {tok} ok")
 
 
-@pytest.mark.parametrize("ff,af", [("fp16", "int4"), ("int4", "int2")])
+@pytest.mark.parametrize("ff,af", [("fp16", "int4"), ("int4", "int2"), ("fp16", "sign2")])
 def test_host_pinned_bitwise_equals_device(ff, af):
     import torch
     hidden, inter = 1024, 2816
