@@ -36,8 +36,12 @@ Other workloads (one JSON line each, same keys; no roofline / CPU legs):
                  the selected columns cross the host link
     --config 5   70B-shaped FFN, int4 full tier, int2 approx, 50/30/20
 
+    --approx sign2  the headline workload with the SpAx page's two-scale 2-bit
+                 sign code (section 5.1, Eq. 4) as the middle tier
+
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--eager]
                     [--no-cpu-baseline] [--calib-copy] [--config N] [--host]
+                    [--approx int4|sign2]
 """
 from __future__ import annotations
 
@@ -125,9 +129,9 @@ class Spec:
                 + (", weights in pinned host memory" if self.host else ""))
 
 
-def headline_spec() -> Spec:
+def headline_spec(approx_fmt: str = "int4") -> Spec:
     return Spec(2, "7B-shaped attention projections q,k,v,o 4096x4096", 4096, 0, True,
-                split=(40, 30, 30))
+                approx_fmt=approx_fmt, split=(40, 30, 30))
 
 
 def specs_for(config: int, host: bool):
@@ -151,7 +155,7 @@ def specs_for(config: int, host: bool):
     raise SystemExit(f"unknown --config {config}")
 
 
-FMT = {"fp16": 1, "int4": 2, "int2": 3}
+FMT = {"fp16": 1, "int4": 2, "int2": 3, "sign2": 4}
 
 
 class Workload:
@@ -376,7 +380,7 @@ def host_link_peak_gbs() -> float:
     return 3 * n / (e0.elapsed_time(e1) * 1e-3) / 1e9
 
 
-def cpu_baseline(kf: int, ka: int, budget_s: float = 15.0):
+def cpu_baseline(kf: int, ka: int, budget_s: float = 15.0, approx_fmt: str = "int4"):
     """The CPU oracle on a bounded sample of the headline workload: weight set
     0, tokens 0, 1, ... each ranking h and z and forming q, k, v and o, until
     about `budget_s` seconds of timed work are done."""
@@ -392,8 +396,8 @@ def cpu_baseline(kf: int, ka: int, budget_s: float = 15.0):
     mats = {}
     for m in ("q", "k", "v", "o"):
         Wt = WL.weights_fp16(cfg, 0, m, H, H, 0.02)
-        mats[m] = (O.ColumnStore("fp16", Wt), O.ColumnStore("int4", Wt))
-    per_proj = gemv_algorithmic_bytes(H, H, kf, ka, "fp16", "int4")
+        mats[m] = (O.ColumnStore("fp16", Wt), O.ColumnStore(approx_fmt, Wt))
+    per_proj = gemv_algorithmic_bytes(H, H, kf, ka, "fp16", approx_fmt)
     done, t_acc, tok = 0, 0.0, 0
     while t_acc < budget_s and tok < 32:
         h = WL.laplace_fp16(cfg, 0, "h", tok, H)
@@ -457,7 +461,7 @@ def run_headline(args):
     spax.lib()  # fails loudly when the HIP library is missing
     if not torch.cuda.is_available():
         raise SystemExit("bench.py needs a GPU (torch.cuda.is_available() is False)")
-    spec = headline_spec()
+    spec = headline_spec(args.approx)
     spec.sets = args.sets
     log(f"device {torch.cuda.get_device_name(0)}; building {spec.sets} weight sets")
     t0 = time.perf_counter()
@@ -483,9 +487,11 @@ def run_headline(args):
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
-            "traffic": measured_traffic(),
+            # the committed counters were taken on the int4 workload
+            "traffic": measured_traffic() if args.approx == "int4" else None,
             "kernel": "gemv_kernel: fused tier selection + tiered gather-GEMV "
-                      "(fp16 full, int4 g128 approx)",
+                      + ("(fp16 full, int4 g128 approx)" if args.approx == "int4" else
+                         "(fp16 full, two-scale 2-bit sign approx)"),
             "avg_launch_us": round((t_qkv + t_o) / 2 * 1e6, 3),
             "launch_us": {"qkv": round(t_qkv * 1e6, 3), "o": round(t_o * 1e6, 3)},
             "bytes_per_launch": {"qkv": qkv_b, "o": o_b},
@@ -501,7 +507,7 @@ def run_headline(args):
     base = None
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on a bounded sample")
-        base = cpu_baseline(*wl.k[0])
+        base = cpu_baseline(*wl.k[0], approx_fmt=args.approx)
     return result_line(spec, wl, args, sec_step, mode, {"roofline": roof, "cpu_baseline": base})
 
 
@@ -556,6 +562,9 @@ def parse():
                    help="run another benchmark workload (1, 3, 4, 5) instead of the headline")
     p.add_argument("--host", action="store_true",
                    help="with --config 4: weights in pinned host memory")
+    p.add_argument("--approx", choices=("int4", "sign2"), default="int4",
+                   help="middle tier of the headline workload: int4 group-128 (default) or "
+                        "the two-scale 2-bit sign code")
     p.add_argument("--select", choices=("fused", "separate"), default="fused",
                    help="tier selection inside the product (default) or a separate kernel")
     return p.parse_args()

@@ -26,6 +26,8 @@ def column_bytes(fmt: str, rows: int) -> int:
         return rows // 2 + 2 * (rows // GROUP)
     if fmt == "int2":
         return rows // 4 + 2 * (rows // GROUP)
+    if fmt == "sign2":                      # 2-bit codes and two fp16 scales
+        return rows // 4 + 4
     if fmt == "none":
         return 0
     raise ValueError(fmt)
