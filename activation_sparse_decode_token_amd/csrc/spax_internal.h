@@ -30,11 +30,12 @@ constexpr size_t kCounterRegionBytes = sizeof(uint32_t) * kCountersPerTile * kMa
 constexpr int kGroup = 128;
 // List positions one workgroup of the fused rank + product keeps in LDS.
 constexpr int kListCap = 2048;
-// Largest input length the fused rank + product handles (64 per ranking
-// thread, 4 ranking waves);
-// longer inputs are ranked by the sliced selection kernels first (measured:
-// at n = 11008 the fused form is faster, at n = 28672 the sliced one).
-constexpr int kRankMaxN = kGemvThreads * 16;
+// Largest input length the fused rank + product handles (8 ranking waves,
+// up to 64 entries per ranking thread); longer inputs are ranked by the
+// sliced selection kernels first. Measured at n = 28672 (70B down): the
+// fused form is faster now that its histograms run on the ranking waves
+// only; the sliced form's three launches cost about 14 us of latency.
+constexpr int kRankMaxN = kGemvThreads * 32;
 // Sliced selection: entries per slice (one workgroup, 4 per thread) and the
 // most slices (inputs up to 65536 entries).
 constexpr int kSliceEntries = kGemvThreads * 4;

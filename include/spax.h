@@ -206,7 +206,7 @@ int spax_layer_step(const spax_layer* L, const spax_layer_io* io,
 /* spax_set_kernel_choice -- how spax_layer_step runs a group whose weights
  * are device-resident (process-wide; set it before concurrent calls, not
  * during them):
- *   SPAX_KERNEL_AUTO      inputs up to 16384 long: the tiered product ranks
+ *   SPAX_KERNEL_AUTO      inputs up to 32768 long: the tiered product ranks
  *                         the input itself (every workgroup selects the tiers
  *                         in LDS) where the list pieces fit; longer inputs:
  *                         the selection runs first as four short launches over
