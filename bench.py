@@ -38,6 +38,8 @@ Other workloads (one JSON line each, same keys; no roofline / CPU legs):
 
     --approx sign2  the headline workload with the SpAx page's two-scale 2-bit
                  sign code (section 5.1, Eq. 4) as the middle tier
+    --calibrate  the offline tier-size calibration of section 5.2 (steps 1 and
+                 2) on the 7B attention groups, through the library
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--eager]
                     [--no-cpu-baseline] [--calib-copy] [--config N] [--host]
@@ -546,6 +548,73 @@ def run_config(args):
     return lines
 
 
+def run_calibrate(args):
+    """Offline tier-size calibration (SpAx page section 5.2) on the 7B
+    attention groups: Step 1 to a 40 % layer budget, then Step 2's grid at
+    each group's budget, every evaluation through the library's kernels.
+    One JSON line: evaluations per second (one evaluation = one grid
+    setting over the calibration tokens, each token one ranking plus one
+    tiered product, against dense references taken once)."""
+    import torch
+
+    import activation_sparse_decode_token_amd as spax
+    import activation_sparse_decode_token_amd.calibrate as K
+    import workloads as WL
+    from activation_sparse_decode_token_amd.layouts import build_matrix, stack_rows
+    spax.lib()
+    if not torch.cuda.is_available():
+        raise SystemExit("bench.py needs a GPU (torch.cuda.is_available() is False)")
+    dev = torch.device("cuda:0")
+    H, tokens, steps, target = 4096, 8, 10, 40
+    gen = lambda m: WL.weights_fp16_torch(2, 0, m, H, H, 0.02, dev)
+    qkv = build_matrix(stack_rows([gen("q"), gen("k"), gen("v")]))
+    o = build_matrix(gen("o"))
+    vec = lambda nm, t: WL.laplace_fp16_torch(2, 0, nm, t, H, dev)
+    t0 = time.perf_counter()
+    groups = [K.Group(qkv, [vec("h", t) for t in range(tokens)]),
+              K.Group(o, [vec("z", t) for t in range(tokens)])]
+    counted = [0]
+    for g in groups:          # count evaluations (one per grid setting or budget tried)
+        g.error = (lambda f: (lambda kt, km: (counted.__setitem__(0, counted[0] + 1), f(kt, km))[1]))(g.error)
+    budgets, rounds = K.step1(groups, target)
+    chosen = [K.step2(g, b, steps) for g, b in zip(groups, budgets)]
+    torch.cuda.synchronize()
+    sec = time.perf_counter() - t0
+    evals = counted[0]
+    line = {
+        "metric": "offline tier-size calibration (SpAx page section 5.2, steps 1 and 2): "
+                  "evaluations per second",
+        "value": round(evals / sec, 2), "unit": "evaluations/s", "n_gpus": 1,
+        "higher_is_better": True, "data": "synthetic", "dtype": "fp32",
+        "seconds": round(sec, 3), "evaluations": evals,
+        "config": {"workload": "7B-shaped attention groups (q,k,v stacked 12288x4096; o "
+                               "4096x4096), fp16 full + int4 g128 approx, W ~N(0,0.02), "
+                               f"{tokens} calibration tokens of Laplace(0,1) inputs per group, "
+                               f"layer budget target {target} %, step-2 grid of {steps} steps",
+                   "tokens": tokens},
+        "step1_budgets_pct": {"qkv": budgets[0], "o": budgets[1]},
+        "step1_rounds": len(rounds),
+        "step2_choice": {"qkv": list(chosen[0][0]), "o": list(chosen[1][0])},
+        "step2_tables": {"qkv": [list(r[:2]) + [r[2]] for r in chosen[0][1]],
+                         "o": [list(r[:2]) + [r[2]] for r in chosen[1][1]]},
+    }
+    if not args.no_cpu_baseline:
+        import oracle as O
+        import oracle.spax_calibrate as C
+        Wt = WL.weights_fp16(2, 0, "o", H, H, 0.02)
+        mats = [(O.ColumnStore("fp16", Wt), O.ColumnStore("int4", Wt))]
+        xs = [WL.laplace_fp16(2, 0, "z", t, H) for t in range(tokens)]
+        kt, km = chosen[1][0]
+        c0 = time.perf_counter()
+        C.group_error(mats, xs, kt, km)
+        csec = time.perf_counter() - c0
+        line["cpu_baseline"] = {"value": round(1.0 / csec, 4), "unit": "evaluations/s",
+                                "kind": "oracle", "cores": os.cpu_count(),
+                                "sample": f"one evaluation of the o group ({tokens} tokens, "
+                                          f"k_top={kt}, k_mid={km}; numpy fp64)"}
+    print(json.dumps(line), flush=True)
+
+
 def parse():
     p = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     p.add_argument("--gpus", type=int, default=1)
@@ -565,6 +634,9 @@ def parse():
     p.add_argument("--approx", choices=("int4", "sign2"), default="int4",
                    help="middle tier of the headline workload: int4 group-128 (default) or "
                         "the two-scale 2-bit sign code")
+    p.add_argument("--calibrate", action="store_true",
+                   help="run the offline tier-size calibration (steps 1 and 2) on the 7B "
+                        "attention groups instead of the decode benchmark")
     p.add_argument("--select", choices=("fused", "separate"), default="fused",
                    help="tier selection inside the product (default) or a separate kernel")
     return p.parse_args()
@@ -579,6 +651,9 @@ def main():
     if args.select != "fused":
         import activation_sparse_decode_token_amd as spax
         spax.set_kernel_choice(spax.KERNEL_SEPARATE)
+    if args.calibrate:
+        run_calibrate(args)
+        return
     if args.config is not None and args.config != 2:
         run_config(args)
         return

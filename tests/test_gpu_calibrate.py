@@ -1,0 +1,85 @@
+"""Offline tier-size calibration on the GPU (SpAx page section 5.2) against
+the calibration oracle: the same grids of tier sizes, errors within the fp16
+output rounding, the same choices (up to near ties), the same Step 1 rounds."""
+from fractions import Fraction
+
+import numpy as np
+import pytest
+
+import oracle as O
+import oracle.spax_calibrate as C
+import workloads as WL
+from tests.spax_testlib import log, to_dev
+
+pytestmark = pytest.mark.gpu
+
+HIDDEN, INTER = 512, 1408
+
+
+def _layer():
+    """A small layer's four groups as stored matrices, host copies and inputs."""
+    import activation_sparse_decode_token_amd as spax
+    from activation_sparse_decode_token_amd.layouts import build_matrix, glu_interleave, stack_rows
+    w = {m: WL.weights_fp16(840, 0, m, r, c, 0.02) for m, r, c in
+         [("q", HIDDEN, HIDDEN), ("k", HIDDEN, HIDDEN), ("v", HIDDEN, HIDDEN),
+          ("o", HIDDEN, HIDDEN), ("gate", INTER, HIDDEN), ("up", INTER, HIDDEN),
+          ("down", HIDDEN, INTER)]}
+    d = {m: to_dev(v) for m, v in w.items()}
+    stored = {
+        "qkv": (build_matrix(stack_rows([d["q"], d["k"], d["v"]])),
+                np.concatenate([w["q"], w["k"], w["v"]], axis=1)),
+        "o": (build_matrix(d["o"]), w["o"]),
+        "gu": (build_matrix(glu_interleave(d["gate"], d["up"]),
+                            layout=spax.LAYOUT_GLU_INTERLEAVED),
+               np.concatenate([w["gate"].reshape(HIDDEN, -1, 1, 128),
+                               w["up"].reshape(HIDDEN, -1, 1, 128)], axis=2).reshape(HIDDEN, -1)),
+        "down": (build_matrix(d["down"]), w["down"]),
+    }
+    xs = {g: [WL.laplace_fp16(840, i, "x", t, stored[g][1].shape[0]) for t in range(2)]
+          for i, g in enumerate(stored)}
+    return stored, xs
+
+
+def test_step2_grid_matches_the_oracle():
+    import activation_sparse_decode_token_amd.calibrate as K
+    stored, xs = _layer()
+    for g, (W, Wt) in stored.items():
+        grp = K.Group(W, [to_dev(x) for x in xs[g]])
+        mats = [(O.ColumnStore("fp16", Wt), O.ColumnStore("int4", Wt))]
+        rho = Fraction(W.rows // 2 + 2 * (W.rows // 128), 2 * W.rows)
+        assert K.rho_of(W) == rho
+        (kt, km), table = K.step2(grp, 40, 6)
+        (okt, okm), otable = C.step2_grid(lambda a, b: C.group_error(mats, xs[g], a, b),
+                                          grp.n, 40, rho, 6)
+        assert [r[:2] for r in table] == [r[:2] for r in otable], g
+        for (_, _, e), (_, _, oe) in zip(table, otable):
+            assert abs(e - oe) <= 1e-2 * oe + 1e-9, (g, e, oe)
+        oerr = {r[:2]: r[2] for r in otable}
+        assert oerr[(kt, km)] <= min(oerr.values()) * (1 + 1e-2), g
+        log(f"step 2 {g}: GPU picks ({kt}, {km}), oracle ({okt}, {okm})")
+
+
+def test_step1_rounds_match_the_oracle():
+    import activation_sparse_decode_token_amd.calibrate as K
+    stored, xs = _layer()
+    names = list(stored)
+    groups = [K.Group(stored[g][0], [to_dev(x) for x in xs[g]]) for g in names]
+    budgets, rounds = K.step1(groups, 70)
+    mats = [[(O.ColumnStore("fp16", stored[g][1]), O.ColumnStore("int4", stored[g][1]))]
+            for g in names]
+    err_of = [lambda b, i=i: C.group_error(mats[i], xs[names[i]], b * groups[i].n // 100, 0)
+              for i in range(len(names))]
+    dense = [gr.dense_bytes() for gr in groups]
+    obudgets, orounds = C.step1_greedy(err_of, dense, 70)
+    assert C.layer_budget(budgets, dense) <= Fraction(70, 100)
+    if rounds != orounds:
+        # the searches may part only at a near tie: at the first differing
+        # round, both choices raise the oracle's error by nearly the same amount
+        r = next(i for i, (a, b) in enumerate(zip(rounds, orounds)) if a != b)
+        b = [100] * len(names)
+        for g, nb in orounds[:r]:
+            b[g] = nb
+        rise = lambda g: err_of[g](b[g] - 5) - err_of[g](b[g])
+        ga, go = rounds[r][0], orounds[r][0]
+        assert abs(rise(ga) - rise(go)) <= 1e-2 * max(rise(ga), rise(go)), (r, ga, go)
+    log(f"step 1: budgets {dict(zip(names, budgets))} in {len(rounds)} rounds")
