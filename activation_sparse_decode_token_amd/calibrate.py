@@ -82,6 +82,7 @@ class Group:
     def __init__(self, W: Matrix, xs: Sequence, stream=None):
         import torch
         self.W, self.xs, self.stream = W, list(xs), stream
+        self.evaluations = 0   # error() calls, for reporting
         dev = self.xs[0].device
         self.n = W.cols
         self.ws = torch.zeros(gemv_workspace_bytes(W), dtype=torch.uint8, device=dev)
@@ -103,6 +104,7 @@ class Group:
 
     def error(self, k_top: int, k_mid: int) -> float:
         """sum over tokens of ||y_tiered - y_dense||^2 over the stored rows."""
+        self.evaluations += 1
         return float(sum(((self._product(x, k_top, k_mid) - d) ** 2).sum()
                          for x, d in zip(self.xs, self.dense)))
 

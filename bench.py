@@ -573,14 +573,11 @@ def run_calibrate(args):
     t0 = time.perf_counter()
     groups = [K.Group(qkv, [vec("h", t) for t in range(tokens)]),
               K.Group(o, [vec("z", t) for t in range(tokens)])]
-    counted = [0]
-    for g in groups:          # count evaluations (one per grid setting or budget tried)
-        g.error = (lambda f: (lambda kt, km: (counted.__setitem__(0, counted[0] + 1), f(kt, km))[1]))(g.error)
     budgets, rounds = K.step1(groups, target)
     chosen = [K.step2(g, b, steps) for g, b in zip(groups, budgets)]
     torch.cuda.synchronize()
     sec = time.perf_counter() - t0
-    evals = counted[0]
+    evals = sum(g.evaluations for g in groups)   # one per budget or grid setting tried
     line = {
         "metric": "offline tier-size calibration (SpAx page section 5.2, steps 1 and 2): "
                   "evaluations per second",
