@@ -5,7 +5,7 @@ leg of bench.py may import this module. It shares no code with the HIP
 library and imports nothing from it.
 
 Source: the SpAx page, "Activation Sparsity with Weight Approximation for
-Faster LLM Decoding on Offloaded Weights" (paperpeel.com/paper/2610.02598).
+Faster LLM Decoding on Offloaded Weights".
 Each function names the section, equation or figure it follows.
 
 Everything is written as the plain definition:
@@ -15,8 +15,7 @@ Everything is written as the plain definition:
     the one step) and is rounded once to fp16 by the caller's choice.
 
 Readings of points the page leaves open (tie-break, list order, code format,
-group orientation, rounding) are listed in the design doc and restated at each
-function below.
+group orientation, rounding) are stated at each function below.
 
 Storage convention: a matrix of R rows and n columns is an array of shape
 [n, R] (column-major); row j of the array is column j of the matrix.
