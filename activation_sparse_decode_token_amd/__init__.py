@@ -18,7 +18,8 @@ __all__ = [
     "GROUP_QKV", "GROUP_O", "GROUP_GATE_UP", "GROUP_DOWN",
     "Matrix", "Layer", "LayerIO",
     "plan_tiers", "tiered_gemv", "gemv_workspace_bytes", "layer_step",
-    "layer_workspace_bytes", "pack_g128", "pack_sign2", "workspace_clear", "version",
+    "layer_workspace_bytes", "pack_g128", "pack_sign2", "pack_trellis_host",
+    "workspace_clear", "version",
     "status_string", "last_error", "EXPORTS",
 ]
 
@@ -36,6 +37,7 @@ STATUS = {0: "SPAX_OK", -1: "SPAX_EINVAL", -2: "SPAX_ENULL", -3: "SPAX_EALIGN",
 EXPORTS = (
     "spax_plan_tiers", "spax_gemv_workspace_bytes", "spax_tiered_gemv",
     "spax_layer_workspace_bytes", "spax_layer_step", "spax_pack_g128", "spax_pack_sign2",
+    "spax_pack_trellis_host",
     "spax_workspace_clear", "spax_status_string", "spax_last_error", "spax_version",
     "spax_set_kernel_choice",
 )
@@ -176,6 +178,8 @@ def _declare(L: ctypes.CDLL) -> None:
     L.spax_pack_g128.restype = ctypes.c_int
     L.spax_pack_sign2.argtypes = [vp, i32, i32, vp, vp, vp]
     L.spax_pack_sign2.restype = ctypes.c_int
+    L.spax_pack_trellis_host.argtypes = [vp, i32, i32, vp, vp, vp, i32]
+    L.spax_pack_trellis_host.restype = ctypes.c_int
     L.spax_workspace_clear.argtypes = [vp, sz, vp]
     L.spax_workspace_clear.restype = ctypes.c_int
     L.spax_status_string.argtypes = [ctypes.c_int]
@@ -255,6 +259,21 @@ def pack_sign2(w, rows, cols, codes, scales, stream=None) -> None:
     _check(lib().spax_pack_sign2(_ptr(w), int(rows), int(cols), _ptr(codes), _ptr(scales),
                                  _stream(stream)),
            "spax_pack_sign2")
+
+
+def pack_trellis_host(w, rows, cols, codebook, codes, scales, threads=None) -> None:
+    """spax_pack_trellis_host: trellis codes and fp16 scales of w (host numpy
+    arrays: w fp16 [cols, rows], codebook fp16 [65536], codes uint8
+    [cols, rows/4], scales fp16 [cols])."""
+    import numpy as np
+    for a, dt in ((w, np.float16), (codebook, np.float16), (codes, np.uint8),
+                  (scales, np.float16)):
+        if not (isinstance(a, np.ndarray) and a.dtype == dt and a.flags.c_contiguous):
+            raise TypeError("pack_trellis_host takes C-contiguous numpy arrays")
+    n = threads if threads else max(1, min(16, os.cpu_count() or 1))
+    _check(lib().spax_pack_trellis_host(w.ctypes.data, int(rows), int(cols), codebook.ctypes.data,
+                                        codes.ctypes.data, scales.ctypes.data, int(n)),
+           "spax_pack_trellis_host")
 
 
 def workspace_clear(ws, nbytes=None, stream=None) -> None:

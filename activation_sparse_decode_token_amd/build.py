@@ -13,7 +13,10 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libspax.so")
 
-SOURCES = ["plan.hip", "select.hip", "gemv.hip", "aux.hip", "api.cpp"]
+SOURCES = ["plan.hip", "select.hip", "gemv.hip", "aux.hip", "api.cpp", "trellis_pack.cpp"]
+# per-source flags: the trellis encoder's fp32 error arithmetic is defined
+# operation by operation (no contraction into fused multiply-adds)
+EXTRA = {"trellis_pack.cpp": ["-ffp-contract=off"]}
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
@@ -41,7 +44,7 @@ def build(verbose: bool = False) -> str:
     inc = ["-I", os.path.join(ROOT, "include"), "-I", CSRC]
     with tempfile.TemporaryDirectory(prefix="spax_build_") as tmpdir:
         objs = [os.path.join(tmpdir, s + ".o") for s in SOURCES]
-        cmds = [[HIPCC, *FLAGS, *inc, "-c", os.path.join(CSRC, s), "-o", o]
+        cmds = [[HIPCC, *FLAGS, *EXTRA.get(s, []), *inc, "-c", os.path.join(CSRC, s), "-o", o]
                 for s, o in zip(SOURCES, objs)]
         workers = max(1, min(len(cmds), os.cpu_count() or 1, 8))
         with concurrent.futures.ThreadPoolExecutor(workers) as ex:

@@ -251,6 +251,30 @@ int spax_pack_g128(const uint16_t* w, int32_t rows, int32_t cols, int32_t fmt,
 int spax_pack_sign2(const uint16_t* w, int32_t rows, int32_t cols, uint8_t* codes,
                     uint16_t* scales, hipStream_t stream);
 
+/* spax_pack_trellis_host -- encode the trellis-coded middle tier of a matrix
+ * (SpAx page section 5.1, trellis coding; offline, on the host, Figure 2
+ * step 1). Per column: 2-bit codes c_i and one scale s, the column's
+ * root-mean-square; weight i is rebuilt as codebook[index_i] * s with
+ * index_i = (index_{i-1} >> 2) | (c_i << 14), index_{-1} = 0 (the window of
+ * the codes of rows i-7..i, the oldest in the low bits). The codes minimise
+ * sum_i (w_i / s - codebook[index_i])^2 (Viterbi over the 2^14 states of the
+ * last seven codes), with the arithmetic fixed operation by operation:
+ *   s = fp16(sqrt(fp64(fp64(S) / rows)) 2^-24), S = sum w_i^2 exactly;
+ *   v_i = fp32(w_i / s); per candidate d = v_i - cb, e = d * d, cost + e in
+ *   fp32; ties keep the smallest dropped code, then the smallest final state.
+ * A zero column gets s = 0 and zero codes.
+ *   w        host fp16 [cols][rows] (column-major), finite, rows % 128 == 0.
+ *   codebook host fp16 [65536] (values the caller drew once, e.g. N(0, 1)).
+ *   codes    host out, [cols][rows/4] bytes, row 4i + r in bits 2r..2r+1 of
+ *            byte i.
+ *   scales   host out, fp16 [cols].
+ *   threads  host threads to use (columns are independent), >= 1.
+ *   Memory: about rows * 16 KB of host scratch per thread.
+ *   Errors: SPAX_ENULL, SPAX_EINVAL.                                         */
+int spax_pack_trellis_host(const uint16_t* w, int32_t rows, int32_t cols,
+                           const uint16_t* codebook, uint8_t* codes, uint16_t* scales,
+                           int32_t threads);
+
 /* spax_workspace_clear -- zero `bytes` bytes of ws with a kernel (no memset
  * node, so it may be captured in a graph). bytes % 4 == 0. */
 int spax_workspace_clear(void* ws, size_t bytes, hipStream_t stream);

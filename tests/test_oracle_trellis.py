@@ -97,3 +97,21 @@ def test_trellis_beats_the_scalar_code_at_two_bits():
     c2, s2 = O.pack_sign2(W)
     es = ((w - O.dequant_sign2(c2, s2)) ** 2).sum()
     assert et < 0.75 * es
+
+
+def test_library_host_encoder_matches_the_oracle():
+    """spax_pack_trellis_host (the library's offline encoder, host code) against
+    the oracle: codes and scales bit for bit, zero and outlier columns
+    included."""
+    import activation_sparse_decode_token_amd as spax
+    cb = _codebook(10)
+    W = WL.weights_fp16(63, 0, "w", 256, 5, 0.02)
+    W[1] = 0
+    W[2, 7] = np.float16(3.0)
+    W[3] = (np.random.default_rng(6).integers(-9, 10, 256) * 2.0 ** -24).astype(np.float16)
+    codes = np.zeros((5, 64), dtype=np.uint8)
+    scales = np.zeros(5, dtype=np.float16)
+    spax.pack_trellis_host(W, 256, 5, cb, codes, scales, threads=3)
+    oc, os_ = T.pack_trellis(W, cb)
+    assert np.array_equal(scales.view(np.uint16), os_.view(np.uint16))
+    assert np.array_equal(codes, oc)
