@@ -13,7 +13,7 @@ from typing import Optional, Sequence
 
 __all__ = [
     "SpaxError", "lib", "library_path",
-    "FMT_NONE", "FMT_FP16", "FMT_INT4_G128", "FMT_INT2_G128", "FMT_SIGN2",
+    "FMT_NONE", "FMT_FP16", "FMT_INT4_G128", "FMT_INT2_G128", "FMT_SIGN2", "FMT_TRELLIS",
     "RES_DEVICE", "RES_HOST_PINNED", "LAYOUT_PLAIN", "LAYOUT_GLU_INTERLEAVED",
     "GROUP_QKV", "GROUP_O", "GROUP_GATE_UP", "GROUP_DOWN",
     "Matrix", "Layer", "LayerIO",
@@ -23,7 +23,7 @@ __all__ = [
     "status_string", "last_error", "EXPORTS",
 ]
 
-FMT_NONE, FMT_FP16, FMT_INT4_G128, FMT_INT2_G128, FMT_SIGN2 = 0, 1, 2, 3, 4
+FMT_NONE, FMT_FP16, FMT_INT4_G128, FMT_INT2_G128, FMT_SIGN2, FMT_TRELLIS = 0, 1, 2, 3, 4, 5
 RES_DEVICE, RES_HOST_PINNED = 0, 1
 LAYOUT_PLAIN, LAYOUT_GLU_INTERLEAVED = 0, 1
 GROUP_QKV, GROUP_O, GROUP_GATE_UP, GROUP_DOWN = 0, 1, 2, 3
@@ -82,15 +82,17 @@ class Matrix(ctypes.Structure):
         ("residency", ctypes.c_int32), ("layout", ctypes.c_int32),
         ("full_data", ctypes.c_void_p), ("full_scales", ctypes.c_void_p),
         ("approx_codes", ctypes.c_void_p), ("approx_scales", ctypes.c_void_p),
+        ("approx_codebook", ctypes.c_void_p),
     ]
 
     @classmethod
     def make(cls, rows, cols, full_fmt, approx_fmt, full_data, full_scales=None,
              approx_codes=None, approx_scales=None, residency=RES_DEVICE,
-             layout=LAYOUT_PLAIN) -> "Matrix":
+             layout=LAYOUT_PLAIN, approx_codebook=None) -> "Matrix":
         m = cls(rows, cols, full_fmt, approx_fmt, residency, layout,
-                _ptr(full_data), _ptr(full_scales), _ptr(approx_codes), _ptr(approx_scales))
-        m._keep = (full_data, full_scales, approx_codes, approx_scales)
+                _ptr(full_data), _ptr(full_scales), _ptr(approx_codes), _ptr(approx_scales),
+                _ptr(approx_codebook))
+        m._keep = (full_data, full_scales, approx_codes, approx_scales, approx_codebook)
         return m
 
 

@@ -33,12 +33,14 @@ int64_t col_bytes(int32_t fmt, int64_t rows) {
     case kInt4: return rows / 2;
     case kInt2: return rows / 4;
     case kSign2: return rows / 4;
+    case kTrellis: return rows / 4;
     default: return 0;
   }
 }
 // fp16 scales per stored column (0 for fp16 values; 2 for the sign code).
 int64_t col_scales(int32_t fmt, int64_t rows) {
   if (fmt == kSign2) return 2;
+  if (fmt == kTrellis) return 1;
   return (fmt == kInt4 || fmt == kInt2) ? rows / kGroup : 0;
 }
 // Bytes one 512-row tile of a column costs, used to balance the splits.
@@ -48,6 +50,7 @@ int64_t tile_bytes(int32_t fmt) {
     case kInt4: return kTileRows / 2 + 2 * (kTileRows / kGroup);
     case kInt2: return kTileRows / 4 + 2 * (kTileRows / kGroup);
     case kSign2: return kTileRows / 4 + 4;
+    case kTrellis: return kTileRows / 4 + 2;
     default: return 0;
   }
 }
@@ -58,9 +61,14 @@ int validate_matrix(const spax_matrix* W) {
     return SPAX_EINVAL;
   if (W->full_fmt != kFp16 && W->full_fmt != kInt4) return SPAX_EFORMAT;
   if (W->approx_fmt != kNone && W->approx_fmt != kInt4 && W->approx_fmt != kInt2 &&
-      W->approx_fmt != kSign2)
+      W->approx_fmt != kSign2 && W->approx_fmt != kTrellis)
     return SPAX_EFORMAT;
-  if (W->approx_fmt == kSign2 && W->full_fmt != kFp16) return SPAX_EFORMAT;
+  if ((W->approx_fmt == kSign2 || W->approx_fmt == kTrellis) && W->full_fmt != kFp16)
+    return SPAX_EFORMAT;
+  if (W->approx_fmt == kTrellis) {
+    if (!W->approx_codebook) return SPAX_ENULL;
+    if (!aligned16(W->approx_codebook)) return SPAX_EALIGN;
+  }
   if (W->residency != SPAX_RES_DEVICE && W->residency != SPAX_RES_HOST_PINNED)
     return SPAX_EINVAL;
   if (W->layout != SPAX_LAYOUT_PLAIN && W->layout != SPAX_LAYOUT_GLU_INTERLEAVED)
@@ -123,6 +131,8 @@ int64_t max_piece(const ProductPlan& p, int32_t kf, int32_t ka) {
 // would not fit. Returns false when no split count fits.
 bool plan_piece(const spax_matrix* W, int32_t kf, int32_t ka, ProductPlan* out) {
   if (W->residency != SPAX_RES_DEVICE) return false;
+  // the trellis tier's codebook takes the LDS a list piece would need
+  if (W->approx_fmt == kTrellis) return false;
   ProductPlan p = plan_product(W, kf, ka);
   while (max_piece(p, kf, ka) > kListCap) {
     if (p.splits >= kMaxSplits || p.splits >= (int64_t)kf + ka) return false;
@@ -215,6 +225,7 @@ int run_product(const spax_matrix* W, const uint16_t* x, const int32_t* fidx, in
   a.glu_a = ga;
   a.glu_g = gg;
   a.glu_u = gu;
+  a.codebook = W->approx_codebook;
   const int64_t fb = col_bytes(W->full_fmt, W->rows), fsn = col_scales(W->full_fmt, W->rows);
   const int64_t ab = col_bytes(W->approx_fmt, W->rows), asn = col_scales(W->approx_fmt, W->rows);
   a.full_stride = fb;

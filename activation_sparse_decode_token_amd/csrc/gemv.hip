@@ -99,6 +99,8 @@ struct TierStream {
   static constexpr bool kCode = FMT == kInt4 || FMT == kInt2;
   // two-scale sign code: two factors per column, lane-uniform (readlane)
   static constexpr bool kTwo = FMT == kSign2;
+  // trellis code: one factor per column (readlane), codebook in LDS
+  static constexpr bool kTrel = FMT == kTrellis;
 
   WaveMeta& wm;
   __amdgpu_buffer_rsrc_t rs;
@@ -116,6 +118,7 @@ struct TierStream {
   int mycol;       // this lane's column of the pending batch
   float xv;        // this lane's activation of the pending batch (0 past it)
   float xb;        // sign code: x_j s_{j,1} (xv then holds x_j s_{j,0})
+  const uint16_t* cbk = nullptr;  // trellis code: the codebook in LDS
   uint32_t sc[4];  // this lane's raw fp16 scales of the pending batch (codes)
 
   __device__ __forceinline__ TierStream(WaveMeta& wm_, const uint8_t* base, int64_t stride,
@@ -151,6 +154,7 @@ struct TierStream {
         xv = h2f(x[j]);
       }
       mycol = MODE == kListStaged ? q : j;
+      if constexpr (kTrel) xv = xv * h2f(scales[mycol]);  // x_j s_j
       if constexpr (kTwo) {
         // the column's (s0, s1) in one 4-byte load
         const uint32_t sv = *reinterpret_cast<const uint32_t*>(scales + (int64_t)mycol * 2);
@@ -195,6 +199,8 @@ struct TierStream {
   __device__ __forceinline__ void add(float (&acc)[8], float& corr, int c, const V& v) {
     if constexpr (kTwo)
       T::fma2(acc, v, readlane_f(xv, c), readlane_f(xb, c), vmask);
+    else if constexpr (kTrel)
+      T::fma_cb(acc, v, readlane_f(xv, c), cbk);
     else
       T::fma(acc, corr, v, kCode ? wm.fac[c][gsel] : readlane_f(xv, c), vmask);
   }
@@ -276,16 +282,23 @@ template <int FF, int AF, int MODE, int EPI, int E>
 __global__ __launch_bounds__(kGemvThreads) void gemv_kernel(GemvArgs a) {
   // The rank scratch is dead once the list piece is in LDS; the wave
   // partials reuse it.
+  // The trellis tier keeps its 128 KB codebook in LDS; its kernels then add
+  // the 16 wave partials in two halves and have no code-factor rows.
+  constexpr bool kTrel = AF == kTrellis;
+  constexpr int kRedWaves = kTrel ? kWaves / 2 : kWaves;
   union Scratch {
     RankShared rank;
-    float red[kWaves][kTileRows];
+    float red[kRedWaves][kTileRows];
   };
   __shared__ Scratch sm;
   constexpr bool kPiece = MODE == kListRank || MODE == kListSliced;  // list piece in LDS
   __shared__ int32_t lidx[kPiece ? kListCap : 1];
   __shared__ float lx[kPiece ? kListCap : 1];
-  __shared__ WaveMeta wmeta[2][kWaves];  // per tier and wave
+  __shared__ WaveMeta wmeta[kTrel ? 1 : 2][kTrel ? 1 : kWaves];  // per tier and wave
+  __shared__ __attribute__((aligned(16))) uint16_t cbk[kTrel ? 65536 : 8];
   __shared__ uint32_t last_flag;
+  static_assert(!kTrel || (MODE == kListGlobal || MODE == kListStaged),
+                "the trellis tier is read by the list-reading product only");
 
   const int t = threadIdx.x;
   const int lane = t & 63;
@@ -325,18 +338,28 @@ __global__ __launch_bounds__(kGemvThreads) void gemv_kernel(GemvArgs a) {
     a_lo = a0;
     a_hi = a1;
   }
+  if constexpr (kTrel) {
+    // the codebook into LDS: 8192 16-byte pieces, 8 per thread
+    const uint4* src = reinterpret_cast<const uint4*>(a.codebook);
+    uint4* dst = reinterpret_cast<uint4*>(cbk);
+#pragma unroll
+    for (int k = 0; k < 65536 / 8 / kGemvThreads; ++k)
+      dst[t + k * kGemvThreads] = src[t + k * kGemvThreads];
+    __syncthreads();
+  }
   {
     const int lf = f_hi - f_lo, la = a_hi - a_lo;
-    TierStream<FF, MODE> sf(wmeta[0][wave], a.full_base, a.full_stride, a.full_bytes,
+    TierStream<FF, MODE> sf(wmeta[0][kTrel ? 0 : wave], a.full_base, a.full_stride, a.full_bytes,
                             a.full_scales, a.full_sstride, a.full_idx, a.x, lidx, lx,
                             f_lo + (lf * wave) / kWaves, f_lo + (lf * (wave + 1)) / kWaves, row0,
                             a.rows, lane, ld_lane);
     sf.begin();
     if constexpr (AF != kNone) {
-      TierStream<AF, MODE> sa(wmeta[1][wave], a.approx_base, a.approx_stride, a.approx_bytes,
+      TierStream<AF, MODE> sa(wmeta[kTrel ? 0 : 1][kTrel ? 0 : wave], a.approx_base, a.approx_stride, a.approx_bytes,
                               a.approx_scales, a.approx_sstride, a.approx_idx, a.x,
                               lidx, lx, a_lo + (la * wave) / kWaves,
                               a_lo + (la * (wave + 1)) / kWaves, row0, a.rows, lane, ld_lane);
+      if constexpr (kTrel) sa.cbk = cbk;
       sa.begin();
       sf.run(acc, corr);
       sa.run(acc, corr);
@@ -349,9 +372,24 @@ __global__ __launch_bounds__(kGemvThreads) void gemv_kernel(GemvArgs a) {
     for (int r = 0; r < 8; ++r) acc[r] -= corr;
   }
 
-  float4* dst = reinterpret_cast<float4*>(&sm.red[wave][8 * lane]);
-  dst[0] = make_float4(acc[0], acc[1], acc[2], acc[3]);
-  dst[1] = make_float4(acc[4], acc[5], acc[6], acc[7]);
+  if constexpr (kTrel) {
+    // waves 8..15 store, waves 0..7 add theirs: slot w holds waves w, w + 8
+    float4* dst = reinterpret_cast<float4*>(&sm.red[wave & (kRedWaves - 1)][8 * lane]);
+    if (wave >= kRedWaves) {
+      dst[0] = make_float4(acc[0], acc[1], acc[2], acc[3]);
+      dst[1] = make_float4(acc[4], acc[5], acc[6], acc[7]);
+    }
+    __syncthreads();
+    if (wave < kRedWaves) {
+      const float4 u0 = dst[0], u1 = dst[1];
+      dst[0] = make_float4(acc[0] + u0.x, acc[1] + u0.y, acc[2] + u0.z, acc[3] + u0.w);
+      dst[1] = make_float4(acc[4] + u1.x, acc[5] + u1.y, acc[6] + u1.z, acc[7] + u1.w);
+    }
+  } else {
+    float4* dst = reinterpret_cast<float4*>(&sm.red[wave][8 * lane]);
+    dst[0] = make_float4(acc[0], acc[1], acc[2], acc[3]);
+    dst[1] = make_float4(acc[4], acc[5], acc[6], acc[7]);
+  }
   __syncthreads();
 
   // thread t < kTileRows owns row t of the tile from here on
@@ -359,7 +397,7 @@ __global__ __launch_bounds__(kGemvThreads) void gemv_kernel(GemvArgs a) {
   float p = 0.0f;
   if (owner) {
 #pragma unroll
-    for (int w = 0; w < kWaves; ++w) p += sm.red[w][t];
+    for (int w = 0; w < kRedWaves; ++w) p += sm.red[w][t];
   }
   const int r = row0 + t;
 
@@ -452,16 +490,20 @@ template <int FF, int AF>
 hipError_t launch_mode(const GemvArgs& a, int32_t mode, int32_t epi, hipStream_t s) {
   if (mode == kListStaged) return launch_epi<FF, AF, kListStaged, 0>(a, epi, s);
   if (mode == kListGlobal) return launch_epi<FF, AF, kListGlobal, 0>(a, epi, s);
-  if (mode == kListSliced) return launch_epi<FF, AF, kListSliced, 0>(a, epi, s);
-  // entries per ranking thread: the smallest of 8, 16, 24, 32, 48, 64 that
-  // covers n
-  static_assert(kRankMaxN == kRankThreads * 64, "fused ranking at up to 64 entries per thread");
-  if (a.n <= kRankThreads * 8) return launch_epi<FF, AF, kListRank, 8>(a, epi, s);
-  if (a.n <= kRankThreads * 16) return launch_epi<FF, AF, kListRank, 16>(a, epi, s);
-  if (a.n <= kRankThreads * 24) return launch_epi<FF, AF, kListRank, 24>(a, epi, s);
-  if (a.n <= kRankThreads * 32) return launch_epi<FF, AF, kListRank, 32>(a, epi, s);
-  if (a.n <= kRankThreads * 48) return launch_epi<FF, AF, kListRank, 48>(a, epi, s);
-  if (a.n <= kRankThreads * 64) return launch_epi<FF, AF, kListRank, 64>(a, epi, s);
+  if constexpr (AF == kTrellis) {
+    return hipErrorInvalidValue;  // list modes only
+  } else {
+    if (mode == kListSliced) return launch_epi<FF, AF, kListSliced, 0>(a, epi, s);
+    // entries per ranking thread: the smallest of 8, 16, 24, 32, 48, 64 that
+    // covers n
+    static_assert(kRankMaxN == kRankThreads * 64, "fused ranking at up to 64 entries per thread");
+    if (a.n <= kRankThreads * 8) return launch_epi<FF, AF, kListRank, 8>(a, epi, s);
+    if (a.n <= kRankThreads * 16) return launch_epi<FF, AF, kListRank, 16>(a, epi, s);
+    if (a.n <= kRankThreads * 24) return launch_epi<FF, AF, kListRank, 24>(a, epi, s);
+    if (a.n <= kRankThreads * 32) return launch_epi<FF, AF, kListRank, 32>(a, epi, s);
+    if (a.n <= kRankThreads * 48) return launch_epi<FF, AF, kListRank, 48>(a, epi, s);
+    if (a.n <= kRankThreads * 64) return launch_epi<FF, AF, kListRank, 64>(a, epi, s);
+  }
   return hipErrorInvalidValue;
 }
 
@@ -474,6 +516,7 @@ hipError_t launch_gemv(const GemvArgs& a, int32_t full_fmt, int32_t approx_fmt, 
     if (approx_fmt == kInt4) return launch_mode<kFp16, kInt4>(a, mode, epi, s);
     if (approx_fmt == kInt2) return launch_mode<kFp16, kInt2>(a, mode, epi, s);
     if (approx_fmt == kSign2) return launch_mode<kFp16, kSign2>(a, mode, epi, s);
+    if (approx_fmt == kTrellis) return launch_mode<kFp16, kTrellis>(a, mode, epi, s);
   } else if (full_fmt == kInt4) {
     if (approx_fmt == kNone) return launch_mode<kInt4, kNone>(a, mode, epi, s);
     if (approx_fmt == kInt4) return launch_mode<kInt4, kInt4>(a, mode, epi, s);

@@ -41,7 +41,7 @@ constexpr int kRankMaxN = kGemvThreads * 32;
 constexpr int kSliceEntries = kGemvThreads * 4;
 constexpr int kMaxSlices = 65536 / kSliceEntries;
 
-enum Fmt : int32_t { kNone = 0, kFp16 = 1, kInt4 = 2, kInt2 = 3, kSign2 = 4 };
+enum Fmt : int32_t { kNone = 0, kFp16 = 1, kInt4 = 2, kInt2 = 3, kSign2 = 4, kTrellis = 5 };
 enum Epi : int32_t { kEpiPlain = 0, kEpiGlu = 1 };
 // Where the tiered product takes its tier lists from.
 enum ListMode : int32_t {
@@ -86,6 +86,7 @@ struct GemvArgs {
   uint16_t* glu_u;               // optional
   const struct SelectScratch* sel;  // kListSliced: thresholds and slice counts
   int32_t slices;                // kListSliced: slices of x
+  const uint16_t* codebook;      // trellis approx tier: fp16[65536]
 };
 
 // Workspace region of the sliced selection: per-slice histograms and counts,

@@ -16,9 +16,9 @@ from typing import Optional, Sequence
 
 import torch
 
-from . import (FMT_FP16, FMT_INT2_G128, FMT_INT4_G128, FMT_NONE, FMT_SIGN2,
+from . import (FMT_FP16, FMT_INT2_G128, FMT_INT4_G128, FMT_NONE, FMT_SIGN2, FMT_TRELLIS,
                LAYOUT_GLU_INTERLEAVED, LAYOUT_PLAIN, RES_DEVICE, RES_HOST_PINNED, Matrix,
-               pack_g128, pack_sign2)
+               pack_g128, pack_sign2, pack_trellis_host)
 
 GROUP = 128
 
@@ -45,9 +45,22 @@ def glu_deinterleave(stacked: torch.Tensor):
     return v[..., 0, :].reshape(*lead, R2 // 2), v[..., 1, :].reshape(*lead, R2 // 2)
 
 
-def pack(w_cm: torch.Tensor, fmt: int, stream=None):
-    """Codes and scales of a column-major fp16 device tensor [n, R]."""
+def pack(w_cm: torch.Tensor, fmt: int, stream=None, codebook: Optional[torch.Tensor] = None):
+    """Codes and scales of a column-major fp16 device tensor [n, R]. The
+    trellis code is encoded on the host (spax_pack_trellis_host) with the
+    given device codebook (fp16 [65536])."""
     n, R = w_cm.shape
+    if fmt == FMT_TRELLIS:
+        import numpy as np
+        if codebook is None:
+            raise ValueError("the trellis code needs a codebook")
+        w_h = w_cm.detach().cpu().contiguous().numpy()
+        cb_h = codebook.detach().cpu().contiguous().numpy()
+        codes = np.zeros((n, R // 4), dtype=np.uint8)
+        scales = np.zeros(n, dtype=np.float16)
+        pack_trellis_host(w_h, R, n, cb_h, codes, scales)
+        return (torch.from_numpy(codes).to(w_cm.device),
+                torch.from_numpy(scales).to(w_cm.device))
     if fmt == FMT_SIGN2:
         # two-scale sign code: 2 bits per weight, (s0, s1) per column
         codes = torch.empty((n, R // 4), dtype=torch.uint8, device=w_cm.device)
@@ -71,7 +84,8 @@ def _pin(t: Optional[torch.Tensor]) -> Optional[torch.Tensor]:
 
 def build_matrix(w_cm: torch.Tensor, full_fmt: int = FMT_FP16,
                  approx_fmt: int = FMT_INT4_G128, layout: int = LAYOUT_PLAIN,
-                 residency: int = RES_DEVICE, stream=None) -> Matrix:
+                 residency: int = RES_DEVICE, stream=None,
+                 codebook: Optional[torch.Tensor] = None) -> Matrix:
     """A spax_matrix for a column-major fp16 device tensor [n, R].
 
     The full tier is w_cm itself (fp16) or its int4 code; the approx tier is
@@ -87,8 +101,10 @@ def build_matrix(w_cm: torch.Tensor, full_fmt: int = FMT_FP16,
         fd, fs = pack(w_cm, full_fmt, stream)
     ac = asc = None
     if approx_fmt != FMT_NONE:
-        ac, asc = pack(w_cm, approx_fmt, stream)
+        ac, asc = pack(w_cm, approx_fmt, stream, codebook)
     if residency == RES_HOST_PINNED:
         torch.cuda.synchronize()
         fd, fs, ac, asc = _pin(fd), _pin(fs), _pin(ac), _pin(asc)
-    return Matrix.make(R, n, full_fmt, approx_fmt, fd, fs, ac, asc, residency, layout)
+    # the trellis codebook stays in device memory (the product loads it to LDS)
+    cb = codebook if approx_fmt == FMT_TRELLIS else None
+    return Matrix.make(R, n, full_fmt, approx_fmt, fd, fs, ac, asc, residency, layout, cb)

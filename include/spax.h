@@ -68,6 +68,16 @@ extern "C" {
  * 4i + r in bits 2r..2r+1 of byte i); scales [cols][2] = (s0, s1). Approx
  * tier only, with an fp16 full tier. Produced by spax_pack_sign2. */
 #define SPAX_FMT_SIGN2      4
+/* Trellis-coded middle tier (SpAx page section 5.1, trellis coding): 2-bit
+ * codes, rows/4 bytes per column in the int2 packing, one fp16 scale per
+ * column (scales [cols]), and a shared fp16 codebook of 65536 values
+ * (spax_matrix.approx_codebook, device memory). Weight i of a column is
+ * codebook[index_i] * scale, index_i = (index_{i-1} >> 2) | (c_i << 14),
+ * index_{-1} = 0. Approx tier only, with an fp16 full tier, and read by the
+ * list-reading product only (spax_tiered_gemv; spax_layer_step then runs the
+ * stand-alone selection first): the product keeps the codebook in LDS.
+ * Produced by spax_pack_trellis_host. */
+#define SPAX_FMT_TRELLIS    5
 
 #define SPAX_RES_DEVICE       0  /* weights in device memory (HBM)            */
 #define SPAX_RES_HOST_PINNED  1  /* weights in pinned host memory that the GPU
@@ -89,14 +99,17 @@ typedef struct spax_matrix {
   int32_t rows;            /* output length R (multiple of 128)            */
   int32_t cols;            /* input length n                                */
   int32_t full_fmt;        /* SPAX_FMT_FP16 or SPAX_FMT_INT4_G128           */
-  int32_t approx_fmt;      /* SPAX_FMT_NONE, _INT4_G128, _INT2_G128 or
-                              _SIGN2 (the last with an fp16 full tier)    */
+  int32_t approx_fmt;      /* SPAX_FMT_NONE, _INT4_G128, _INT2_G128, _SIGN2
+                              or _TRELLIS (the last two with an fp16 full
+                              tier)                                         */
   int32_t residency;       /* SPAX_RES_*                                    */
   int32_t layout;          /* SPAX_LAYOUT_*                                 */
   const void* full_data;   /* fp16 [cols][rows] or int4 codes [cols][rows/2] */
   const uint16_t* full_scales;   /* int4 full tier only: [cols][rows/128]   */
   const uint8_t* approx_codes;   /* approx codes, layout per approx_fmt     */
-  const uint16_t* approx_scales; /* [cols][rows/128]; SIGN2: [cols][2]      */
+  const uint16_t* approx_scales; /* [cols][rows/128]; SIGN2: [cols][2];
+                                    TRELLIS: [cols]                         */
+  const uint16_t* approx_codebook; /* TRELLIS only: device fp16 [65536]     */
 } spax_matrix;
 
 /* ---- tier selection ----------------------------------------------------- */

@@ -52,6 +52,9 @@ def abs_sum(x, F, A, full: O.ColumnStore, approx) -> np.ndarray:
     S = np.zeros(full.rows)
 
     def code_part(store, idx):
+        if store.fmt == "trellis":
+            # one term per element: the codebook value times x_j s_j
+            return np.abs(xf[idx])[:, None] * np.abs(store.columns(idx))
         if store.fmt == "sign2":
             # two exact terms per element: +-x_j s_{j,0} and +-x_j s_{j,1}
             s = store.scales[idx].astype(np.float64)
@@ -128,3 +131,18 @@ def sample_groups(R: int, n_groups: int, seed: int) -> np.ndarray:
     pick |= set(rs.choice(G, size=min(n_groups, G), replace=False).tolist())
     g = np.array(sorted(pick))
     return (g[:, None] * GROUP + np.arange(GROUP)[None, :]).ravel()
+
+
+class TrellisStore:
+    """Oracle view of a trellis-coded copy (codes, scales, codebook): the
+    columns are the oracle's reconstruction cb[index_i] s_j."""
+    fmt = "trellis"
+
+    def __init__(self, codes: np.ndarray, scales: np.ndarray, cb: np.ndarray):
+        self.codes, self.scales, self.cb = codes, scales, cb
+        self.rows = codes.shape[1] * 4
+
+    def columns(self, idx):
+        from oracle.spax_trellis import dequant_trellis
+        idx = np.asarray(idx, dtype=np.int64)
+        return dequant_trellis(self.codes[idx], self.scales[idx], self.cb)

@@ -82,6 +82,14 @@ def test_gemv_validation_errors():
     assert _gemv(W, x=P + 2) == -3
     assert _gemv(_matrix(ff=spax.FMT_INT2_G128)) == -4
     assert _gemv(_matrix(af=7)) == -4
+    # the trellis tier needs its codebook and an fp16 full tier
+    assert _gemv(_matrix(af=spax.FMT_TRELLIS)) == -2
+    Wt = spax.Matrix.make(4096, 4096, spax.FMT_FP16, spax.FMT_TRELLIS, P, None, P, P,
+                          approx_codebook=P + 8)
+    assert _gemv(Wt) == -3
+    Wt = spax.Matrix.make(4096, 4096, spax.FMT_INT4_G128, spax.FMT_TRELLIS, P, P, P, P,
+                          approx_codebook=P)
+    assert _gemv(Wt) == -4
     # the sign code is an approx tier under an fp16 full tier only
     assert _gemv(_matrix(ff=spax.FMT_INT4_G128, af=spax.FMT_SIGN2)) == -4
     assert _gemv(_matrix(af=spax.FMT_SIGN2), ws_bytes=1024) == -5
@@ -135,6 +143,11 @@ def test_layer_and_helper_validation_errors():
     assert g(P, 4096, 16, spax.FMT_FP16, P, P, None) == -4
     assert g(P, 100, 16, spax.FMT_INT4_G128, P, P, None) == -1
     assert g(None, 128, 16, spax.FMT_INT2_G128, P, P, None) == -2
+    import numpy as np
+    tr = spax.lib().spax_pack_trellis_host
+    assert tr(P, 100, 4, P, P, P, 1) == -1
+    assert tr(None, 128, 4, P, P, P, 1) == -2
+    assert tr(P, 128, 4, None, P, P, 1) == -2
     s2 = spax.lib().spax_pack_sign2
     assert s2(P, 100, 16, P, P, None) == -1
     assert s2(P, 128, 0, P, P, None) == -1

@@ -1,0 +1,124 @@
+"""The trellis-coded middle tier on the GPU (SpAx page section 5.1) against
+the oracle: the list-reading product (codebook in LDS), the layer step (which
+ranks separately for this tier) and the host-resident mode.
+
+The codes come from the library's offline host encoder, which is pinned bit
+for bit against the oracle's encoder on the CPU (tests/test_oracle_trellis.py;
+rechecked here on one small case); the oracle then rebuilds the columns from
+those codes itself."""
+import numpy as np
+import pytest
+
+import oracle as O
+import oracle.spax_trellis as T
+import workloads as WL
+from tests.spax_testlib import TrellisStore, check_product, log, to_dev, to_host
+
+pytestmark = pytest.mark.gpu
+
+
+def _matrix(Wt, residency=0):
+    import activation_sparse_decode_token_amd as spax
+    from activation_sparse_decode_token_amd.layouts import build_matrix
+    cb = WL.trellis_codebook(1)
+    W = build_matrix(to_dev(Wt), spax.FMT_FP16, spax.FMT_TRELLIS, residency=residency,
+                     codebook=to_dev(cb))
+    codes = to_host(W._keep[2]) if residency == 0 else W._keep[2].numpy()
+    scales = to_host(W._keep[3]) if residency == 0 else W._keep[3].numpy()
+    return W, TrellisStore(codes, scales, cb)
+
+
+def _run(W, x16, F, A, ws=None, copy_stream=None):
+    import torch
+    import activation_sparse_decode_token_amd as spax
+    dev = torch.device("cuda:0")
+    if ws is None:
+        ws = torch.zeros(spax.gemv_workspace_bytes(W), dtype=torch.uint8, device=dev)
+    y = torch.full((W.rows,), 0x7E00, dtype=torch.int16, device=dev)
+    Fd = to_dev(F.astype(np.int32)) if len(F) else torch.zeros(1, dtype=torch.int32, device=dev)
+    Ad = to_dev(A.astype(np.int32)) if len(A) else torch.zeros(1, dtype=torch.int32, device=dev)
+    spax.tiered_gemv(W, to_dev(x16), Fd, len(F), Ad, len(A), y, ws, copy_stream=copy_stream)
+    torch.cuda.synchronize()
+    return to_host(y).view(np.float16), ws
+
+
+def test_host_encoder_matches_oracle_encoder():
+    Wt = WL.weights_fp16(850, 0, "w", 128, 3, 0.02)
+    _, st = _matrix(Wt)
+    oc, os_ = T.pack_trellis(Wt, WL.trellis_codebook(1))
+    assert np.array_equal(st.codes, oc)
+    assert np.array_equal(st.scales.view(np.uint16), os_.view(np.uint16))
+
+
+CASES = [
+    # R, n, k_full, k_approx
+    (640, 300, 60, 90),       # ragged last tile (512 + 128)
+    (1536, 200, 50, 80),
+    (512, 7, 3, 4),
+    (3072, 128, 0, 128),      # all approx
+    (1024, 256, 64, 64),
+]
+
+
+@pytest.mark.parametrize("R,n,kf,ka", CASES)
+def test_trellis_product_vs_oracle(R, n, kf, ka):
+    log(f"trellis R={R} n={n} kf={kf} ka={ka}")
+    Wt = WL.weights_fp16(851, R, "w", R, n, 0.02)
+    Wt[0] = 0                               # a zero column: scale 0
+    x = WL.laplace_fp16(851, R, "x", n, n)
+    F, A = O.plan_tiers(x, kf, ka)
+    W, st = _matrix(Wt)
+    y, ws = _run(W, x, F, A)
+    err = check_product(y, x, F, A, O.ColumnStore("fp16", Wt), st, f"trellis R={R} n={n}")
+    y2, _ = _run(W, x, F, A, ws)
+    assert np.array_equal(y.view(np.uint16), y2.view(np.uint16))
+    log(f"  norm-wise error {err:.2e}")
+
+
+@pytest.mark.parametrize("choice", [0, 1])
+def test_trellis_layer_step(choice):
+    """A one-group layer with the trellis tier: the layer step ranks with the
+    stand-alone selection, then runs the list-reading product."""
+    import torch
+    import activation_sparse_decode_token_amd as spax
+    spax.set_kernel_choice(choice)
+    try:
+        R, n = 1024, 512
+        Wt = WL.weights_fp16(852, 0, "w", R, n, 0.02)
+        W, st = _matrix(Wt)
+        kf, ka = WL.tier_counts(n, WL.TierSplit(40, 30, 30))
+        L = spax.Layer.make([W, None, None, None], [kf, 0, 0, 0], [ka, 0, 0, 0])
+        dev = torch.device("cuda:0")
+        ws = torch.zeros(spax.layer_workspace_bytes(L), dtype=torch.uint8, device=dev)
+        for tok in range(2):
+            x = WL.laplace_fp16(852, 0, "x", tok, n)
+            Fd = torch.empty(kf, dtype=torch.int32, device=dev)
+            Ad = torch.empty(ka, dtype=torch.int32, device=dev)
+            y = torch.empty(R, dtype=torch.float16, device=dev)
+            io = spax.LayerIO.make(h=to_dev(x), qkv=y, full_idx=(Fd, None, None, None),
+                                   approx_idx=(Ad, None, None, None))
+            spax.layer_step(L, io, ws)
+            torch.cuda.synchronize()
+            F, A = O.plan_tiers(x, kf, ka)
+            assert np.array_equal(to_host(Fd), F) and np.array_equal(to_host(Ad), A)
+            check_product(to_host(y), x, F, A, O.ColumnStore("fp16", Wt), st,
+                          f"trellis layer token {tok}")
+    finally:
+        spax.set_kernel_choice(0)
+
+
+def test_trellis_host_pinned_bitwise_equals_device():
+    import torch
+    R, n = 1536, 384
+    Wt = WL.weights_fp16(853, 0, "w", R, n, 0.02)
+    Wd, st = _matrix(Wt)
+    Wh, sth = _matrix(Wt, residency=1)
+    assert np.array_equal(st.codes, sth.codes)
+    cs = torch.cuda.Stream()
+    for tok in range(2):
+        x = WL.laplace_fp16(853, 0, "x", tok, n)
+        F, A = O.plan_tiers(x, 100, 150)
+        yd, _ = _run(Wd, x, F, A)
+        yh, _ = _run(Wh, x, F, A, copy_stream=cs)
+        assert np.array_equal(yd.view(np.uint16), yh.view(np.uint16)), tok
+    log("trellis host-pinned == device bitwise")

@@ -89,7 +89,7 @@ CONFIGS: Dict[int, Config] = {
 
 # Matrix ids used in seeds (stable across configs).
 MATRIX_ID = {"w": 0, "q": 1, "k": 2, "v": 3, "o": 4, "gate": 5, "up": 6, "down": 7,
-             "h": 10, "z": 11, "x": 12}
+             "h": 10, "z": 11, "x": 12, "codebook": 13}
 
 
 def seed_of(config: int, layer: int, matrix: str, token: int = 0) -> np.random.SeedSequence:
@@ -144,3 +144,11 @@ def laplace_fp16_torch(config: int, layer: int, name: str, token: int, n: int, d
     """x ~ Laplace(0, 1) drawn on the host (laplace_fp16) and moved to device."""
     import torch
     return torch.from_numpy(laplace_fp16(config, layer, name, token, n)).to(device)
+
+
+def trellis_codebook(config: int = 0) -> np.ndarray:
+    """The trellis code's shared codebook: 2^16 draws of N(0, 1) rounded to
+    fp16 (the method draws it once; both the library and the oracle take it
+    as an input)."""
+    g = rng(config, 0, "codebook")
+    return g.standard_normal(65536).astype(np.float16)
