@@ -40,6 +40,8 @@ Other workloads (one JSON line each, same keys; no roofline / CPU legs):
                  sign code (section 5.1, Eq. 4) as the middle tier
     --calibrate  the offline tier-size calibration of section 5.2 (steps 1 and
                  2) on the 7B attention groups, through the library
+    --config 1 --approx trellis   the 1024 x 1024 layer with the trellis-coded
+                 middle tier (section 5.1; host encoder, two weight sets)
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--eager]
                     [--no-cpu-baseline] [--calib-copy] [--config N] [--host]
@@ -124,8 +126,11 @@ class Spec:
 
     def describe(self) -> str:
         s, a, f = self.split
-        return (f"{self.name}: skip/approx/full {s}/{a}/{f} %, {self.full_fmt} full + "
-                f"{self.approx_fmt} g128 approx, W ~N(0,{self.std}) column-major, "
+        approx = {"int4": "int4 g128", "int2": "int2 g128", "sign2": "two-scale 2-bit sign",
+                  "trellis": "trellis-coded 2-bit"}[self.approx_fmt]
+        full = {"fp16": "fp16", "int4": "int4 g128"}[self.full_fmt]
+        return (f"{self.name}: skip/approx/full {s}/{a}/{f} %, {full} full + "
+                f"{approx} approx, W ~N(0,{self.std}) column-major, "
                 f"x ~Laplace(0,1) fp16, batch 1, {self.tokens} tokens x "
                 f"{self.layers_per_token} layer(s) per step over {self.sets} weight sets"
                 + (", weights in pinned host memory" if self.host else ""))
@@ -136,9 +141,15 @@ def headline_spec(approx_fmt: str = "int4") -> Spec:
                 approx_fmt=approx_fmt, split=(40, 30, 30))
 
 
-def specs_for(config: int, host: bool):
+def specs_for(config: int, host: bool, approx: str = "int4"):
     if config == 1:
-        return [Spec(1, "single linear layer 1024x1024", 1024, 0, False, o_only=True)]
+        if approx == "trellis":
+            # the trellis encoder runs on the host (65536 candidates per weight):
+            # two weight sets
+            return [Spec(1, "single linear layer 1024x1024", 1024, 0, False, o_only=True,
+                         approx_fmt="trellis", sets=2)]
+        return [Spec(1, "single linear layer 1024x1024", 1024, 0, False, o_only=True,
+                     approx_fmt=approx)]
     if config == 2:
         return [headline_spec()]
     if config == 3:
@@ -157,7 +168,7 @@ def specs_for(config: int, host: bool):
     raise SystemExit(f"unknown --config {config}")
 
 
-FMT = {"fp16": 1, "int4": 2, "int2": 3, "sign2": 4}
+FMT = {"fp16": 1, "int4": 2, "int2": 3, "sign2": 4, "trellis": 5}
 
 
 class Workload:
@@ -182,6 +193,11 @@ class Workload:
         def gen(s, m, rows, cols):
             return WL.weights_fp16_torch(spec.config, s, m, rows, cols, spec.std, dev)
 
+        # the trellis tier's shared codebook (seeded N(0, 1) draws, fp16)
+        cb = (torch.from_numpy(WL.trellis_codebook(spec.config)).to(dev)
+              if spec.approx_fmt == "trellis" else None)
+        self.codebook = cb
+
         # tier counts per group: QKV, O, GATE_UP, DOWN
         kq = WL.tier_counts(H, split)
         kd = WL.tier_counts(I, split) if I else (0, 0)
@@ -201,7 +217,7 @@ class Workload:
                 del st
             if spec.attn or spec.o_only:
                 o = gen(s, "o" if spec.attn else "w", H, H)
-                mats[1] = build_matrix(o, ff, af, residency=res)
+                mats[1] = build_matrix(o, ff, af, residency=res, codebook=cb)
                 del o
             if I:
                 g_, u_ = gen(s, "gate", I, H), gen(s, "up", I, H)
@@ -463,6 +479,8 @@ def run_headline(args):
     spax.lib()  # fails loudly when the HIP library is missing
     if not torch.cuda.is_available():
         raise SystemExit("bench.py needs a GPU (torch.cuda.is_available() is False)")
+    if args.approx == "trellis":
+        raise SystemExit("--approx trellis runs with --config 1 (its encoder is host code)")
     spec = headline_spec(args.approx)
     spec.sets = args.sets
     log(f"device {torch.cuda.get_device_name(0)}; building {spec.sets} weight sets")
@@ -521,7 +539,7 @@ def run_config(args):
     if not torch.cuda.is_available():
         raise SystemExit("bench.py needs a GPU (torch.cuda.is_available() is False)")
     lines = []
-    for spec in specs_for(args.config, args.host):
+    for spec in specs_for(args.config, args.host, args.approx):
         log(f"config {spec.config}: {spec.describe()}")
         t0 = time.perf_counter()
         wl = Workload(spec)
@@ -628,9 +646,9 @@ def parse():
                    help="run another benchmark workload (1, 3, 4, 5) instead of the headline")
     p.add_argument("--host", action="store_true",
                    help="with --config 4: weights in pinned host memory")
-    p.add_argument("--approx", choices=("int4", "sign2"), default="int4",
-                   help="middle tier of the headline workload: int4 group-128 (default) or "
-                        "the two-scale 2-bit sign code")
+    p.add_argument("--approx", choices=("int4", "sign2", "trellis"), default="int4",
+                   help="middle tier: int4 group-128 (default), the two-scale 2-bit sign code "
+                        "(headline or --config 1) or the trellis code (--config 1 only)")
     p.add_argument("--calibrate", action="store_true",
                    help="run the offline tier-size calibration (steps 1 and 2) on the 7B "
                         "attention groups instead of the decode benchmark")

@@ -28,6 +28,8 @@ def column_bytes(fmt: str, rows: int) -> int:
         return rows // 4 + 2 * (rows // GROUP)
     if fmt == "sign2":                      # 2-bit codes and two fp16 scales
         return rows // 4 + 4
+    if fmt == "trellis":                    # 2-bit codes and one fp16 scale
+        return rows // 4 + 2
     if fmt == "none":
         return 0
     raise ValueError(fmt)
