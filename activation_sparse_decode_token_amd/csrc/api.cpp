@@ -131,10 +131,10 @@ int64_t max_piece(const ProductPlan& p, int32_t kf, int32_t ka) {
 // would not fit. Returns false when no split count fits.
 bool plan_piece(const spax_matrix* W, int32_t kf, int32_t ka, ProductPlan* out) {
   if (W->residency != SPAX_RES_DEVICE) return false;
-  // the trellis tier's codebook takes the LDS a list piece would need
-  if (W->approx_fmt == kTrellis) return false;
+  // the trellis tier's codebook leaves room for a smaller piece
+  const int64_t cap = W->approx_fmt == kTrellis ? kListCapTrellis : kListCap;
   ProductPlan p = plan_product(W, kf, ka);
-  while (max_piece(p, kf, ka) > kListCap) {
+  while (max_piece(p, kf, ka) > cap) {
     if (p.splits >= kMaxSplits || p.splits >= (int64_t)kf + ka) return false;
     p.splits = (int32_t)std::min<int64_t>({(int64_t)p.splits * 2, kMaxSplits, (int64_t)kf + ka});
   }

@@ -292,17 +292,26 @@ __global__ __launch_bounds__(kGemvThreads) void gemv_kernel(GemvArgs a) {
   };
   __shared__ Scratch sm;
   constexpr bool kPiece = MODE == kListRank || MODE == kListSliced;  // list piece in LDS
-  __shared__ int32_t lidx[kPiece ? kListCap : 1];
-  __shared__ float lx[kPiece ? kListCap : 1];
+  constexpr int kCap = kTrel ? kListCapTrellis : kListCap;
+  __shared__ int32_t lidx[kPiece ? kCap : 1];
+  __shared__ float lx[kPiece ? kCap : 1];
   __shared__ WaveMeta wmeta[kTrel ? 1 : 2][kTrel ? 1 : kWaves];  // per tier and wave
   __shared__ __attribute__((aligned(16))) uint16_t cbk[kTrel ? 65536 : 8];
   __shared__ uint32_t last_flag;
-  static_assert(!kTrel || (MODE == kListGlobal || MODE == kListStaged),
-                "the trellis tier is read by the list-reading product only");
 
   const int t = threadIdx.x;
   const int lane = t & 63;
   const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
+  if constexpr (kTrel) {
+    // the codebook into LDS (8192 16-byte pieces, 8 per thread) first: with
+    // the fused ranking its latency overlaps the ranking; it is complete
+    // after the barrier below
+    const uint4* src = reinterpret_cast<const uint4*>(a.codebook);
+    uint4* dst = reinterpret_cast<uint4*>(cbk);
+#pragma unroll
+    for (int k = 0; k < 65536 / 8 / kGemvThreads; ++k)
+      dst[t + k * kGemvThreads] = src[t + k * kGemvThreads];
+  }
   int s_loc, tile;
   map_block(blockIdx.x, a.n_tiles, a.splits_here, s_loc, tile);
   const int split = a.split_lo + s_loc;
@@ -338,15 +347,7 @@ __global__ __launch_bounds__(kGemvThreads) void gemv_kernel(GemvArgs a) {
     a_lo = a0;
     a_hi = a1;
   }
-  if constexpr (kTrel) {
-    // the codebook into LDS: 8192 16-byte pieces, 8 per thread
-    const uint4* src = reinterpret_cast<const uint4*>(a.codebook);
-    uint4* dst = reinterpret_cast<uint4*>(cbk);
-#pragma unroll
-    for (int k = 0; k < 65536 / 8 / kGemvThreads; ++k)
-      dst[t + k * kGemvThreads] = src[t + k * kGemvThreads];
-    __syncthreads();
-  }
+  if constexpr (kTrel) __syncthreads();  // the codebook is in LDS
   {
     const int lf = f_hi - f_lo, la = a_hi - a_lo;
     TierStream<FF, MODE> sf(wmeta[0][kTrel ? 0 : wave], a.full_base, a.full_stride, a.full_bytes,
@@ -490,20 +491,16 @@ template <int FF, int AF>
 hipError_t launch_mode(const GemvArgs& a, int32_t mode, int32_t epi, hipStream_t s) {
   if (mode == kListStaged) return launch_epi<FF, AF, kListStaged, 0>(a, epi, s);
   if (mode == kListGlobal) return launch_epi<FF, AF, kListGlobal, 0>(a, epi, s);
-  if constexpr (AF == kTrellis) {
-    return hipErrorInvalidValue;  // list modes only
-  } else {
-    if (mode == kListSliced) return launch_epi<FF, AF, kListSliced, 0>(a, epi, s);
-    // entries per ranking thread: the smallest of 8, 16, 24, 32, 48, 64 that
-    // covers n
-    static_assert(kRankMaxN == kRankThreads * 64, "fused ranking at up to 64 entries per thread");
-    if (a.n <= kRankThreads * 8) return launch_epi<FF, AF, kListRank, 8>(a, epi, s);
-    if (a.n <= kRankThreads * 16) return launch_epi<FF, AF, kListRank, 16>(a, epi, s);
-    if (a.n <= kRankThreads * 24) return launch_epi<FF, AF, kListRank, 24>(a, epi, s);
-    if (a.n <= kRankThreads * 32) return launch_epi<FF, AF, kListRank, 32>(a, epi, s);
-    if (a.n <= kRankThreads * 48) return launch_epi<FF, AF, kListRank, 48>(a, epi, s);
-    if (a.n <= kRankThreads * 64) return launch_epi<FF, AF, kListRank, 64>(a, epi, s);
-  }
+  if (mode == kListSliced) return launch_epi<FF, AF, kListSliced, 0>(a, epi, s);
+  // entries per ranking thread: the smallest of 8, 16, 24, 32, 48, 64 that
+  // covers n
+  static_assert(kRankMaxN == kRankThreads * 64, "fused ranking at up to 64 entries per thread");
+  if (a.n <= kRankThreads * 8) return launch_epi<FF, AF, kListRank, 8>(a, epi, s);
+  if (a.n <= kRankThreads * 16) return launch_epi<FF, AF, kListRank, 16>(a, epi, s);
+  if (a.n <= kRankThreads * 24) return launch_epi<FF, AF, kListRank, 24>(a, epi, s);
+  if (a.n <= kRankThreads * 32) return launch_epi<FF, AF, kListRank, 32>(a, epi, s);
+  if (a.n <= kRankThreads * 48) return launch_epi<FF, AF, kListRank, 48>(a, epi, s);
+  if (a.n <= kRankThreads * 64) return launch_epi<FF, AF, kListRank, 64>(a, epi, s);
   return hipErrorInvalidValue;
 }
 

@@ -30,6 +30,8 @@ constexpr size_t kCounterRegionBytes = sizeof(uint32_t) * kCountersPerTile * kMa
 constexpr int kGroup = 128;
 // List positions one workgroup of the fused rank + product keeps in LDS.
 constexpr int kListCap = 2048;
+// The same with the trellis tier, whose 128 KB codebook shares the LDS.
+constexpr int kListCapTrellis = 1024;
 // Largest input length the fused rank + product handles (8 ranking waves,
 // up to 64 entries per ranking thread); longer inputs are ranked by the
 // sliced selection kernels first. Measured at n = 28672 (70B down): the

@@ -73,10 +73,9 @@ extern "C" {
  * column (scales [cols]), and a shared fp16 codebook of 65536 values
  * (spax_matrix.approx_codebook, device memory). Weight i of a column is
  * codebook[index_i] * scale, index_i = (index_{i-1} >> 2) | (c_i << 14),
- * index_{-1} = 0. Approx tier only, with an fp16 full tier, and read by the
- * list-reading product only (spax_tiered_gemv; spax_layer_step then runs the
- * stand-alone selection first): the product keeps the codebook in LDS.
- * Produced by spax_pack_trellis_host. */
+ * index_{-1} = 0. Approx tier only, with an fp16 full tier. The product
+ * keeps the codebook in LDS (its fused ranking then holds list pieces of at
+ * most 1024 positions). Produced by spax_pack_trellis_host. */
 #define SPAX_FMT_TRELLIS    5
 
 #define SPAX_RES_DEVICE       0  /* weights in device memory (HBM)            */

@@ -122,3 +122,33 @@ def test_trellis_host_pinned_bitwise_equals_device():
         yh, _ = _run(Wh, x, F, A, copy_stream=cs)
         assert np.array_equal(yd.view(np.uint16), yh.view(np.uint16)), tok
     log("trellis host-pinned == device bitwise")
+
+
+@pytest.mark.parametrize("R,n,kf,ka", [(640, 300, 60, 90), (256, 2000, 500, 600),
+                                       (1152, 513, 100, 300)])
+def test_trellis_fused_ranking(R, n, kf, ka):
+    """A one-group layer step with the trellis tier and device-resident
+    weights: the product ranks x itself (list piece of at most 1024 positions
+    beside the LDS codebook); lists bit-exact, product within the bound."""
+    import torch
+    import activation_sparse_decode_token_amd as spax
+    Wt = WL.weights_fp16(854, R, "w", R, n, 0.02)
+    W, st = _matrix(Wt)
+    L = spax.Layer.make([W, None, None, None], [kf, 0, 0, 0], [ka, 0, 0, 0])
+    dev = torch.device("cuda:0")
+    ws = torch.zeros(spax.layer_workspace_bytes(L), dtype=torch.uint8, device=dev)
+    x = WL.laplace_fp16(854, R, "x", 0, n)
+    Fd = torch.full((kf + 8,), -7, dtype=torch.int32, device=dev)
+    Ad = torch.full((ka + 8,), -7, dtype=torch.int32, device=dev)
+    y = torch.empty(R, dtype=torch.float16, device=dev)
+    io = spax.LayerIO.make(h=to_dev(x), qkv=y, full_idx=(Fd, None, None, None),
+                           approx_idx=(Ad, None, None, None))
+    spax.layer_step(L, io, ws)
+    torch.cuda.synchronize()
+    F, A = O.plan_tiers(x, kf, ka)
+    Fh, Ah = to_host(Fd), to_host(Ad)
+    assert np.array_equal(Fh[:kf], F) and np.array_equal(Ah[:ka], A)
+    assert np.all(Fh[kf:] == -7) and np.all(Ah[ka:] == -7)
+    err = check_product(to_host(y), x, F, A, O.ColumnStore("fp16", Wt), st,
+                        f"trellis fused R={R} n={n}")
+    log(f"trellis fused R={R} n={n}: norm-wise error {err:.2e}")
