@@ -99,7 +99,7 @@ struct ProductPlan {
 #define SPAX_MIN_SPLIT_BYTES 32768
 #endif
 
-// Number of column splits: at most one 8-wave workgroup per compute unit
+// Number of column splits: at most one 16-wave workgroup per compute unit
 // (tiles x splits <= SPAX_TARGET_BLOCKS, so the grid runs in one pass), at
 // least SPAX_MIN_SPLIT_BYTES of weights per workgroup.
 ProductPlan plan_product(const spax_matrix* W, int32_t kf, int32_t ka) {

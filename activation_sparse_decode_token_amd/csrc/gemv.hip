@@ -15,9 +15,11 @@
 //       int4 column segment: 256 B, one 4-byte load per lane;
 //       int2 column segment: 128 B, one 2-byte load per lane.
 //     Every wave-wide load reads one column's contiguous segment.
-//   * The selected columns form one virtual list [F..., A...]; it is cut into
-//     n_splits pieces of equal bytes. Workgroup (split, tile) streams its
-//     piece for its tile; its 8 waves take contiguous eighths of the piece.
+//   * Every split takes the same share of each tier's list (F positions
+//     [k_f s / S, k_f (s+1) / S) and the same share of A), so every
+//     workgroup gets the same mix of bytes and dequantisation work.
+//     Workgroup (split, tile) streams its piece for its tile; its 16 waves
+//     take contiguous sixteenths of each tier's piece.
 //   * Where the list comes from:
 //       kListGlobal  index lists in device memory (spax_tiered_gemv); column
 //                    indices and activations are fetched 64 at a time (one
@@ -30,12 +32,16 @@
 //                    same boundaries, so no list crosses global memory before
 //                    the product; the tile-0 workgroups also write the lists
 //                    out for the caller.
-//   * Code tiers fold 2^b x_j s_{j,g} into one fp32 factor per column and
-//     lane, turn each code u into the fp16 value 1 + u / 2^b with bit
-//     operations and multiply it in with fp16 x fp32 FMAs; the constant part
-//     (2^b plus the code offset, 8 for int4, 1.5 for int2) is removed once at
-//     the end through a per-lane running sum.
-//   * The 8 wave partials are added in LDS in a fixed order. With one split
+//   * Group-128 code tiers fold 2^b x_j s_{j,g} into one fp32 factor per
+//     column and lane, turn each code u into the fp16 value 1 + u / 2^b with
+//     bit operations and multiply it in with fp16 x fp32 FMAs; the constant
+//     part (2^b plus the code offset, 8 for int4, 1.5 for int2) is removed
+//     once at the end through a per-lane running sum. The two-scale sign
+//     code adds +-x_j s_{j,0} +-x_j s_{j,1} per weight (signs moved into fp16
+//     1.0s); the trellis code looks each weight's 16-bit window up in a
+//     codebook held in LDS (section 5.1 of the SpAx page).
+//   * The 16 wave partials are added in LDS in a fixed order (in two halves
+//     for the trellis kernels, whose codebook takes 128 KB of LDS). With one split
 //     the workgroup writes y; otherwise each workgroup stores its fp32 partial
 //     and the last workgroup of a tile (agent-scope counter) adds the n_splits
 //     partials in split order and writes y (arrivals are counted in two
@@ -350,13 +356,15 @@ __global__ __launch_bounds__(kGemvThreads) void gemv_kernel(GemvArgs a) {
   if constexpr (kTrel) __syncthreads();  // the codebook is in LDS
   {
     const int lf = f_hi - f_lo, la = a_hi - a_lo;
-    TierStream<FF, MODE> sf(wmeta[0][kTrel ? 0 : wave], a.full_base, a.full_stride, a.full_bytes,
+    TierStream<FF, MODE> sf(wmeta[0][kTrel ? 0 : wave], a.full_base, a.full_stride,
+                            a.full_bytes,
                             a.full_scales, a.full_sstride, a.full_idx, a.x, lidx, lx,
                             f_lo + (lf * wave) / kWaves, f_lo + (lf * (wave + 1)) / kWaves, row0,
                             a.rows, lane, ld_lane);
     sf.begin();
     if constexpr (AF != kNone) {
-      TierStream<AF, MODE> sa(wmeta[kTrel ? 0 : 1][kTrel ? 0 : wave], a.approx_base, a.approx_stride, a.approx_bytes,
+      TierStream<AF, MODE> sa(wmeta[kTrel ? 0 : 1][kTrel ? 0 : wave], a.approx_base,
+                              a.approx_stride, a.approx_bytes,
                               a.approx_scales, a.approx_sstride, a.approx_idx, a.x,
                               lidx, lx, a_lo + (la * wave) / kWaves,
                               a_lo + (la * (wave + 1)) / kWaves, row0, a.rows, lane, ld_lane);
