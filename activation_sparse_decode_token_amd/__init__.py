@@ -18,7 +18,7 @@ __all__ = [
     "GROUP_QKV", "GROUP_O", "GROUP_GATE_UP", "GROUP_DOWN",
     "Matrix", "Layer", "LayerIO",
     "plan_tiers", "tiered_gemv", "gemv_workspace_bytes", "layer_step",
-    "layer_workspace_bytes", "pack_g128", "pack_sign2", "pack_trellis_host",
+    "layer_workspace_bytes", "pack_g128", "pack_sign2", "pack_trellis_host", "pack_trellis",
     "workspace_clear", "version",
     "status_string", "last_error", "EXPORTS",
 ]
@@ -37,7 +37,7 @@ STATUS = {0: "SPAX_OK", -1: "SPAX_EINVAL", -2: "SPAX_ENULL", -3: "SPAX_EALIGN",
 EXPORTS = (
     "spax_plan_tiers", "spax_gemv_workspace_bytes", "spax_tiered_gemv",
     "spax_layer_workspace_bytes", "spax_layer_step", "spax_pack_g128", "spax_pack_sign2",
-    "spax_pack_trellis_host",
+    "spax_pack_trellis_host", "spax_pack_trellis", "spax_pack_trellis_workspace_bytes",
     "spax_workspace_clear", "spax_status_string", "spax_last_error", "spax_version",
     "spax_set_kernel_choice",
 )
@@ -182,6 +182,10 @@ def _declare(L: ctypes.CDLL) -> None:
     L.spax_pack_sign2.restype = ctypes.c_int
     L.spax_pack_trellis_host.argtypes = [vp, i32, i32, vp, vp, vp, i32]
     L.spax_pack_trellis_host.restype = ctypes.c_int
+    L.spax_pack_trellis.argtypes = [vp, i32, i32, vp, vp, vp, vp, sz, vp]
+    L.spax_pack_trellis.restype = ctypes.c_int
+    L.spax_pack_trellis_workspace_bytes.argtypes = [i32, i32]
+    L.spax_pack_trellis_workspace_bytes.restype = sz
     L.spax_workspace_clear.argtypes = [vp, sz, vp]
     L.spax_workspace_clear.restype = ctypes.c_int
     L.spax_status_string.argtypes = [ctypes.c_int]
@@ -276,6 +280,19 @@ def pack_trellis_host(w, rows, cols, codebook, codes, scales, threads=None) -> N
     _check(lib().spax_pack_trellis_host(w.ctypes.data, int(rows), int(cols), codebook.ctypes.data,
                                         codes.ctypes.data, scales.ctypes.data, int(n)),
            "spax_pack_trellis_host")
+
+
+def pack_trellis(w, rows, cols, codebook, codes, scales, ws, ws_bytes=None,
+                 stream=None) -> None:
+    """spax_pack_trellis: the trellis encoding on the GPU (device tensors)."""
+    nbytes = ws.numel() * ws.element_size() if ws_bytes is None else ws_bytes
+    _check(lib().spax_pack_trellis(_ptr(w), int(rows), int(cols), _ptr(codebook), _ptr(codes),
+                                   _ptr(scales), _ptr(ws), int(nbytes), _stream(stream)),
+           "spax_pack_trellis")
+
+
+def pack_trellis_workspace_bytes(rows, batch) -> int:
+    return int(lib().spax_pack_trellis_workspace_bytes(int(rows), int(batch)))
 
 
 def workspace_clear(ws, nbytes=None, stream=None) -> None:

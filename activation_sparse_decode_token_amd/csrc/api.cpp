@@ -480,6 +480,25 @@ int spax_pack_sign2(const uint16_t* w, int32_t rows, int32_t cols, uint8_t* code
   return e == hipSuccess ? SPAX_OK : hip_fail(e);
 }
 
+size_t spax_pack_trellis_workspace_bytes(int32_t rows, int32_t batch) {
+  if (rows <= 0 || batch <= 0) return 0;
+  return (size_t)batch * trellis_ws_per_column(rows);
+}
+
+int spax_pack_trellis(const uint16_t* w, int32_t rows, int32_t cols, const uint16_t* codebook,
+                      uint8_t* codes, uint16_t* scales, void* ws, size_t ws_bytes,
+                      hipStream_t stream) {
+  if (!w || !codebook || !codes || !scales || !ws) return SPAX_ENULL;
+  if (rows <= 0 || cols <= 0 || rows % kGroup || rows > kMaxRows) return SPAX_EINVAL;
+  if (!aligned16(w) || !aligned16(codebook) || !aligned16(codes) || !aligned16(scales) ||
+      !aligned16(ws))
+    return SPAX_EALIGN;
+  if (ws_bytes < trellis_ws_per_column(rows)) return SPAX_EWORKSPACE;
+  const hipError_t e =
+      launch_pack_trellis(w, rows, cols, codebook, codes, scales, ws, ws_bytes, stream);
+  return e == hipSuccess ? SPAX_OK : hip_fail(e);
+}
+
 int spax_workspace_clear(void* ws, size_t bytes, hipStream_t stream) {
   if (bytes % 4) return SPAX_EINVAL;
   if (bytes == 0) return SPAX_OK;

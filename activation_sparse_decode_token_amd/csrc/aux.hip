@@ -1,5 +1,6 @@
 // Selected-column copy, packer and workspace clear (gfx950).
 #include <hip/hip_fp16.h>
+#include <algorithm>
 #include <hip/hip_runtime.h>
 
 #include "spax_internal.h"
@@ -226,6 +227,204 @@ __global__ __launch_bounds__(kSign2Threads) void pack_sign2_kernel(
   }
 }
 
+// ---------------------------------------------------------------------------
+// Trellis encoder on the GPU (offline). SpAx page section 5.1: per column a
+// sequence of 2-bit codes minimising the squared error between the weights
+// divided by their root-mean-square and codebook[window], chosen jointly by
+// the Viterbi algorithm. The arithmetic is the host encoder's, operation by
+// operation (so both give the same codes): the exact sum of squares in
+// 128-bit integers, one rounding each for S -> fp64, / rows, sqrt, -> fp16;
+// fp32 errors without contraction; the smallest dropped code and then the
+// smallest final state win ties.
+// One 1024-thread workgroup per column; thread T owns the 16 trellis states
+// 16T .. 16T+15, whose predecessors are the 64 consecutive states
+// 64 (T mod 256) .. +63 and whose windows are codebook[64T .. 64T+63] (kept in
+// registers). Each row: read the 64 predecessor costs, barrier, write the 16
+// new costs and one 32-bit word of backpointers (2 bits per state) to the
+// workspace, barrier. Thread 0 then traces the best path back.
+// ---------------------------------------------------------------------------
+constexpr int kTrelThreads = 1024;
+constexpr int kTrelStates = 1 << 14;
+constexpr int kTrelVChunk = 1024;
+
+struct U128 {
+  uint64_t hi, lo;
+};
+__device__ __forceinline__ U128 add128(U128 a, U128 b) {
+  const uint64_t lo = a.lo + b.lo;
+  return U128{a.hi + b.hi + (lo < a.lo ? 1u : 0u), lo};
+}
+// u * u for u < 2^40
+__device__ __forceinline__ U128 square40(uint64_t u) {
+  const uint64_t uh = u >> 32, ul = u & 0xFFFFFFFFu;
+  const uint64_t ll = ul * ul;        // < 2^64
+  const uint64_t hl = 2u * uh * ul;   // < 2^41
+  const uint64_t hh = uh * uh;        // < 2^16
+  U128 r{hh, ll};
+  return add128(r, U128{hl >> 32, hl << 32});
+}
+// round a 128-bit unsigned integer to fp64, ties to even
+__device__ __forceinline__ double u128_to_f64(U128 v) {
+  if (v.hi == 0) return (double)v.lo;  // u64 -> f64, one rounding
+  const int n = 128 - __builtin_clzll(v.hi);  // significant bits, > 64
+  const int sh = n - 53;                      // 12 .. 75
+  uint64_t mant, rem_hi, rem_lo, half_hi, half_lo;
+  if (sh < 64) {
+    mant = (v.hi << (64 - sh)) | (v.lo >> sh);
+    rem_hi = 0;
+    rem_lo = v.lo & ((uint64_t(1) << sh) - 1);
+    half_hi = 0;
+    half_lo = uint64_t(1) << (sh - 1);
+  } else {
+    mant = v.hi >> (sh - 64);
+    rem_hi = sh == 64 ? 0 : v.hi & ((uint64_t(1) << (sh - 64)) - 1);
+    rem_lo = v.lo;
+    half_hi = sh == 64 ? 0 : uint64_t(1) << (sh - 65);
+    half_lo = sh == 64 ? uint64_t(1) << 63 : 0;
+  }
+  const bool above = rem_hi > half_hi || (rem_hi == half_hi && rem_lo > half_lo);
+  const bool tie = rem_hi == half_hi && rem_lo == half_lo;
+  if (above || (tie && (mant & 1u))) ++mant;  // 2^53 stays exact in fp64
+  return ldexp((double)mant, sh);
+}
+
+__global__ __launch_bounds__(kTrelThreads) void trellis_encode_kernel(
+    const uint16_t* __restrict__ w, int rows, int col0, const uint16_t* __restrict__ cb,
+    uint8_t* __restrict__ codes, uint16_t* __restrict__ scales, uint32_t* __restrict__ bp) {
+#pragma clang fp contract(off)
+  // two cost buffers (row i reads one, writes the other); the reductions
+  // before and after the trellis borrow them
+  __shared__ __attribute__((aligned(16))) float cost[2][kTrelStates];
+  __shared__ float vbuf[kTrelVChunk];
+  const int t = threadIdx.x;
+  const int64_t col = col0 + (int64_t)blockIdx.x;
+  const uint16_t* src = w + col * rows;
+  uint32_t* bpc = bp + (int64_t)blockIdx.x * rows * kTrelThreads;
+  uint64_t* rhi = reinterpret_cast<uint64_t*>(&cost[0][0]);
+  uint64_t* rlo = rhi + kTrelThreads;
+
+  // scale: exact sum of squares, then one rounding per step
+  U128 acc{0, 0};
+  for (int i = t; i < rows; i += kTrelThreads) {
+    const int64_t u = h_units(src[i]);
+    acc = add128(acc, square40((uint64_t)(u < 0 ? -u : u)));
+  }
+  rhi[t] = acc.hi;
+  rlo[t] = acc.lo;
+  __syncthreads();
+  for (int k = kTrelThreads / 2; k > 0; k >>= 1) {
+    if (t < k) {
+      const U128 r = add128(U128{rhi[t], rlo[t]}, U128{rhi[t + k], rlo[t + k]});
+      rhi[t] = r.hi;
+      rlo[t] = r.lo;
+    }
+    __syncthreads();
+  }
+  const double q = u128_to_f64(U128{rhi[0], rlo[0]}) / (double)rows;
+  const uint16_t sh = f64_to_h_rne(ldexp(sqrt(q), -24));
+  __syncthreads();  // the reduction's words are read; cost[0] is free again
+  if (t == 0) scales[col] = sh;
+  uint8_t* cc = codes + col * (rows / 4);
+  if (sh == 0) {
+    for (int b = t; b < rows / 4; b += kTrelThreads) cc[b] = 0;
+    return;
+  }
+  const double s = ldexp((double)h_units(sh), -24);
+
+  // this thread's 64 windows as fp16 pairs; d = v - cb is taken as the
+  // fused fp16 x fp32 + fp32 operation fma(cb, -1, v): one rounding of the
+  // exact difference, as an fp32 subtraction
+  uint32_t cbp[32];
+#pragma unroll
+  for (int k = 0; k < 32; ++k)
+    cbp[k] = (uint32_t)cb[64 * t + 2 * k] | ((uint32_t)cb[64 * t + 2 * k + 1] << 16);
+  const float inf = __builtin_inff();
+#pragma unroll
+  for (int k = 0; k < 16; ++k) cost[0][16 * t + k] = (t == 0 && k == 0) ? 0.0f : inf;
+  const int pbase = 64 * (t & 0xFF);
+  int cur = 0;
+
+  for (int c0 = 0; c0 < rows; c0 += kTrelVChunk) {
+    const int cn = min(kTrelVChunk, rows - c0);
+    __syncthreads();
+    for (int i = t; i < cn; i += kTrelThreads)
+      vbuf[i] = (float)(ldexp((double)h_units(src[c0 + i]), -24) / s);
+    __syncthreads();
+    for (int i = 0; i < cn; ++i) {
+      const float v = vbuf[i];
+      const float* pc = cost[cur];
+      float* nx = cost[cur ^ 1];
+      uint32_t bits = 0;
+#pragma unroll
+      for (int k = 0; k < 16; ++k) {
+        const float4 q4 = *reinterpret_cast<const float4*>(&pc[pbase + 4 * k]);
+        const float pk[4] = {q4.x, q4.y, q4.z, q4.w};
+        float best = 0.0f;
+        uint32_t bo = 0;
+#pragma unroll
+        for (int o = 0; o < 4; ++o) {
+          const uint32_t pair = cbp[2 * k + (o >> 1)];
+          const float cbo = h2f((uint16_t)((o & 1) ? pair >> 16 : pair & 0xFFFFu));
+          const float d = fmaf(cbo, -1.0f, v);
+          const float e = d * d;
+          const float c = pk[o] + e;
+          if (o == 0 || c < best) {
+            best = c;
+            bo = (uint32_t)o;
+          }
+        }
+        nx[16 * t + k] = best;
+        bits |= bo << (2 * k);
+      }
+      bpc[(int64_t)(c0 + i) * kTrelThreads + t] = bits;
+      cur ^= 1;
+      __syncthreads();
+    }
+  }
+
+  // the best final state (smallest cost, then smallest state)
+  float bv = cost[cur][16 * t];
+  int bi = 16 * t;
+#pragma unroll
+  for (int k = 1; k < 16; ++k) {
+    const float c = cost[cur][16 * t + k];
+    if (c < bv) {
+      bv = c;
+      bi = 16 * t + k;
+    }
+  }
+  float* rv = cost[cur ^ 1];
+  int32_t* ri = reinterpret_cast<int32_t*>(rv + kTrelThreads);
+  rv[t] = bv;
+  ri[t] = bi;
+  __syncthreads();
+  for (int k = kTrelThreads / 2; k > 0; k >>= 1) {
+    if (t < k) {
+      const float o = rv[t + k];
+      const int oi = ri[t + k];
+      if (o < rv[t] || (o == rv[t] && oi < ri[t])) {
+        rv[t] = o;
+        ri[t] = oi;
+      }
+    }
+    __syncthreads();
+  }
+  // trace back (thread 0): the code of row i is the state's top two bits
+  if (t == 0) {
+    int state = ri[0];
+    uint32_t byte = 0;
+    for (int i = rows - 1; i >= 0; --i) {
+      byte |= ((uint32_t)state >> 12) << (2 * (i & 3));
+      if ((i & 3) == 0) {
+        cc[i >> 2] = (uint8_t)byte;
+        byte = 0;
+      }
+      const uint32_t word = bpc[(int64_t)i * kTrelThreads + (state >> 4)];
+      state = ((state & 0xFFF) << 2) | (int)((word >> (2 * (state & 15))) & 3u);
+    }
+  }
+}
+
 __global__ void clear_kernel(uint32_t* __restrict__ p, int64_t n) {
   for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
        i += (int64_t)gridDim.x * blockDim.x)
@@ -260,6 +459,22 @@ hipError_t launch_pack_sign2(const uint16_t* w, int32_t rows, int32_t cols, uint
   hipLaunchKernelGGL(pack_sign2_kernel, dim3((unsigned)cols), dim3(kSign2Threads), 0, s, w,
                      rows, codes, scales);
   return hipGetLastError();
+}
+
+size_t trellis_ws_per_column(int32_t rows) { return (size_t)rows * kTrelThreads * 4; }
+
+hipError_t launch_pack_trellis(const uint16_t* w, int32_t rows, int32_t cols,
+                               const uint16_t* codebook, uint8_t* codes, uint16_t* scales,
+                               void* ws, size_t ws_bytes, hipStream_t s) {
+  const int64_t batch = std::min<int64_t>(cols, (int64_t)(ws_bytes / trellis_ws_per_column(rows)));
+  for (int64_t c0 = 0; c0 < cols; c0 += batch) {
+    const int64_t nb = std::min<int64_t>(batch, cols - c0);
+    hipLaunchKernelGGL(trellis_encode_kernel, dim3((unsigned)nb), dim3(kTrelThreads), 0, s, w,
+                       rows, (int)c0, codebook, codes, scales, static_cast<uint32_t*>(ws));
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
 }
 
 hipError_t launch_clear(void* ws, size_t bytes, hipStream_t s) {

@@ -138,6 +138,13 @@ hipError_t launch_pack(const uint16_t* w, int32_t rows, int32_t cols, int32_t fm
 hipError_t launch_pack_sign2(const uint16_t* w, int32_t rows, int32_t cols, uint8_t* codes,
                              uint16_t* scales, hipStream_t s);
 
+// Trellis encoder: backpointer workspace per column in flight, and the
+// launches (columns in batches that fit the workspace).
+size_t trellis_ws_per_column(int32_t rows);
+hipError_t launch_pack_trellis(const uint16_t* w, int32_t rows, int32_t cols,
+                               const uint16_t* codebook, uint8_t* codes, uint16_t* scales,
+                               void* ws, size_t ws_bytes, hipStream_t s);
+
 hipError_t launch_clear(void* ws, size_t bytes, hipStream_t s);
 
 // List positions of split s of n_splits: every split takes the same share

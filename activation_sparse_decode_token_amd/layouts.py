@@ -18,7 +18,8 @@ import torch
 
 from . import (FMT_FP16, FMT_INT2_G128, FMT_INT4_G128, FMT_NONE, FMT_SIGN2, FMT_TRELLIS,
                LAYOUT_GLU_INTERLEAVED, LAYOUT_PLAIN, RES_DEVICE, RES_HOST_PINNED, Matrix,
-               pack_g128, pack_sign2, pack_trellis_host)
+               pack_g128, pack_sign2, pack_trellis, pack_trellis_host,
+               pack_trellis_workspace_bytes)
 
 GROUP = 128
 
@@ -45,22 +46,33 @@ def glu_deinterleave(stacked: torch.Tensor):
     return v[..., 0, :].reshape(*lead, R2 // 2), v[..., 1, :].reshape(*lead, R2 // 2)
 
 
-def pack(w_cm: torch.Tensor, fmt: int, stream=None, codebook: Optional[torch.Tensor] = None):
+def pack(w_cm: torch.Tensor, fmt: int, stream=None, codebook: Optional[torch.Tensor] = None,
+         trellis_on_host: bool = False, trellis_ws_bytes: int = 1 << 31):
     """Codes and scales of a column-major fp16 device tensor [n, R]. The
-    trellis code is encoded on the host (spax_pack_trellis_host) with the
-    given device codebook (fp16 [65536])."""
+    trellis code uses the given device codebook (fp16 [65536]) and is encoded
+    on the GPU (spax_pack_trellis, a backpointer workspace of up to
+    trellis_ws_bytes) or, with trellis_on_host, by the host encoder
+    (spax_pack_trellis_host); both give the same bits."""
     n, R = w_cm.shape
     if fmt == FMT_TRELLIS:
         import numpy as np
         if codebook is None:
             raise ValueError("the trellis code needs a codebook")
-        w_h = w_cm.detach().cpu().contiguous().numpy()
-        cb_h = codebook.detach().cpu().contiguous().numpy()
-        codes = np.zeros((n, R // 4), dtype=np.uint8)
-        scales = np.zeros(n, dtype=np.float16)
-        pack_trellis_host(w_h, R, n, cb_h, codes, scales)
-        return (torch.from_numpy(codes).to(w_cm.device),
-                torch.from_numpy(scales).to(w_cm.device))
+        if trellis_on_host:
+            w_h = w_cm.detach().cpu().contiguous().numpy()
+            cb_h = codebook.detach().cpu().contiguous().numpy()
+            codes = np.zeros((n, R // 4), dtype=np.uint8)
+            scales = np.zeros(n, dtype=np.float16)
+            pack_trellis_host(w_h, R, n, cb_h, codes, scales)
+            return (torch.from_numpy(codes).to(w_cm.device),
+                    torch.from_numpy(scales).to(w_cm.device))
+        codes = torch.empty((n, R // 4), dtype=torch.uint8, device=w_cm.device)
+        scales = torch.empty(n, dtype=torch.float16, device=w_cm.device)
+        per = pack_trellis_workspace_bytes(R, 1)
+        ws = torch.empty(max(per, min(trellis_ws_bytes, per * n)), dtype=torch.uint8,
+                         device=w_cm.device)
+        pack_trellis(w_cm, R, n, codebook, codes, scales, ws, stream=stream)
+        return codes, scales
     if fmt == FMT_SIGN2:
         # two-scale sign code: 2 bits per weight, (s0, s1) per column
         codes = torch.empty((n, R // 4), dtype=torch.uint8, device=w_cm.device)

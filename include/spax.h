@@ -287,6 +287,22 @@ int spax_pack_trellis_host(const uint16_t* w, int32_t rows, int32_t cols,
                            const uint16_t* codebook, uint8_t* codes, uint16_t* scales,
                            int32_t threads);
 
+/* spax_pack_trellis -- the same encoding as spax_pack_trellis_host, on the
+ * GPU (every code and scale bit-identical): one 1024-thread workgroup per
+ * column runs the 16384-state Viterbi, two barriers' worth of work per row,
+ * and traces the best path back from backpointers kept in the workspace.
+ *   w, codebook, codes, scales  device memory, layouts as in
+ *            spax_pack_trellis_host; 16-byte aligned.
+ *   ws       device workspace of ws_bytes >= spax_pack_trellis_workspace_bytes(
+ *            rows, 1); columns are encoded in launches of
+ *            ws_bytes / spax_pack_trellis_workspace_bytes(rows, 1) columns.
+ *   Enqueues only; results are valid after the stream synchronises.
+ *   Errors: SPAX_ENULL, SPAX_EINVAL, SPAX_EALIGN, SPAX_EWORKSPACE, SPAX_EHIP. */
+size_t spax_pack_trellis_workspace_bytes(int32_t rows, int32_t batch);
+int spax_pack_trellis(const uint16_t* w, int32_t rows, int32_t cols, const uint16_t* codebook,
+                      uint8_t* codes, uint16_t* scales, void* ws, size_t ws_bytes,
+                      hipStream_t stream);
+
 /* spax_workspace_clear -- zero `bytes` bytes of ws with a kernel (no memset
  * node, so it may be captured in a graph). bytes % 4 == 0. */
 int spax_workspace_clear(void* ws, size_t bytes, hipStream_t stream);

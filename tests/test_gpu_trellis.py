@@ -152,3 +152,42 @@ def test_trellis_fused_ranking(R, n, kf, ka):
     err = check_product(to_host(y), x, F, A, O.ColumnStore("fp16", Wt), st,
                         f"trellis fused R={R} n={n}")
     log(f"trellis fused R={R} n={n}: norm-wise error {err:.2e}")
+
+
+def test_gpu_encoder_matches_oracle_and_host_encoder():
+    """spax_pack_trellis (the Viterbi on the GPU) against the oracle on small
+    columns with special cases, and against the host encoder (itself pinned
+    to the oracle) on a larger matrix, in several launches."""
+    import torch
+    import activation_sparse_decode_token_amd as spax
+    dev = torch.device("cuda:0")
+    cb = WL.trellis_codebook(1)
+    rs = np.random.default_rng(855)
+    Wt = WL.weights_fp16(855, 0, "w", 256, 6, 0.02)
+    Wt[0] = 0                                                        # zero column
+    Wt[1, 9] = np.float16(5.0)                                       # an outlier
+    Wt[2] = (rs.integers(-30, 31, 256) * 2.0 ** -24).astype(np.float16)  # subnormal
+    Wt[3] = (rs.choice([-1.0, 1.0], 256) * 0.25).astype(np.float16)  # one magnitude
+
+    def gpu(W, per_launch):
+        n, R = W.shape
+        codes = torch.empty((n, R // 4), dtype=torch.uint8, device=dev)
+        scales = torch.empty(n, dtype=torch.float16, device=dev)
+        ws = torch.empty(spax.pack_trellis_workspace_bytes(R, per_launch), dtype=torch.uint8,
+                         device=dev)
+        spax.pack_trellis(to_dev(W), R, n, to_dev(cb), codes, scales, ws)
+        torch.cuda.synchronize()
+        return to_host(codes), to_host(scales)
+
+    c, s = gpu(Wt, 4)                      # two launches
+    oc, os_ = T.pack_trellis(Wt, cb)
+    assert np.array_equal(s.view(np.uint16), os_.view(np.uint16))
+    assert np.array_equal(c, oc)
+    W2 = WL.weights_fp16(856, 0, "w", 1024, 48, 0.02)
+    c2, s2 = gpu(W2, 20)                   # three launches
+    hc = np.zeros((48, 256), dtype=np.uint8)
+    hs = np.zeros(48, dtype=np.float16)
+    spax.pack_trellis_host(W2, 1024, 48, cb, hc, hs)
+    assert np.array_equal(s2.view(np.uint16), hs.view(np.uint16))
+    assert np.array_equal(c2, hc)
+    log("GPU trellis encoder == oracle / host encoder")
