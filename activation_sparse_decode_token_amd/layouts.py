@@ -46,8 +46,13 @@ def glu_deinterleave(stacked: torch.Tensor):
     return v[..., 0, :].reshape(*lead, R2 // 2), v[..., 1, :].reshape(*lead, R2 // 2)
 
 
+# Largest backpointer workspace the GPU trellis encoder may take (columns are
+# encoded in launches of as many columns as fit; 4 KB per row per column).
+TRELLIS_WS_BYTES = 1 << 31
+
+
 def pack(w_cm: torch.Tensor, fmt: int, stream=None, codebook: Optional[torch.Tensor] = None,
-         trellis_on_host: bool = False, trellis_ws_bytes: int = 1 << 31):
+         trellis_on_host: bool = False, trellis_ws_bytes: Optional[int] = None):
     """Codes and scales of a column-major fp16 device tensor [n, R]. The
     trellis code uses the given device codebook (fp16 [65536]) and is encoded
     on the GPU (spax_pack_trellis, a backpointer workspace of up to
@@ -69,8 +74,8 @@ def pack(w_cm: torch.Tensor, fmt: int, stream=None, codebook: Optional[torch.Ten
         codes = torch.empty((n, R // 4), dtype=torch.uint8, device=w_cm.device)
         scales = torch.empty(n, dtype=torch.float16, device=w_cm.device)
         per = pack_trellis_workspace_bytes(R, 1)
-        ws = torch.empty(max(per, min(trellis_ws_bytes, per * n)), dtype=torch.uint8,
-                         device=w_cm.device)
+        cap = TRELLIS_WS_BYTES if trellis_ws_bytes is None else trellis_ws_bytes
+        ws = torch.empty(max(per, min(cap, per * n)), dtype=torch.uint8, device=w_cm.device)
         pack_trellis(w_cm, R, n, codebook, codes, scales, ws, stream=stream)
         return codes, scales
     if fmt == FMT_SIGN2:

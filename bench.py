@@ -40,8 +40,9 @@ Other workloads (one JSON line each, same keys; no roofline / CPU legs):
                  sign code (section 5.1, Eq. 4) as the middle tier
     --calibrate  the offline tier-size calibration of section 5.2 (steps 1 and
                  2) on the 7B attention groups, through the library
-    --config 1 --approx trellis   the 1024 x 1024 layer with the trellis-coded
-                 middle tier (section 5.1; host encoder, two weight sets)
+    --approx trellis  the headline workload with the trellis-coded middle
+                 tier (section 5.1; GPU Viterbi encoder, 8 weight sets); also
+                 with --config 1
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--eager]
                     [--no-cpu-baseline] [--calib-copy] [--config N] [--host]
@@ -213,7 +214,7 @@ class Workload:
                 q, k_, v = (gen(s, m, H, H) for m in ("q", "k", "v"))
                 st = stack_rows([q, k_, v])
                 del q, k_, v
-                mats[0] = build_matrix(st, ff, af, residency=res)
+                mats[0] = build_matrix(st, ff, af, residency=res, codebook=cb)
                 del st
             if spec.attn or spec.o_only:
                 o = gen(s, "o" if spec.attn else "w", H, H)
@@ -479,10 +480,15 @@ def run_headline(args):
     spax.lib()  # fails loudly when the HIP library is missing
     if not torch.cuda.is_available():
         raise SystemExit("bench.py needs a GPU (torch.cuda.is_available() is False)")
-    if args.approx == "trellis":
-        raise SystemExit("--approx trellis runs with --config 1 (its encoder is host code)")
     spec = headline_spec(args.approx)
     spec.sets = args.sets
+    if args.approx == "trellis":
+        # the offline Viterbi encoding takes about a second per weight set
+        # (on the GPU, 16 GB of backpointers per launch): 8 sets (1.4 GB of
+        # weights, still far past the 256 MB last-level cache)
+        import activation_sparse_decode_token_amd.layouts as LY
+        LY.TRELLIS_WS_BYTES = 16 << 30
+        spec.sets = min(args.sets, 8)
     log(f"device {torch.cuda.get_device_name(0)}; building {spec.sets} weight sets")
     t0 = time.perf_counter()
     wl = Workload(spec)
@@ -510,8 +516,10 @@ def run_headline(args):
             # the committed counters were taken on the int4 workload
             "traffic": measured_traffic() if args.approx == "int4" else None,
             "kernel": "gemv_kernel: fused tier selection + tiered gather-GEMV "
-                      + ("(fp16 full, int4 g128 approx)" if args.approx == "int4" else
-                         "(fp16 full, two-scale 2-bit sign approx)"),
+                      + {"int4": "(fp16 full, int4 g128 approx)",
+                         "sign2": "(fp16 full, two-scale 2-bit sign approx)",
+                         "trellis": "(fp16 full, trellis-coded 2-bit approx, codebook in LDS)"}
+                      [args.approx],
             "avg_launch_us": round((t_qkv + t_o) / 2 * 1e6, 3),
             "launch_us": {"qkv": round(t_qkv * 1e6, 3), "o": round(t_o * 1e6, 3)},
             "bytes_per_launch": {"qkv": qkv_b, "o": o_b},
@@ -525,7 +533,9 @@ def run_headline(args):
         torch.cuda.synchronize()
         log("calibration copy: 268435456 bytes read, 268435456 bytes written")
     base = None
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and args.approx != "trellis":
+        # (the trellis oracle's numpy Viterbi needs seconds per 4096-row
+        # column, so that line has no CPU leg)
         log("timing the CPU oracle on a bounded sample")
         base = cpu_baseline(*wl.k[0], approx_fmt=args.approx)
     return result_line(spec, wl, args, sec_step, mode, {"roofline": roof, "cpu_baseline": base})
@@ -647,8 +657,8 @@ def parse():
     p.add_argument("--host", action="store_true",
                    help="with --config 4: weights in pinned host memory")
     p.add_argument("--approx", choices=("int4", "sign2", "trellis"), default="int4",
-                   help="middle tier: int4 group-128 (default), the two-scale 2-bit sign code "
-                        "(headline or --config 1) or the trellis code (--config 1 only)")
+                   help="middle tier of the headline workload or of --config 1: int4 "
+                        "group-128 (default), the two-scale 2-bit sign code or the trellis code")
     p.add_argument("--calibrate", action="store_true",
                    help="run the offline tier-size calibration (steps 1 and 2) on the 7B "
                         "attention groups instead of the decode benchmark")
