@@ -500,14 +500,15 @@ hipError_t launch_mode(const GemvArgs& a, int32_t mode, int32_t epi, hipStream_t
   if (mode == kListStaged) return launch_epi<FF, AF, kListStaged, 0>(a, epi, s);
   if (mode == kListGlobal) return launch_epi<FF, AF, kListGlobal, 0>(a, epi, s);
   if (mode == kListSliced) return launch_epi<FF, AF, kListSliced, 0>(a, epi, s);
-  // entries per ranking thread: the smallest of 8, 16, 24, 32, 48, 64 that
-  // covers n
+  // entries per ranking thread: the smallest of 8, 16, 24, 32, 48, 56, 64
+  // that covers n (56: the 70B down projection's 28672 exactly)
   static_assert(kRankMaxN == kRankThreads * 64, "fused ranking at up to 64 entries per thread");
   if (a.n <= kRankThreads * 8) return launch_epi<FF, AF, kListRank, 8>(a, epi, s);
   if (a.n <= kRankThreads * 16) return launch_epi<FF, AF, kListRank, 16>(a, epi, s);
   if (a.n <= kRankThreads * 24) return launch_epi<FF, AF, kListRank, 24>(a, epi, s);
   if (a.n <= kRankThreads * 32) return launch_epi<FF, AF, kListRank, 32>(a, epi, s);
   if (a.n <= kRankThreads * 48) return launch_epi<FF, AF, kListRank, 48>(a, epi, s);
+  if (a.n <= kRankThreads * 56) return launch_epi<FF, AF, kListRank, 56>(a, epi, s);
   if (a.n <= kRankThreads * 64) return launch_epi<FF, AF, kListRank, 64>(a, epi, s);
   return hipErrorInvalidValue;
 }
