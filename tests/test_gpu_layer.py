@@ -4,7 +4,8 @@ import pytest
 
 import oracle as O
 import workloads as WL
-from tests.spax_testlib import check_product, log, sample_groups, to_dev, to_host
+from tests.spax_testlib import (TrellisStore, check_product, log, sample_groups, to_dev,
+                                to_host)
 
 pytestmark = pytest.mark.gpu
 
@@ -33,13 +34,14 @@ def _build_layer(w: LayerWeights, ff, af, residency, ks):
     spax = _spax()
     from activation_sparse_decode_token_amd.layouts import build_matrix, glu_interleave, stack_rows
     F = {"fp16": 1, "int4": 2}[ff]
-    A = {"int4": 2, "int2": 3, "sign2": 4}[af]
+    A = {"int4": 2, "int2": 3, "sign2": 4, "trellis": 5}[af]
+    cb = to_dev(WL.trellis_codebook(2)) if af == "trellis" else None
     qkv = build_matrix(stack_rows([to_dev(w.q), to_dev(w.k), to_dev(w.v)]), F, A,
-                       residency=residency)
-    o = build_matrix(to_dev(w.o), F, A, residency=residency)
+                       residency=residency, codebook=cb)
+    o = build_matrix(to_dev(w.o), F, A, residency=residency, codebook=cb)
     gu = build_matrix(glu_interleave(to_dev(w.gate), to_dev(w.up)), F, A,
-                      layout=spax.LAYOUT_GLU_INTERLEAVED, residency=residency)
-    dn = build_matrix(to_dev(w.down), F, A, residency=residency)
+                      layout=spax.LAYOUT_GLU_INTERLEAVED, residency=residency, codebook=cb)
+    dn = build_matrix(to_dev(w.down), F, A, residency=residency, codebook=cb)
     torch.cuda.synchronize()
     kf = [ks[g][0] for g in ("qkv", "o", "ffn", "down")]
     ka = [ks[g][1] for g in ("qkv", "o", "ffn", "down")]
@@ -81,7 +83,19 @@ def _run_layer(L, h, z, x, ws=None, copy_stream=None):
     return res, ws
 
 
-def _check_layer(res, w: LayerWeights, ks, h, z, x, ff, af, label, rows_per=None):
+class RowsOf:
+    """Some rows of a store whose columns are rebuilt whole (the trellis
+    window runs down the stored column)."""
+
+    def __init__(self, inner, rows):
+        self.inner, self.rows_idx = inner, np.asarray(rows)
+        self.fmt, self.rows = inner.fmt, len(self.rows_idx)
+
+    def columns(self, idx):
+        return self.inner.columns(idx)[:, self.rows_idx]
+
+
+def _check_layer(res, w: LayerWeights, ks, h, z, x, ff, af, label, rows_per=None, L=None):
     """Stage-wise parity: each group is compared with the oracle fed the same
     inputs the GPU group saw (down is fed the GPU's a)."""
     packed = {}
@@ -92,6 +106,13 @@ def _check_layer(res, w: LayerWeights, ks, h, z, x, ff, af, label, rows_per=None
         (stacked q/k/v, interleaved gate/up): smap gives the stored row of
         every row of Wt."""
         sub = Wt if rows is None else np.ascontiguousarray(Wt[:, rows])
+        if af == "trellis":
+            # the library's codes of the stored matrix (its encoder is pinned to
+            # the oracle's), rebuilt by the oracle over whole stored columns
+            W = L_of[id(stored)] if stored is not None else L_of[id(Wt)]
+            smap_ = smap if stored is not None else np.arange(Wt.shape[1])
+            r = smap_ if rows is None else smap_[rows]
+            return O.ColumnStore(ff, sub), RowsOf(TrellisStore(*W), r)
         if af != "sign2":
             return O.ColumnStore(ff, sub), O.ColumnStore(af, sub)
         if stored is None:
@@ -111,10 +132,16 @@ def _check_layer(res, w: LayerWeights, ks, h, z, x, ff, af, label, rows_per=None
     Wgu = np.empty((w.gate.shape[0], 2 * w.inter), dtype=np.float16)
     Wgu[:, gmap] = w.gate
     Wgu[:, gmap + 128] = w.up
+    Wqkv = np.concatenate([w.q, w.k, w.v], axis=1)
+    L_of = {}
+    if af == "trellis":
+        cbh = WL.trellis_codebook(2)
+        for key, g in ((Wqkv, 0), (w.o, 1), (Wgu, 2), (w.down, 3)):
+            keep = L._keep[g]._keep
+            L_of[id(key)] = (to_host(keep[2]), to_host(keep[3]), cbh)
 
     L0 = O.plan_tiers(h, *ks["qkv"])
     assert all(np.array_equal(a, b) for a, b in zip(res["lists"][0], L0)), f"{label}: qkv lists"
-    Wqkv = np.concatenate([w.q, w.k, w.v], axis=1)
     rows = sample_groups(Wqkv.shape[1], 8, 1) if rows_per else None
     check_product(res["qkv"], h, *L0, *stores(Wqkv, rows), f"{label} qkv", rows=rows)
 
@@ -149,7 +176,7 @@ def _ks(hidden, inter, split):
 
 
 @pytest.mark.parametrize("ff,af", [("fp16", "int4"), ("int4", "int2"), ("fp16", "int2"),
-                                   ("fp16", "sign2")])
+                                   ("fp16", "sign2"), ("fp16", "trellis")])
 def test_layer_small(ff, af, kernel_choice):
     hidden, inter = 512, 1408          # ragged tiles: 1408 = 2*512 + 384; gate/up 2816 rows
     w = LayerWeights(810, 0, hidden, inter, 0.02)
@@ -160,7 +187,7 @@ def test_layer_small(ff, af, kernel_choice):
         z = WL.laplace_fp16(810, 0, "z", tok, hidden)
         x = WL.laplace_fp16(810, 0, "x", tok, hidden)
         res, _ = _run_layer(L, h, z, x)
-        _check_layer(res, w, ks, h, z, x, ff, af, f"small {ff}/{af} token {tok}")
+        _check_layer(res, w, ks, h, z, x, ff, af, f"small {ff}/{af} token {tok}", L=L)
     log(f"layer small {ff}/{af} ok")
 
 
