@@ -31,7 +31,8 @@ KERNEL_AUTO, KERNEL_SEPARATE = 0, 1
 MAX_ROWS = 1 << 20
 
 STATUS = {0: "SPAX_OK", -1: "SPAX_EINVAL", -2: "SPAX_ENULL", -3: "SPAX_EALIGN",
-          -4: "SPAX_EFORMAT", -5: "SPAX_EWORKSPACE", -6: "SPAX_ESTREAM", -7: "SPAX_EHIP"}
+          -4: "SPAX_EFORMAT", -5: "SPAX_EWORKSPACE", -6: "SPAX_ESTREAM", -7: "SPAX_EHIP",
+          -8: "SPAX_ENOMEM"}
 
 # Every entry point declared in include/spax.h.
 EXPORTS = (

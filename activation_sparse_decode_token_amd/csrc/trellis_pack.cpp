@@ -18,10 +18,13 @@
 //     floating-point contraction): v_i = fp32(w_i / s), d = v_i - cb,
 //     e = d * d, cost' = cost + e; the smallest o wins ties, the smallest
 //     final state wins ties; a zero column gets scale 0 and zero codes.
+#include <atomic>
 #include <cmath>
 #include <cstdint>
 #include <limits>
+#include <new>
 #include <thread>
+#include <utility>
 #include <vector>
 
 #include "spax.h"
@@ -116,18 +119,46 @@ extern "C" int spax_pack_trellis_host(const uint16_t* w, int32_t rows, int32_t c
   if (rows <= 0 || cols <= 0 || rows % 128 || rows > (1 << 20)) return SPAX_EINVAL;
   if (threads < 1) threads = 1;
   if (threads > cols) threads = cols;
-  std::vector<float> cb(65536);
+  // Every allocation happens here, before any thread starts, so that a
+  // shortage becomes fewer threads or an error code, never an exception
+  // escaping a worker (which would end the process).
+  struct Scratch {
+    std::vector<float> cost, next;
+    std::vector<uint8_t> back;
+  };
+  std::vector<float> cb;
+  std::vector<Scratch> scratch;
+  try {
+    cb.resize(65536);
+    scratch.reserve((size_t)threads);
+    for (int k = 0; k < threads; ++k) {
+      Scratch sc;
+      sc.cost.resize(kStates);
+      sc.next.resize(kStates);
+      sc.back.resize((size_t)rows * kStates);
+      scratch.push_back(std::move(sc));
+    }
+  } catch (const std::bad_alloc&) {
+    if (cb.size() != 65536 || scratch.empty()) return SPAX_ENOMEM;
+  }
   for (int k = 0; k < 65536; ++k) cb[k] = (float)h2d(codebook[k]);
-  auto work = [&](int first) {
-    std::vector<float> cost(kStates), next(kStates);
-    std::vector<uint8_t> back((size_t)rows * kStates);
-    for (int j = first; j < cols; j += threads)
+  // columns are handed out one at a time, so any number of workers covers
+  // all of them
+  std::atomic<int> next_col{0};
+  auto work = [&](Scratch* sc) {
+    for (int j = next_col.fetch_add(1); j < cols; j = next_col.fetch_add(1))
       encode_column(w + (size_t)j * rows, rows, cb.data(), codes + (size_t)j * (rows / 4),
-                    scales + j, cost, next, back);
+                    scales + j, sc->cost, sc->next, sc->back);
   };
   std::vector<std::thread> pool;
-  for (int k = 1; k < threads; ++k) pool.emplace_back(work, k);
-  work(0);
+  for (size_t k = 1; k < scratch.size(); ++k) {
+    try {
+      pool.emplace_back(work, &scratch[k]);
+    } catch (const std::exception&) {
+      break;  // the threads already started and this one share the columns
+    }
+  }
+  work(&scratch[0]);
   for (auto& th : pool) th.join();
   return SPAX_OK;
 }

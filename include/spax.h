@@ -55,6 +55,7 @@ extern "C" {
 #define SPAX_ESTREAM    -6  /* host-resident matrix but no copy stream given   */
 #define SPAX_EHIP       -7  /* the HIP runtime reported an error; see
                                spax_last_error()                               */
+#define SPAX_ENOMEM     -8  /* host memory for scratch could not be allocated  */
 
 /* ---- formats, residency, layout ---------------------------------------- */
 #define SPAX_FMT_NONE       0  /* tier absent (its count must be 0)          */
@@ -281,8 +282,11 @@ int spax_pack_sign2(const uint16_t* w, int32_t rows, int32_t cols, uint8_t* code
  *            byte i.
  *   scales   host out, fp16 [cols].
  *   threads  host threads to use (columns are independent), >= 1.
- *   Memory: about rows * 16 KB of host scratch per thread.
- *   Errors: SPAX_ENULL, SPAX_EINVAL.                                         */
+ *   Memory: about rows * 16 KB of host scratch per thread, allocated before
+ *   any thread starts; when only some threads' scratch fits, fewer threads
+ *   run (and fewer again if a thread cannot be started).
+ *   Errors: SPAX_ENULL, SPAX_EINVAL; SPAX_ENOMEM when not even one thread's
+ *   scratch can be allocated (codes and scales are then left unwritten).     */
 int spax_pack_trellis_host(const uint16_t* w, int32_t rows, int32_t cols,
                            const uint16_t* codebook, uint8_t* codes, uint16_t* scales,
                            int32_t threads);

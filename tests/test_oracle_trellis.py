@@ -115,3 +115,9 @@ def test_library_host_encoder_matches_the_oracle():
     oc, os_ = T.pack_trellis(W, cb)
     assert np.array_equal(scales.view(np.uint16), os_.view(np.uint16))
     assert np.array_equal(codes, oc)
+    # columns are handed out one at a time: any thread count gives the same
+    for th in (1, 8):
+        c2 = np.zeros_like(codes)
+        s2 = np.zeros_like(scales)
+        spax.pack_trellis_host(W, 256, 5, cb, c2, s2, threads=th)
+        assert np.array_equal(c2, codes) and np.array_equal(s2.view(np.uint16), scales.view(np.uint16))
