@@ -26,8 +26,8 @@ from typing import List, Sequence, Tuple
 
 import numpy as np
 
-from . import (FMT_FP16, FMT_INT2_G128, FMT_INT4_G128, FMT_NONE, FMT_SIGN2, Matrix,
-               gemv_workspace_bytes, plan_tiers, tiered_gemv)
+from . import (FMT_FP16, FMT_INT2_G128, FMT_INT4_G128, FMT_NONE, FMT_SIGN2, FMT_TRELLIS,
+               Matrix, gemv_workspace_bytes, plan_tiers, tiered_gemv)
 
 __all__ = ["column_bytes", "rho_of", "k_mid_for_budget", "grid", "Group", "step2", "step1",
            "layer_budget"]
@@ -43,6 +43,8 @@ def column_bytes(fmt: int, rows: int) -> int:
         return rows // 4 + 2 * (rows // 128)
     if fmt == FMT_SIGN2:
         return rows // 4 + 4
+    if fmt == FMT_TRELLIS:   # the codebook is shared by every column
+        return rows // 4 + 2
     if fmt == FMT_NONE:
         return 0
     raise ValueError(fmt)

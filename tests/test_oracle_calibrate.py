@@ -76,3 +76,18 @@ def test_step1_reduces_a_group_that_costs_nothing_first():
     budgets2, rounds2 = C.step1_greedy(err_of, dense, 30)
     assert rounds2[:20] == rounds and budgets2 == [60, 0]
     assert [b for g, b in rounds2 if g == 0] == [95, 90, 85, 80, 75, 70, 65, 60]
+
+
+def test_library_calibration_prices_every_format_like_the_workloads():
+    """The library's calibration (Eq. 5's rho) and the workloads' byte
+    accounting count a stored column's bytes the same way, for every tier
+    format (host logic, no GPU)."""
+    import activation_sparse_decode_token_amd as spax
+    from activation_sparse_decode_token_amd import calibrate as K
+    from workloads.accounting import column_bytes
+    names = {spax.FMT_FP16: "fp16", spax.FMT_INT4_G128: "int4", spax.FMT_INT2_G128: "int2",
+             spax.FMT_SIGN2: "sign2", spax.FMT_TRELLIS: "trellis"}
+    for fmt, name in names.items():
+        for rows in (128, 4096, 12288, 28672):
+            assert K.column_bytes(fmt, rows) == column_bytes(name, rows), (name, rows)
+    assert K.column_bytes(spax.FMT_NONE, 4096) == 0
