@@ -59,6 +59,34 @@ def test_step2_grid_matches_the_oracle():
         log(f"step 2 {g}: GPU picks ({kt}, {km}), oracle ({okt}, {okm})")
 
 
+
+def test_step2_with_the_trellis_tier():
+    """Step 2 on a group whose middle tier is trellis-coded: rho from the
+    trellis column bytes (codes plus one fp16 scale), the library's errors
+    against the oracle's, which rebuilds the same codes itself."""
+    import activation_sparse_decode_token_amd as spax
+    import activation_sparse_decode_token_amd.calibrate as K
+    from activation_sparse_decode_token_amd.layouts import build_matrix
+    from tests.spax_testlib import TrellisStore, to_host
+    R, n = 512, 512
+    Wt = WL.weights_fp16(841, 0, "w", R, n, 0.02)
+    cb = WL.trellis_codebook(1)
+    W = build_matrix(to_dev(Wt), spax.FMT_FP16, spax.FMT_TRELLIS, codebook=to_dev(cb))
+    st = TrellisStore(to_host(W._keep[2]), to_host(W._keep[3]), cb)
+    xs = [WL.laplace_fp16(841, t, "x", n, n) for t in range(2)]
+    grp = K.Group(W, [to_dev(x) for x in xs])
+    rho = Fraction(R // 4 + 2, 2 * R)
+    assert K.rho_of(W) == rho
+    (kt, km), table = K.step2(grp, 40, 6)
+    mats = [(O.ColumnStore("fp16", Wt), st)]
+    (okt, okm), otable = C.step2_grid(lambda a, b: C.group_error(mats, xs, a, b), n, 40, rho, 6)
+    assert [r[:2] for r in table] == [r[:2] for r in otable]
+    for (_, _, e), (_, _, oe) in zip(table, otable):
+        assert abs(e - oe) <= 1e-2 * oe + 1e-9, (e, oe)
+    oerr = {r[:2]: r[2] for r in otable}
+    assert oerr[(kt, km)] <= min(oerr.values()) * (1 + 1e-2)
+    log(f"step 2 trellis: GPU picks ({kt}, {km}), oracle ({okt}, {okm})")
+
 def test_step1_rounds_match_the_oracle():
     import activation_sparse_decode_token_amd.calibrate as K
     stored, xs = _layer()
