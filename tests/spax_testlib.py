@@ -146,3 +146,15 @@ class TrellisStore:
         from oracle.spax_trellis import dequant_trellis
         idx = np.asarray(idx, dtype=np.int64)
         return dequant_trellis(self.codes[idx], self.scales[idx], self.cb)
+
+
+class RowsOf:
+    """Some rows of a store whose columns are rebuilt whole (the trellis
+    window runs down the stored column)."""
+
+    def __init__(self, inner, rows):
+        self.inner, self.rows_idx = inner, np.asarray(rows)
+        self.fmt, self.rows = inner.fmt, len(self.rows_idx)
+
+    def columns(self, idx):
+        return self.inner.columns(idx)[:, self.rows_idx]

@@ -4,7 +4,7 @@ import pytest
 
 import oracle as O
 import workloads as WL
-from tests.spax_testlib import (TrellisStore, check_product, log, sample_groups, to_dev,
+from tests.spax_testlib import (RowsOf, TrellisStore, check_product, log, sample_groups, to_dev,
                                 to_host)
 
 pytestmark = pytest.mark.gpu
@@ -81,18 +81,6 @@ def _run_layer(L, h, z, x, ws=None, copy_stream=None):
     res["lists"] = [(to_host(out["F"][g])[:L.k_full[g]], to_host(out["A"][g])[:L.k_approx[g]])
                     for g in range(4)]
     return res, ws
-
-
-class RowsOf:
-    """Some rows of a store whose columns are rebuilt whole (the trellis
-    window runs down the stored column)."""
-
-    def __init__(self, inner, rows):
-        self.inner, self.rows_idx = inner, np.asarray(rows)
-        self.fmt, self.rows = inner.fmt, len(self.rows_idx)
-
-    def columns(self, idx):
-        return self.inner.columns(idx)[:, self.rows_idx]
 
 
 def _check_layer(res, w: LayerWeights, ks, h, z, x, ff, af, label, rows_per=None, L=None):

@@ -12,7 +12,8 @@ import pytest
 import oracle as O
 import oracle.spax_trellis as T
 import workloads as WL
-from tests.spax_testlib import TrellisStore, check_product, log, to_dev, to_host
+from tests.spax_testlib import (RowsOf, TrellisStore, check_product, log, sample_groups, to_dev,
+                                 to_host)
 
 pytestmark = pytest.mark.gpu
 
@@ -191,3 +192,51 @@ def test_gpu_encoder_matches_oracle_and_host_encoder():
     assert np.array_equal(s2.view(np.uint16), hs.view(np.uint16))
     assert np.array_equal(c2, hc)
     log("GPU trellis encoder == oracle / host encoder")
+
+
+def test_full_size_7b_attention_trellis():
+    """The 7B attention projections with the trellis tier at full size (o:
+    4096 x 4096; q, k, v stacked: 12288 x 4096; 40/30/30 %), in the launch the
+    benchmark times (a one-group layer step, which ranks x inside the
+    product; codes from the GPU encoder): lists bit-exact; whole 128-row
+    groups of y against the oracle, which rebuilds those columns from the
+    codes itself."""
+    import torch
+    import activation_sparse_decode_token_amd as spax
+    import activation_sparse_decode_token_amd.layouts as LY
+    from activation_sparse_decode_token_amd.layouts import build_matrix
+    dev = torch.device("cuda:0")
+    cb = WL.trellis_codebook(1)
+    n = 4096
+    kf, ka = WL.tier_counts(n, WL.CONFIGS[2].splits[0])
+    saved = LY.TRELLIS_WS_BYTES
+    LY.TRELLIS_WS_BYTES = 8 << 30    # backpointers of 160+ columns per encoder launch
+    try:
+        for R, stacked, label in [(4096, None, "7B o-proj trellis"),
+                                  (12288, ("q", "k", "v"), "7B qkv stacked trellis")]:
+            if stacked is None:
+                Wt = WL.weights_fp16(2, 0, "w", R, n, 0.02)
+            else:
+                Wt = np.concatenate([WL.weights_fp16(2, 0, m, R // 3, n, 0.02) for m in stacked],
+                                    axis=1)
+            W = build_matrix(to_dev(Wt), spax.FMT_FP16, spax.FMT_TRELLIS, codebook=to_dev(cb))
+            st = TrellisStore(to_host(W._keep[2]), to_host(W._keep[3]), cb)
+            rows = sample_groups(R, 8, 14 + R)
+            full = O.ColumnStore("fp16", np.ascontiguousarray(Wt[:, rows]))
+            L = spax.Layer.make([W, None, None, None], [kf, 0, 0, 0], [ka, 0, 0, 0])
+            ws = torch.zeros(spax.layer_workspace_bytes(L), dtype=torch.uint8, device=dev)
+            Fd = torch.empty(kf, dtype=torch.int32, device=dev)
+            Ad = torch.empty(ka, dtype=torch.int32, device=dev)
+            y = torch.empty(R, dtype=torch.float16, device=dev)
+            x = WL.laplace_fp16(2, 0, "x", 0, n)
+            io = spax.LayerIO.make(h=to_dev(x), qkv=y, full_idx=(Fd, None, None, None),
+                                   approx_idx=(Ad, None, None, None))
+            spax.layer_step(L, io, ws)
+            torch.cuda.synchronize()
+            F, A = O.plan_tiers(x, kf, ka)
+            assert np.array_equal(to_host(Fd), F) and np.array_equal(to_host(Ad), A), label
+            err = check_product(to_host(y), x, F, A, full, RowsOf(st, rows), label, rows=rows)
+            assert np.all(np.isfinite(to_host(y).astype(np.float32)))
+            log(f"{label}: norm-wise error {err:.2e} (kf={kf} ka={ka})")
+    finally:
+        LY.TRELLIS_WS_BYTES = saved
