@@ -16,10 +16,12 @@ __all__ = [
     "FMT_NONE", "FMT_FP16", "FMT_INT4_G128", "FMT_INT2_G128", "FMT_SIGN2", "FMT_TRELLIS",
     "RES_DEVICE", "RES_HOST_PINNED", "LAYOUT_PLAIN", "LAYOUT_GLU_INTERLEAVED",
     "GROUP_QKV", "GROUP_O", "GROUP_GATE_UP", "GROUP_DOWN",
-    "Matrix", "Layer", "LayerIO",
+    "Matrix", "Layer", "LayerIO", "Copy",
+    "KERNEL_AUTO", "KERNEL_SEPARATE", "KERNEL_PER_GROUP",
     "plan_tiers", "tiered_gemv", "gemv_workspace_bytes", "layer_step",
     "layer_workspace_bytes", "pack_g128", "pack_sign2", "pack_trellis_host", "pack_trellis",
-    "workspace_clear", "version",
+    "workspace_clear", "version", "copy_init", "copy_release", "layer_schedule",
+    "workspace_status",
     "status_string", "last_error", "EXPORTS",
 ]
 
@@ -27,7 +29,10 @@ FMT_NONE, FMT_FP16, FMT_INT4_G128, FMT_INT2_G128, FMT_SIGN2, FMT_TRELLIS = 0, 1,
 RES_DEVICE, RES_HOST_PINNED = 0, 1
 LAYOUT_PLAIN, LAYOUT_GLU_INTERLEAVED = 0, 1
 GROUP_QKV, GROUP_O, GROUP_GATE_UP, GROUP_DOWN = 0, 1, 2, 3
-KERNEL_AUTO, KERNEL_SEPARATE = 0, 1
+KERNEL_AUTO, KERNEL_SEPARATE, KERNEL_PER_GROUP = 0, 1, 2
+COPY_CHUNKS = 4
+# Fields of one spax_layer_schedule record.
+SCHEDULE_FIELDS = ("workgroup", "group", "tile", "f0", "f1", "a0", "a1", "w_lo", "w_hi")
 MAX_ROWS = 1 << 20
 
 STATUS = {0: "SPAX_OK", -1: "SPAX_EINVAL", -2: "SPAX_ENULL", -3: "SPAX_EALIGN",
@@ -40,7 +45,7 @@ EXPORTS = (
     "spax_layer_workspace_bytes", "spax_layer_step", "spax_pack_g128", "spax_pack_sign2",
     "spax_pack_trellis_host", "spax_pack_trellis", "spax_pack_trellis_workspace_bytes",
     "spax_workspace_clear", "spax_status_string", "spax_last_error", "spax_version",
-    "spax_set_kernel_choice",
+    "spax_copy_init", "spax_copy_release", "spax_layer_schedule", "spax_workspace_status",
 )
 
 library_path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libspax.so")
@@ -98,20 +103,34 @@ class Matrix(ctypes.Structure):
 
 
 class Layer(ctypes.Structure):
+    """spax_layer: the four groups, their tier counts, the launch form
+    (KERNEL_AUTO: the one-launch layer kernel where it applies) and the
+    layer kernel's workgroup cap (0: one per compute unit)."""
     _fields_ = [("group", Matrix * 4), ("k_full", ctypes.c_int32 * 4),
-                ("k_approx", ctypes.c_int32 * 4)]
+                ("k_approx", ctypes.c_int32 * 4), ("kernel", ctypes.c_int32),
+                ("workgroups", ctypes.c_int32)]
 
     @classmethod
     def make(cls, groups: Sequence[Optional[Matrix]], k_full: Sequence[int],
-             k_approx: Sequence[int]) -> "Layer":
+             k_approx: Sequence[int], kernel: int = KERNEL_AUTO,
+             workgroups: int = 0) -> "Layer":
         L = cls()
         for g in range(4):
             if groups[g] is not None:
                 L.group[g] = groups[g]
             L.k_full[g] = int(k_full[g])
             L.k_approx[g] = int(k_approx[g])
+        L.kernel = int(kernel)
+        L.workgroups = int(workgroups)
         L._keep = tuple(groups)
         return L
+
+
+class Copy(ctypes.Structure):
+    """spax_copy: the copy stream and events of host-resident products, set
+    up once by copy_init and released by copy_release."""
+    _fields_ = [("stream", ctypes.c_void_p), ("ready", ctypes.c_void_p),
+                ("chunk", ctypes.c_void_p * COPY_CHUNKS), ("device", ctypes.c_int32)]
 
 
 class LayerIO(ctypes.Structure):
@@ -171,11 +190,12 @@ def _declare(L: ctypes.CDLL) -> None:
     L.spax_gemv_workspace_bytes.argtypes = [ctypes.POINTER(Matrix)]
     L.spax_gemv_workspace_bytes.restype = sz
     L.spax_tiered_gemv.argtypes = [ctypes.POINTER(Matrix), vp, vp, i32, vp, i32, vp, vp, sz,
-                                   vp, vp]
+                                   vp, ctypes.POINTER(Copy)]
     L.spax_tiered_gemv.restype = ctypes.c_int
     L.spax_layer_workspace_bytes.argtypes = [ctypes.POINTER(Layer)]
     L.spax_layer_workspace_bytes.restype = sz
-    L.spax_layer_step.argtypes = [ctypes.POINTER(Layer), ctypes.POINTER(LayerIO), vp, sz, vp, vp]
+    L.spax_layer_step.argtypes = [ctypes.POINTER(Layer), ctypes.POINTER(LayerIO), vp, sz, vp,
+                                  ctypes.POINTER(Copy)]
     L.spax_layer_step.restype = ctypes.c_int
     L.spax_pack_g128.argtypes = [vp, i32, i32, i32, vp, vp, vp]
     L.spax_pack_g128.restype = ctypes.c_int
@@ -195,19 +215,21 @@ def _declare(L: ctypes.CDLL) -> None:
     L.spax_last_error.restype = ctypes.c_char_p
     L.spax_version.argtypes = []
     L.spax_version.restype = ctypes.c_int
-    L.spax_set_kernel_choice.argtypes = [i32]
-    L.spax_set_kernel_choice.restype = ctypes.c_int
+    L.spax_copy_init.argtypes = [ctypes.POINTER(Copy), vp]
+    L.spax_copy_init.restype = ctypes.c_int
+    L.spax_copy_release.argtypes = [ctypes.POINTER(Copy)]
+    L.spax_copy_release.restype = ctypes.c_int
+    i64 = ctypes.c_int64
+    L.spax_layer_schedule.argtypes = [ctypes.POINTER(Layer), i32, vp, i64, ctypes.POINTER(i64)]
+    L.spax_layer_schedule.restype = ctypes.c_int
+    L.spax_workspace_status.argtypes = [vp, vp, i32, ctypes.POINTER(ctypes.c_uint32)]
+    L.spax_workspace_status.restype = ctypes.c_int
 
 
 # ---------------------------------------------------------------- entry points
 
 def version() -> int:
     return lib().spax_version()
-
-
-def set_kernel_choice(choice: int) -> None:
-    """spax_set_kernel_choice: fused or separate selection in layer_step (KERNEL_*)."""
-    _check(lib().spax_set_kernel_choice(int(choice)), "spax_set_kernel_choice")
 
 
 def status_string(status: int) -> str:
@@ -229,14 +251,31 @@ def gemv_workspace_bytes(W: Matrix) -> int:
     return int(lib().spax_gemv_workspace_bytes(ctypes.byref(W)))
 
 
+def copy_init(copy_stream) -> Copy:
+    """spax_copy_init: events for host-resident products on the current
+    device, with the given copy stream (kept alive by the returned object)."""
+    c = Copy()
+    _check(lib().spax_copy_init(ctypes.byref(c), _stream(copy_stream)), "spax_copy_init")
+    c._keep = copy_stream
+    return c
+
+
+def copy_release(c: Copy) -> None:
+    """spax_copy_release: destroys the events of copy_init."""
+    _check(lib().spax_copy_release(ctypes.byref(c)), "spax_copy_release")
+
+
+def _copy_arg(copy: Optional[Copy]):
+    return None if copy is None else ctypes.byref(copy)
+
+
 def tiered_gemv(W: Matrix, x, full_idx, k_full, approx_idx, k_approx, y, ws, ws_bytes=None,
-                stream=None, copy_stream=None) -> None:
+                stream=None, copy: Optional[Copy] = None) -> None:
     """spax_tiered_gemv: y = W[:,F] x_F + W^[:,A] x_A (fp32 accumulate, fp16 out)."""
     nbytes = ws.numel() * ws.element_size() if ws_bytes is None else ws_bytes
-    cs = None if copy_stream is None else _stream(copy_stream)
     _check(lib().spax_tiered_gemv(ctypes.byref(W), _ptr(x), _ptr(full_idx), int(k_full),
                                   _ptr(approx_idx), int(k_approx), _ptr(y), _ptr(ws),
-                                  int(nbytes), _stream(stream), cs),
+                                  int(nbytes), _stream(stream), _copy_arg(copy)),
            "spax_tiered_gemv")
 
 
@@ -245,13 +284,35 @@ def layer_workspace_bytes(L: Layer) -> int:
 
 
 def layer_step(L: Layer, io: LayerIO, ws, ws_bytes=None, compute_stream=None,
-               copy_stream=None) -> None:
+               copy: Optional[Copy] = None) -> None:
     """spax_layer_step: the four ranking groups of one decoder layer."""
     nbytes = ws.numel() * ws.element_size() if ws_bytes is None else ws_bytes
-    cs = None if copy_stream is None else _stream(copy_stream)
     _check(lib().spax_layer_step(ctypes.byref(L), ctypes.byref(io), _ptr(ws), int(nbytes),
-                                 _stream(compute_stream), cs),
+                                 _stream(compute_stream), _copy_arg(copy)),
            "spax_layer_step")
+
+
+def layer_schedule(L: Layer, workgroups: int = 0):
+    """spax_layer_schedule: the layer kernel's work pieces as an int32 array
+    of shape [count, 9] (fields SCHEDULE_FIELDS)."""
+    import numpy as np
+    count = ctypes.c_int64(0)
+    _check(lib().spax_layer_schedule(ctypes.byref(L), int(workgroups), None, 0,
+                                     ctypes.byref(count)), "spax_layer_schedule")
+    out = np.zeros((count.value, 9), dtype=np.int32)
+    if count.value:
+        _check(lib().spax_layer_schedule(ctypes.byref(L), int(workgroups), out.ctypes.data,
+                                         count.value, ctypes.byref(count)),
+               "spax_layer_schedule")
+    return out
+
+
+def workspace_status(ws, stream=None, reset: bool = False) -> int:
+    """spax_workspace_status: the layer kernel's sticky status bits in ws."""
+    v = ctypes.c_uint32(0)
+    _check(lib().spax_workspace_status(_ptr(ws), _stream(stream), int(bool(reset)),
+                                       ctypes.byref(v)), "spax_workspace_status")
+    return int(v.value)
 
 
 def pack_g128(w, rows, cols, fmt, codes, scales, stream=None) -> None:

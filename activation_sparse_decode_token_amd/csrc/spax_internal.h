@@ -52,6 +52,8 @@ enum ListMode : int32_t {
   kListRank = 2,    // every workgroup ranks x itself (fused selection)
   kListSliced = 3,  // thresholds and slice counts from the sliced selection;
                     // every workgroup places its piece from its slices
+  kListPacked = 4,  // the layer kernel's whole ranked lists in LDS, 16-bit
+                    // column indices; activations read from the input
 };
 
 // Arguments of one launch of the tiered product.

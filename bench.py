@@ -64,6 +64,8 @@ if ROOT not in sys.path:
 METRIC = ("µs per tiered projection & effective weight GB/s (% of HBM peak), "
           "batch-1 decode")
 HBM_PEAK_GBS = 8000.0
+# spax_layer.kernel of every layer step (SPAX_KERNEL_*; --select)
+KERNEL = 0
 PCIE5_X16_GBS = 64.0
 
 
@@ -231,12 +233,12 @@ class Workload:
                 mats[3] = build_matrix(d, ff, af, residency=res)
                 del d
             torch.cuda.synchronize()
-            self.layers.append(spax.Layer.make(mats, kf, ka))
+            self.layers.append(spax.Layer.make(mats, kf, ka, kernel=KERNEL))
             for g in range(4):
                 if mats[g] is not None:
                     only = [None] * 4
                     only[g] = mats[g]
-                    self.single[g].append(spax.Layer.make(only, kf, ka))
+                    self.single[g].append(spax.Layer.make(only, kf, ka, kernel=KERNEL))
                     self.shapes[g] = (mats[g].rows, mats[g].cols)
             if s % 8 == 7 or s == spec.sets - 1:
                 log(f"  {s + 1}/{spec.sets} weight sets built")
@@ -261,7 +263,7 @@ class Workload:
         wsb = spax.layer_workspace_bytes(self.layers[0])
         self.ws = torch.zeros(wsb, dtype=torch.uint8, device=dev)
         self.ws_bytes = wsb
-        self.copy_stream = torch.cuda.Stream() if spec.host else None
+        self.copy = spax.copy_init(torch.cuda.Stream()) if spec.host else None
         torch.cuda.synchronize()
 
     # bytes the method must move (selected columns, codes and scales, x,
@@ -301,7 +303,7 @@ class Workload:
         spax = self.spax
         for i in range(self.slots):
             spax.layer_step(self.layer_of(i), self.io[i], self.ws, self.ws_bytes,
-                            compute_stream=stream, copy_stream=self.copy_stream)
+                            compute_stream=stream, copy=self.copy)
 
     def launches(self, group: int):
         """The product launches of one group for every slot, back to back."""
@@ -662,8 +664,11 @@ def parse():
     p.add_argument("--calibrate", action="store_true",
                    help="run the offline tier-size calibration (steps 1 and 2) on the 7B "
                         "attention groups instead of the decode benchmark")
-    p.add_argument("--select", choices=("fused", "separate"), default="fused",
-                   help="tier selection inside the product (default) or a separate kernel")
+    p.add_argument("--select", choices=("fused", "layer", "per_group", "separate"),
+                   default="fused",
+                   help="launch form of each layer step: the one-launch layer kernel "
+                        "(fused, the default), one fused launch per group, or a separate "
+                        "selection kernel per group")
     return p.parse_args()
 
 
@@ -674,8 +679,8 @@ def main():
               "(the path has no multi-GPU mode)", file=sys.stderr)
         sys.exit(2)
     if args.select != "fused":
-        import activation_sparse_decode_token_amd as spax
-        spax.set_kernel_choice(spax.KERNEL_SEPARATE)
+        global KERNEL
+        KERNEL = {"layer": 0, "separate": 1, "per_group": 2}[args.select]
     if args.calibrate:
         run_calibrate(args)
         return

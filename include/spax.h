@@ -52,10 +52,12 @@ extern "C" {
 /* Largest matrix height (rows) the product accepts. */
 #define SPAX_MAX_ROWS 1048576
 #define SPAX_EWORKSPACE -5  /* workspace smaller than the *_workspace_bytes()  */
-#define SPAX_ESTREAM    -6  /* host-resident matrix but no copy stream given   */
+#define SPAX_ESTREAM    -6  /* host-resident matrix without a spax_copy set up
+                               on the current device                           */
 #define SPAX_EHIP       -7  /* the HIP runtime reported an error; see
                                spax_last_error()                               */
-#define SPAX_ENOMEM     -8  /* host memory for scratch could not be allocated  */
+#define SPAX_ENOMEM     -8  /* host memory for scratch could not be allocated
+                               (spax_pack_trellis_host)                        */
 
 /* ---- formats, residency, layout ---------------------------------------- */
 #define SPAX_FMT_NONE       0  /* tier absent (its count must be 0)          */
@@ -76,7 +78,8 @@ extern "C" {
  * codebook[index_i] * scale, index_i = (index_{i-1} >> 2) | (c_i << 14),
  * index_{-1} = 0. Approx tier only, with an fp16 full tier. The product
  * keeps the codebook in LDS (its fused ranking then holds list pieces of at
- * most 1024 positions). Produced by spax_pack_trellis_host. */
+ * most 1024 positions). Produced by spax_pack_trellis (GPU) or
+ * spax_pack_trellis_host (host), which give the same bits. */
 #define SPAX_FMT_TRELLIS    5
 
 #define SPAX_RES_DEVICE       0  /* weights in device memory (HBM)            */
@@ -111,6 +114,24 @@ typedef struct spax_matrix {
                                     TRELLIS: [cols]                         */
   const uint16_t* approx_codebook; /* TRELLIS only: device fp16 [65536]     */
 } spax_matrix;
+
+/* ---- host-resident copies ---------------------------------------------- */
+/* The stream and events a host-resident product uses to copy the selected
+ * columns into device staging while the product consumes earlier chunks
+ * (section 5, Figure 2 step 4). spax_copy_init creates the events on the
+ * current device once; the per-token calls only record and wait on them.
+ * spax_copy_release destroys them. The caller owns the stream.
+ *   Errors: SPAX_ENULL, SPAX_EHIP.                                           */
+#define SPAX_COPY_CHUNKS 4
+typedef struct spax_copy {
+  hipStream_t stream;                    /* the copy stream (caller's)       */
+  hipEvent_t ready;                      /* lists ready on the compute stream */
+  hipEvent_t chunk[SPAX_COPY_CHUNKS];    /* chunk k landed in staging        */
+  int32_t device;                        /* device the events belong to      */
+} spax_copy;
+
+int spax_copy_init(spax_copy* copy, hipStream_t copy_stream);
+int spax_copy_release(spax_copy* copy);
 
 /* ---- tier selection ----------------------------------------------------- */
 /* spax_plan_tiers -- rank x by magnitude and split its entries into tiers.
@@ -155,19 +176,21 @@ size_t spax_gemv_workspace_bytes(const spax_matrix* W);
  *              every workspace, so one workspace (sized for the largest
  *              matrix) may serve any mix of matrices and calls. Calls that
  *              share a workspace must be ordered on one stream.
- *   stream     compute stream. copy_stream: required when W is
- *              SPAX_RES_HOST_PINNED (only the selected columns are copied to
- *              device staging inside ws, in chunks overlapped with the
- *              product), ignored otherwise.
+ *   stream     compute stream. copy: required when W is
+ *              SPAX_RES_HOST_PINNED (a spax_copy set up by spax_copy_init on
+ *              this device: only the selected columns are copied to device
+ *              staging inside ws, in chunks overlapped with the product),
+ *              ignored otherwise (may be null).
  *   k_full = k_approx = 0 writes zeros. The result is deterministic: the
  *   same inputs give the same bits, in both residency modes.
  *   Errors: SPAX_ENULL, SPAX_EINVAL, SPAX_EALIGN, SPAX_EFORMAT,
- *   SPAX_EWORKSPACE, SPAX_ESTREAM, SPAX_EHIP.                                */
+ *   SPAX_EWORKSPACE, SPAX_ESTREAM (host-resident W without a copy set up on
+ *   this device), SPAX_EHIP.                                                 */
 int spax_tiered_gemv(const spax_matrix* W, const uint16_t* x,
                      const int32_t* full_idx, int32_t k_full,
                      const int32_t* approx_idx, int32_t k_approx,
                      uint16_t* y, void* ws, size_t ws_bytes,
-                     hipStream_t stream, hipStream_t copy_stream);
+                     hipStream_t stream, const spax_copy* copy);
 
 /* ---- one decoder layer -------------------------------------------------- */
 #define SPAX_GROUP_QKV     0  /* W_q, W_k, W_v stacked row-wise; input h   */
@@ -181,10 +204,45 @@ int spax_tiered_gemv(const spax_matrix* W, const uint16_t* x,
  * SPAX_LAYOUT_GLU_INTERLEAVED; with both present, DOWN must have
  * cols == GATE_UP.rows / 2 and reads the a that GATE_UP writes. DOWN alone
  * reads a caller-provided a (io->a). */
+/* How spax_layer_step runs the groups (per call, field spax_layer.kernel):
+ *   SPAX_KERNEL_AUTO       one launch for the whole layer (the layer kernel:
+ *                          persistent workgroups, one per compute unit, whose
+ *                          ranking waves rank each group's input in LDS while
+ *                          the streaming waves read the previous group's
+ *                          columns) when every present group is
+ *                          device-resident, all groups share one format pair
+ *                          other than the trellis code, every input is at most
+ *                          32768 long and the groups' lists fit its LDS
+ *                          (24576 positions in all); otherwise as
+ *                          SPAX_KERNEL_PER_GROUP;
+ *   SPAX_KERNEL_SEPARATE   per group, the stand-alone selection kernel, then
+ *                          the tiered product reading the lists from memory;
+ *   SPAX_KERNEL_PER_GROUP  per group, one launch whose workgroups each rank
+ *                          the input in LDS (inputs up to 32768 long; longer
+ *                          ones are ranked by three short launches over
+ *                          4096-entry slices first) where the list pieces fit,
+ *                          else as SPAX_KERNEL_SEPARATE. Host-resident groups
+ *                          always take the stand-alone selection and the
+ *                          staged copy.
+ * All compute the same lists; the products agree within the error bound of
+ * spax_tiered_gemv. Each choice is deterministic; SEPARATE and PER_GROUP
+ * add the partial sums in the same order (and host-resident groups give the
+ * same bits as device-resident ones under them), the layer kernel cuts the
+ * columns differently and so may differ from them in the last bits. */
+#define SPAX_KERNEL_AUTO      0
+#define SPAX_KERNEL_SEPARATE  1
+#define SPAX_KERNEL_PER_GROUP 2
+
 typedef struct spax_layer {
   spax_matrix group[4];
   int32_t k_full[4];
   int32_t k_approx[4];
+  int32_t kernel;          /* SPAX_KERNEL_*                                 */
+  int32_t workgroups;      /* layer kernel: most workgroups of the launch;
+                            * 0 = one per compute unit. At most 512 and
+                            * never more than the device's compute units
+                            * (larger values are cut to that: the launch
+                            * needs all of its workgroups resident).      */
 } spax_layer;
 
 /* Inputs, outputs and per-group tier lists (all device pointers). */
@@ -210,29 +268,41 @@ size_t spax_layer_workspace_bytes(const spax_layer* L);
  * math on the fp16 g and u, one rounding); a -> down.
  *   SpAx page section 2 (matrices and inputs), sections 5.2-5.3 (groups).
  *   ws / ws_bytes as for spax_tiered_gemv, sized by
- *   spax_layer_workspace_bytes(L). copy_stream is required when any group is
- *   host-resident. Deterministic. Errors: as spax_tiered_gemv.              */
+ *   spax_layer_workspace_bytes(L). copy is required when any group is
+ *   host-resident. L->kernel picks the launch form (SPAX_KERNEL_*).
+ *   The layer kernel waits, inside the launch, for the gate/up tiles before
+ *   ranking a; it assumes its workgroups (one per compute unit) run at the
+ *   same time, i.e. no other work holds compute units for long while it
+ *   runs. Its waits are bounded: one that runs out sets a bit of the
+ *   workspace status (spax_workspace_status) and the results of that call
+ *   are not valid. Deterministic.
+ *   Errors: as spax_tiered_gemv; SPAX_EINVAL for an unknown L->kernel or
+ *   L->workgroups outside [0, 512].                                          */
 int spax_layer_step(const spax_layer* L, const spax_layer_io* io,
                     void* ws, size_t ws_bytes,
-                    hipStream_t compute_stream, hipStream_t copy_stream);
+                    hipStream_t compute_stream, const spax_copy* copy);
 
-/* spax_set_kernel_choice -- how spax_layer_step runs a group whose weights
- * are device-resident (process-wide; set it before concurrent calls, not
- * during them):
- *   SPAX_KERNEL_AUTO      inputs up to 32768 long: the tiered product ranks
- *                         the input itself (every workgroup selects the tiers
- *                         in LDS) where the list pieces fit; longer inputs:
- *                         the selection runs first as four short launches over
- *                         4096-entry slices (workspace scratch), then the
- *                         tiered product reads the lists; otherwise as below;
- *   SPAX_KERNEL_SEPARATE  always the stand-alone selection kernel, then the
- *                         tiered product reading the lists from memory.
- * Both compute the same lists; the products agree within the error bound of
- * spax_tiered_gemv (bitwise when both cut the lists into the same splits).
- * Errors: SPAX_EINVAL for an unknown value.                                 */
-#define SPAX_KERNEL_AUTO     0
-#define SPAX_KERNEL_SEPARATE 1
-int spax_set_kernel_choice(int32_t choice);
+/* spax_layer_schedule -- the layer kernel's work schedule, for inspection
+ * (host only, enqueues nothing). For every workgroup w of `workgroups`
+ * (0: the number the library would launch on the current device) and every
+ * piece of work in processing order, 9 int32 values: w, group id (SPAX_GROUP_*),
+ * row tile, first and end full-tier list positions, first and end
+ * approx-tier list positions, and the first and last workgroup that work on
+ * the same tile. Tile t covers stored rows [512 t, 512 t + 512); a
+ * workgroup's positions of a tile index the ascending tier lists of the
+ * group. Writes at most `cap` records to `out` (may be null with cap 0) and
+ * the total number of records to *count.
+ *   Errors: SPAX_ENULL, SPAX_EINVAL (the layer kernel does not apply to L,
+ *   or workgroups out of range), SPAX_EHIP (workgroups 0 without a device). */
+int spax_layer_schedule(const spax_layer* L, int32_t workgroups, int32_t* out, int64_t cap,
+                        int64_t* count);
+
+/* spax_workspace_status -- the sticky status bits the layer kernel leaves in
+ * a workspace (0: none; bit 0: an LDS wait ran out, bit 1: the wait for the
+ * gate/up tiles ran out). Copies 4 bytes to the host and synchronises the
+ * stream. reset != 0 also clears the bits.
+ *   Errors: SPAX_ENULL, SPAX_EHIP.                                           */
+int spax_workspace_status(void* ws, hipStream_t stream, int32_t reset, uint32_t* status);
 
 /* ---- offline helpers ---------------------------------------------------- */
 /* spax_pack_g128 -- encode the compressed copy of a matrix (SpAx page

@@ -20,13 +20,14 @@ def golden_dir():
     return GOLDEN
 
 
-@pytest.fixture(params=["fused", "separate"])
+# spax_layer.kernel values (SPAX_KERNEL_*), by test id
+KERNELS = {"layer": 0, "separate": 1, "per_group": 2}
+
+
+@pytest.fixture(params=["layer", "per_group", "separate"])
 def kernel_choice(request):
-    """Runs a GPU test once with the selection fused into the product (the
-    default of spax_layer_step) and once with the stand-alone selection
-    kernel followed by the list-reading product."""
-    import activation_sparse_decode_token_amd as spax
-    spax.set_kernel_choice({"fused": spax.KERNEL_AUTO,
-                            "separate": spax.KERNEL_SEPARATE}[request.param])
-    yield request.param
-    spax.set_kernel_choice(spax.KERNEL_AUTO)
+    """Runs a GPU test once per launch form of spax_layer_step: the one-launch
+    layer kernel (the default), one fused rank + product launch per group,
+    and the stand-alone selection kernel followed by the list-reading
+    product. Returns the spax_layer.kernel value."""
+    return KERNELS[request.param]

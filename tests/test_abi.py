@@ -30,12 +30,13 @@ def test_library_loads_and_exports_every_declared_symbol():
     assert declared == sorted(spax.EXPORTS)
     for name in declared:
         assert hasattr(L, name), name
-    assert spax.version() == 100
+    assert spax.version() == 200
 
 
 def test_status_strings():
-    for code in range(0, -8, -1):
+    for code in range(0, -9, -1):
         assert spax.status_string(code) not in ("", "unknown status")
+    assert "memory" in spax.status_string(-8)
     assert spax.status_string(-99) == "unknown status"
 
 
@@ -48,11 +49,12 @@ def _matrix(rows=4096, cols=4096, ff=spax.FMT_FP16, af=spax.FMT_INT4_G128,
 def test_workspace_sizes():
     W = _matrix()
     ws = spax.gemv_workspace_bytes(W)
-    # fixed counter region (2048 tiles x 9 counters), the sliced selection's
-    # region (16 slices of 256 + 256 + 4 counts, 8 results; 256-byte padded),
-    # 64 splits of fp32 partials
+    # fixed counter region (2048 tiles x 9 counters), the layer kernel's sync
+    # words (256 bytes), the sliced selection's region (16 slices of 256 +
+    # 256 + 4 counts, 8 results; 256-byte padded), 64 splits of fp32 partials
     sel = (16 * (256 + 256 + 4) * 4 + 8 * 4 + 255) // 256 * 256
-    assert ws == 2048 * 9 * 4 + sel + 64 * 4096 * 4
+    head = 2048 * 9 * 4 + 256 + sel
+    assert ws == head + 64 * 4096 * 4
     Wh = _matrix(res=spax.RES_HOST_PINNED)
     assert spax.gemv_workspace_bytes(Wh) >= ws + 4096 * 2 * 4096
     bad = _matrix(rows=100)
@@ -61,12 +63,13 @@ def test_workspace_sizes():
     Ws = _matrix(af=spax.FMT_SIGN2, res=spax.RES_HOST_PINNED)
     assert spax.gemv_workspace_bytes(Ws) == spax.gemv_workspace_bytes(Wh)
     L = spax.Layer.make([W, _matrix(), None, None], [1, 1, 0, 0], [1, 1, 0, 0])
-    assert spax.layer_workspace_bytes(L) == ws
+    # the layer kernel: per group (tiles + 512 workgroups) x 512 rows of fp32
+    assert spax.layer_workspace_bytes(L) == head + 2 * (8 + 512) * 512 * 4
 
 
-def _gemv(W, x=P, fidx=P, kf=10, aidx=P, ka=10, y=P, ws=P2, ws_bytes=1 << 30, cs=None):
+def _gemv(W, x=P, fidx=P, kf=10, aidx=P, ka=10, y=P, ws=P2, ws_bytes=1 << 30, cp=None):
     return spax.lib().spax_tiered_gemv(ctypes.byref(W), x, fidx, kf, aidx, ka, y, ws, ws_bytes,
-                                       None, cs)
+                                       None, cp)
 
 
 def test_gemv_validation_errors():
@@ -95,6 +98,8 @@ def test_gemv_validation_errors():
     assert _gemv(_matrix(af=spax.FMT_SIGN2), ws_bytes=1024) == -5
     assert _gemv(W, ws_bytes=1024) == -5
     assert _gemv(_matrix(res=spax.RES_HOST_PINNED)) == -6
+    # a copy context that was never set up (no stream, no events)
+    assert _gemv(_matrix(res=spax.RES_HOST_PINNED), cp=ctypes.byref(spax.Copy())) == -6
     assert _gemv(_matrix(layout=spax.LAYOUT_GLU_INTERLEAVED, rows=128 * 3)) == -1
     assert spax.lib().spax_tiered_gemv(None, P, P, 1, P, 1, P, P, 1 << 30, None, None) == -2
 
@@ -139,6 +144,13 @@ def test_layer_and_helper_validation_errors():
                             approx_idx=(P,) * 4)
     assert f(ctypes.byref(L), ctypes.byref(io2), P2, 1 << 30, None, None) == -2
     assert f(None, ctypes.byref(io), P2, 1 << 30, None, None) == -2
+    # an unknown launch form
+    L = spax.Layer.make([W, None, gu, dn], [1] * 4, [1] * 4, kernel=7)
+    assert f(ctypes.byref(L), ctypes.byref(io), P2, 1 << 30, None, None) == -1
+    # a workgroup cap past the partial-sum region, or negative
+    for wg in (-1, 513):
+        L = spax.Layer.make([W, None, gu, dn], [1] * 4, [1] * 4, workgroups=wg)
+        assert f(ctypes.byref(L), ctypes.byref(io), P2, 1 << 30, None, None) == -1
     g = spax.lib().spax_pack_g128
     assert g(P, 4096, 16, spax.FMT_FP16, P, P, None) == -4
     assert g(P, 100, 16, spax.FMT_INT4_G128, P, P, None) == -1
@@ -157,6 +169,15 @@ def test_layer_and_helper_validation_errors():
     assert c(P, 6, None) == -1
     assert c(None, 8, None) == -2
     assert c(P, 0, None) == 0
+    st = spax.lib().spax_workspace_status
+    assert st(None, None, 0, ctypes.byref(ctypes.c_uint32())) == -2
+    assert st(P, None, 0, None) == -2
+    # the copy context: a stream is required; releasing an empty one is a no-op
+    ci = spax.lib().spax_copy_init
+    assert ci(ctypes.byref(spax.Copy()), None) == -2
+    assert ci(None, P) == -2
+    assert spax.lib().spax_copy_release(ctypes.byref(spax.Copy())) == 0
+    assert spax.lib().spax_copy_release(None) == -2
 
 
 def test_python_wrapper_raises_with_status():

@@ -18,14 +18,14 @@ pytestmark = pytest.mark.gpu
 FMT = {"fp16": 1, "int4": 2, "int2": 3, "sign2": 4, "none": 0}
 
 
-def _one_group(Wt, x, ff, af, kf, ka, ws=None):
+def _one_group(Wt, x, ff, af, kf, ka, ws=None, kernel=0):
     import torch
     import activation_sparse_decode_token_amd as spax
     from activation_sparse_decode_token_amd.layouts import build_matrix
     dev = torch.device("cuda:0")
     n, R = Wt.shape
     W = build_matrix(to_dev(Wt), FMT[ff], FMT[af])
-    L = spax.Layer.make([W, None, None, None], [kf, 0, 0, 0], [ka, 0, 0, 0])
+    L = spax.Layer.make([W, None, None, None], [kf, 0, 0, 0], [ka, 0, 0, 0], kernel=kernel)
     F = torch.full((max(kf, 1) + 8,), -7, dtype=torch.int32, device=dev)
     A = torch.full((max(ka, 1) + 8,), -7, dtype=torch.int32, device=dev)
     y = torch.full((R,), 0x7E00, dtype=torch.int16, device=dev)
@@ -40,15 +40,15 @@ def _one_group(Wt, x, ff, af, kf, ka, ws=None):
     return to_host(y).view(np.float16), Fh[:kf], Ah[:ka], ws
 
 
-def _check(Wt, x, ff, af, kf, ka, label):
-    y, F, A, ws = _one_group(Wt, x, ff, af, kf, ka)
+def _check(Wt, x, ff, af, kf, ka, label, kernel=0):
+    y, F, A, ws = _one_group(Wt, x, ff, af, kf, ka, kernel=kernel)
     oF, oA = O.plan_tiers(x, kf, ka)
     assert np.array_equal(F, oF), f"{label}: full list"
     assert np.array_equal(A, oA), f"{label}: approx list"
     full = O.ColumnStore(ff, Wt)
     approx = O.ColumnStore(af, Wt) if af != "none" else None
     err = check_product(y, x, oF, oA, full, approx, label)
-    y2, F2, A2, _ = _one_group(Wt, x, ff, af, kf, ka, ws)
+    y2, F2, A2, _ = _one_group(Wt, x, ff, af, kf, ka, ws, kernel=kernel)
     assert np.array_equal(y.view(np.uint16), y2.view(np.uint16)), f"{label}: not reproducible"
     return err
 
@@ -73,7 +73,7 @@ CASES = [
     (1024, 11008, "fp16", "int4", 2752, 2752),
     (640, 16385, "fp16", "int2", 4000, 6000),
     (1024, 28672, "int4", "int2", 5734, 8602),
-    (512, 32768, "fp16", "int4", 9000, 9000),    # sliced selection, 8 slices
+    (512, 32768, "fp16", "int4", 9000, 9000),    # longest input ranked in one workgroup
     (512, 32769, "fp16", "int4", 9000, 9000),    # sliced selection, ragged last slice
     (256, 65536, "fp16", "int2", 20000, 30000),  # longest input: 16 slices
     (128, 6000, "fp16", "none", 6000, 0),        # one tile, one split, long list
@@ -88,12 +88,15 @@ def test_fused_vs_oracle(R, n, ff, af, kf, ka, kernel_choice):
     log(f"fused ({kernel_choice}) R={R} n={n} {ff}/{af} kf={kf} ka={ka}")
     Wt = WL.weights_fp16(820, R, "w", R, n, 0.02)
     x = WL.laplace_fp16(820, R, "x", n % 1000, n)
-    err = _check(Wt, x, ff, af, kf, ka, f"R={R} n={n} {ff}/{af} kf={kf} ka={ka}")
+    err = _check(Wt, x, ff, af, kf, ka, f"R={R} n={n} {ff}/{af} kf={kf} ka={ka}",
+                 kernel=kernel_choice)
     log(f"  norm-wise error {err:.2e}")
 
 
-# 20000: past the fused ranking's limit, so the sliced selection's placement
-@pytest.mark.parametrize("n", [300, 4096, 11008, 20000])
+# 32768: the longest input one workgroup (or the layer kernel) ranks; 32769
+# and 65536: past it, so the sliced selection and its placement (the layer
+# kernel falls back to the per-group launches there)
+@pytest.mark.parametrize("n", [300, 4096, 11008, 20000, 32768, 32769, 65536])
 def test_fused_ties(n, kernel_choice):
     rs = np.random.default_rng(31 + n)
     Wt = WL.weights_fp16(821, 0, "w", 512, n, 0.02)
@@ -106,5 +109,6 @@ def test_fused_ties(n, kernel_choice):
     for name, x in cases.items():
         for kf, ka in [(n // 4, n // 4), (n // 2, 0), (1, n - 1), (n // 3, n // 2)]:
             log(f"fused ties {name} n={n} kf={kf} ka={ka}")
-            _check(Wt, x, "fp16", "int4", kf, ka, f"{name} n={n} kf={kf} ka={ka}")
+            _check(Wt, x, "fp16", "int4", kf, ka, f"{name} n={n} kf={kf} ka={ka}",
+                   kernel=kernel_choice)
 

@@ -29,7 +29,7 @@ class LayerWeights:
         self.down = WL.weights_fp16(cfg, layer, "down", hidden, inter, std)
 
 
-def _build_layer(w: LayerWeights, ff, af, residency, ks):
+def _build_layer(w: LayerWeights, ff, af, residency, ks, kernel=0):
     import torch
     spax = _spax()
     from activation_sparse_decode_token_amd.layouts import build_matrix, glu_interleave, stack_rows
@@ -45,7 +45,7 @@ def _build_layer(w: LayerWeights, ff, af, residency, ks):
     torch.cuda.synchronize()
     kf = [ks[g][0] for g in ("qkv", "o", "ffn", "down")]
     ka = [ks[g][1] for g in ("qkv", "o", "ffn", "down")]
-    return spax.Layer.make([qkv, o, gu, dn], kf, ka)
+    return spax.Layer.make([qkv, o, gu, dn], kf, ka, kernel=kernel)
 
 
 def _io(L, h, z, x):
@@ -69,13 +69,15 @@ def _io(L, h, z, x):
     return io, out
 
 
-def _run_layer(L, h, z, x, ws=None, copy_stream=None):
+def _run_layer(L, h, z, x, ws=None, copy=None):
     import torch
     spax = _spax()
     if ws is None:
         ws = torch.zeros(spax.layer_workspace_bytes(L), dtype=torch.uint8, device="cuda:0")
     io, out = _io(L, h, z, x)
-    spax.layer_step(L, io, ws, copy_stream=copy_stream)
+    spax.layer_step(L, io, ws, copy=copy)
+    torch.cuda.synchronize()
+    assert spax.workspace_status(ws) == 0, "a bounded wait of the layer kernel ran out"
     torch.cuda.synchronize()
     res = {k: to_host(out[k]) for k in ("qkv", "o", "g", "u", "a", "down")}
     res["lists"] = [(to_host(out["F"][g])[:L.k_full[g]], to_host(out["A"][g])[:L.k_approx[g]])
@@ -169,7 +171,7 @@ def test_layer_small(ff, af, kernel_choice):
     hidden, inter = 512, 1408          # ragged tiles: 1408 = 2*512 + 384; gate/up 2816 rows
     w = LayerWeights(810, 0, hidden, inter, 0.02)
     ks = _ks(hidden, inter, WL.TierSplit(40, 30, 30))
-    L = _build_layer(w, ff, af, 0, ks)
+    L = _build_layer(w, ff, af, 0, ks, kernel_choice)
     for tok in range(3):
         h = WL.laplace_fp16(810, 0, "h", tok, hidden)
         z = WL.laplace_fp16(810, 0, "z", tok, hidden)
@@ -179,13 +181,47 @@ def test_layer_small(ff, af, kernel_choice):
     log(f"layer small {ff}/{af} ok")
 
 
+@pytest.mark.parametrize("wgs", [1, 2, 5, 37])
+def test_layer_kernel_workgroup_caps(wgs):
+    """The layer kernel on a few workgroups: each one meets many row tiles of
+    a group (several segments per group, the ranking then places whole
+    lists), and at one workgroup q/k/v and o share it."""
+    hidden, inter = 512, 1408
+    w = LayerWeights(811, 0, hidden, inter, 0.02)
+    ks = _ks(hidden, inter, WL.TierSplit(40, 30, 30))
+    L = _build_layer(w, "fp16", "int4", 0, ks, 0)
+    L.workgroups = wgs
+    for tok in range(2):
+        h = WL.laplace_fp16(811, 0, "h", tok, hidden)
+        z = WL.laplace_fp16(811, 0, "z", tok, hidden)
+        x = WL.laplace_fp16(811, 0, "x", tok, hidden)
+        res, _ = _run_layer(L, h, z, x)
+        _check_layer(res, w, ks, h, z, x, "fp16", "int4", f"{wgs} workgroups token {tok}")
+    log(f"layer kernel on {wgs} workgroups ok")
+
+
+def test_layer_kernel_7b_on_37_workgroups():
+    """A full-size 7B layer on 37 workgroups: runs of units that cross many
+    tiles, contributors that differ per tile."""
+    w = LayerWeights(4, 0, 4096, 11008, 0.02)
+    ks = _ks(4096, 11008, WL.CONFIGS[4].splits[0])
+    L = _build_layer(w, "fp16", "int4", 0, ks, 0)
+    L.workgroups = 37
+    h = WL.laplace_fp16(4, 0, "h", 0, 4096)
+    z = WL.laplace_fp16(4, 0, "z", 0, 4096)
+    x = WL.laplace_fp16(4, 0, "x", 0, 4096)
+    res, _ = _run_layer(L, h, z, x)
+    _check_layer(res, w, ks, h, z, x, "fp16", "int4", "7B layer on 37 workgroups", rows_per=True)
+    log("7B layer on 37 workgroups ok")
+
+
 @pytest.mark.parametrize("af", ["int4", "sign2"])
 def test_layer_7b_shapes(kernel_choice, af):
     """A full-size 7B layer step (the launches the benchmarks time), with the
     int4 or the two-scale sign middle tier, on sampled whole row groups."""
     w = LayerWeights(4, 0, 4096, 11008, 0.02)
     ks = _ks(4096, 11008, WL.CONFIGS[4].splits[0])
-    L = _build_layer(w, "fp16", af, 0, ks)
+    L = _build_layer(w, "fp16", af, 0, ks, kernel_choice)
     # (the oracle fits the sign code's scales over whole stored columns: one
     # token keeps that case short)
     for tok in ((0, 1) if af == "int4" else (0,)):
@@ -204,21 +240,24 @@ def test_host_pinned_bitwise_equals_device(ff, af):
     hidden, inter = 1024, 2816
     w = LayerWeights(811, 0, hidden, inter, 0.02)
     ks = _ks(hidden, inter, WL.TierSplit(50, 25, 25))
-    Ld = _build_layer(w, ff, af, 0, ks)
+    # host-resident groups run the per-group launches, which the device-resident
+    # layer gives bit for bit under SPAX_KERNEL_PER_GROUP
+    Ld = _build_layer(w, ff, af, 0, ks, kernel=2)
     Lh = _build_layer(w, ff, af, 1, ks)
     _host_vs_device(w, ks, Ld, Lh, ff, af, hidden)
 
 
 def _host_vs_device(w, ks, Ld, Lh, ff, af, hidden):
     import torch
-    cs = torch.cuda.Stream()
+    spax = _spax()
+    cs = spax.copy_init(torch.cuda.Stream())
     ws_d = ws_h = None
     for tok in range(3):
         h = WL.laplace_fp16(811, 0, "h", tok, hidden)
         z = WL.laplace_fp16(811, 0, "z", tok, hidden)
         x = WL.laplace_fp16(811, 0, "x", tok, hidden)
         rd, ws_d = _run_layer(Ld, h, z, x, ws_d)
-        rh, ws_h = _run_layer(Lh, h, z, x, ws_h, copy_stream=cs)
+        rh, ws_h = _run_layer(Lh, h, z, x, ws_h, copy=cs)
         for k in ("qkv", "o", "g", "u", "a", "down"):
             assert np.array_equal(rd[k].view(np.uint16), rh[k].view(np.uint16)), (k, tok)
         for g in range(4):
@@ -226,4 +265,5 @@ def _host_vs_device(w, ks, Ld, Lh, ff, af, hidden):
                 assert np.array_equal(rd["lists"][g][i], rh["lists"][g][i])
         if tok == 0:
             _check_layer(rh, w, ks, h, z, x, ff, af, f"host {ff}/{af}")
+    spax.copy_release(cs)
     log(f"host-pinned {ff}/{af} == device bitwise")

@@ -29,7 +29,7 @@ def _matrix(Wt, residency=0):
     return W, TrellisStore(codes, scales, cb)
 
 
-def _run(W, x16, F, A, ws=None, copy_stream=None):
+def _run(W, x16, F, A, ws=None, copy=None):
     import torch
     import activation_sparse_decode_token_amd as spax
     dev = torch.device("cuda:0")
@@ -38,7 +38,7 @@ def _run(W, x16, F, A, ws=None, copy_stream=None):
     y = torch.full((W.rows,), 0x7E00, dtype=torch.int16, device=dev)
     Fd = to_dev(F.astype(np.int32)) if len(F) else torch.zeros(1, dtype=torch.int32, device=dev)
     Ad = to_dev(A.astype(np.int32)) if len(A) else torch.zeros(1, dtype=torch.int32, device=dev)
-    spax.tiered_gemv(W, to_dev(x16), Fd, len(F), Ad, len(A), y, ws, copy_stream=copy_stream)
+    spax.tiered_gemv(W, to_dev(x16), Fd, len(F), Ad, len(A), y, ws, copy=copy)
     torch.cuda.synchronize()
     return to_host(y).view(np.float16), ws
 
@@ -76,19 +76,19 @@ def test_trellis_product_vs_oracle(R, n, kf, ka):
     log(f"  norm-wise error {err:.2e}")
 
 
-@pytest.mark.parametrize("choice", [0, 1])
+@pytest.mark.parametrize("choice", [0, 1, 2])
 def test_trellis_layer_step(choice):
-    """A one-group layer with the trellis tier: the layer step ranks with the
-    stand-alone selection, then runs the list-reading product."""
+    """A one-group layer with the trellis tier, under each launch form (the
+    layer kernel does not take the trellis tier: AUTO runs the per-group
+    launch)."""
     import torch
     import activation_sparse_decode_token_amd as spax
-    spax.set_kernel_choice(choice)
-    try:
+    if True:
         R, n = 1024, 512
         Wt = WL.weights_fp16(852, 0, "w", R, n, 0.02)
         W, st = _matrix(Wt)
         kf, ka = WL.tier_counts(n, WL.TierSplit(40, 30, 30))
-        L = spax.Layer.make([W, None, None, None], [kf, 0, 0, 0], [ka, 0, 0, 0])
+        L = spax.Layer.make([W, None, None, None], [kf, 0, 0, 0], [ka, 0, 0, 0], kernel=choice)
         dev = torch.device("cuda:0")
         ws = torch.zeros(spax.layer_workspace_bytes(L), dtype=torch.uint8, device=dev)
         for tok in range(2):
@@ -104,8 +104,6 @@ def test_trellis_layer_step(choice):
             assert np.array_equal(to_host(Fd), F) and np.array_equal(to_host(Ad), A)
             check_product(to_host(y), x, F, A, O.ColumnStore("fp16", Wt), st,
                           f"trellis layer token {tok}")
-    finally:
-        spax.set_kernel_choice(0)
 
 
 def test_trellis_host_pinned_bitwise_equals_device():
@@ -115,13 +113,15 @@ def test_trellis_host_pinned_bitwise_equals_device():
     Wd, st = _matrix(Wt)
     Wh, sth = _matrix(Wt, residency=1)
     assert np.array_equal(st.codes, sth.codes)
-    cs = torch.cuda.Stream()
+    import activation_sparse_decode_token_amd as spax
+    cs = spax.copy_init(torch.cuda.Stream())
     for tok in range(2):
         x = WL.laplace_fp16(853, 0, "x", tok, n)
         F, A = O.plan_tiers(x, 100, 150)
         yd, _ = _run(Wd, x, F, A)
-        yh, _ = _run(Wh, x, F, A, copy_stream=cs)
+        yh, _ = _run(Wh, x, F, A, copy=cs)
         assert np.array_equal(yd.view(np.uint16), yh.view(np.uint16)), tok
+    spax.copy_release(cs)
     log("trellis host-pinned == device bitwise")
 
 
