@@ -16,7 +16,14 @@ LIB = os.path.join(HERE, "libspax.so")
 SOURCES = ["plan.hip", "select.hip", "gemv.hip", "layer.hip", "aux.hip", "api.cpp", "trellis_pack.cpp"]
 # per-source flags: the trellis encoder's fp32 error arithmetic is defined
 # operation by operation (no contraction into fused multiply-adds)
-EXTRA = {"trellis_pack.cpp": ["-ffp-contract=off"]}
+EXTRA = {
+    "trellis_pack.cpp": ["-ffp-contract=off"],
+    # the layer kernel reads its argument struct (736 bytes, in the kernel
+    # argument segment) from many places; past LLVM's default limit of 300
+    # users the compiler keeps a private copy of it in scratch, whose loads
+    # then wait for every global load in flight
+    "layer.hip": ["-mllvm", "-instcombine-max-copied-from-constant-users=100000"],
+}
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 

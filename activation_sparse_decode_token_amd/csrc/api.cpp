@@ -312,13 +312,23 @@ int device_cus(int32_t* out) {
   return SPAX_OK;
 }
 
-// The layer kernel's launch for L on the current device.
-int plan_layer_kernel(const spax_layer* L, LayerArgs* A) {
+// Whether every workgroup of schedule A stays within its segment table in
+// both phases (the second: down, when gate/up runs in the same launch).
+bool layer_segs_fit(const LayerArgs& A) {
+  auto late = [&](int g) { return g == SPAX_GROUP_DOWN && A.down_waits; };
+  return layer_phase_segs_bound(A, [&](int g) { return !late(g); }) <= (uint32_t)kLayerSegTab &&
+         layer_phase_segs_bound(A, late) <= (uint32_t)kLayerSegTab;
+}
+
+// The layer kernel's launch for L on the current device, or *ok = false
+// when a workgroup could meet more segments than its table holds.
+int plan_layer_kernel(const spax_layer* L, LayerArgs* A, bool* ok) {
   int32_t cus = 0;
   const int st = device_cus(&cus);
   if (st) return st;
   const int32_t G = layer_workgroups(cus);
   layer_schedule(L, L->workgroups > 0 ? std::min(L->workgroups, G) : G, A);
+  *ok = layer_segs_fit(*A);
   return SPAX_OK;
 }
 
@@ -629,9 +639,10 @@ int spax_layer_step(const spax_layer* L, const spax_layer_io* io, void* ws, size
   int32_t ff = 0, af = 0;
   if (L->kernel == SPAX_KERNEL_AUTO && layer_fits(L, &ff, &af)) {
     LayerArgs A;
-    const int st = plan_layer_kernel(L, &A);
+    bool ok = false;
+    const int st = plan_layer_kernel(L, &A, &ok);
     if (st) return st;
-    return run_layer_kernel(L, io, ws, ff, af, A, compute_stream);
+    if (ok) return run_layer_kernel(L, io, ws, ff, af, A, compute_stream);
   }
   const bool separate = L->kernel == SPAX_KERNEL_SEPARATE;
   for (int g = 0; g < 4; ++g) {
@@ -697,6 +708,7 @@ int spax_layer_schedule(const spax_layer* L, int32_t workgroups, int32_t* out, i
   }
   LayerArgs A;
   layer_schedule(L, G, &A);
+  if (!layer_segs_fit(A)) return SPAX_EINVAL;
   int64_t n = 0;
   for (int32_t w = 0; w < A.G; ++w) {
     for (int oi = 0; oi < A.n_order; ++oi) {

@@ -17,16 +17,17 @@
 //     adds the contributors' partials in workgroup order and writes the
 //     output (with the SwiGLU epilogue for gate/up). The streaming waves
 //     never wait on global memory round trips of the reduction;
-//   * waves 12..15 rank: for each group the workgroup meets they rank the
-//     group's input (two-level radix select on the fp16 magnitude key, lower
-//     index first among equal keys) and write the whole ascending F and A
-//     lists, with the activations, into LDS. The lists of the next group are
-//     ready before the streaming waves reach it, so only the first ranking
-//     of a launch is on the critical path.
-// Down's input a is complete only when every gate/up tile is: its ranking
-// waits for the count of finished gate/up tiles (a bounded wait; gate/up
-// runs first on every workgroup, so the count is reached while the q/k/v
-// and o columns stream).
+//   * waves 12..15 rank: for each further group the workgroup meets they
+//     rank the group's input (two-level radix select on the fp16 magnitude
+//     key, lower index first among equal keys) and place the list positions
+//     the workgroup reads into LDS, as 16-bit column indices. The lists of
+//     the next group are ready before the streaming waves reach it.
+// The first group a workgroup meets is ranked by all 16 waves before the
+// roles begin. Down's input a is complete only when every gate/up tile is,
+// so down runs in a second phase: once the workgroup's other groups are
+// done, one wave waits for the count of finished gate/up tiles (a bounded
+// wait), all 16 waves rank a, and the streaming and reduction waves run
+// down's segments.
 //
 // Every wait is bounded. A wait that runs out sets a status bit in the
 // workspace and goes on, so the launch always ends. Partial sums are added
@@ -57,16 +58,19 @@ constexpr int kCoherent = 16;
 struct LayerShared {
   uint16_t lists[kLayerListCap];             // every group's F then A lists
   uint16_t keys[kLayerMaxN];                 // ranking: the input's fp16 bits
-  float slot[kNS][kTileRows];                // streaming waves' partials
-  WaveMeta wm[2][kNS];                       // code factors per tier and wave
+  float slot[2][kNS][kTileRows];             // streaming waves' partials
   uint32_t hist[256 * kHistCopies];          // ranking: top-level histogram
   uint32_t sub[256 * kHistCopies];           // ranking: the two sub-histograms
   uint32_t rtot[kRankMaxRounds][4];          // ranking: per-round counts
   uint32_t need[8];                          // ranking: positions to place
+  uint32_t own[4];                           // ranking: positions to store out
   uint64_t rank_out[2];                      // ranking: the caller's lists
+  uint4 segtab[kLayerSegTab];                // the phase's segments: g | t << 8,
+                                             // f0 | f1 << 16, a0 | a1 << 16
+  uint32_t nseg;                             // entries of segtab
   uint32_t ready[4];                         // a group's lists are in LDS
   uint32_t rbar;                             // ranking waves' barrier count
-  uint32_t seg_arrive;                       // streaming-wave arrivals
+  uint32_t seg_arrive[2];                    // streaming-wave arrivals per slot set
   uint32_t seg_free;                         // segments whose slots were read
 };
 static_assert(sizeof(LayerShared) <= 160 * 1024, "LDS of one workgroup");
@@ -74,8 +78,27 @@ static_assert(sizeof(LayerShared) <= 160 * 1024, "LDS of one workgroup");
 // The workgroup's LDS (one instance per launch of any layer kernel).
 static __shared__ LayerShared g_sm;
 
-__device__ __forceinline__ uint32_t lds_acquire(uint32_t* p) {
-  return __hip_atomic_load(p, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP);
+// The LDS flags order LDS accesses only: their fences are restricted to
+// LDS, so a wave's global loads in flight are not waited for (a full
+// workgroup fence would wait for all of them).
+__device__ __forceinline__ uint32_t lds_relaxed(uint32_t* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+}
+__device__ __forceinline__ void lds_release() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+}
+__device__ __forceinline__ void lds_acquire() {
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+// Adds v to the LDS counter p, after this wave's earlier LDS writes.
+__device__ __forceinline__ void lds_signal_add(uint32_t* p, uint32_t v) {
+  lds_release();
+  __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+}
+// Stores v to the LDS flag p, after this wave's earlier LDS accesses.
+__device__ __forceinline__ void lds_signal_store(uint32_t* p, uint32_t v) {
+  lds_release();
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
 }
 
 __device__ __forceinline__ void set_status(uint32_t* status, uint32_t bit) {
@@ -84,13 +107,14 @@ __device__ __forceinline__ void set_status(uint32_t* status, uint32_t bit) {
 
 // Waits until the LDS word p reaches v (bounded).
 __device__ __forceinline__ void wait_lds_ge(uint32_t* p, uint32_t v, uint32_t* status) {
-  for (uint32_t it = 0; lds_acquire(p) < v; ++it) {
+  for (uint32_t it = 0; lds_relaxed(p) < v; ++it) {
     if (it >= kSpinLds) {
       if ((threadIdx.x & 63) == 0) set_status(status, kStatusLdsWait);
       break;
     }
     __builtin_amdgcn_s_sleep(1);
   }
+  lds_acquire();
 }
 
 // A pointer that is the same in every lane, moved to scalar registers (each
@@ -107,12 +131,6 @@ __device__ __forceinline__ uint32_t uniform(uint32_t v) {
   return (uint32_t)__builtin_amdgcn_readfirstlane((int)v);
 }
 
-// Number of set bits of m in the lanes below this one.
-__device__ __forceinline__ uint32_t lanes_below(uint64_t m) {
-  return __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32),
-                                   __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
-}
-
 // Barrier of the ranking waves: the hardware barrier when every wave of the
 // workgroup ranks, else an LDS count (bounded).
 template <int RW>
@@ -121,8 +139,7 @@ __device__ __forceinline__ void rank_sync(uint32_t& epoch, uint32_t* status) {
     __syncthreads();
   } else {
     epoch += RW;
-    if ((threadIdx.x & 63) == 0)
-      __hip_atomic_fetch_add(&g_sm.rbar, 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
+    if ((threadIdx.x & 63) == 0) lds_signal_add(&g_sm.rbar, 1u);
     wait_lds_ge(&g_sm.rbar, epoch, status);
   }
 }
@@ -137,13 +154,29 @@ __device__ __forceinline__ void hist8(const uint4& v, uint32_t copy) {
   }
 }
 
+// Counts over the 8 keys in v (fp16 magnitude bits): c1 = #(key > t1) |
+// #(key == t1) << 16, c2 the same for t2.
+__device__ __forceinline__ void lane_counts(const uint4& v, uint32_t t1, uint32_t t2,
+                                            uint32_t& c1, uint32_t& c2) {
+  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+  c1 = 0u;
+  c2 = 0u;
+#pragma unroll
+  for (int h = 0; h < 8; ++h) {
+    const uint32_t k = (w[h >> 1] >> (16 * (h & 1))) & 0x7FFFu;
+    c1 += k > t1 ? 1u : (k == t1 ? 0x10000u : 0u);
+    c2 += k > t2 ? 1u : (k == t2 ? 0x10000u : 0u);
+  }
+}
+
 // Ranks x[0, n) on RW waves (the last RW of the workgroup) and places the
 // list positions this workgroup needs: the ascending F list (the K1 largest
 // |x_j|) at list[0, K1) and the A list (the next K2 - K1) at list[K1, K2),
-// one 16-bit column index per entry, each placed entry also stored to the
-// caller's lists. The positions needed are g_sm.need: full-tier positions
-// [need0, need1) and [need2, need3), approx-tier [need4, need5) and
-// [need6, need7). Keys go to LDS once, in rounds of 512 entries (round r on
+// one 16-bit column index per entry. The positions needed are g_sm.need:
+// full-tier positions [need0, need1) and [need2, need3), approx-tier
+// [need4, need5) and [need6, need7); placed entries at full-tier positions
+// [own0, own1) and approx-tier [own2, own3) are also stored to the caller's
+// lists (g_sm.rank_out). Keys go to LDS once, in rounds of 512 entries (round r on
 // ranking wave r mod RW); entries past n are key 0 and are taken out of the
 // counts of key 0 (they come after every real entry, so a boundary at key 0
 // keeps real zeros first). Steps:
@@ -154,12 +187,12 @@ __device__ __forceinline__ void hist8(const uint4& v, uint32_t copy) {
 //   4. each ranking wave finds the boundary keys t1, t2 and the numbers q1,
 //      q2 of entries equal to them that are kept;
 //   5. per round, the counts of key > t1, key == t1, key > t2, key == t2
-//      (ballots and scalar bit counts);
+//      (per-lane counts of its 8 entries, then a wave sum);
 //   6. their exclusive scans over the rounds give each round's range of
-//      list positions; the rounds that meet a needed range are placed in
-//      index order, slot by slot (slot h of round r: entries 512 r + 64 h +
-//      lane): #F before entry i is gt1 + min(eq1, q1), #(F or A) before it
-//      gt2 + min(eq2, q2), counted with ballots and mbcnt.
+//      list positions; in the rounds that meet a needed range, each lane
+//      places its 8 entries (512 r + 8 l + h, h ascending) from its
+//      exclusive counts within the round: #F before entry i is
+//      gt1 + min(eq1, q1), #(F or A) before it gt2 + min(eq2, q2).
 // The histograms are cleared again before the last barrier.
 template <int RW>
 __device__ __attribute__((noinline)) uint32_t rank_group(const uint16_t* __restrict__ x, int n,
@@ -292,77 +325,86 @@ __device__ __attribute__((noinline)) uint32_t rank_group(const uint16_t* __restr
   }
   t1 = uniform(t1); q1 = uniform(q1); t2 = uniform(t2); q2 = uniform(q2);
 
-  // 5. per-round counts (ballots and scalar bit counts)
+  // 5. per-round counts of key > t1, key == t1, key > t2, key == t2: each
+  // lane counts its 8 entries (two counts per register), a wave sum gives
+  // the round's
   for (int r = rw; r < R; r += RW) {
     const uint4 v = *reinterpret_cast<const uint4*>(&sm.keys[r * kRankRound + 8 * lane]);
-    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-    uint32_t c0 = 0u, c1 = 0u, c2 = 0u, c3 = 0u;
-#pragma unroll
-    for (int h = 0; h < 8; ++h) {
-      const uint32_t k = (w[h >> 1] >> (16 * (h & 1))) & 0x7FFFu;
-      c0 += (uint32_t)__builtin_popcountll(__ballot(k > t1));
-      c1 += (uint32_t)__builtin_popcountll(__ballot(k == t1));
-      c2 += (uint32_t)__builtin_popcountll(__ballot(k > t2));
-      c3 += (uint32_t)__builtin_popcountll(__ballot(k == t2));
-    }
-    if (lane == 0) *reinterpret_cast<uint4*>(&sm.rtot[r][0]) = make_uint4(c0, c1, c2, c3);
+    uint32_t c1, c2;
+    lane_counts(v, t1, t2, c1, c2);
+    c1 = wave_incl_scan(c1);
+    c2 = wave_incl_scan(c2);
+    if (lane == 63)
+      *reinterpret_cast<uint4*>(&sm.rtot[r][0]) =
+          make_uint4(c1 & 0xFFFFu, c1 >> 16, c2 & 0xFFFFu, c2 >> 16);
   }
   rank_sync<RW>(epoch, status);
 
   // 6. exclusive scans of the four counts over the rounds (lane l holds
-  // round l), the needed rounds, then placement slot by slot
+  // round l), the needed rounds, then placement: lane l of round r places
+  // its entries 512 r + 8 l + h in order, from the counts before it
   static_assert(kRankMaxRounds <= 64, "one round per lane");
-  uint32_t ex[4], own[4];
+  uint32_t ex[4], inc[4];
   {
     const uint4 u = lane < R ? *reinterpret_cast<const uint4*>(&sm.rtot[lane][0])
                              : make_uint4(0u, 0u, 0u, 0u);
-    own[0] = u.x; own[1] = u.y; own[2] = u.z; own[3] = u.w;
+    const uint32_t own[4] = {u.x, u.y, u.z, u.w};
 #pragma unroll
-    for (int q = 0; q < 4; ++q) ex[q] = wave_incl_scan(own[q]) - own[q];
+    for (int q = 0; q < 4; ++q) {
+      inc[q] = wave_incl_scan(own[q]);
+      ex[q] = inc[q] - own[q];
+    }
   }
   const uint4 nf = *reinterpret_cast<const uint4*>(&sm.need[0]);
   const uint4 na = *reinterpret_cast<const uint4*>(&sm.need[4]);
   const uint32_t nf0 = uniform(nf.x), nf1 = uniform(nf.y), nf2 = uniform(nf.z), nf3 = uniform(nf.w);
   const uint32_t na0 = uniform(na.x), na1 = uniform(na.y), na2 = uniform(na.z), na3 = uniform(na.w);
+  const uint4 ow = *reinterpret_cast<const uint4*>(&sm.own[0]);
+  const uint32_t of0 = uniform(ow.x), of1 = uniform(ow.y), oa0 = uniform(ow.z), oa1 = uniform(ow.w);
   int32_t* out_f = uniform_ptr(reinterpret_cast<int32_t*>(sm.rank_out[0]));
   int32_t* out_a = uniform_ptr(reinterpret_cast<int32_t*>(sm.rank_out[1]));
   for (int r = rw; r < R; r += RW) {
-    uint32_t G1 = uniform((uint32_t)__builtin_amdgcn_readlane((int)ex[0], r));
-    uint32_t E1 = uniform((uint32_t)__builtin_amdgcn_readlane((int)ex[1], r));
-    uint32_t G2 = uniform((uint32_t)__builtin_amdgcn_readlane((int)ex[2], r));
-    uint32_t E2 = uniform((uint32_t)__builtin_amdgcn_readlane((int)ex[3], r));
-    const uint32_t G1e = G1 + (uint32_t)__builtin_amdgcn_readlane((int)own[0], r);
-    const uint32_t E1e = E1 + (uint32_t)__builtin_amdgcn_readlane((int)own[1], r);
-    const uint32_t G2e = G2 + (uint32_t)__builtin_amdgcn_readlane((int)own[2], r);
-    const uint32_t E2e = E2 + (uint32_t)__builtin_amdgcn_readlane((int)own[3], r);
+    const uint32_t G1 = uniform((uint32_t)__builtin_amdgcn_readlane((int)ex[0], r));
+    const uint32_t E1 = uniform((uint32_t)__builtin_amdgcn_readlane((int)ex[1], r));
+    const uint32_t G2 = uniform((uint32_t)__builtin_amdgcn_readlane((int)ex[2], r));
+    const uint32_t E2 = uniform((uint32_t)__builtin_amdgcn_readlane((int)ex[3], r));
+    const uint32_t G1e = uniform((uint32_t)__builtin_amdgcn_readlane((int)inc[0], r));
+    const uint32_t E1e = uniform((uint32_t)__builtin_amdgcn_readlane((int)inc[1], r));
+    const uint32_t G2e = uniform((uint32_t)__builtin_amdgcn_readlane((int)inc[2], r));
+    const uint32_t E2e = uniform((uint32_t)__builtin_amdgcn_readlane((int)inc[3], r));
     // the round's full-tier and approx-tier position ranges
     const uint32_t fb = G1 + min(E1, q1), fe = G1e + min(E1e, q1);
     const uint32_t ab = G2 + min(E2, q2) - fb, ae = G2e + min(E2e, q2) - fe;
     const bool need = (fb < nf1 && fe > nf0) || (fb < nf3 && fe > nf2) ||
                       (ab < na1 && ae > na0) || (ab < na3 && ae > na2);
     if (!need) continue;  // wave-uniform
+    const uint4 v = *reinterpret_cast<const uint4*>(&sm.keys[r * kRankRound + 8 * lane]);
+    uint32_t c1, c2;
+    lane_counts(v, t1, t2, c1, c2);
+    const uint32_t x1 = wave_incl_scan(c1) - c1, x2 = wave_incl_scan(c2) - c2;
+    uint32_t g1 = G1 + (x1 & 0xFFFFu), e1 = E1 + (x1 >> 16);
+    uint32_t g2 = G2 + (x2 & 0xFFFFu), e2 = E2 + (x2 >> 16);
+    const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
+    const uint32_t e0 = (uint32_t)(r * kRankRound + 8 * lane);
 #pragma unroll
     for (int h = 0; h < 8; ++h) {
-      const uint32_t e = (uint32_t)(r * kRankRound + 64 * h + lane);
-      const uint32_t k = (uint32_t)sm.keys[e] & 0x7FFFu;
-      const uint64_t mg1 = __ballot(k > t1), me1 = __ballot(k == t1);
-      const uint64_t mg2 = __ballot(k > t2), me2 = __ballot(k == t2);
-      const uint32_t e1 = E1 + lanes_below(me1), e2 = E2 + lanes_below(me2);
+      const uint32_t k = (w4[h >> 1] >> (16 * (h & 1))) & 0x7FFFu;
+      const uint32_t fpos = g1 + min(e1, q1);
+      const uint32_t apos = g2 + min(e2, q2) - fpos;
       const bool in_f = k > t1 || (k == t1 && e1 < q1);
       const bool in_fa = k > t2 || (k == t2 && e2 < q2);
-      const uint32_t fpos = G1 + lanes_below(mg1) + min(e1, q1);
-      const uint32_t apos = G2 + lanes_below(mg2) + min(e2, q2) - fpos;
+      const uint32_t e = e0 + (uint32_t)h;
       if (in_f) {
         list[fpos] = (uint16_t)e;
-        out_f[fpos] = (int32_t)e;
+        if (fpos >= of0 && fpos < of1) out_f[fpos] = (int32_t)e;
       } else if (in_fa) {
         list[K1 + apos] = (uint16_t)e;
-        out_a[apos] = (int32_t)e;
+        if (apos >= oa0 && apos < oa1) out_a[apos] = (int32_t)e;
       }
-      G1 += (uint32_t)__builtin_popcountll(mg1);
-      E1 += (uint32_t)__builtin_popcountll(me1);
-      G2 += (uint32_t)__builtin_popcountll(mg2);
-      E2 += (uint32_t)__builtin_popcountll(me2);
+      g1 += k > t1 ? 1u : 0u;
+      e1 += k == t1 ? 1u : 0u;
+      g2 += k > t2 ? 1u : 0u;
+      e2 += k == t2 ? 1u : 0u;
     }
   }
   static_assert(256 * kHistCopies == 4 * kLayerRankThreads, "one 16-byte clear per thread");
@@ -374,15 +416,29 @@ __device__ __attribute__((noinline)) uint32_t rank_group(const uint16_t* __restr
   return epoch;
 }
 
+// Whether group g runs in the launch's second phase: down, when its input
+// is the a this launch's gate/up writes.
+__device__ __forceinline__ bool late_group(const LayerArgs& A, int g) {
+  return g == SPAX_GROUP_DOWN && A.down_waits;
+}
+
 // The positions of group g that workgroup w reads (its segments' ranges,
 // two intervals per tier: a workgroup meets at most two partial tiles of a
-// group, and a third tile makes the whole list needed), and the caller's
-// list pointers, into LDS for the ranking.
+// group, and a third tile makes the whole list needed), the positions it
+// stores to the caller's lists (those of its segment of tile 0: tile 0's
+// segments cover every position once) and the caller's list pointers, into
+// LDS for the ranking.
 __device__ __forceinline__ void set_need(const LayerArgs& A, int g, uint32_t w) {
   const LayerGroupArgs& gr = A.g[g];
-  uint32_t f[4] = {0u, 0u, 0u, 0u}, a[4] = {0u, 0u, 0u, 0u};
+  uint32_t f[4] = {0u, 0u, 0u, 0u}, a[4] = {0u, 0u, 0u, 0u}, o[4] = {0u, 0u, 0u, 0u};
   int cnt = 0;
   layer_group_segs(A, g, w, [&](const LayerSeg& s) {
+    if (s.t == 0) {
+      o[0] = (uint32_t)s.f0;
+      o[1] = (uint32_t)s.f1;
+      o[2] = (uint32_t)s.a0;
+      o[3] = (uint32_t)s.a1;
+    }
     const int i = cnt < 2 ? cnt : 1;
     f[2 * i] = (uint32_t)s.f0;
     f[2 * i + 1] = (uint32_t)s.f1;
@@ -396,6 +452,7 @@ __device__ __forceinline__ void set_need(const LayerArgs& A, int g, uint32_t w) 
   }
   *reinterpret_cast<uint4*>(&g_sm.need[0]) = make_uint4(f[0], f[1], f[2], f[3]);
   *reinterpret_cast<uint4*>(&g_sm.need[4]) = make_uint4(a[0], a[1], a[2], a[3]);
+  *reinterpret_cast<uint4*>(&g_sm.own[0]) = make_uint4(o[0], o[1], o[2], o[3]);
   g_sm.rank_out[0] = reinterpret_cast<uint64_t>(gr.out_full);
   g_sm.rank_out[1] = reinterpret_cast<uint64_t>(gr.out_approx);
 }
@@ -404,15 +461,30 @@ __device__ __forceinline__ void set_need(const LayerArgs& A, int g, uint32_t w) 
 __device__ __forceinline__ int first_ranked(const LayerArgs& A, uint32_t w) {
   for (int oi = 0; oi < A.n_order; ++oi) {
     const int g = A.order[oi];
-    if (layer_meets(A, g, w) && A.g[g].k_full + A.g[g].k_approx > 0 &&
-        !(g == SPAX_GROUP_DOWN && A.down_waits))
+    if (layer_meets(A, g, w) && A.g[g].k_full + A.g[g].k_approx > 0 && !late_group(A, g))
       return g;
   }
   return -1;
 }
 
-// Ranking waves: rank each further group the workgroup meets, in processing
-// order (the first was ranked by the whole workgroup).
+// Waits (bounded) until every gate/up tile has written its a.
+__device__ __forceinline__ void wait_gate_up(const LayerArgs& A) {
+  uint32_t* status = A.sync + 2;
+  const uint32_t need = (uint32_t)A.g[SPAX_GROUP_GATE_UP].tiles;
+  for (uint32_t k = 0;
+       __hip_atomic_load(&A.sync[0], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < need; ++k) {
+    if (k >= kSpinGlobal) {
+      if ((threadIdx.x & 63) == 0) set_status(status, kStatusGlobalWait);
+      break;
+    }
+    __builtin_amdgcn_s_sleep(2);
+  }
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
+// Ranking waves: rank each further group of the first phase that the
+// workgroup meets, in processing order (the first was ranked by the whole
+// workgroup).
 __device__ __forceinline__ void rank_role(const LayerArgs& A, int first, uint32_t epoch) {
   __builtin_amdgcn_s_setprio(3);
   uint32_t* status = A.sync + 2;
@@ -420,92 +492,388 @@ __device__ __forceinline__ void rank_role(const LayerArgs& A, int first, uint32_
   const int rt = (int)threadIdx.x - (kLayerStreamWaves + 1) * 64;
   for (int oi = 0; oi < A.n_order; ++oi) {
     const int g = A.order[oi];
-    if (g == first || !layer_meets(A, g, w)) continue;
+    if (g == first || late_group(A, g) || !layer_meets(A, g, w)) continue;
     const LayerGroupArgs& gr = A.g[g];
     const uint32_t K1 = (uint32_t)gr.k_full, K2 = (uint32_t)(gr.k_full + gr.k_approx);
     if (K2 == 0u) continue;  // no lists: the group's segments are empty
-    if (g == SPAX_GROUP_DOWN && A.down_waits) {
-      // every gate/up tile has written its a (bounded wait)
-      const uint32_t need = (uint32_t)A.g[SPAX_GROUP_GATE_UP].tiles;
-      for (uint32_t k = 0;
-           __hip_atomic_load(&A.sync[0], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < need;
-           ++k) {
-        if (k >= kSpinGlobal) {
-          if ((threadIdx.x & 63) == 0) set_status(status, kStatusGlobalWait);
-          break;
-        }
-        __builtin_amdgcn_s_sleep(2);
-      }
-      __atomic_signal_fence(__ATOMIC_SEQ_CST);
-    }
     if (rt == 0) set_need(A, g, w);
     epoch = rank_group<kLayerRankWaves>(gr.x, gr.n, K1, K2, gr.list_off, epoch, status);
-    if (rt == 0)
-      __hip_atomic_store(&g_sm.ready[g], 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
+    if (rt == 0) lds_signal_store(&g_sm.ready[g], 1u);
   }
 }
 
-// Streaming waves: per segment, this wave's share of each tier; then the
-// wave's partial of the tile into LDS for the reduction wave.
-template <int FF, int AF>
-__device__ __forceinline__ void stream_role(const LayerArgs& A, int sw) {
-  LayerShared& sm = g_sm;
-  uint32_t* status = A.sync + 2;
+// ---- streaming ---------------------------------------------------------
+// In each phase the streaming waves split between the two tiers once, in
+// proportion to the tiers' streaming cost over the workgroup's segments of
+// the phase; in every segment a wave takes an equal share of its tier's
+// list positions. A wave streams all its shares as one sequence through a
+// ring of loads in registers: the load for ring slot u is issued as soon as
+// slot u's previous load has been added, across segment boundaries, so the
+// ring never drains between segments. When a segment's last load has been
+// added, the wave hands its fp32 partial of the tile's 512 rows to the
+// reduction wave through LDS (two slot sets, so a wave can run one segment
+// ahead) and starts the next sum. A share with no positions still costs one
+// load, with a zero factor, so every wave hands over every segment.
+// Column indices come from the LDS list: lane l holds the entry of position
+// 64 b + l of the share's batch b that the issue pointer is in.
+
+// Streaming cost of one column's 512-row tile per format: its bytes,
+// weighted by how much slower a code wave streams a byte than an fp16 wave
+// (more vector work, and two small loads per code load; measured on 7B
+// layers).
+__host__ __device__ constexpr uint32_t form_tile_cost(int fmt) {
+  return fmt == kFp16 ? 1026u : fmt == kInt4 ? 426u : 276u;
+}
+
+// Per-format streaming: fp16 columns load one column per load, lane l
+// reading rows 8 l .. 8 l + 7 of the tile (16 bytes). Code tiers load four
+// columns per load: lane (q, i) = (lane / 16, lane mod 16) reads rows
+// 32 i .. 32 i + 31 of the load's q-th column (16 bytes of int4 codes, 8 of
+// 2-bit codes), so one load moves as many bytes as an fp16 column; the
+// lane's rows lie in one 128-row group g = i / 4, and it loads its own x_j
+// and scale s_{j,g} with the codes.
+template <int FMT>
+struct Form;
+template <>
+struct Form<kFp16> {
+  using V = uint4;
+  static constexpr int kRing = 8;
+  static constexpr int kPos = 1;  // list positions per load
+};
+template <>
+struct Form<kInt4> {
+  using V = uint4;
+  static constexpr int kRing = 6;
+  static constexpr int kPos = 4;
+  static constexpr uint32_t kLaneBytes = 16;
+  static __device__ __forceinline__ V load(__amdgpu_buffer_rsrc_t r, uint32_t o) {
+    return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, o, 0, 0));
+  }
+  static __device__ __forceinline__ uint32_t piece(const V& v, int k) {
+    return k == 0 ? v.x : k == 1 ? v.y : k == 2 ? v.z : v.w;
+  }
+};
+template <>
+struct Form<kInt2> {
+  using V = uint2;
+  static constexpr int kRing = 8;
+  static constexpr int kPos = 4;
+  static constexpr uint32_t kLaneBytes = 8;
+  static __device__ __forceinline__ V load(__amdgpu_buffer_rsrc_t r, uint32_t o) {
+    return __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(r, o, 0, 0));
+  }
+  static __device__ __forceinline__ uint32_t piece(const V& v, int k) {
+    const uint32_t w = k < 2 ? v.x : v.y;
+    return (k & 1) ? (w >> 16) : (w & 0xFFFFu);
+  }
+};
+template <>
+struct Form<kSign2> : Form<kInt2> {};
+
+// Workgroup w's segments of one phase into the LDS table, in processing
+// order, by one wave: lane i builds entries i, i + 64, ...
+__device__ __forceinline__ void build_segtab(const LayerArgs& A, uint32_t w, bool late) {
   const int lane = (int)threadIdx.x & 63;
-  const uint32_t w = blockIdx.x;
-  uint32_t k = 0u;
+  uint32_t first[4], step[4], cnt[4], u0[4], u1[4];
+  int gid[4];
+  int ng = 0;
+  uint32_t total = 0u;
   for (int oi = 0; oi < A.n_order; ++oi) {
     const int g = A.order[oi];
-    layer_group_segs(A, g, w, [&](const LayerSeg& s) {
-      const LayerGroupArgs& gr = A.g[g];
-      const int row0 = s.t * kTileRows;
-      // lanes past the last row of a ragged tile read lane 0's rows; their
-      // sums are never stored
-      const int ld_lane = row0 + 8 * lane < gr.rows ? lane : 0;
-      float acc[8];
-#pragma unroll
-      for (int r = 0; r < 8; ++r) acc[r] = 0.0f;
-      float corr = 0.0f;
-      const int nf = s.f1 - s.f0, na = s.a1 - s.a0;
-      const int flo = s.f0 + nf * sw / kNS, fhi = s.f0 + nf * (sw + 1) / kNS;
-      const int alo = s.a0 + na * sw / kNS, ahi = s.a0 + na * (sw + 1) / kNS;
-      if (fhi > flo || ahi > alo) {
-        wait_lds_ge(&sm.ready[g], 1u, status);
-        const int32_t* pl = reinterpret_cast<const int32_t*>(sm.lists + gr.list_off);
-        TierStream<FF, kListPacked> sf(sm.wm[0][sw], gr.full_base, gr.full_stride, gr.full_bytes,
-                                       gr.full_scales, gr.full_sstride, nullptr, gr.x, pl,
-                                       nullptr, flo, fhi, row0, gr.rows, lane, ld_lane);
-        sf.begin();
-        if constexpr (AF != kNone) {
-          const int32_t* pa =
-              reinterpret_cast<const int32_t*>(sm.lists + gr.list_off + gr.k_full);
-          TierStream<AF, kListPacked> sa(sm.wm[1][sw], gr.approx_base, gr.approx_stride,
-                                         gr.approx_bytes, gr.approx_scales, gr.approx_sstride,
-                                         nullptr, gr.x, pa, nullptr, alo, ahi, row0, gr.rows,
-                                         lane, ld_lane);
-          sa.begin();
-          sf.run(acc, corr);
-          sa.run(acc, corr);
-        } else {
-          sf.run(acc, corr);
-        }
-        if constexpr (FF == kInt4 || AF != kNone) {
-#pragma unroll
-          for (int r = 0; r < 8; ++r) acc[r] -= corr;
-        }
-      }
-      // hand the partial to the reduction wave once it has read the
-      // previous segment's slots
-      wait_lds_ge(&sm.seg_free, k, status);
-      float4* dst = reinterpret_cast<float4*>(&sm.slot[sw][8 * lane]);
-      dst[0] = make_float4(acc[0], acc[1], acc[2], acc[3]);
-      dst[1] = make_float4(acc[4], acc[5], acc[6], acc[7]);
-      if (lane == 0)
-        __hip_atomic_fetch_add(&sm.seg_arrive, 1u, __ATOMIC_RELEASE,
-                               __HIP_MEMORY_SCOPE_WORKGROUP);
-      ++k;
-    });
+    uint32_t t_end;
+    if (late_group(A, g) != late ||
+        !layer_group_range(A, g, w, first[ng], step[ng], t_end, u0[ng], u1[ng]))
+      continue;
+    cnt[ng] = (t_end - first[ng] + step[ng] - 1u) / step[ng];
+    gid[ng] = g;
+    total += cnt[ng];
+    ++ng;
   }
+  total = min(total, (uint32_t)kLayerSegTab);  // the host keeps every phase within
+  for (uint32_t i = (uint32_t)lane; i < total; i += 64u) {
+    uint32_t r = i;
+    int k = 0;
+    while (k + 1 < ng && r >= cnt[k]) r -= cnt[k++];
+    const LayerSeg s = layer_make_seg(A, gid[k], w, first[k] + r * step[k], u0[k], u1[k]);
+    g_sm.segtab[i] = make_uint4((uint32_t)s.g | ((uint32_t)s.t << 8),
+                                (uint32_t)s.f0 | ((uint32_t)s.f1 << 16),
+                                (uint32_t)s.a0 | ((uint32_t)s.a1 << 16), 0u);
+  }
+  if (lane == 0) g_sm.nseg = total;
+}
+
+// Entry i of the segment table (wave-uniform).
+__device__ __forceinline__ LayerSeg table_seg(uint32_t i) {
+  const uint4 e = g_sm.segtab[i];
+  LayerSeg s;
+  s.g = (int)uniform(e.x & 0xFFu);
+  s.t = (int)uniform(e.x >> 8);
+  s.f0 = (int)uniform(e.y & 0xFFFFu);
+  s.f1 = (int)uniform(e.y >> 16);
+  s.a0 = (int)uniform(e.z & 0xFFFFu);
+  s.a1 = (int)uniform(e.z >> 16);
+  s.w_lo = s.w_hi = -1;
+  return s;
+}
+
+// floor(a / b) for a < 2^24 and 1 <= b <= 16, with b's reciprocal rb.
+__device__ __forceinline__ int small_div(int a, int b, float rb) {
+  int q = (int)((float)a * rb);
+  q += (q + 1) * b <= a ? 1 : 0;
+  q -= q * b > a ? 1 : 0;
+  return q;
+}
+
+// A segment's share of one tier, as the issue side of a streaming wave sees
+// it (all wave-uniform but the per-lane offsets).
+struct Share {
+  const uint16_t* list;   // the share's first list entry (LDS)
+  int n;                  // positions
+  int loads;              // max(1, ceil(n / positions per load))
+  __amdgpu_buffer_rsrc_t rs, xr, sr;
+  uint32_t stride, sstride;
+  uint32_t off;           // fp16: the lane's byte offset in a column
+  uint32_t sg;            // codes: the lane's scale index in a column
+};
+
+// The share of tier `full` of segment s for wave wi of nw on that tier.
+template <int FMT>
+__device__ __forceinline__ Share make_share(const LayerArgs& A, const LayerSeg& s, bool full,
+                                            int wi, int nw, float rnw) {
+  const LayerGroupArgs& gr = A.g[s.g];
+  const int lane = (int)threadIdx.x & 63;
+  const int p0 = full ? s.f0 : s.a0, np = full ? s.f1 - s.f0 : s.a1 - s.a0;
+  const int lo = p0 + small_div(np * wi, nw, rnw), hi = p0 + small_div(np * (wi + 1), nw, rnw);
+  Share h;
+  h.list = g_sm.lists + gr.list_off + (full ? 0 : gr.k_full) + lo;
+  h.n = hi - lo;
+  h.loads = max(1, (h.n + Form<FMT>::kPos - 1) / Form<FMT>::kPos);
+  h.rs = tier_rsrc(full ? gr.full_base : gr.approx_base, full ? gr.full_bytes : gr.approx_bytes);
+  h.xr = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(gr.x), (short)0, 0x7FFFFFFF,
+                                           0x00020000);
+  const uint16_t* sc = full ? gr.full_scales : gr.approx_scales;
+  h.sr = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(sc), (short)0, 0x7FFFFFFF,
+                                           0x00020000);
+  h.stride = (uint32_t)(full ? gr.full_stride : gr.approx_stride);
+  h.sstride = (uint32_t)(full ? gr.full_sstride : gr.approx_sstride);
+  const int row0 = s.t * kTileRows;
+  if constexpr (FMT == kFp16) {
+    // lanes past the last row of a ragged tile read lane 0's rows; their
+    // sums are never stored
+    const int ld = row0 + 8 * lane < gr.rows ? lane : 0;
+    h.off = 2u * (uint32_t)(row0 + 8 * ld);
+    h.sg = 0u;
+  } else {
+    const int li = row0 + 32 * (lane & 15) < gr.rows ? (lane & 15) : 0;
+    h.off = (uint32_t)(row0 + 32 * li) / 32u * Form<FMT>::kLaneBytes;
+    h.sg = (uint32_t)(row0 / kGroup + li / 4);
+  }
+  return h;
+}
+
+// Hands partial p (the 8 rows of row block `block`) of the wave's segment k
+// to the reduction wave.
+__device__ __forceinline__ void hand_over(int sw, uint32_t k, int block, const float (&p)[8],
+                                          uint32_t* status) {
+  LayerShared& sm = g_sm;
+  // slot set k & 1 was last read for segment k - 2
+  if (k >= 2u) wait_lds_ge(&sm.seg_free, k - 1u, status);
+  float4* dst = reinterpret_cast<float4*>(&sm.slot[k & 1u][sw][8 * block]);
+  dst[0] = make_float4(p[0], p[1], p[2], p[3]);
+  dst[1] = make_float4(p[4], p[5], p[6], p[7]);
+  if ((threadIdx.x & 63) == 0) lds_signal_add(&sm.seg_arrive[k & 1u], 1u);
+}
+
+// Wave wi of the nw streaming waves on tier `full` (format FMT) of one
+// phase: every segment's share, as one ring sequence.
+template <int FMT>
+__device__ __forceinline__ void stream_seq(const LayerArgs& A, bool late, bool full, int wi,
+                                           int nw, int sw, uint32_t& k) {
+  using Fm = Form<FMT>;
+  constexpr int R = Fm::kRing;
+  uint32_t* status = A.sync + 2;
+  const int lane = (int)threadIdx.x & 63;
+  const float rnw = 1.0f / (float)nw;
+  const uint32_t nseg = uniform(g_sm.nseg);
+  // loads of the whole sequence
+  int L = 0;
+  for (uint32_t i = 0; i < nseg; ++i) {
+    const LayerSeg s = table_seg(i);
+    const int np = full ? s.f1 - s.f0 : s.a1 - s.a0;
+    const int n = small_div(np * (wi + 1), nw, rnw) - small_div(np * wi, nw, rnw);
+    L += max(1, (n + Fm::kPos - 1) / Fm::kPos);
+  }
+  if (L == 0) return;
+  uint32_t si = 0u;  // next table entry
+  Share sh;
+  sh.loads = 0;
+  int j = 0;         // next load of the current share
+  int colv = 0;      // list entries of the issue pointer's batch
+  uint32_t ends = 0; // ring slots holding the last load of a share
+  // fp16: 8 sums; codes: 32 (rows 32 i + 8 k + r) and the offset sum
+  constexpr int kAcc = FMT == kFp16 ? 1 : 4;
+  float acc[kAcc][8];
+#pragma unroll
+  for (int q = 0; q < kAcc; ++q)
+#pragma unroll
+    for (int r = 0; r < 8; ++r) acc[q][r] = 0.0f;
+  float corr = 0.0f;
+  typename Fm::V d[R];
+  uint32_t xs[R], ss[R];
+  const uint32_t kM = [] {
+    uint32_t m = FMT == kFp16 ? 0u : Tier<FMT>::kMask;
+    asm volatile("" : "+v"(m));  // a VGPR, not a literal
+    return m;
+  }();
+
+  // issue side: the next load into ring slot u (past the sequence, the last
+  // load again; it is never added)
+  auto issue = [&](int u) {
+    bool redo = false;
+    if (j == sh.loads) {
+      if (si < nseg) {
+        const LayerSeg seg = table_seg(si++);
+        sh = make_share<FMT>(A, seg, full, wi, nw, rnw);
+        j = 0;
+        if (sh.n > 0) {
+          wait_lds_ge(&g_sm.ready[seg.g], 1u, status);
+          colv = (int)sh.list[min(lane, sh.n - 1)];
+        }
+      } else {
+        redo = true;
+      }
+    }
+    const int jj = redo ? sh.loads - 1 : j;
+    if (!redo) {
+      if ((jj * Fm::kPos & 63) == 0 && jj > 0)
+        colv = (int)sh.list[min(jj * Fm::kPos + lane, sh.n - 1)];  // the next batch
+      ends = (ends & ~(1u << u)) | ((jj == sh.loads - 1 ? 1u : 0u) << u);
+      ++j;
+    }
+    if constexpr (FMT == kFp16) {
+      const bool live = jj < sh.n;  // wave-uniform
+      const uint32_t col = live ? (uint32_t)__builtin_amdgcn_readlane(colv, jj & 63) : 0u;
+      d[u] = __builtin_bit_cast(
+          uint4, __builtin_amdgcn_raw_buffer_load_b128(sh.rs, sh.off, col * sh.stride, 0));
+      xs[u] = live ? __builtin_amdgcn_raw_buffer_load_b16(sh.xr, 0u, 2u * col, kCoherent) : 0u;
+    } else {
+      const int q = lane >> 4;
+      const int pos = 4 * jj + q;
+      const bool live = pos < sh.n;
+      const uint32_t col =
+          (uint32_t)__builtin_amdgcn_ds_bpermute((min(pos, max(sh.n - 1, 0)) & 63) << 2, colv);
+      const uint32_t c = sh.n > 0 ? col : 0u;
+      d[u] = Fm::load(sh.rs, c * sh.stride + sh.off);
+      xs[u] = live ? __builtin_amdgcn_raw_buffer_load_b16(sh.xr, 2u * c, 0, kCoherent) : 0u;
+      if constexpr (FMT == kSign2)
+        ss[u] = __builtin_amdgcn_raw_buffer_load_b32(sh.sr, 4u * c, 0, 0);
+      else
+        ss[u] = __builtin_amdgcn_raw_buffer_load_b16(sh.sr, 2u * (c * sh.sstride + sh.sg), 0, 0);
+    }
+  };
+
+  // consume side: adds ring slot u; at a share's last load hands the
+  // segment's partial over
+  auto consume = [&](int u) {
+    if constexpr (FMT == kFp16) {
+      const float f = h2f(xs[u]);
+      const uint4 v = d[u];
+      acc[0][0] = fmaf(h2f(v.x & 0xFFFFu), f, acc[0][0]);
+      acc[0][1] = fmaf(h2f(v.x >> 16), f, acc[0][1]);
+      acc[0][2] = fmaf(h2f(v.y & 0xFFFFu), f, acc[0][2]);
+      acc[0][3] = fmaf(h2f(v.y >> 16), f, acc[0][3]);
+      acc[0][4] = fmaf(h2f(v.z & 0xFFFFu), f, acc[0][4]);
+      acc[0][5] = fmaf(h2f(v.z >> 16), f, acc[0][5]);
+      acc[0][6] = fmaf(h2f(v.w & 0xFFFFu), f, acc[0][6]);
+      acc[0][7] = fmaf(h2f(v.w >> 16), f, acc[0][7]);
+    } else if constexpr (FMT == kSign2) {
+      const float xj = h2f(xs[u]);
+      const float fa = xj * h2f(ss[u] & 0xFFFFu), fb = xj * h2f(ss[u] >> 16);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) Tier<FMT>::fma2(acc[q], Fm::piece(d[u], q), fa, fb, kM);
+    } else {
+      const float f = h2f(xs[u]) * h2f(ss[u]) * Tier<FMT>::kScale;
+      float unused = 0.0f;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) Tier<FMT>::fma(acc[q], unused, Fm::piece(d[u], q), f, kM);
+      corr = fmaf(FMT == kInt4 ? 1.5f : 1.375f, f, corr);
+    }
+    if ((ends >> u) & 1u) {  // wave-uniform
+      float p[8];
+      int block = lane;
+      if constexpr (FMT == kFp16) {
+#pragma unroll
+        for (int r = 0; r < 8; ++r) p[r] = acc[0][r];
+      } else {
+        // the four quarters' sums, added across lanes: q with q ^ 2 (lanes
+        // q < 2 keep row pieces 0, 1), then q with q ^ 1 (even q keep the
+        // first piece); lane (q, i) ends with rows 32 i + 8 q .. + 7
+        if constexpr (FMT != kSign2) {
+#pragma unroll
+          for (int q = 0; q < 4; ++q)
+#pragma unroll
+            for (int r = 0; r < 8; ++r) acc[q][r] -= corr;
+        }
+        const int q = lane >> 4;
+        const bool lo = q < 2, ev = (q & 1) == 0;
+        float h[2][8];
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+          for (int r = 0; r < 8; ++r) {
+            const float keep = lo ? acc[kk][r] : acc[kk + 2][r];
+            const float send = lo ? acc[kk + 2][r] : acc[kk][r];
+            h[kk][r] = keep + __shfl_xor(send, 32, 64);
+          }
+#pragma unroll
+        for (int r = 0; r < 8; ++r) {
+          const float keep = ev ? h[0][r] : h[1][r];
+          const float send = ev ? h[1][r] : h[0][r];
+          p[r] = keep + __shfl_xor(send, 16, 64);
+        }
+        block = 4 * (lane & 15) + q;
+      }
+      hand_over(sw, k, block, p, status);
+      ++k;
+#pragma unroll
+      for (int q = 0; q < kAcc; ++q)
+#pragma unroll
+        for (int r = 0; r < 8; ++r) acc[q][r] = 0.0f;
+      corr = 0.0f;
+    }
+  };
+
+#pragma unroll
+  for (int u = 0; u < R; ++u) issue(u);
+  for (int c0 = 0; c0 < L; c0 += R) {
+#pragma unroll
+    for (int u = 0; u < R; ++u) {
+      if (c0 + u < L) consume(u);  // wave-uniform
+      issue(u);
+    }
+  }
+}
+
+// Streaming waves of one phase: the split between the tiers, then the wave's
+// sequence.
+template <int FF, int AF>
+__device__ __forceinline__ void stream_role(const LayerArgs& A, int sw, bool late, uint32_t& k) {
+  const uint32_t nseg = uniform(g_sm.nseg);
+  uint64_t cf = 0, ca = 0;
+  for (uint32_t i = 0; i < nseg; ++i) {
+    const LayerSeg s = table_seg(i);
+    cf += (uint64_t)(s.f1 - s.f0) * form_tile_cost(FF);
+    ca += (uint64_t)(s.a1 - s.a0) * form_tile_cost(AF);
+  }
+  int wf = kNS;
+  if (AF != kNone && ca > 0) {
+    wf = cf == 0 ? 0 : (int)((2u * kNS * cf + cf + ca) / (2u * (cf + ca)));
+    if (cf > 0) wf = min(max(wf, 1), kNS - 1);
+  }
+  if (sw < wf)
+    stream_seq<FF>(A, late, true, sw, wf, sw, k);
+  else if constexpr (AF != kNone)
+    stream_seq<AF>(A, late, false, sw - wf, kNS - wf, sw, k);
 }
 
 // Output of one tile: fp16 y, or for gate/up a = silu(g) * u from the fp16
@@ -567,35 +935,34 @@ __device__ __forceinline__ void finish_tile(const LayerArgs& A, const LayerSeg& 
 
 // Reduction wave: per segment, the workgroup's partial of the tile, then the
 // cross-workgroup sum by the tile's last contributor.
-__device__ __forceinline__ void reduce_role(const LayerArgs& A) {
+__device__ __forceinline__ void reduce_role(const LayerArgs& A, uint32_t& k) {
   LayerShared& sm = g_sm;
   __builtin_amdgcn_s_setprio(3);
   uint32_t* status = A.sync + 2;
   const int lane = (int)threadIdx.x & 63;
   const uint32_t w = blockIdx.x;
-  uint32_t k = 0u;
-  for (int oi = 0; oi < A.n_order; ++oi) {
-    const int g = A.order[oi];
-    layer_group_segs(A, g, w, [&](const LayerSeg& s0) {
-      LayerSeg s = s0;
-      wait_lds_ge(&sm.seg_arrive, (uint32_t)kNS * (k + 1u), status);
+  const uint32_t nseg = uniform(sm.nseg);
+  for (uint32_t si = 0; si < nseg; ++si) {
+    {
+      LayerSeg s = table_seg(si);
+      const int g = s.g;
+      wait_lds_ge(&sm.seg_arrive[k & 1u], (uint32_t)kNS * (k / 2u + 1u), status);
       float p[8];
 #pragma unroll
       for (int r = 0; r < 8; ++r) p[r] = 0.0f;
 #pragma unroll
       for (int q = 0; q < kNS; ++q) {
-        const float4* src = reinterpret_cast<const float4*>(&sm.slot[q][8 * lane]);
+        const float4* src = reinterpret_cast<const float4*>(&sm.slot[k & 1u][q][8 * lane]);
         const float4 u0 = src[0], u1 = src[1];
         p[0] += u0.x; p[1] += u0.y; p[2] += u0.z; p[3] += u0.w;
         p[4] += u1.x; p[5] += u1.y; p[6] += u1.z; p[7] += u1.w;
       }
       ++k;
-      if (lane == 0)
-        __hip_atomic_store(&sm.seg_free, k, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
+      if (lane == 0) lds_signal_store(&sm.seg_free, k);
       layer_contributors(A, s);
       if (s.w_lo == s.w_hi) {  // the only contributor
         finish_tile(A, s, p, lane);
-        return;
+        continue;
       }
       const LayerGroupArgs& gr = A.g[g];
       const uint32_t pbytes = (uint32_t)((gr.tiles + gr.n_wg) * kTileRows * 4);
@@ -618,7 +985,7 @@ __device__ __forceinline__ void reduce_role(const LayerArgs& A) {
       if (lane == 0)
         old = __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       old = (uint32_t)__builtin_amdgcn_readlane((int)old, 0);
-      if (old != (uint32_t)(s.w_hi - s.w_lo)) return;
+      if (old != (uint32_t)(s.w_hi - s.w_lo)) continue;
       if (lane == 0) __hip_atomic_store(ctr, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       __atomic_signal_fence(__ATOMIC_SEQ_CST);
       // the last contributor: add every contributor's partial in workgroup
@@ -647,7 +1014,7 @@ __device__ __forceinline__ void reduce_role(const LayerArgs& A) {
         }
       }
       finish_tile(A, s, q8, lane);
-    });
+    }
   }
 }
 
@@ -660,14 +1027,17 @@ __global__ __launch_bounds__(kGemvThreads) void layer_kernel(LayerArgs A) {
   if (t < 4) sm.ready[t] = 0u;
   if (t == 0) {
     sm.rbar = 0u;
-    sm.seg_arrive = 0u;
+    sm.seg_arrive[0] = 0u;
+    sm.seg_arrive[1] = 0u;
     sm.seg_free = 0u;
   }
   // the first group the workgroup ranks: every wave ranks it (the streaming
   // waves have nothing to read before it)
   const uint32_t w = blockIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
   const int first = first_ranked(A, w);
   if (first >= 0 && t == 0) set_need(A, first, w);
+  if (wave == kWaves - 1) build_segtab(A, w, false);  // the first phase's segments
   __syncthreads();
   uint32_t epoch = 0u;
   if (first >= 0) {
@@ -677,13 +1047,36 @@ __global__ __launch_bounds__(kGemvThreads) void layer_kernel(LayerArgs A) {
     if (t == 0) sm.ready[first] = 1u;
     __syncthreads();
   }
-  const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
-  if (wave < kLayerStreamWaves)
-    stream_role<FF, AF>(A, wave);
-  else if (wave == kLayerReduceWave)
-    reduce_role(A);
-  else
-    rank_role(A, first, epoch);
+  uint32_t k = 0u;  // segments handed over (streaming and reduction waves)
+  // phase 0: every group but a late down; phase 1: down, once every gate/up
+  // tile has written a (one call site per role keeps the streaming code
+  // inlined once)
+  for (int phase = 0; phase < 2; ++phase) {
+    if (phase == 1) {
+      if (!(A.down_waits && layer_meets(A, SPAX_GROUP_DOWN, w))) break;
+      // the whole workgroup ranks a: its streaming waves are done with phase 0
+      __syncthreads();
+      if (wave == 0) {
+        wait_gate_up(A);
+        if (t == 0) set_need(A, SPAX_GROUP_DOWN, w);
+      } else if (wave == 1) {
+        build_segtab(A, w, true);
+      }
+      __syncthreads();
+      const LayerGroupArgs& gd = A.g[SPAX_GROUP_DOWN];
+      if (gd.k_full + gd.k_approx > 0)
+        rank_group<kWaves>(gd.x, gd.n, (uint32_t)gd.k_full,
+                           (uint32_t)(gd.k_full + gd.k_approx), gd.list_off, 0u, A.sync + 2);
+      if (t == 0) sm.ready[SPAX_GROUP_DOWN] = 1u;
+      __syncthreads();
+    }
+    if (wave < kLayerStreamWaves)
+      stream_role<FF, AF>(A, wave, phase == 1, k);
+    else if (wave == kLayerReduceWave)
+      reduce_role(A, k);
+    else if (phase == 0)
+      rank_role(A, first, epoch);
+  }
   __syncthreads();
   if (t == 0) {
     // the last workgroup to finish resets the launch's counts

@@ -51,6 +51,9 @@ constexpr int kRankRound = 512;
 constexpr int kRankMaxRounds = kLayerMaxN / kRankRound;
 // Most workgroups of one launch (the partial-sum region is sized for it).
 constexpr int kLayerMaxWgs = 512;
+// Most segments one workgroup meets in one phase (its LDS segment table);
+// the host runs the layer kernel only when every workgroup stays within it.
+constexpr int kLayerSegTab = 160;
 
 // One group of the layer (indexed by the public group id).
 struct LayerGroupArgs {
@@ -130,49 +133,96 @@ __host__ __device__ inline bool layer_meets(const LayerArgs& A, int g, uint32_t 
   return w >= (uint32_t)gr.wg_lo && w < (uint32_t)(gr.wg_lo + gr.n_wg);
 }
 
-// Calls f(seg) for each segment of workgroup w in group g, in tile order,
-// with w_lo = w_hi = -1 (the contributors are found by layer_contributors).
+// The tiles of group g that workgroup w meets: t_first, t_first + step, ...
+// below t_end, and w's run [u0, u1) of the group's units. False when w does
+// not work on g.
+__host__ __device__ inline bool layer_group_range(const LayerArgs& A, int g, uint32_t w,
+                                                  uint32_t& t_first, uint32_t& step,
+                                                  uint32_t& t_end, uint32_t& u0, uint32_t& u1) {
+  const LayerGroupArgs& gr = A.g[g];
+  if (!gr.present) return false;
+  u0 = u1 = 0u;
+  if (gr.units == 0) {
+    t_first = w;
+    step = (uint32_t)A.G;
+    t_end = (uint32_t)gr.tiles;
+    return t_first < t_end;
+  }
+  if (w < (uint32_t)gr.wg_lo || w >= (uint32_t)(gr.wg_lo + gr.n_wg)) return false;
+  const uint32_t i = w - (uint32_t)gr.wg_lo;
+  const uint32_t K = (uint32_t)(gr.k_full + gr.k_approx);
+  u0 = layer_run_start(gr, i);
+  u1 = layer_run_start(gr, i + 1);
+  t_first = u0 / K;
+  step = 1u;
+  t_end = (u1 + K - 1u) / K;
+  return t_first < t_end;
+}
+
+// Workgroup w's segment of tile t of group g (its run [u0, u1)), with
+// w_lo = w_hi = -1 unless the group has no selected columns (the contributors
+// are found by layer_contributors).
+__host__ __device__ inline LayerSeg layer_make_seg(const LayerArgs& A, int g, uint32_t w,
+                                                   uint32_t t, uint32_t u0, uint32_t u1) {
+  const LayerGroupArgs& gr = A.g[g];
+  LayerSeg s;
+  s.g = g;
+  s.t = (int32_t)t;
+  if (gr.units == 0) {
+    s.f0 = s.f1 = s.a0 = s.a1 = 0;
+    s.w_lo = s.w_hi = (int32_t)w;
+  } else {
+    const uint32_t K = (uint32_t)(gr.k_full + gr.k_approx);
+    const uint32_t q0 = (u0 > t * K ? u0 - t * K : 0u);
+    const uint32_t q1 = (u1 < (t + 1) * K ? u1 - t * K : K);
+    s.f0 = (int32_t)(q0 * (uint32_t)gr.k_full / K);
+    s.f1 = (int32_t)(q1 * (uint32_t)gr.k_full / K);
+    s.a0 = (int32_t)(q0 * (uint32_t)gr.k_approx / K);
+    s.a1 = (int32_t)(q1 * (uint32_t)gr.k_approx / K);
+    s.w_lo = s.w_hi = -1;
+  }
+  return s;
+}
+
+// Calls f(seg) for each segment of workgroup w in group g, in tile order.
 // A group with no selected columns (units 0) still writes its output: its
 // tiles are dealt to the workgroups round-robin as empty one-contributor
 // segments.
 template <class F>
 __host__ __device__ inline void layer_group_segs(const LayerArgs& A, int g, uint32_t w, F f) {
-  const LayerGroupArgs& gr = A.g[g];
-  if (!gr.present) return;
-  const uint32_t K = (uint32_t)(gr.k_full + gr.k_approx);
-  uint32_t t, step, t_end, u0 = 0u, u1 = 0u;
-  if (gr.units == 0) {
-    t = w;
-    step = (uint32_t)A.G;
-    t_end = (uint32_t)gr.tiles;
-  } else {
-    if (w < (uint32_t)gr.wg_lo || w >= (uint32_t)(gr.wg_lo + gr.n_wg)) return;
-    const uint32_t i = w - (uint32_t)gr.wg_lo;
-    u0 = layer_run_start(gr, i);
-    u1 = layer_run_start(gr, i + 1);
-    t = u0 / K;
-    step = 1u;
-    t_end = (u1 + K - 1u) / K;
-  }
+  uint32_t t, step, t_end, u0, u1;
+  if (!layer_group_range(A, g, w, t, step, t_end, u0, u1)) return;
   // one call site of f (its body is large in the kernel)
-  for (; t < t_end; t += step) {
-    LayerSeg s;
-    s.g = g;
-    s.t = (int32_t)t;
-    if (gr.units == 0) {
-      s.f0 = s.f1 = s.a0 = s.a1 = 0;
-      s.w_lo = s.w_hi = (int32_t)w;
-    } else {
-      const uint32_t q0 = (u0 > t * K ? u0 - t * K : 0u);
-      const uint32_t q1 = (u1 < (t + 1) * K ? u1 - t * K : K);
-      s.f0 = (int32_t)(q0 * (uint32_t)gr.k_full / K);
-      s.f1 = (int32_t)(q1 * (uint32_t)gr.k_full / K);
-      s.a0 = (int32_t)(q0 * (uint32_t)gr.k_approx / K);
-      s.a1 = (int32_t)(q1 * (uint32_t)gr.k_approx / K);
-      s.w_lo = s.w_hi = -1;
-    }
-    f(s);
+  for (; t < t_end; t += step) f(layer_make_seg(A, g, w, t, u0, u1));
+}
+
+// Resumable walk over workgroup w's segments of the groups selected by a
+// predicate, in processing order.
+struct LayerCursor {
+  int32_t oi;
+  uint32_t t, step, t_end, u0, u1;
+};
+
+__host__ __device__ inline void layer_cursor_init(LayerCursor& c) {
+  c.oi = -1;
+  c.t = c.t_end = 0u;
+  c.step = 1u;
+  c.u0 = c.u1 = 0u;
+}
+
+template <class Pred>
+__host__ __device__ inline bool layer_cursor_next(const LayerArgs& A, uint32_t w, Pred take,
+                                                  LayerCursor& c, LayerSeg& s) {
+  while (c.t >= c.t_end) {
+    if (++c.oi >= A.n_order) return false;
+    const int g = A.order[c.oi];
+    c.t = c.t_end = 0u;
+    if (!take(g)) continue;
+    if (!layer_group_range(A, g, w, c.t, c.step, c.t_end, c.u0, c.u1)) c.t = c.t_end = 0u;
   }
+  s = layer_make_seg(A, A.order[c.oi], w, c.t, c.u0, c.u1);
+  c.t += c.step;
+  return true;
 }
 
 // The first and last workgroup that meet tile s.t of group s.g.
@@ -182,6 +232,29 @@ __host__ __device__ inline void layer_contributors(const LayerArgs& A, LayerSeg&
   const uint32_t K = (uint32_t)(gr.k_full + gr.k_approx);
   s.w_lo = gr.wg_lo + (int32_t)layer_run_of(gr, (uint32_t)s.t * K);
   s.w_hi = gr.wg_lo + (int32_t)layer_run_of(gr, ((uint32_t)s.t + 1u) * K - 1u);
+}
+
+// An upper bound on the segments any workgroup meets in the phase of the
+// groups selected by take: per group, the tiles a run of ceil(U / n_wg)
+// units can touch (or, with no selected columns, the tiles dealt
+// round-robin).
+template <class Pred>
+inline uint32_t layer_phase_segs_bound(const LayerArgs& A, Pred take) {
+  uint32_t b = 0;
+  for (int oi = 0; oi < A.n_order; ++oi) {
+    const int g = A.order[oi];
+    const LayerGroupArgs& gr = A.g[g];
+    if (!take(g)) continue;
+    if (gr.units == 0) {
+      b += ((uint32_t)gr.tiles + (uint32_t)A.G - 1u) / (uint32_t)A.G;
+    } else {
+      const uint32_t K = (uint32_t)(gr.k_full + gr.k_approx);
+      const uint32_t run = (gr.units + (uint32_t)gr.n_wg - 1u) / (uint32_t)gr.n_wg;
+      const uint32_t t = (run + K - 2u) / K + 1u;
+      b += t < (uint32_t)gr.tiles ? t : (uint32_t)gr.tiles;
+    }
+  }
+  return b;
 }
 
 hipError_t launch_layer(const LayerArgs& a, int32_t full_fmt, int32_t approx_fmt,

@@ -293,7 +293,8 @@ int spax_layer_step(const spax_layer* L, const spax_layer_io* io,
  * group. Writes at most `cap` records to `out` (may be null with cap 0) and
  * the total number of records to *count.
  *   Errors: SPAX_ENULL, SPAX_EINVAL (the layer kernel does not apply to L,
- *   or workgroups out of range), SPAX_EHIP (workgroups 0 without a device). */
+ *   a workgroup would meet more than 160 row tiles in one phase, or
+ *   workgroups out of range), SPAX_EHIP (workgroups 0 without a device).   */
 int spax_layer_schedule(const spax_layer* L, int32_t workgroups, int32_t* out, int64_t cap,
                         int64_t* count);
 
