@@ -214,9 +214,9 @@ __device__ __attribute__((noinline)) uint32_t rank_group(const uint16_t* __restr
   const uint32_t pad = (uint32_t)(R * kRankRound - n);  // key-0 entries past n
   const uint32_t copy = (uint32_t)(lane & (kHistCopies - 1));
 
-  // 1. keys into LDS (read coherently: down's a is written by this launch),
-  // eight rounds of loads in flight per wave; the round that holds the end
-  // of x is read entry by entry
+  // 1. keys into LDS (plain loads: a launch's own down input is read only
+  // after an agent-scope acquire), eight rounds of loads in flight per wave;
+  // the round that holds the end of x is read entry by entry
   const __amdgpu_buffer_rsrc_t rs = tier_rsrc(reinterpret_cast<const uint8_t*>(x), 2u * n);
   const int Rfull = n / kRankRound;  // rounds entirely inside x
   for (int r0 = rw; r0 < Rfull; r0 += 8 * RW) {
@@ -226,7 +226,7 @@ __device__ __attribute__((noinline)) uint32_t rank_group(const uint16_t* __restr
       const int r = min(r0 + u * RW, Rfull - 1);
       v[u] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
                                            rs, 2u * (uint32_t)(r * kRankRound + 8 * lane), 0,
-                                           kCoherent));
+                                           0));
     }
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
@@ -243,9 +243,9 @@ __device__ __attribute__((noinline)) uint32_t rank_group(const uint16_t* __restr
 #pragma unroll
     for (int h = 0; h < 8; h += 2) {
       uint32_t lo = 0u, hi = 0u;
-      if (e + h < n) lo = __builtin_amdgcn_raw_buffer_load_b16(rs, 2u * (e + h), 0, kCoherent);
+      if (e + h < n) lo = __builtin_amdgcn_raw_buffer_load_b16(rs, 2u * (e + h), 0, 0);
       if (e + h + 1 < n)
-        hi = __builtin_amdgcn_raw_buffer_load_b16(rs, 2u * (e + h + 1), 0, kCoherent);
+        hi = __builtin_amdgcn_raw_buffer_load_b16(rs, 2u * (e + h + 1), 0, 0);
       wd[h / 2] = lo | (hi << 16);
     }
     const uint4 v = make_uint4(wd[0], wd[1], wd[2], wd[3]);
@@ -479,7 +479,9 @@ __device__ __forceinline__ void wait_gate_up(const LayerArgs& A) {
     }
     __builtin_amdgcn_s_sleep(2);
   }
-  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  // acquire at agent scope: the caches are invalidated, so plain loads of a
+  // by any wave of the workgroup (after its barrier) see the gate/up stores
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
 }
 
 // Ranking waves: rank each further group of the first phase that the
@@ -509,7 +511,9 @@ __device__ __forceinline__ void rank_role(const LayerArgs& A, int first, uint32_
 // list positions. A wave streams all its shares as one sequence through a
 // ring of loads in registers: the load for ring slot u is issued as soon as
 // slot u's previous load has been added, across segment boundaries, so the
-// ring never drains between segments. When a segment's last load has been
+// ring never drains between segments. The rings are short (4 KB in flight
+// per wave): with more requests in flight the chip's scattered 1 KB reads
+// got slower, not faster (measured on 7B layers). When a segment's last load has been
 // added, the wave hands its fp32 partial of the tile's 512 rows to the
 // reduction wave through LDS (two slot sets, so a wave can run one segment
 // ahead) and starts the next sum. A share with no positions still costs one
@@ -537,13 +541,13 @@ struct Form;
 template <>
 struct Form<kFp16> {
   using V = uint4;
-  static constexpr int kRing = 8;
+  static constexpr int kRing = 4;
   static constexpr int kPos = 1;  // list positions per load
 };
 template <>
 struct Form<kInt4> {
   using V = uint4;
-  static constexpr int kRing = 6;
+  static constexpr int kRing = 4;
   static constexpr int kPos = 4;
   static constexpr uint32_t kLaneBytes = 16;
   static __device__ __forceinline__ V load(__amdgpu_buffer_rsrc_t r, uint32_t o) {
@@ -556,7 +560,7 @@ struct Form<kInt4> {
 template <>
 struct Form<kInt2> {
   using V = uint2;
-  static constexpr int kRing = 8;
+  static constexpr int kRing = 6;
   static constexpr int kPos = 4;
   static constexpr uint32_t kLaneBytes = 8;
   static __device__ __forceinline__ V load(__amdgpu_buffer_rsrc_t r, uint32_t o) {
@@ -755,7 +759,7 @@ __device__ __forceinline__ void stream_seq(const LayerArgs& A, bool late, bool f
       const uint32_t col = live ? (uint32_t)__builtin_amdgcn_readlane(colv, jj & 63) : 0u;
       d[u] = __builtin_bit_cast(
           uint4, __builtin_amdgcn_raw_buffer_load_b128(sh.rs, sh.off, col * sh.stride, 0));
-      xs[u] = live ? __builtin_amdgcn_raw_buffer_load_b16(sh.xr, 0u, 2u * col, kCoherent) : 0u;
+      xs[u] = live ? __builtin_amdgcn_raw_buffer_load_b16(sh.xr, 0u, 2u * col, 0) : 0u;
     } else {
       const int q = lane >> 4;
       const int pos = 4 * jj + q;
@@ -764,7 +768,7 @@ __device__ __forceinline__ void stream_seq(const LayerArgs& A, bool late, bool f
           (uint32_t)__builtin_amdgcn_ds_bpermute((min(pos, max(sh.n - 1, 0)) & 63) << 2, colv);
       const uint32_t c = sh.n > 0 ? col : 0u;
       d[u] = Fm::load(sh.rs, c * sh.stride + sh.off);
-      xs[u] = live ? __builtin_amdgcn_raw_buffer_load_b16(sh.xr, 2u * c, 0, kCoherent) : 0u;
+      xs[u] = live ? __builtin_amdgcn_raw_buffer_load_b16(sh.xr, 2u * c, 0, 0) : 0u;
       if constexpr (FMT == kSign2)
         ss[u] = __builtin_amdgcn_raw_buffer_load_b32(sh.sr, 4u * c, 0, 0);
       else
@@ -1037,16 +1041,18 @@ __global__ __launch_bounds__(kGemvThreads) void layer_kernel(LayerArgs A) {
   const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
   const int first = first_ranked(A, w);
   if (first >= 0 && t == 0) set_need(A, first, w);
-  if (wave == kWaves - 1) build_segtab(A, w, false);  // the first phase's segments
   __syncthreads();
+  // the first phase's segments, by the last wave while the others load the
+  // first ranking's keys (it has no keys to load for inputs up to 7680)
+  if (wave == kWaves - 1) build_segtab(A, w, false);
   uint32_t epoch = 0u;
   if (first >= 0) {
     const LayerGroupArgs& gr = A.g[first];
     rank_group<kWaves>(gr.x, gr.n, (uint32_t)gr.k_full, (uint32_t)(gr.k_full + gr.k_approx),
                        gr.list_off, 0u, A.sync + 2);
     if (t == 0) sm.ready[first] = 1u;
-    __syncthreads();
   }
+  __syncthreads();  // the first lists and the segment table are in LDS
   uint32_t k = 0u;  // segments handed over (streaming and reduction waves)
   // phase 0: every group but a late down; phase 1: down, once every gate/up
   // tile has written a (one call site per role keeps the streaming code

@@ -1,19 +1,16 @@
 """Benchmark of the three-tier activation-sparse decode path on one MI355X.
 
-Headline workload (no --config): 7B-shaped attention projections (q, k, v, o,
-each 4096 x 4096, fp16 weights ~ N(0, 0.02), column-major) with an int4
-group-128 compressed copy, tiers skip / approx / full = 40 / 30 / 30 % of the
-4096 inputs, batch 1, 32 decode tokens of fresh Laplace(0, 1) activations per
-step.
-
-One step = the whole per-token path for 32 tokens, through spax_layer_step:
-    rank h -> tier lists -> tiered product of q, k, v (rows stacked)
-    rank z -> tier lists -> tiered product of o
-(each group is one fused launch: the ranking runs inside the product).
-Token t reads weight set t (32 distinct sets = 32 decoder layers' attention
-weights, 5.4 GB), so a set is read again only after the other 31 have
-streamed through, as in decoding a 32-layer model: weights come from HBM,
-not from the 256 MB last-level cache.
+Headline workload (no --config): config 4, the 32-layer 7B projection
+stream. Each layer has the seven projections of a 7B decoder layer in four
+groups (q, k, v stacked 12288 x 4096 on h; o 4096 x 4096 on z; gate/up
+interleaved 22016 x 4096 on x; down 4096 x 11008 on a = silu(g) * u), fp16
+weights ~ N(0, 0.02) column-major with an int4 group-128 compressed copy,
+tiers skip / approx / full = 50 / 25 / 25 % of each group's inputs, batch 1,
+inputs ~ Laplace(0, 1) fp16. One step = 4 tokens x 32 layers = 128 layer
+steps through spax_layer_step (one launch of the layer kernel each: every
+group's ranking, tiered product and the SwiGLU epilogue). Layer l reads
+weight set l (32 distinct sets, 13 GB), so weights come from HBM, not from
+the 256 MB last-level cache.
 
 The step is captured once in a HIP graph (through torch's graph capture on
 the stream the library launches on) and replayed; warmup replays are
@@ -22,31 +19,30 @@ synchronisations. Inputs are resident in HBM before timing starts.
 
 Printed: ONE JSON line with the throughput (effective weight GB/s on the
 algorithmic bytes), microseconds per tiered projection, the roofline of the
-product kernel and the CPU oracle timed on a bounded sample of the same
-workload. The per-launch duration of the product kernel comes from graph
-replays of one group's 32 launches back to back, timed with events on the
-launch stream.
+layer kernel (its average launch duration from the timed replays, events
+on the launch stream) and the CPU oracle timed on a bounded sample of the
+same workload at one thread and at all host cores.
 
-Other workloads (one JSON line each, same keys; no roofline / CPU legs):
-    --config 1   single 1024 x 1024 layer, 50/25/25
+Other workloads (one JSON line each, same legs):
+    --config 1   single 1024 x 1024 layer, 50/25/25 (no CPU leg)
+    --config 2   7B-shaped attention projections q, k, v, o (4096 x 4096),
+                 40/30/30, 32 tokens over 32 weight sets
     --config 3   7B SwiGLU FFN (gate/up 11008x4096, down 4096x11008), skip
-                 30 / 50 / 70 %, approx 20 % (three lines)
-    --config 4   32-layer 7B projection stream, 50/25/25, weights in HBM;
-                 with --host the weights sit in pinned host memory and only
-                 the selected columns cross the host link
+                 30 / 50 / 70 %, approx 20 % (three lines, no CPU leg)
+    --config 4 --host   weights in pinned host memory; only the selected
+                 columns cross the host link
     --config 5   70B-shaped FFN, int4 full tier, int2 approx, 50/30/20
 
-    --approx sign2  the headline workload with the SpAx page's two-scale 2-bit
+    --approx sign2   config 2 (or 1) with the SpAx page's two-scale 2-bit
                  sign code (section 5.1, Eq. 4) as the middle tier
+    --approx trellis config 2 (or 1) with the trellis-coded middle tier
+                 (section 5.1; GPU Viterbi encoder, 8 weight sets)
     --calibrate  the offline tier-size calibration of section 5.2 (steps 1 and
                  2) on the 7B attention groups, through the library
-    --approx trellis  the headline workload with the trellis-coded middle
-                 tier (section 5.1; GPU Viterbi encoder, 8 weight sets); also
-                 with --config 1
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--eager]
                     [--no-cpu-baseline] [--calib-copy] [--config N] [--host]
-                    [--approx int4|sign2]
+                    [--approx int4|sign2|trellis] [--select ...]
 """
 from __future__ import annotations
 
@@ -69,8 +65,12 @@ KERNEL = 0
 PCIE5_X16_GBS = 64.0
 
 
-PMC_SUMMARY = os.path.join(ROOT, "profiles", "gemv_kernel_7b_attention_pmc.txt")
-KERNEL_SOURCES = ("gemv.hip", "block_common.h", "api.cpp", "spax_internal.h")
+# counter summaries of the layer kernel per workload (FETCH_SIZE and
+# WRITE_SIZE runs), valid while the kernel sources are unchanged
+PMC_SUMMARY = {4: os.path.join(ROOT, "profiles", "layer_kernel_7b_stream_pmc.txt"),
+               5: os.path.join(ROOT, "profiles", "layer_kernel_70b_ffn_pmc.txt"),
+               2: os.path.join(ROOT, "profiles", "layer_kernel_7b_attention_pmc.txt")}
+KERNEL_SOURCES = ("layer.hip", "layer_plan.h", "block_common.h", "spax_internal.h", "api.cpp")
 
 
 def kernel_source_hash() -> str:
@@ -82,13 +82,14 @@ def kernel_source_hash() -> str:
     return h.hexdigest()
 
 
-def measured_traffic():
-    """HBM bytes per launch of the product kernel from the committed counter
-    summary (FETCH_SIZE and WRITE_SIZE, scaled by a plain copy's reading),
-    or None when the kernel sources changed since the counters were taken."""
+def measured_traffic(config: int):
+    """HBM bytes per launch of the layer kernel from the committed counter
+    summary of this workload (FETCH_SIZE and WRITE_SIZE, scaled by a plain
+    copy's reading), or None when there is none or the kernel sources
+    changed since the counters were taken."""
     try:
-        text = open(PMC_SUMMARY).read()
-    except OSError:
+        text = open(PMC_SUMMARY[config]).read()
+    except (OSError, KeyError):
         return None
     vals = {}
     for line in text.splitlines():
@@ -99,6 +100,17 @@ def measured_traffic():
     if vals.get("sha") != kernel_source_hash() or "traffic" not in vals:
         return None
     return int(vals["traffic"])
+
+
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    import platform
+    return platform.processor() or "unknown"
 
 
 def log(msg: str) -> None:
@@ -139,9 +151,12 @@ class Spec:
                 + (", weights in pinned host memory" if self.host else ""))
 
 
-def headline_spec(approx_fmt: str = "int4") -> Spec:
+def attention_spec(approx_fmt: str = "int4") -> Spec:
     return Spec(2, "7B-shaped attention projections q,k,v,o 4096x4096", 4096, 0, True,
                 approx_fmt=approx_fmt, split=(40, 30, 30))
+
+
+HEADLINE_CONFIG = 4
 
 
 def specs_for(config: int, host: bool, approx: str = "int4"):
@@ -154,7 +169,7 @@ def specs_for(config: int, host: bool, approx: str = "int4"):
         return [Spec(1, "single linear layer 1024x1024", 1024, 0, False, o_only=True,
                      approx_fmt=approx)]
     if config == 2:
-        return [headline_spec()]
+        return [attention_spec(approx)]
     if config == 3:
         return [Spec(3, f"7B-shaped SwiGLU FFN gate/up 11008x4096, down 4096x11008", 4096, 11008,
                      False, split=(s, 20, 80 - s), sets=16) for s in (30, 50, 70)]
@@ -172,6 +187,43 @@ def specs_for(config: int, host: bool, approx: str = "int4"):
 
 
 FMT = {"fp16": 1, "int4": 2, "int2": 3, "sign2": 4, "trellis": 5}
+
+
+def group_shapes(spec: Spec) -> dict:
+    """Stored (rows, cols) of each present group: QKV, O, GATE_UP, DOWN."""
+    H, I = spec.hidden, spec.inter
+    shapes = {}
+    if spec.attn:
+        shapes[0] = (3 * H, H)
+    if spec.attn or spec.o_only:
+        shapes[1] = (H, H)
+    if I:
+        shapes[2] = (2 * I, H)
+        shapes[3] = (H, I)
+    return shapes
+
+
+def group_counts(spec: Spec, g: int):
+    import workloads as WL
+    n = spec.inter if g == 3 else spec.hidden
+    return WL.tier_counts(n, WL.TierSplit(*spec.split))
+
+
+def group_bytes(spec: Spec, g: int) -> int:
+    """Bytes the method must move for group g of one layer step (selected
+    columns, codes and scales, x, index lists, y) -- see
+    workloads.accounting."""
+    from workloads.accounting import gemv_algorithmic_bytes
+    rows, cols = group_shapes(spec)[g]
+    kf, ka = group_counts(spec, g)
+    b = gemv_algorithmic_bytes(rows, cols, kf, ka, spec.full_fmt, spec.approx_fmt)
+    if g == 2:          # gate/up writes a = silu(g) * u: half the stored rows
+        b -= rows
+    return b
+
+
+def layer_bytes(spec: Spec) -> int:
+    return sum(group_bytes(spec, g) for g in group_shapes(spec))
 
 
 class Workload:
@@ -266,19 +318,11 @@ class Workload:
         self.copy = spax.copy_init(torch.cuda.Stream()) if spec.host else None
         torch.cuda.synchronize()
 
-    # bytes the method must move (selected columns, codes and scales, x,
-    # index lists, y) -- see workloads.accounting
     def group_bytes(self, g: int) -> int:
-        from workloads.accounting import gemv_algorithmic_bytes
-        rows, cols = self.shapes[g]
-        kf, ka = self.k[g]
-        b = gemv_algorithmic_bytes(rows, cols, kf, ka, self.spec.full_fmt, self.spec.approx_fmt)
-        if g == 2:          # gate/up writes a = silu(g) * u: half the stored rows
-            b -= rows
-        return b
+        return group_bytes(self.spec, g)
 
     def layer_bytes(self) -> int:
-        return sum(self.group_bytes(g) for g in range(4) if self.present[g])
+        return layer_bytes(self.spec)
 
     def step_bytes(self) -> int:
         return self.slots * self.layer_bytes()
@@ -299,46 +343,11 @@ class Workload:
 
     def step(self, stream=None):
         """Enqueue one step: every (token, layer) slot runs the layer's groups
-        (one fused launch per group with device-resident weights)."""
+        (one layer-kernel launch per slot with device-resident weights)."""
         spax = self.spax
         for i in range(self.slots):
             spax.layer_step(self.layer_of(i), self.io[i], self.ws, self.ws_bytes,
                             compute_stream=stream, copy=self.copy)
-
-    def launches(self, group: int):
-        """The product launches of one group for every slot, back to back."""
-        spax = self.spax
-        layers = self.single[group]
-
-        def run(stream):
-            for i in range(self.slots):
-                spax.layer_step(layers[i % len(layers)], self.io[i], self.ws, self.ws_bytes,
-                                compute_stream=stream)
-        return run
-
-
-def graph_launch_time(run, stream, launches: int, reps: int = 5) -> float:
-    """Average duration (s) of one launch: `run` (launches kernels back to
-    back) is captured in a HIP graph, replayed `reps` times between two
-    events on the launch stream."""
-    import torch
-    with torch.cuda.stream(stream):
-        run(stream)
-        torch.cuda.synchronize()
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g, stream=stream):
-            run(stream)
-        torch.cuda.synchronize()
-        g.replay()
-        torch.cuda.synchronize()
-        e0 = torch.cuda.Event(enable_timing=True)
-        e1 = torch.cuda.Event(enable_timing=True)
-        e0.record(stream)
-        for _ in range(reps):
-            g.replay()
-        e1.record(stream)
-        torch.cuda.synchronize()
-    return e0.elapsed_time(e1) * 1e-3 / (reps * launches)
 
 
 def time_steps(wl: Workload, steps: int, warmup: int, eager: bool):
@@ -401,43 +410,88 @@ def host_link_peak_gbs() -> float:
     return 3 * n / (e0.elapsed_time(e1) * 1e-3) / 1e9
 
 
-def cpu_baseline(kf: int, ka: int, budget_s: float = 15.0, approx_fmt: str = "int4"):
-    """The CPU oracle on a bounded sample of the headline workload: weight set
-    0, tokens 0, 1, ... each ranking h and z and forming q, k, v and o, until
-    about `budget_s` seconds of timed work are done."""
+def _oracle_layer(spec: Spec, layer: int = 0):
+    """The oracle's stores of one layer of the workload (weight set `layer`)
+    and its tier counts per group."""
     import oracle as O
     import workloads as WL
-    from workloads.accounting import gemv_algorithmic_bytes
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
-    except Exception:  # pragma: no cover - threadpoolctl missing
-        threads = 1
-    H, cfg = 4096, 2
+    H, I = spec.hidden, spec.inter
+    split = WL.TierSplit(*spec.split)
     mats = {}
-    for m in ("q", "k", "v", "o"):
-        Wt = WL.weights_fp16(cfg, 0, m, H, H, 0.02)
-        mats[m] = (O.ColumnStore("fp16", Wt), O.ColumnStore(approx_fmt, Wt))
-    per_proj = gemv_algorithmic_bytes(H, H, kf, ka, "fp16", approx_fmt)
-    done, t_acc, tok = 0, 0.0, 0
-    while t_acc < budget_s and tok < 32:
-        h = WL.laplace_fp16(cfg, 0, "h", tok, H)
-        z = WL.laplace_fp16(cfg, 0, "z", tok, H)
-        t0 = time.perf_counter()
-        Fh, Ah = O.plan_tiers(h, kf, ka)
-        for m in ("q", "k", "v"):
-            O.tiered_gemv_fp16(h, Fh, Ah, *mats[m])
-        Fz, Az = O.plan_tiers(z, kf, ka)
-        O.tiered_gemv_fp16(z, Fz, Az, *mats["o"])
-        t_acc += time.perf_counter() - t0
-        done += 4
-        tok += 1
-    gbs = done * per_proj / t_acc / 1e9
-    return {"value": round(gbs, 4), "unit": "GB/s", "cores": int(threads), "kind": "oracle",
-            "sample": (f"{tok} tokens x (rank h, q, k, v; rank z, o) on weight set 0 "
-                       f"({done} projections, {t_acc:.1f} s; numpy fp64)"),
-            "us_per_projection": round(t_acc / done * 1e6, 1),
-            "host_cores": os.cpu_count()}
+
+    def add(name, rows, cols):
+        Wt = WL.weights_fp16(spec.config, layer, name, rows, cols, spec.std)
+        mats[name] = (O.ColumnStore(spec.full_fmt, Wt), O.ColumnStore(spec.approx_fmt, Wt))
+
+    if spec.attn:
+        for m in ("q", "k", "v", "o"):
+            add(m, H, H)
+    elif spec.o_only:
+        Wt = WL.weights_fp16(spec.config, layer, "w", H, H, spec.std)
+        mats["o"] = (O.ColumnStore(spec.full_fmt, Wt), O.ColumnStore(spec.approx_fmt, Wt))
+    if I:
+        add("gate", I, H)
+        add("up", I, H)
+        add("down", H, I)
+    kq = WL.tier_counts(H, split)
+    ks = {"qkv": kq, "o": kq, "ffn": kq, "down": WL.tier_counts(I, split) if I else (0, 0)}
+    return mats, ks
+
+
+def cpu_baseline(spec: Spec, layer_bytes: int, budget_s: float = 8.0, max_tokens: int = 32):
+    """The CPU oracle (numpy fp64, test infrastructure) on a bounded sample
+    of the workload: weight set 0, tokens 0, 1, ... each running every group
+    of the layer (rank, tiered products, SwiGLU, rank a, down) until about
+    `budget_s` seconds of timed work are done, once with the BLAS pool at one
+    thread and once at all host cores."""
+    import oracle as O
+    import workloads as WL
+    from threadpoolctl import threadpool_info, threadpool_limits
+    t_build = time.perf_counter()
+    mats, ks = _oracle_layer(spec)
+    log(f"oracle stores built in {time.perf_counter() - t_build:.1f} s")
+    H = spec.hidden
+
+    def leg(threads):
+        with threadpool_limits(limits=threads):
+            used = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+            done, t_acc = 0, 0.0
+            while t_acc < budget_s and done < max_tokens:
+                tok = done
+                h = WL.laplace_fp16(spec.config, 0, "h", tok, H) if spec.attn else None
+                z = (WL.laplace_fp16(spec.config, 0, "z", tok, H)
+                     if spec.attn or spec.o_only else None)
+                x = WL.laplace_fp16(spec.config, 0, "x", tok, H) if spec.inter else None
+                t0 = time.perf_counter()
+                O.layer_step(mats, ks, h=h, z=z, x=x)
+                t_acc += time.perf_counter() - t0
+                done += 1
+        return {"value": round(done * layer_bytes / t_acc / 1e9, 4), "cores": int(used),
+                "layer_steps": done, "seconds": round(t_acc, 2),
+                "ms_per_layer_step": round(t_acc / done * 1e3, 1)}
+
+    one = leg(1)
+    log(f"oracle, 1 thread: {one['value']} GB/s ({one['ms_per_layer_step']} ms per layer step)")
+    ncpu = os.cpu_count() or 1
+    allc = leg(ncpu)
+    log(f"oracle, {allc['cores']} threads: {allc['value']} GB/s")
+    return {"value": allc["value"], "unit": "GB/s", "cores": allc["cores"], "kind": "oracle",
+            "sample": (f"weight set 0 (one layer's groups), tokens 0..{allc['layer_steps'] - 1}:"
+                       f" {allc['layer_steps']} layer steps in {allc['seconds']} s at "
+                       f"{allc['cores']} threads; {one['layer_steps']} in {one['seconds']} s at "
+                       "1 thread; numpy fp64, algorithmic bytes as on the GPU"),
+            "one_thread": {"value": one["value"], "unit": "GB/s", "cores": 1,
+                           "ms_per_layer_step": one["ms_per_layer_step"]},
+            "all_cores": {"value": allc["value"], "unit": "GB/s", "cores": allc["cores"],
+                          "ms_per_layer_step": allc["ms_per_layer_step"]},
+            "cpu_model": cpu_model(), "nproc": ncpu}
+
+
+def dtype_label(spec: Spec) -> str:
+    name = {"fp16": "fp16", "int4": "int4 g128 codes", "int2": "int2 g128 codes",
+            "sign2": "2-bit sign codes", "trellis": "2-bit trellis codes"}
+    return (f"{name[spec.full_fmt]} full + {name[spec.approx_fmt]} approx weights, fp16 "
+            "activations, fp32 accumulate, fp16 out")
 
 
 def result_line(spec: Spec, wl: Workload, args, sec_step: float, mode: str, extra=None):
@@ -455,7 +509,7 @@ def result_line(spec: Spec, wl: Workload, args, sec_step: float, mode: str, extr
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "fp32",
+        "dtype": dtype_label(spec),
         "data": "synthetic",
         "us_per_projection": round(sec_step / n_proj * 1e6, 3),
         "frac_hbm_peak": round(gbs / HBM_PEAK_GBS, 4),
@@ -475,57 +529,62 @@ def result_line(spec: Spec, wl: Workload, args, sec_step: float, mode: str, extr
     return line
 
 
-def run_headline(args):
-    import torch
+def layer_kernel_runs(wl: Workload) -> bool:
+    """Whether spax_layer_step runs these layers as one layer-kernel launch."""
+    if KERNEL != 0 or wl.spec.host:
+        return False
+    try:
+        wl.spax.layer_schedule(wl.layers[0], 0)
+        return True
+    except wl.spax.SpaxError:
+        return False
 
-    import activation_sparse_decode_token_amd as spax
-    spax.lib()  # fails loudly when the HIP library is missing
-    if not torch.cuda.is_available():
-        raise SystemExit("bench.py needs a GPU (torch.cuda.is_available() is False)")
-    spec = headline_spec(args.approx)
-    spec.sets = args.sets
-    if args.approx == "trellis":
-        # the offline Viterbi encoding takes about a second per weight set
-        # (on the GPU, 16 GB of backpointers per launch): 8 sets (1.4 GB of
-        # weights, still far past the 256 MB last-level cache)
-        import activation_sparse_decode_token_amd.layouts as LY
-        LY.TRELLIS_WS_BYTES = 16 << 30
-        spec.sets = min(args.sets, 8)
-    log(f"device {torch.cuda.get_device_name(0)}; building {spec.sets} weight sets")
+
+def roofline(spec: Spec, wl: Workload, sec_step: float, mode: str):
+    """The layer kernel's roofline: algorithmic bytes of one layer step over
+    its average launch duration (the timed replays' event time on the launch
+    stream over the launches they hold)."""
+    if mode != "graph" or not layer_kernel_runs(wl):
+        return None
+    t_launch = sec_step / wl.slots
+    achieved = wl.layer_bytes() / t_launch / 1e9
+    log(f"layer kernel: {t_launch * 1e6:.2f} us per launch, {achieved:.0f} GB/s on algorithmic "
+        "bytes")
+    return {
+        "bound": "hbm",
+        "achieved": round(achieved, 1),
+        "peak": HBM_PEAK_GBS,
+        "unit": "GB/s",
+        "frac": round(achieved / HBM_PEAK_GBS, 4),
+        "traffic": measured_traffic(spec.config) if spec.approx_fmt in ("int4", "int2") else None,
+        "kernel": "layer_kernel: every group of one decoder layer (ranking, tiered "
+                  "gather-GEMV, SwiGLU) in one launch",
+        "avg_launch_us": round(t_launch * 1e6, 3),
+        "launches_per_step": wl.slots,
+        "bytes_per_launch": wl.layer_bytes(),
+    }
+
+
+def run_spec(spec: Spec, args, cpu_leg: bool):
+    import torch
+    log(f"config {spec.config}: {spec.describe()}")
     t0 = time.perf_counter()
     wl = Workload(spec)
-    log(f"weights ready in {time.perf_counter() - t0:.1f} s; k_full={wl.k[0][0]} "
-        f"k_approx={wl.k[0][1]}")
-    sec_step, _, mode, stream = time_steps(wl, args.steps, args.warmup, args.eager)
-
-    # Per-launch duration of the product kernel, event-timed on its stream:
-    # each group's launches back to back in a graph (host launch cost is not
-    # on the GPU timeline).
-    qkv_b, o_b = wl.group_bytes(0), wl.group_bytes(1)
-    roof = None
-    if mode == "graph":
-        t_qkv = graph_launch_time(wl.launches(0), stream, wl.slots)
-        t_o = graph_launch_time(wl.launches(1), stream, wl.slots)
-        achieved = (qkv_b + o_b) / (t_qkv + t_o) / 1e9
-        log(f"product kernel: qkv {t_qkv * 1e6:.2f} us, o {t_o * 1e6:.2f} us per launch, "
-            f"{achieved:.0f} GB/s on algorithmic bytes")
-        roof = {
-            "bound": "hbm",
-            "achieved": round(achieved, 1),
-            "peak": HBM_PEAK_GBS,
-            "unit": "GB/s",
-            "frac": round(achieved / HBM_PEAK_GBS, 4),
-            # the committed counters were taken on the int4 workload
-            "traffic": measured_traffic() if args.approx == "int4" else None,
-            "kernel": "gemv_kernel: fused tier selection + tiered gather-GEMV "
-                      + {"int4": "(fp16 full, int4 g128 approx)",
-                         "sign2": "(fp16 full, two-scale 2-bit sign approx)",
-                         "trellis": "(fp16 full, trellis-coded 2-bit approx, codebook in LDS)"}
-                      [args.approx],
-            "avg_launch_us": round((t_qkv + t_o) / 2 * 1e6, 3),
-            "launch_us": {"qkv": round(t_qkv * 1e6, 3), "o": round(t_o * 1e6, 3)},
-            "bytes_per_launch": {"qkv": qkv_b, "o": o_b},
+    log(f"weights ready in {time.perf_counter() - t0:.1f} s")
+    eager = args.eager or spec.host
+    sec_step, _, mode, _ = time_steps(wl, args.steps, args.warmup, eager)
+    extra = {"roofline": roofline(spec, wl, sec_step, mode)}
+    if spec.host:
+        peak = host_link_peak_gbs()
+        link = wl.step_bytes() / sec_step / 1e9
+        extra["host_link"] = {
+            "achieved": round(link, 2), "unit": "GB/s",
+            "copy_peak_measured": round(peak, 2), "nominal_pcie5_x16": PCIE5_X16_GBS,
+            "frac_of_measured_peak": round(link / peak, 4),
+            "note": "selected columns and scales copied from pinned host memory each "
+                    "step, overlapped with the product; bytes = algorithmic bytes",
         }
+        log(f"host link: {link:.1f} GB/s effective, plain pinned copy {peak:.1f} GB/s")
     if args.calib_copy:
         a = torch.empty(256 << 20, dtype=torch.uint8, device="cuda:0")
         b = torch.empty_like(a)
@@ -534,48 +593,42 @@ def run_headline(args):
         b.copy_(a)
         torch.cuda.synchronize()
         log("calibration copy: 268435456 bytes read, 268435456 bytes written")
+    layer_b = wl.layer_bytes()
+    line = result_line(spec, wl, args, sec_step, mode, extra)
+    del wl
+    torch.cuda.empty_cache()
     base = None
-    if not args.no_cpu_baseline and args.approx != "trellis":
-        # (the trellis oracle's numpy Viterbi needs seconds per 4096-row
-        # column, so that line has no CPU leg)
+    if cpu_leg and not args.no_cpu_baseline and spec.approx_fmt != "trellis":
+        # (the trellis oracle's numpy Viterbi needs seconds per column, so
+        # that line has no CPU leg)
         log("timing the CPU oracle on a bounded sample")
-        base = cpu_baseline(*wl.k[0], approx_fmt=args.approx)
-    return result_line(spec, wl, args, sec_step, mode, {"roofline": roof, "cpu_baseline": base})
+        base = cpu_baseline(spec, layer_b, max_tokens=2 if spec.config == 5 else 32)
+    line["cpu_baseline"] = base
+    return line
 
 
-def run_config(args):
+def run_main(args):
     import torch
 
     import activation_sparse_decode_token_amd as spax
-    spax.lib()
+    spax.lib()  # fails loudly when the HIP library is missing
     if not torch.cuda.is_available():
         raise SystemExit("bench.py needs a GPU (torch.cuda.is_available() is False)")
-    lines = []
-    for spec in specs_for(args.config, args.host, args.approx):
-        log(f"config {spec.config}: {spec.describe()}")
-        t0 = time.perf_counter()
-        wl = Workload(spec)
-        log(f"weights ready in {time.perf_counter() - t0:.1f} s")
-        eager = args.eager or spec.host
-        sec_step, _, mode, _ = time_steps(wl, args.steps, args.warmup, eager)
-        extra = {}
-        if spec.host:
-            peak = host_link_peak_gbs()
-            link = wl.step_bytes() / sec_step / 1e9
-            extra["host_link"] = {
-                "achieved": round(link, 2), "unit": "GB/s",
-                "copy_peak_measured": round(peak, 2), "nominal_pcie5_x16": PCIE5_X16_GBS,
-                "frac_of_measured_peak": round(link / peak, 4),
-                "note": "selected columns and scales copied from pinned host memory each "
-                        "step, overlapped with the product; bytes = algorithmic bytes",
-            }
-            log(f"host link: {link:.1f} GB/s effective, plain pinned copy {peak:.1f} GB/s")
-        line = result_line(spec, wl, args, sec_step, mode, extra)
+    log(f"device {torch.cuda.get_device_name(0)}")
+    config = HEADLINE_CONFIG if args.config is None else args.config
+    specs = specs_for(config, args.host, args.approx)
+    for spec in specs:
+        if config == 2:
+            spec.sets = args.sets
+            if spec.approx_fmt == "trellis":
+                # the offline Viterbi encoding takes about a second per weight
+                # set (16 GB of backpointers per launch): 8 sets, still far
+                # past the 256 MB last-level cache
+                import activation_sparse_decode_token_amd.layouts as LY
+                LY.TRELLIS_WS_BYTES = 16 << 30
+                spec.sets = min(args.sets, 8)
+        line = run_spec(spec, args, cpu_leg=config in (2, 4, 5) and not spec.host)
         print(json.dumps(line), flush=True)
-        lines.append(line)
-        del wl
-        torch.cuda.empty_cache()
-    return lines
 
 
 def run_calibrate(args):
@@ -648,18 +701,18 @@ def parse():
     p.add_argument("--steps", type=int, default=50)
     p.add_argument("--warmup", type=int, default=5)
     p.add_argument("--sets", type=int, default=32,
-                   help="distinct weight sets rotated over the tokens (headline; default 32)")
+                   help="distinct weight sets rotated over the tokens (config 2; default 32)")
     p.add_argument("--eager", action="store_true",
                    help="launch every kernel from Python instead of replaying a graph")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--calib-copy", action="store_true",
                    help="also run one plain 256 MiB device copy (counter calibration)")
     p.add_argument("--config", type=int, default=None,
-                   help="run another benchmark workload (1, 3, 4, 5) instead of the headline")
+                   help="benchmark workload (1-5; default 4, the 32-layer 7B stream)")
     p.add_argument("--host", action="store_true",
                    help="with --config 4: weights in pinned host memory")
     p.add_argument("--approx", choices=("int4", "sign2", "trellis"), default="int4",
-                   help="middle tier of the headline workload or of --config 1: int4 "
+                   help="middle tier of config 2 or config 1: int4 "
                         "group-128 (default), the two-scale 2-bit sign code or the trellis code")
     p.add_argument("--calibrate", action="store_true",
                    help="run the offline tier-size calibration (steps 1 and 2) on the 7B "
@@ -684,10 +737,7 @@ def main():
     if args.calibrate:
         run_calibrate(args)
         return
-    if args.config is not None and args.config != 2:
-        run_config(args)
-        return
-    print(json.dumps(run_headline(args)), flush=True)
+    run_main(args)
 
 
 if __name__ == "__main__":

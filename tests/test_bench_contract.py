@@ -35,17 +35,45 @@ def test_headline_algorithmic_bytes_by_hand():
     assert gemv_algorithmic_bytes(12288, 4096, kf, ka, "fp16", "int4") == qkv
 
 
+def test_headline_is_the_32_layer_7b_stream():
+    spec = bench.specs_for(bench.HEADLINE_CONFIG, False)[0]
+    assert bench.HEADLINE_CONFIG == 4 and not spec.host
+    assert (spec.hidden, spec.inter, spec.attn, spec.split) == (4096, 11008, True, (50, 25, 25))
+    assert spec.tokens * spec.layers_per_token == 128 and spec.sets == 32
+
+
+def test_config4_layer_bytes_by_hand():
+    # 7B layer at skip/approx/full 50/25/25: 1024 + 1024 of 4096 inputs, 2752 +
+    # 2752 of down's 11008; per group: fp16 full columns, int4 code columns
+    # (half a byte per row plus an fp16 scale per 128 rows), x, the two int32
+    # index lists, y (gate/up: a, half its stored rows)
+    spec = bench.specs_for(4, False)[0]
+    assert bench.group_counts(spec, 0) == (1024, 1024)
+    assert bench.group_counts(spec, 3) == (2752, 2752)
+    qkv = 1024 * 12288 * 2 + 1024 * (12288 // 2 + 2 * 96) + 4096 * 2 + 4 * 2048 + 12288 * 2
+    o = 1024 * 4096 * 2 + 1024 * (4096 // 2 + 2 * 32) + 4096 * 2 + 4 * 2048 + 4096 * 2
+    gu = 1024 * 22016 * 2 + 1024 * (22016 // 2 + 2 * 172) + 4096 * 2 + 4 * 2048 + 11008 * 2
+    dn = 2752 * 4096 * 2 + 2752 * (4096 // 2 + 2 * 32) + 11008 * 2 + 4 * 5504 + 4096 * 2
+    assert [bench.group_bytes(spec, g) for g in range(4)] == [qkv, o, gu, dn]
+    assert bench.layer_bytes(spec) == qkv + o + gu + dn == 127_431_168
+
+
 def test_traffic_is_null_once_the_kernel_changed(monkeypatch):
     monkeypatch.setattr(bench, "kernel_source_hash", lambda: "0" * 64)
-    assert bench.measured_traffic() is None
+    for config in bench.PMC_SUMMARY:
+        assert bench.measured_traffic(config) is None
 
 
 def test_traffic_comes_from_the_committed_summary():
-    text = open(bench.PMC_SUMMARY).read()
-    sha = next(line for line in text.splitlines()
-               if line.startswith("kernel sources sha256")).rsplit(":", 1)[1].strip()
-    t = bench.measured_traffic()
-    if sha == bench.kernel_source_hash():
-        assert t is not None and t > 0
-    else:
-        assert t is None
+    for config, path in bench.PMC_SUMMARY.items():
+        if not os.path.exists(path):
+            assert bench.measured_traffic(config) is None
+            continue
+        text = open(path).read()
+        sha = next(line for line in text.splitlines()
+                   if line.startswith("kernel sources sha256")).rsplit(":", 1)[1].strip()
+        t = bench.measured_traffic(config)
+        if sha == bench.kernel_source_hash():
+            assert t is not None and t > 0
+        else:
+            assert t is None
