@@ -18,7 +18,7 @@ __all__ = [
     "GROUP_QKV", "GROUP_O", "GROUP_GATE_UP", "GROUP_DOWN",
     "Matrix", "Layer", "LayerIO", "Copy",
     "KERNEL_AUTO", "KERNEL_SEPARATE", "KERNEL_PER_GROUP",
-    "plan_tiers", "tiered_gemv", "gemv_workspace_bytes", "layer_step",
+    "plan_tiers", "tiered_gemv", "gemv_workspace_bytes", "layer_step", "layer_step_static",
     "layer_workspace_bytes", "pack_g128", "pack_sign2", "pack_trellis_host", "pack_trellis",
     "workspace_clear", "version", "copy_init", "copy_release", "layer_schedule",
     "workspace_status",
@@ -46,6 +46,7 @@ EXPORTS = (
     "spax_pack_trellis_host", "spax_pack_trellis", "spax_pack_trellis_workspace_bytes",
     "spax_workspace_clear", "spax_status_string", "spax_last_error", "spax_version",
     "spax_copy_init", "spax_copy_release", "spax_layer_schedule", "spax_workspace_status",
+    "spax_layer_step_static",
 )
 
 library_path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libspax.so")
@@ -197,6 +198,8 @@ def _declare(L: ctypes.CDLL) -> None:
     L.spax_layer_step.argtypes = [ctypes.POINTER(Layer), ctypes.POINTER(LayerIO), vp, sz, vp,
                                   ctypes.POINTER(Copy)]
     L.spax_layer_step.restype = ctypes.c_int
+    L.spax_layer_step_static.argtypes = [ctypes.POINTER(Layer), ctypes.POINTER(LayerIO), vp]
+    L.spax_layer_step_static.restype = ctypes.c_int
     L.spax_pack_g128.argtypes = [vp, i32, i32, i32, vp, vp, vp]
     L.spax_pack_g128.restype = ctypes.c_int
     L.spax_pack_sign2.argtypes = [vp, i32, i32, vp, vp, vp]
@@ -290,6 +293,15 @@ def layer_step(L: Layer, io: LayerIO, ws, ws_bytes=None, compute_stream=None,
     _check(lib().spax_layer_step(ctypes.byref(L), ctypes.byref(io), _ptr(ws), int(nbytes),
                                  _stream(compute_stream), _copy_arg(copy)),
            "spax_layer_step")
+
+
+def layer_step_static(L: Layer, io: LayerIO, compute_stream=None) -> None:
+    """spax_layer_step_static: spax_layer_step on the library's static
+    scratch (no workspace, no allocation; calls on one GPU must not
+    overlap)."""
+    _check(lib().spax_layer_step_static(ctypes.byref(L), ctypes.byref(io),
+                                        _stream(compute_stream)),
+           "spax_layer_step_static")
 
 
 def layer_schedule(L: Layer, workgroups: int = 0):

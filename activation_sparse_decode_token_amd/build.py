@@ -13,7 +13,8 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libspax.so")
 
-SOURCES = ["plan.hip", "select.hip", "gemv.hip", "layer.hip", "aux.hip", "api.cpp", "trellis_pack.cpp"]
+SOURCES = ["plan.hip", "select.hip", "gemv.hip", "layer.hip", "aux.hip", "static_ws.hip", "api.cpp",
+           "trellis_pack.cpp"]
 # per-source flags: the trellis encoder's fp32 error arithmetic is defined
 # operation by operation (no contraction into fused multiply-adds)
 EXTRA = {

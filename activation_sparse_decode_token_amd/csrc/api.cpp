@@ -159,6 +159,15 @@ SelectScratch* select_scratch(void* ws) {
                                           kSyncBytes);
 }
 size_t partials_offset() { return counters_bytes() + kSyncBytes + kSelectBytes; }
+
+}  // namespace
+
+namespace spax {
+size_t workspace_head_bytes() { return partials_offset(); }
+void set_last_error(const char* msg) { g_last_error = msg; }
+}  // namespace spax
+
+namespace {
 size_t partials_bytes(const spax_matrix* W) {
   return align256(sizeof(float) * (size_t)kMaxSplits * W->rows);
 }

@@ -148,6 +148,11 @@ hipError_t launch_pack_trellis(const uint16_t* w, int32_t rows, int32_t cols,
                                void* ws, size_t ws_bytes, hipStream_t s);
 
 hipError_t launch_clear(void* ws, size_t bytes, hipStream_t s);
+// Bytes at the start of a workspace that must start at zero (arrival
+// counters, the layer kernel's sync words, the sliced selection's counts).
+size_t workspace_head_bytes();
+// Sets the text spax_last_error returns on this thread.
+void set_last_error(const char* msg);
 
 // List positions of split s of n_splits: every split takes the same share
 // of each tier, [k * s / n_splits, k * (s + 1) / n_splits), so every

@@ -282,6 +282,23 @@ int spax_layer_step(const spax_layer* L, const spax_layer_io* io,
                     void* ws, size_t ws_bytes,
                     hipStream_t compute_stream, const spax_copy* copy);
 
+/* spax_layer_step_static -- spax_layer_step without a caller workspace, for
+ * callers that cannot allocate device memory (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc). It allocates
+ * nothing: its scratch (arrival counters, sync words, partial sums) is one
+ * static 16 MiB device array per GPU, held by the library until the process
+ * ends. Device-resident weights only (no copy context).
+ *   L, io, stream  as for spax_layer_step.
+ *   Every call on one GPU uses that GPU's array: its counters are cleared at
+ *   the start of each call (a fill kernel on `stream`), so calls on one GPU
+ *   must not overlap (one stream, or ordered streams); overlapping calls
+ *   race on the array.
+ *   Errors: as spax_layer_step; SPAX_EWORKSPACE (message in
+ *   spax_last_error) when spax_layer_workspace_bytes(L) exceeds 16 MiB,
+ *   checked before any GPU call.                                           */
+int spax_layer_step_static(const spax_layer* L, const spax_layer_io* io,
+                           hipStream_t stream);
+
 /* spax_layer_schedule -- the layer kernel's work schedule, for inspection
  * (host only, enqueues nothing). For every workgroup w of `workgroups`
  * (0: the number the library would launch on the current device) and every

@@ -180,6 +180,22 @@ def test_layer_and_helper_validation_errors():
     assert spax.lib().spax_copy_release(None) == -2
 
 
+def test_static_layer_step_rejects_what_its_scratch_cannot_hold():
+    f = spax.lib().spax_layer_step_static
+    io = spax.LayerIO.make(h=P, z=P, x=P, qkv=P, o=P, a=P, down=P, full_idx=(P,) * 4,
+                           approx_idx=(P,) * 4)
+    assert f(None, ctypes.byref(io), None) == -2
+    # a 131072-row projection's split partials alone take 32 MiB: refused
+    # before any GPU call, with the reason in spax_last_error
+    big = spax.Layer.make([None, _matrix(rows=131072, cols=4096), None, None], [1] * 4, [1] * 4)
+    assert spax.layer_workspace_bytes(big) > 16 << 20
+    assert f(ctypes.byref(big), ctypes.byref(io), None) == -5
+    assert "16 MiB" in spax.last_error()
+    # an empty layer
+    assert f(ctypes.byref(spax.Layer.make([None] * 4, [0] * 4, [0] * 4)), ctypes.byref(io),
+             None) == -1
+
+
 def test_python_wrapper_raises_with_status():
     with pytest.raises(spax.SpaxError) as ei:
         spax.plan_tiers(None, 10, 1, 1, P, P, stream=0)
