@@ -18,12 +18,14 @@ def _spax():
 class LayerWeights:
     """Column-major fp16 weights of one layer, drawn on the host."""
 
-    def __init__(self, cfg, layer, hidden, inter, std):
+    def __init__(self, cfg, layer, hidden, inter, std, attn=True):
         self.hidden, self.inter = hidden, inter
-        self.q = WL.weights_fp16(cfg, layer, "q", hidden, hidden, std)
-        self.k = WL.weights_fp16(cfg, layer, "k", hidden, hidden, std)
-        self.v = WL.weights_fp16(cfg, layer, "v", hidden, hidden, std)
-        self.o = WL.weights_fp16(cfg, layer, "o", hidden, hidden, std)
+        self.q = self.k = self.v = self.o = None
+        if attn:
+            self.q = WL.weights_fp16(cfg, layer, "q", hidden, hidden, std)
+            self.k = WL.weights_fp16(cfg, layer, "k", hidden, hidden, std)
+            self.v = WL.weights_fp16(cfg, layer, "v", hidden, hidden, std)
+            self.o = WL.weights_fp16(cfg, layer, "o", hidden, hidden, std)
         self.gate = WL.weights_fp16(cfg, layer, "gate", inter, hidden, std)
         self.up = WL.weights_fp16(cfg, layer, "up", inter, hidden, std)
         self.down = WL.weights_fp16(cfg, layer, "down", hidden, inter, std)
@@ -36,9 +38,11 @@ def _build_layer(w: LayerWeights, ff, af, residency, ks, kernel=0):
     F = {"fp16": 1, "int4": 2}[ff]
     A = {"int4": 2, "int2": 3, "sign2": 4, "trellis": 5}[af]
     cb = to_dev(WL.trellis_codebook(2)) if af == "trellis" else None
-    qkv = build_matrix(stack_rows([to_dev(w.q), to_dev(w.k), to_dev(w.v)]), F, A,
-                       residency=residency, codebook=cb)
-    o = build_matrix(to_dev(w.o), F, A, residency=residency, codebook=cb)
+    qkv = o = None
+    if w.q is not None:
+        qkv = build_matrix(stack_rows([to_dev(w.q), to_dev(w.k), to_dev(w.v)]), F, A,
+                           residency=residency, codebook=cb)
+        o = build_matrix(to_dev(w.o), F, A, residency=residency, codebook=cb)
     gu = build_matrix(glu_interleave(to_dev(w.gate), to_dev(w.up)), F, A,
                       layout=spax.LAYOUT_GLU_INTERLEAVED, residency=residency, codebook=cb)
     dn = build_matrix(to_dev(w.down), F, A, residency=residency, codebook=cb)
@@ -54,8 +58,8 @@ def _io(L, h, z, x):
     dev = torch.device("cuda:0")
     G = L.group
     out = {
-        "qkv": torch.empty(G[0].rows, dtype=torch.float16, device=dev),
-        "o": torch.empty(G[1].rows, dtype=torch.float16, device=dev),
+        "qkv": torch.empty(max(1, G[0].rows), dtype=torch.float16, device=dev),
+        "o": torch.empty(max(1, G[1].rows), dtype=torch.float16, device=dev),
         "g": torch.empty(G[2].rows // 2, dtype=torch.float16, device=dev),
         "u": torch.empty(G[2].rows // 2, dtype=torch.float16, device=dev),
         "a": torch.empty(G[2].rows // 2, dtype=torch.float16, device=dev),
@@ -63,7 +67,8 @@ def _io(L, h, z, x):
         "F": [torch.empty(max(1, L.k_full[g]), dtype=torch.int32, device=dev) for g in range(4)],
         "A": [torch.empty(max(1, L.k_approx[g]), dtype=torch.int32, device=dev) for g in range(4)],
     }
-    io = spax.LayerIO.make(h=to_dev(h), z=to_dev(z), x=to_dev(x), qkv=out["qkv"], o=out["o"],
+    io = spax.LayerIO.make(h=None if h is None else to_dev(h), z=None if z is None else to_dev(z),
+                           x=to_dev(x), qkv=out["qkv"], o=out["o"],
                            g=out["g"], u=out["u"], a=out["a"], down=out["down"],
                            full_idx=out["F"], approx_idx=out["A"])
     return io, out
@@ -122,23 +127,29 @@ def _check_layer(res, w: LayerWeights, ks, h, z, x, ff, af, label, rows_per=None
     Wgu = np.empty((w.gate.shape[0], 2 * w.inter), dtype=np.float16)
     Wgu[:, gmap] = w.gate
     Wgu[:, gmap + 128] = w.up
-    Wqkv = np.concatenate([w.q, w.k, w.v], axis=1)
+    attn = w.q is not None
+    Wqkv = np.concatenate([w.q, w.k, w.v], axis=1) if attn else None
     L_of = {}
     if af == "trellis":
         cbh = WL.trellis_codebook(2)
         for key, g in ((Wqkv, 0), (w.o, 1), (Wgu, 2), (w.down, 3)):
+            if key is None:
+                continue
             keep = L._keep[g]._keep
             L_of[id(key)] = (to_host(keep[2]), to_host(keep[3]), cbh)
 
-    L0 = O.plan_tiers(h, *ks["qkv"])
-    assert all(np.array_equal(a, b) for a, b in zip(res["lists"][0], L0)), f"{label}: qkv lists"
-    rows = sample_groups(Wqkv.shape[1], 8, 1) if rows_per else None
-    check_product(res["qkv"], h, *L0, *stores(Wqkv, rows), f"{label} qkv", rows=rows)
+    if attn:
+        L0 = O.plan_tiers(h, *ks["qkv"])
+        assert all(np.array_equal(a, b) for a, b in zip(res["lists"][0], L0)), \
+            f"{label}: qkv lists"
+        rows = sample_groups(Wqkv.shape[1], 8, 1) if rows_per else None
+        check_product(res["qkv"], h, *L0, *stores(Wqkv, rows), f"{label} qkv", rows=rows)
 
-    L1 = O.plan_tiers(z, *ks["o"])
-    assert all(np.array_equal(a, b) for a, b in zip(res["lists"][1], L1)), f"{label}: o lists"
-    rows = sample_groups(w.o.shape[1], 8, 2) if rows_per else None
-    check_product(res["o"], z, *L1, *stores(w.o, rows), f"{label} o", rows=rows)
+        L1 = O.plan_tiers(z, *ks["o"])
+        assert all(np.array_equal(a, b) for a, b in zip(res["lists"][1], L1)), \
+            f"{label}: o lists"
+        rows = sample_groups(w.o.shape[1], 8, 2) if rows_per else None
+        check_product(res["o"], z, *L1, *stores(w.o, rows), f"{label} o", rows=rows)
 
     L2 = O.plan_tiers(x, *ks["ffn"])
     assert all(np.array_equal(a, b) for a, b in zip(res["lists"][2], L2)), f"{label}: ffn lists"
@@ -234,6 +245,20 @@ def test_layer_7b_shapes(kernel_choice, af):
         log(f"7B layer {af} token {tok} ok")
 
 
+def test_layer_70b_ffn_shapes(kernel_choice):
+    """The config-5 launches at full size: the 57344-row GLU-interleaved
+    int4/int2 gate/up with fused ranking and the SwiGLU epilogue, then the
+    8192 x 28672 down ranked on the a it wrote (SpAx page sections 2 and
+    5.2), on sampled whole row groups."""
+    w = LayerWeights(5, 0, 8192, 28672, 0.015, attn=False)
+    ks = _ks(8192, 28672, WL.CONFIGS[5].splits[0])
+    L = _build_layer(w, "int4", "int2", 0, ks, kernel_choice)
+    x = WL.laplace_fp16(5, 0, "x", 0, 8192)
+    res, _ = _run_layer(L, None, None, x)
+    _check_layer(res, w, ks, None, None, x, "int4", "int2", "70B FFN", rows_per=True)
+    log(f"70B FFN layer step ok (kernel {kernel_choice})")
+
+
 @pytest.mark.parametrize("ff,af", [("fp16", "int4"), ("int4", "int2"), ("fp16", "sign2")])
 def test_host_pinned_bitwise_equals_device(ff, af):
     import torch
@@ -245,6 +270,19 @@ def test_host_pinned_bitwise_equals_device(ff, af):
     Ld = _build_layer(w, ff, af, 0, ks, kernel=2)
     Lh = _build_layer(w, ff, af, 1, ks)
     _host_vs_device(w, ks, Ld, Lh, ff, af, hidden)
+
+
+def test_host_pinned_long_input():
+    """Host-resident weights with an input past the one-workgroup ranking
+    (down's 33024 inputs): the host branch that writes the sliced
+    selection's lists for the copy, bitwise equal to the device-resident
+    per-group launches and checked against the oracle."""
+    hidden, inter = 512, 33024
+    w = LayerWeights(811, 0, hidden, inter, 0.02, attn=False)
+    ks = _ks(hidden, inter, WL.TierSplit(50, 25, 25))
+    Ld = _build_layer(w, "fp16", "int4", 0, ks, kernel=2)
+    Lh = _build_layer(w, "fp16", "int4", 1, ks)
+    _host_vs_device(w, ks, Ld, Lh, "fp16", "int4", hidden)
 
 
 def _host_vs_device(w, ks, Ld, Lh, ff, af, hidden):
