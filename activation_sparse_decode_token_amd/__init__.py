@@ -87,6 +87,7 @@ class Matrix(ctypes.Structure):
         ("rows", ctypes.c_int32), ("cols", ctypes.c_int32),
         ("full_fmt", ctypes.c_int32), ("approx_fmt", ctypes.c_int32),
         ("residency", ctypes.c_int32), ("layout", ctypes.c_int32),
+        ("approx_seg_rows", ctypes.c_int32),
         ("full_data", ctypes.c_void_p), ("full_scales", ctypes.c_void_p),
         ("approx_codes", ctypes.c_void_p), ("approx_scales", ctypes.c_void_p),
         ("approx_codebook", ctypes.c_void_p),
@@ -95,8 +96,8 @@ class Matrix(ctypes.Structure):
     @classmethod
     def make(cls, rows, cols, full_fmt, approx_fmt, full_data, full_scales=None,
              approx_codes=None, approx_scales=None, residency=RES_DEVICE,
-             layout=LAYOUT_PLAIN, approx_codebook=None) -> "Matrix":
-        m = cls(rows, cols, full_fmt, approx_fmt, residency, layout,
+             layout=LAYOUT_PLAIN, approx_codebook=None, approx_seg_rows=0) -> "Matrix":
+        m = cls(rows, cols, full_fmt, approx_fmt, residency, layout, int(approx_seg_rows),
                 _ptr(full_data), _ptr(full_scales), _ptr(approx_codes), _ptr(approx_scales),
                 _ptr(approx_codebook))
         m._keep = (full_data, full_scales, approx_codes, approx_scales, approx_codebook)

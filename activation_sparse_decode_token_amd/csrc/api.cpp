@@ -45,6 +45,26 @@ int64_t col_scales(int32_t fmt, int64_t rows) {
   if (fmt == kTrellis) return 1;
   return (fmt == kInt4 || fmt == kInt2) ? rows / kGroup : 0;
 }
+// Matrices in one stored column of a sign / trellis approx tier, each coded
+// as its own column: gate and up in the GLU layout, else rows /
+// approx_seg_rows stacked segments (one when 0).
+int32_t approx_nseg(const spax_matrix* W) {
+  if (W->layout == SPAX_LAYOUT_GLU_INTERLEAVED) return 2;
+  return W->approx_seg_rows > 0 ? W->rows / W->approx_seg_rows : 1;
+}
+// The kernels' segment mode: 0 one matrix, S stacked segments of S rows,
+// -1 GLU gate/up blocks.
+int32_t approx_seg_mode(const spax_matrix* W) {
+  if (W->approx_fmt != kSign2 && W->approx_fmt != kTrellis) return 0;
+  if (W->layout == SPAX_LAYOUT_GLU_INTERLEAVED) return -1;
+  return W->approx_seg_rows;
+}
+// fp16 scales per stored column of the approx tier.
+int64_t approx_col_scales(const spax_matrix* W) {
+  if (W->approx_fmt == kSign2) return 2 * approx_nseg(W);
+  if (W->approx_fmt == kTrellis) return approx_nseg(W);
+  return col_scales(W->approx_fmt, W->rows);
+}
 // Bytes one 512-row tile of a column costs, used to balance the splits.
 int64_t tile_bytes(int32_t fmt) {
   switch (fmt) {
@@ -76,6 +96,12 @@ int validate_matrix(const spax_matrix* W) {
   if (W->layout != SPAX_LAYOUT_PLAIN && W->layout != SPAX_LAYOUT_GLU_INTERLEAVED)
     return SPAX_EINVAL;
   if (W->layout == SPAX_LAYOUT_GLU_INTERLEAVED && W->rows % (2 * kGroup)) return SPAX_EINVAL;
+  // stacked matrices: whole 512-row tiles each, so a tile never holds two
+  if (W->approx_seg_rows < 0) return SPAX_EINVAL;
+  if (W->approx_seg_rows > 0 &&
+      (W->layout != SPAX_LAYOUT_PLAIN || W->approx_seg_rows % kTileRows ||
+       W->rows % W->approx_seg_rows))
+    return SPAX_EINVAL;
   // the product addresses each tier with 32-bit offsets
   if (col_bytes(W->full_fmt, W->rows) * W->cols >= (int64_t(1) << 31) ||
       col_bytes(W->approx_fmt, W->rows) * W->cols >= (int64_t(1) << 31))
@@ -175,7 +201,7 @@ size_t staging_bytes(const spax_matrix* W) {
   if (W->residency != SPAX_RES_HOST_PINNED) return 0;
   const int64_t per_full = col_bytes(W->full_fmt, W->rows) + 2 * col_scales(W->full_fmt, W->rows);
   const int64_t per_apx =
-      col_bytes(W->approx_fmt, W->rows) + 2 * col_scales(W->approx_fmt, W->rows);
+      col_bytes(W->approx_fmt, W->rows) + 2 * approx_col_scales(W);
   return align256((size_t)W->cols * std::max(per_full, per_apx)) + 4 * 256;
 }
 size_t gemv_ws(const spax_matrix* W) {
@@ -361,7 +387,9 @@ int run_layer_kernel(const spax_layer* L, const spax_layer_io* io, void* ws, int
     gr.approx_stride = ab;
     gr.approx_bytes = (uint32_t)(ab * M.cols);
     gr.approx_scales = M.approx_scales;
-    gr.approx_sstride = col_scales(M.approx_fmt, M.rows);
+    gr.approx_sstride = approx_col_scales(&M);
+    gr.approx_seg = approx_seg_mode(&M);
+    gr.approx_nseg = approx_nseg(&M);
     gr.x = inputs[g];
     gr.y = outputs[g];
     gr.out_full = io->full_idx[g];
@@ -419,11 +447,13 @@ int run_product(const spax_matrix* W, const uint16_t* x, const int32_t* fidx, in
   a.glu_u = gu;
   a.codebook = W->approx_codebook;
   const int64_t fb = col_bytes(W->full_fmt, W->rows), fsn = col_scales(W->full_fmt, W->rows);
-  const int64_t ab = col_bytes(W->approx_fmt, W->rows), asn = col_scales(W->approx_fmt, W->rows);
+  const int64_t ab = col_bytes(W->approx_fmt, W->rows), asn = approx_col_scales(W);
   a.full_stride = fb;
   a.full_sstride = fsn;
   a.approx_stride = ab;
   a.approx_sstride = asn;
+  a.approx_seg = approx_seg_mode(W);
+  a.approx_nseg = approx_nseg(W);
   // bytes the product may read from each tier (the staging holds the
   // selected columns in list order)
   const bool staged = W->residency == SPAX_RES_HOST_PINNED;

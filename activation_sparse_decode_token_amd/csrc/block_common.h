@@ -184,11 +184,14 @@ struct Tier<kSign2> {
 
 // The SpAx page's trellis-coded middle tier (section 5.1, trellis coding):
 // weight i of column j is cb[index_i] s_j with index_i the window of the
-// 2-bit codes of rows i-7..i (oldest code in the low bits). Lane l loads the
-// codes of its rows 8l..8l+7 and of the 8 rows before them (two 2-byte
-// loads; none before the column start), so row 8l + r reads its window with
-// one bit-field extract, then one LDS lookup into the codebook and one fp16
-// x fp32 FMA with the column's factor x_j s_j.
+// 2-bit codes of rows i-7..i of the same matrix column (oldest code in the
+// low bits; codes before the column start are zero). Lane l holds the codes
+// of its rows 8l..8l+7 in the high half of V and those of the 8 rows before
+// them in the low half (the streaming code loads both; in a stored column
+// that holds several matrices the rows before come from the same matrix),
+// so row 8l + r reads its window with one bit-field extract, then one LDS
+// lookup into the codebook and one fp16 x fp32 FMA with the column's factor
+// x_j s_j.
 template <>
 struct Tier<kTrellis> {
   using V = uint32_t;  // codes of rows 8l-8 .. 8l+7, two bits each
@@ -196,15 +199,6 @@ struct Tier<kTrellis> {
   static constexpr uint32_t kMask = 0u;
   static __device__ __forceinline__ uint32_t offset(int row0, int lane) {
     return (uint32_t)(row0 + 8 * lane) / 4u;
-  }
-  static __device__ __forceinline__ V load(__amdgpu_buffer_rsrc_t t, uint32_t off, uint32_t col) {
-    const uint32_t cur = __builtin_amdgcn_raw_buffer_load_b16(t, off, col, 0);
-    // the 8 rows before (an in-column load in every lane); a column's first
-    // rows have none: codes before the column start are zero
-    const uint32_t before =
-        __builtin_amdgcn_raw_buffer_load_b16(t, off == 0u ? 0u : off - 2u, col, 0);
-    const uint32_t prev = off == 0u ? 0u : before;
-    return prev | (cur << 16);
   }
   static __device__ __forceinline__ void fma_cb(float (&acc)[8], V v, float f,
                                                 const uint16_t* cb) {

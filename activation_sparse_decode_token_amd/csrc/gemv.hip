@@ -167,7 +167,8 @@ __global__ __launch_bounds__(kGemvThreads) void gemv_kernel(GemvArgs a) {
                               a.approx_stride, a.approx_bytes,
                               a.approx_scales, a.approx_sstride, a.approx_idx, a.x,
                               lidx, lx, a_lo + (la * wave) / kWaves,
-                              a_lo + (la * (wave + 1)) / kWaves, row0, a.rows, lane, ld_lane);
+                              a_lo + (la * (wave + 1)) / kWaves, row0, a.rows, lane, ld_lane,
+                              a.approx_seg);
       if constexpr (kTrel) sa.cbk = cbk;
       sa.begin();
       sf.run(acc, corr);

@@ -637,7 +637,8 @@ struct Share {
   __amdgpu_buffer_rsrc_t rs, xr, sr;
   uint32_t stride, sstride;
   uint32_t off;           // fp16: the lane's byte offset in a column
-  uint32_t sg;            // codes: the lane's scale index in a column
+  uint32_t sg;            // codes: the lane's scale index in a column (the sign
+                          // code: its matrix's (s0, s1) pair)
 };
 
 // The share of tier `full` of segment s for wave wi of nw on that tier.
@@ -670,7 +671,17 @@ __device__ __forceinline__ Share make_share(const LayerArgs& A, const LayerSeg& 
   } else {
     const int li = row0 + 32 * (lane & 15) < gr.rows ? (lane & 15) : 0;
     h.off = (uint32_t)(row0 + 32 * li) / 32u * Form<FMT>::kLaneBytes;
-    h.sg = (uint32_t)(row0 / kGroup + li / 4);
+    if constexpr (FMT == kSign2) {
+      // the matrix of the lane's rows in a stored column that holds several
+      // (each coded as its own column): GLU gate / up by 128-row block
+      // parity, or the stacked segment of the tile
+      const int seg = gr.approx_seg < 0   ? ((row0 + 32 * li) >> 7) & 1
+                      : gr.approx_seg > 0 ? row0 / gr.approx_seg
+                                          : 0;
+      h.sg = (uint32_t)seg;
+    } else {
+      h.sg = (uint32_t)(row0 / kGroup + li / 4);
+    }
   }
   return h;
 }
@@ -770,7 +781,8 @@ __device__ __forceinline__ void stream_seq(const LayerArgs& A, bool late, bool f
       d[u] = Fm::load(sh.rs, c * sh.stride + sh.off);
       xs[u] = live ? __builtin_amdgcn_raw_buffer_load_b16(sh.xr, 2u * c, 0, 0) : 0u;
       if constexpr (FMT == kSign2)
-        ss[u] = __builtin_amdgcn_raw_buffer_load_b32(sh.sr, 4u * c, 0, 0);
+        ss[u] = __builtin_amdgcn_raw_buffer_load_b32(sh.sr, 2u * (c * sh.sstride + 2u * sh.sg), 0,
+                                                     0);
       else
         ss[u] = __builtin_amdgcn_raw_buffer_load_b16(sh.sr, 2u * (c * sh.sstride + sh.sg), 0, 0);
     }

@@ -76,6 +76,7 @@ struct LayerGroupArgs {
   int64_t approx_stride;
   const uint16_t* approx_scales;
   int64_t approx_sstride;
+  int32_t approx_seg, approx_nseg;  // matrices per stored column (as GemvArgs)
   const uint16_t* x;        // the group's input (down: the a gate/up writes)
   uint16_t* y;              // plain output (null for gate/up)
   int32_t* out_full;        // the caller's tier lists

@@ -77,6 +77,10 @@ struct GemvArgs {
   int64_t approx_stride;
   const uint16_t* approx_scales;
   int64_t approx_sstride;
+  // Matrices in a stored column of a sign / trellis approx tier: 0 one,
+  // S > 0 stacked segments of S rows (S % 512 == 0), -1 GLU gate and up
+  // (128-row blocks by parity); approx_nseg their number.
+  int32_t approx_seg, approx_nseg;
   const uint16_t* x;
   const int32_t* full_idx;
   const int32_t* approx_idx;

@@ -73,13 +73,26 @@ struct TierStream {
   float xv;        // this lane's activation of the pending batch (0 past it)
   float xb;        // sign code: x_j s_{j,1} (xv then holds x_j s_{j,0})
   const uint16_t* cbk = nullptr;  // trellis code: the codebook in LDS
+  // Sign / trellis codes of stored columns that hold several matrices (each
+  // coded as its own column): the tile holds rows of at most two of them,
+  // seg_a and seg_b (GLU gate and up; one stacked matrix when equal); the
+  // lane's rows belong to seg_b when seg_sel is set. xv1 / xb1 are the
+  // factors of seg_b.
+  int seg_a = 0, seg_b = 0;
+  bool seg_sel = false, two_segs = false;
+  float xv1 = 0.0f, xb1 = 0.0f;
+  // Trellis code: byte offset of the lane's 8 rows before (in the same
+  // matrix) and whether there are any (none at a matrix's first row).
+  uint32_t boff = 0u;
+  bool has_before = false;
   uint32_t sc[4];  // this lane's raw fp16 scales of the pending batch (codes)
 
   __device__ __forceinline__ TierStream(WaveMeta& wm_, const uint8_t* base, int64_t stride,
                                         uint32_t bytes, const uint16_t* scales_, int64_t sstride_,
                                         const int32_t* idx_, const uint16_t* x_,
                                         const int32_t* lidx_, const float* lx_, int p_lo_,
-                                        int p_hi_, int row0_, int rows, int lane_, int ld_lane)
+                                        int p_hi_, int row0_, int rows, int lane_, int ld_lane,
+                                        int seg_mode = 0)
       : wm(wm_), rs(tier_rsrc(base, bytes)), off(T::offset(row0_, ld_lane)),
         cstride((uint32_t)stride), gsel(kCode ? (ld_lane >> 4) : 0),
         ngrp(min(4, (rows - row0_ + kGroup - 1) / kGroup)), row0(row0_), lane(lane_),
@@ -89,6 +102,30 @@ struct TierStream {
     // a literal (gfx9 VOP3 instructions take no literals)
     vmask = T::kMask;
     asm volatile("" : "+v"(vmask));
+    if constexpr (kTwo || kTrel) {
+      const int r = row0_ + 8 * ld_lane;  // the lane's first row
+      if (seg_mode < 0) {                 // GLU: gate blocks even, up blocks odd
+        seg_a = 0;
+        seg_b = 1;
+        two_segs = true;
+        seg_sel = ((r >> 7) & 1) != 0;
+      } else if (seg_mode > 0) {          // stacked: the tile lies in one matrix
+        seg_a = seg_b = row0_ / seg_mode;
+      }
+      if constexpr (kTrel) {
+        // the 8 rows before the lane's rows, in the same matrix: the previous
+        // 8 stored rows, or in the GLU layout at a 128-row block start the
+        // last 8 rows of the matrix's previous block (256 stored rows back);
+        // none at the matrix's first row
+        if (seg_mode < 0 && (r & 127) == 0) {
+          has_before = r >= 256;
+          boff = has_before ? (uint32_t)(r - 136) / 4u : 0u;
+        } else {
+          has_before = seg_mode > 0 ? (r % seg_mode) != 0 : r != 0;
+          boff = has_before ? (uint32_t)(r - 8) / 4u : 0u;
+        }
+      }
+    }
   }
 
   // This lane's column and activation of the batch at pb, and (codes) its
@@ -96,6 +133,8 @@ struct TierStream {
   __device__ __forceinline__ void fill_cols(int pb, int cnt) {
     xv = 0.0f;
     xb = 0.0f;
+    xv1 = 0.0f;
+    xb1 = 0.0f;
     mycol = 0;
     if (lane < cnt) {
       const int q = pb + lane;
@@ -115,10 +154,17 @@ struct TierStream {
         xv = h2f(x[j]);
       }
       mycol = MODE == kListStaged ? q : j;
-      if constexpr (kTrel) xv = xv * h2f(scales[mycol]);  // x_j s_j
+      if constexpr (kTrel) {  // x_j s_j of the tile's two matrices
+        const uint16_t* sp = scales + (int64_t)mycol * sstride;
+        xv1 = xv * h2f(sp[seg_b]);
+        xv = xv * h2f(sp[seg_a]);
+      }
       if constexpr (kTwo) {
-        // the column's (s0, s1) in one 4-byte load
-        const uint32_t sv = *reinterpret_cast<const uint32_t*>(scales + (int64_t)mycol * 2);
+        // each matrix's (s0, s1) in one 4-byte load
+        const uint32_t* sp = reinterpret_cast<const uint32_t*>(scales + (int64_t)mycol * sstride);
+        const uint32_t sv = sp[seg_a], sv1 = sp[seg_b];
+        xb1 = xv * h2f(sv1 >> 16);
+        xv1 = xv * h2f(sv1 & 0xFFFFu);
         xb = xv * h2f(sv >> 16);
         xv = xv * h2f(sv & 0xFFFFu);
       }
@@ -153,15 +199,31 @@ struct TierStream {
     for (int u = 0; u < U; ++u) {
       const int c = min(r * U + u, cnt - 1);
       const uint32_t col = (uint32_t)__builtin_amdgcn_readlane(mycol, c);
-      v[u] = T::load(rs, off, col * cstride);
+      if constexpr (kTrel) {
+        // the lane's 8 rows (high half) after the 8 rows before them
+        const uint32_t cur = __builtin_amdgcn_raw_buffer_load_b16(rs, off, col * cstride, 0);
+        const uint32_t before = __builtin_amdgcn_raw_buffer_load_b16(rs, boff, col * cstride, 0);
+        v[u] = (has_before ? before : 0u) | (cur << 16);
+      } else {
+        v[u] = T::load(rs, off, col * cstride);
+      }
     }
   }
   // Adds batch column c (loaded as v) to the accumulators.
   __device__ __forceinline__ void add(float (&acc)[8], float& corr, int c, const V& v) {
-    if constexpr (kTwo)
-      T::fma2(acc, v, readlane_f(xv, c), readlane_f(xb, c), vmask);
-    else if constexpr (kTrel)
-      T::fma_cb(acc, v, readlane_f(xv, c), cbk);
+    if constexpr (kTwo) {
+      float fa = readlane_f(xv, c), fb = readlane_f(xb, c);
+      if (two_segs) {  // wave-uniform
+        const float fa1 = readlane_f(xv1, c), fb1 = readlane_f(xb1, c);
+        fa = seg_sel ? fa1 : fa;
+        fb = seg_sel ? fb1 : fb;
+      }
+      T::fma2(acc, v, fa, fb, vmask);
+    } else if constexpr (kTrel) {
+      float f = readlane_f(xv, c);
+      if (two_segs) f = seg_sel ? readlane_f(xv1, c) : f;
+      T::fma_cb(acc, v, f, cbk);
+    }
     else
       T::fma(acc, corr, v, kCode ? wm.fac[c][gsel] : readlane_f(xv, c), vmask);
   }

@@ -7,7 +7,12 @@ indexes are adjacent (SpAx page, section 5.3, Figure 4):
   * q, k, v: rows stacked, column j = [q_j; k_j; v_j];
   * gate, up: rows interleaved in 128-row blocks (SPAX_LAYOUT_GLU_INTERLEAVED).
 The compressed copies are produced by the library's packers (spax_pack_g128,
-spax_pack_sign2).
+spax_pack_sign2, spax_pack_trellis). The sign and trellis codes carry
+per-column scales and (trellis) a window over the column's earlier rows, so
+a stored column that holds several matrices' columns is coded matrix by
+matrix (SpAx page section 5.1: codes and scales per weight column; section
+5.3: stacked columns stay distinct columns): each matrix is packed on its
+own and its codes are placed at its rows, its scales side by side.
 These helpers only move data; nothing here is on the per-token path.
 """
 from __future__ import annotations
@@ -91,6 +96,40 @@ def pack(w_cm: torch.Tensor, fmt: int, stream=None, codebook: Optional[torch.Ten
     return codes, scales
 
 
+def _segments(w_cm: torch.Tensor, layout: int, seg_rows: int):
+    """The matrices of a stored column-major tensor [n, R]: gate and up of
+    the GLU layout, or the stacked segments of seg_rows rows (one when 0)."""
+    if layout == LAYOUT_GLU_INTERLEAVED:
+        return [t.contiguous() for t in glu_deinterleave(w_cm)]
+    if seg_rows:
+        return [t.contiguous() for t in w_cm.split(seg_rows, dim=1)]
+    return [w_cm]
+
+
+def pack_per_matrix(w_cm: torch.Tensor, fmt: int, layout: int = LAYOUT_PLAIN,
+                    seg_rows: int = 0, stream=None, codebook: Optional[torch.Tensor] = None,
+                    **kw):
+    """Sign or trellis codes and scales of a stored tensor whose columns hold
+    several matrices' columns, each matrix coded as its own columns: codes at
+    the matrix's rows (128-row blocks interleaved back for GLU), scales
+    [n, matrices, 2] (sign) or [n, matrices] (trellis) flattened per column."""
+    parts = _segments(w_cm, layout, seg_rows)
+    if len(parts) == 1:
+        return pack(w_cm, fmt, stream, codebook, **kw)
+    coded = [pack(p, fmt, stream, codebook, **kw) for p in parts]
+    codes = [c for c, _ in coded]
+    if layout == LAYOUT_GLU_INTERLEAVED:
+        # 128 rows of 2-bit codes are 32 bytes
+        n, b = codes[0].shape
+        g = codes[0].reshape(n, b // 32, 1, 32)
+        u = codes[1].reshape(n, b // 32, 1, 32)
+        codes = torch.cat([g, u], dim=2).reshape(n, 2 * b).contiguous()
+    else:
+        codes = torch.cat(codes, dim=1).contiguous()
+    scales = torch.stack([sc for _, sc in coded], dim=1)
+    return codes, scales.reshape(scales.shape[0], -1).contiguous()
+
+
 def _pin(t: Optional[torch.Tensor]) -> Optional[torch.Tensor]:
     if t is None:
         return None
@@ -102,14 +141,16 @@ def _pin(t: Optional[torch.Tensor]) -> Optional[torch.Tensor]:
 def build_matrix(w_cm: torch.Tensor, full_fmt: int = FMT_FP16,
                  approx_fmt: int = FMT_INT4_G128, layout: int = LAYOUT_PLAIN,
                  residency: int = RES_DEVICE, stream=None,
-                 codebook: Optional[torch.Tensor] = None) -> Matrix:
+                 codebook: Optional[torch.Tensor] = None, seg_rows: int = 0) -> Matrix:
     """A spax_matrix for a column-major fp16 device tensor [n, R].
 
     The full tier is w_cm itself (fp16) or its int4 code; the approx tier is
-    the int4 / int2 group-128 code or the two-scale sign code of w_cm (the
-    sign code's two scales are fitted per stored column: with stacked
-    matrices, one pair per column of the stack). With RES_HOST_PINNED every buffer is copied
-    to pinned host memory and the device copies are dropped."""
+    the int4 / int2 group-128 code, the two-scale sign code or the trellis
+    code of w_cm. seg_rows > 0 says w_cm stacks matrices of seg_rows rows
+    (stack_rows of q, k, v); the sign and trellis codes are then fitted per
+    matrix column, as they are for gate and up in the GLU layout. With
+    RES_HOST_PINNED every buffer is copied to pinned host memory and the
+    device copies are dropped."""
     n, R = w_cm.shape
     fs = None
     if full_fmt == FMT_FP16:
@@ -117,11 +158,14 @@ def build_matrix(w_cm: torch.Tensor, full_fmt: int = FMT_FP16,
     else:
         fd, fs = pack(w_cm, full_fmt, stream)
     ac = asc = None
-    if approx_fmt != FMT_NONE:
+    if approx_fmt in (FMT_SIGN2, FMT_TRELLIS):
+        ac, asc = pack_per_matrix(w_cm, approx_fmt, layout, seg_rows, stream, codebook)
+    elif approx_fmt != FMT_NONE:
         ac, asc = pack(w_cm, approx_fmt, stream, codebook)
     if residency == RES_HOST_PINNED:
         torch.cuda.synchronize()
         fd, fs, ac, asc = _pin(fd), _pin(fs), _pin(ac), _pin(asc)
     # the trellis codebook stays in device memory (the product loads it to LDS)
     cb = codebook if approx_fmt == FMT_TRELLIS else None
-    return Matrix.make(R, n, full_fmt, approx_fmt, fd, fs, ac, asc, residency, layout, cb)
+    return Matrix.make(R, n, full_fmt, approx_fmt, fd, fs, ac, asc, residency, layout, cb,
+                       approx_seg_rows=seg_rows if layout == LAYOUT_PLAIN else 0)

@@ -268,7 +268,7 @@ class Workload:
                 q, k_, v = (gen(s, m, H, H) for m in ("q", "k", "v"))
                 st = stack_rows([q, k_, v])
                 del q, k_, v
-                mats[0] = build_matrix(st, ff, af, residency=res, codebook=cb)
+                mats[0] = build_matrix(st, ff, af, residency=res, codebook=cb, seg_rows=H)
                 del st
             if spec.attn or spec.o_only:
                 o = gen(s, "o" if spec.attn else "w", H, H)

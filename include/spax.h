@@ -66,14 +66,17 @@ extern "C" {
 #define SPAX_FMT_INT2_G128  3  /* int2 codes + fp16 scale per 128 rows        */
 /* Two-scale 2-bit sign code of the middle tier (SpAx page section 5.1,
  * Eq. 4): weight i of column j is rebuilt as e1 s_{j,0} + e2 s_{j,1} with
- * signs (e1, e2) in {-1, +1} and two fp16 scales per stored column. Code u
+ * signs (e1, e2) in {-1, +1} and two fp16 scales per matrix column. Code u
  * = 2 [e1 = -1] + [e2 = -1], rows/4 bytes per column packed like int2 (row
- * 4i + r in bits 2r..2r+1 of byte i); scales [cols][2] = (s0, s1). Approx
- * tier only, with an fp16 full tier. Produced by spax_pack_sign2. */
+ * 4i + r in bits 2r..2r+1 of byte i); scales [cols][S][2] = (s0, s1) of each
+ * of the S matrices a stored column holds (spax_matrix.approx_seg_rows).
+ * Approx tier only, with an fp16 full tier. Produced by spax_pack_sign2 per
+ * matrix. */
 #define SPAX_FMT_SIGN2      4
 /* Trellis-coded middle tier (SpAx page section 5.1, trellis coding): 2-bit
  * codes, rows/4 bytes per column in the int2 packing, one fp16 scale per
- * column (scales [cols]), and a shared fp16 codebook of 65536 values
+ * matrix column (scales [cols][S], S matrices per stored column, see
+ * spax_matrix.approx_seg_rows), and a shared fp16 codebook of 65536 values
  * (spax_matrix.approx_codebook, device memory). Weight i of a column is
  * codebook[index_i] * scale, index_i = (index_{i-1} >> 2) | (c_i << 14),
  * index_{-1} = 0. Approx tier only, with an fp16 full tier. The product
@@ -107,11 +110,23 @@ typedef struct spax_matrix {
                               tier)                                         */
   int32_t residency;       /* SPAX_RES_*                                    */
   int32_t layout;          /* SPAX_LAYOUT_*                                 */
+  int32_t approx_seg_rows; /* SIGN2 / TRELLIS approx tiers: a stored column
+                              holding several matrices' columns (q, k, v
+                              stacked) has rows / approx_seg_rows segments
+                              of approx_seg_rows rows (a multiple of 512
+                              dividing rows), each coded as its own matrix
+                              column (SpAx page section 5.1: codes and
+                              scales per weight column; section 5.3 Figure
+                              4: stacked columns stay distinct columns).
+                              0: one matrix. GLU_INTERLEAVED always holds two
+                              matrices, gate and up. Ignored by the other
+                              formats (their scales are per 128 rows).     */
   const void* full_data;   /* fp16 [cols][rows] or int4 codes [cols][rows/2] */
   const uint16_t* full_scales;   /* int4 full tier only: [cols][rows/128]   */
   const uint8_t* approx_codes;   /* approx codes, layout per approx_fmt     */
-  const uint16_t* approx_scales; /* [cols][rows/128]; SIGN2: [cols][2];
-                                    TRELLIS: [cols]                         */
+  const uint16_t* approx_scales; /* [cols][rows/128]; SIGN2: [cols][S][2];
+                                    TRELLIS: [cols][S], S the matrices per
+                                    stored column (segment s first)         */
   const uint16_t* approx_codebook; /* TRELLIS only: device fp16 [65536]     */
 } spax_matrix;
 

@@ -2,7 +2,8 @@
 the bitshift trellis with Viterbi encoding; Figure 3).
 
 TEST INFRASTRUCTURE, like spax_oracle. Parity status: pinned on the CPU
-(brute force, closed forms); the GPU path of this code is not built yet.
+(brute force, closed forms); the library's GPU and host encoders and its
+trellis product are checked against it in the GPU tests.
 
 What the page fixes: per column, 2-bit codes and one scale (the column's
 root-mean-square); a shared codebook of 2^16 values drawn once from a

@@ -52,6 +52,9 @@ def abs_sum(x, F, A, full: O.ColumnStore, approx) -> np.ndarray:
     S = np.zeros(full.rows)
 
     def code_part(store, idx):
+        if hasattr(store, "abs_terms"):
+            # a stored column of several matrices, each coded on its own
+            return np.abs(xf[idx])[:, None] * store.abs_terms(idx)
         if store.fmt == "trellis":
             # one term per element: the codebook value times x_j s_j
             return np.abs(xf[idx])[:, None] * np.abs(store.columns(idx))
@@ -149,12 +152,70 @@ class TrellisStore:
 
 
 class RowsOf:
-    """Some rows of a store whose columns are rebuilt whole (the trellis
-    window runs down the stored column)."""
+    """Some rows of a store whose columns are rebuilt whole (the scales and
+    the trellis window run down the whole matrix column)."""
 
     def __init__(self, inner, rows):
         self.inner, self.rows_idx = inner, np.asarray(rows)
         self.fmt, self.rows = inner.fmt, len(self.rows_idx)
+        if hasattr(inner, "abs_terms"):
+            self.abs_terms = lambda idx: inner.abs_terms(idx)[:, self.rows_idx]
+        elif inner.fmt == "sign2":
+            self.abs_terms = lambda idx: np.repeat(
+                inner.scales[np.asarray(idx)].astype(np.float64).sum(axis=1)[:, None],
+                inner.rows, axis=1)[:, self.rows_idx]
 
     def columns(self, idx):
         return self.inner.columns(idx)[:, self.rows_idx]
+
+
+class SegmentedStore:
+    """Oracle view of a stored column that holds several matrices' columns,
+    each coded on its own (SpAx page section 5.1): q, k, v stacked, or gate
+    and up interleaved in 128-row blocks ("glu"). columns(idx) puts each
+    matrix's rebuilt columns at its stored rows; abs_terms(idx) gives the
+    magnitude the kernel adds per element and unit |x_j| (the sign code: its
+    matrix's s0 + s1; the trellis code: |value|)."""
+
+    def __init__(self, stores, layout: str = "stacked"):
+        self.stores, self.layout = list(stores), layout
+        self.fmt = self.stores[0].fmt
+        self.rows = sum(st.rows for st in self.stores)
+
+    def _place(self, parts):
+        if self.layout == "glu":
+            g, u = parts
+            k, I = g.shape
+            out = np.empty((k, 2 * I), dtype=np.float64)
+            v = out.reshape(k, I // GROUP, 2, GROUP)
+            v[:, :, 0, :] = g.reshape(k, I // GROUP, GROUP)
+            v[:, :, 1, :] = u.reshape(k, I // GROUP, GROUP)
+            return out
+        return np.concatenate(parts, axis=1)
+
+    def columns(self, idx):
+        return self._place([st.columns(idx) for st in self.stores])
+
+    def abs_terms(self, idx):
+        idx = np.asarray(idx, dtype=np.int64)
+        if self.fmt == "sign2":
+            parts = [np.repeat(st.scales[idx].astype(np.float64).sum(axis=1)[:, None], st.rows,
+                               axis=1) for st in self.stores]
+        else:
+            parts = [np.abs(st.columns(idx)) for st in self.stores]
+        return self._place(parts)
+
+
+def split_codes(codes: np.ndarray, scales: np.ndarray, n_mat: int, layout: str = "stacked"):
+    """Per-matrix (codes, scales) of a stored 2-bit code (4 rows per byte) whose
+    columns hold n_mat matrices: stacked row segments, or ("glu") gate and up
+    in 128-row (32-byte) blocks; scales [n, n_mat * k] -> [n, k] each."""
+    n, b = codes.shape
+    if layout == "glu":
+        v = codes.reshape(n, b // 64, 2, 32)
+        parts = [np.ascontiguousarray(v[:, :, m, :].reshape(n, b // 2)) for m in range(2)]
+    else:
+        parts = [np.ascontiguousarray(c) for c in np.split(codes, n_mat, axis=1)]
+    k = scales.shape[1] // n_mat
+    sc = [np.ascontiguousarray(scales[:, m * k:(m + 1) * k]) for m in range(n_mat)]
+    return [(p, s_ if k > 1 else s_[:, 0]) for p, s_ in zip(parts, sc)]

@@ -4,8 +4,8 @@ import pytest
 
 import oracle as O
 import workloads as WL
-from tests.spax_testlib import (RowsOf, TrellisStore, check_product, log, sample_groups, to_dev,
-                                to_host)
+from tests.spax_testlib import (RowsOf, SegmentedStore, TrellisStore, check_product, log,
+                                sample_groups, split_codes, to_dev, to_host)
 
 pytestmark = pytest.mark.gpu
 
@@ -41,7 +41,7 @@ def _build_layer(w: LayerWeights, ff, af, residency, ks, kernel=0):
     qkv = o = None
     if w.q is not None:
         qkv = build_matrix(stack_rows([to_dev(w.q), to_dev(w.k), to_dev(w.v)]), F, A,
-                           residency=residency, codebook=cb)
+                           residency=residency, codebook=cb, seg_rows=w.hidden)
         o = build_matrix(to_dev(w.o), F, A, residency=residency, codebook=cb)
     gu = build_matrix(glu_interleave(to_dev(w.gate), to_dev(w.up)), F, A,
                       layout=spax.LAYOUT_GLU_INTERLEAVED, residency=residency, codebook=cb)
@@ -93,70 +93,65 @@ def _run_layer(L, h, z, x, ws=None, copy=None):
 def _check_layer(res, w: LayerWeights, ks, h, z, x, ff, af, label, rows_per=None, L=None):
     """Stage-wise parity: each group is compared with the oracle fed the same
     inputs the GPU group saw (down is fed the GPU's a)."""
-    packed = {}
-
-    def stores(Wt, rows=None, stored=None, smap=None):
-        """Oracle stores of the rows `rows` of Wt. The sign code fits its two
-        scales per stored column, so its codes come from the stored matrix
-        (stacked q/k/v, interleaved gate/up): smap gives the stored row of
-        every row of Wt."""
+    def stores(Wt, rows=None, parts=None, lib=None):
+        """Oracle stores of the matrix Wt (its rows `rows`). The sign and
+        trellis codes are per matrix column (SpAx page section 5.1): for the
+        stacked q/k/v, `parts` are q, k, v, each coded on its own; gate and
+        up are checked as their own matrices. The trellis store rebuilds
+        the library's codes of each matrix (its encoder is pinned to the
+        oracle's), `lib` = [(codes, scales)] per matrix."""
         sub = Wt if rows is None else np.ascontiguousarray(Wt[:, rows])
-        if af == "trellis":
-            # the library's codes of the stored matrix (its encoder is pinned to
-            # the oracle's), rebuilt by the oracle over whole stored columns
-            W = L_of[id(stored)] if stored is not None else L_of[id(Wt)]
-            smap_ = smap if stored is not None else np.arange(Wt.shape[1])
-            r = smap_ if rows is None else smap_[rows]
-            return O.ColumnStore(ff, sub), RowsOf(TrellisStore(*W), r)
-        if af != "sign2":
+        if af not in ("sign2", "trellis"):
             return O.ColumnStore(ff, sub), O.ColumnStore(af, sub)
-        if stored is None:
-            stored, smap = Wt, np.arange(Wt.shape[1])
-        key = id(stored)
-        if key not in packed:
-            packed[key] = O.pack_sign2(stored)
-        codes, scales = packed[key]
-        r = smap if rows is None else smap[rows]
-        return (O.ColumnStore(ff, sub),
-                O.ColumnStore("sign2", codes=np.ascontiguousarray(codes[:, r[0::4] // 4]),
-                              scales=scales))
+        if af == "sign2":
+            per = []
+            for p in (parts or [Wt]):
+                c, sc = O.pack_sign2(p)
+                per.append(O.ColumnStore("sign2", codes=c, scales=sc))
+        else:
+            per = [TrellisStore(c, sc, cbh) for c, sc in lib]
+        approx = SegmentedStore(per) if len(per) > 1 else per[0]
+        if rows is not None:
+            approx = RowsOf(approx, rows)
+        return O.ColumnStore(ff, sub), approx
 
-    # stored rows of gate and up rows in the interleaved gate/up matrix
-    i = np.arange(w.inter)
-    gmap = (i // 128) * 256 + i % 128
-    Wgu = np.empty((w.gate.shape[0], 2 * w.inter), dtype=np.float16)
-    Wgu[:, gmap] = w.gate
-    Wgu[:, gmap + 128] = w.up
     attn = w.q is not None
     Wqkv = np.concatenate([w.q, w.k, w.v], axis=1) if attn else None
-    L_of = {}
+    lib = {}
     if af == "trellis":
         cbh = WL.trellis_codebook(2)
-        for key, g in ((Wqkv, 0), (w.o, 1), (Wgu, 2), (w.down, 3)):
-            if key is None:
+        for g, n_mat, lay in ((0, 3, "stacked"), (1, 1, "stacked"), (2, 2, "glu"),
+                              (3, 1, "stacked")):
+            if g < 2 and not attn:
                 continue
             keep = L._keep[g]._keep
-            L_of[id(key)] = (to_host(keep[2]), to_host(keep[3]), cbh)
+            codes, scales = to_host(keep[2]), to_host(keep[3])
+            lib[g] = (split_codes(codes, scales, n_mat, lay) if n_mat > 1
+                      else [(codes, scales if scales.ndim == 1 else scales[:, 0])])
 
     if attn:
         L0 = O.plan_tiers(h, *ks["qkv"])
         assert all(np.array_equal(a, b) for a, b in zip(res["lists"][0], L0)), \
             f"{label}: qkv lists"
         rows = sample_groups(Wqkv.shape[1], 8, 1) if rows_per else None
-        check_product(res["qkv"], h, *L0, *stores(Wqkv, rows), f"{label} qkv", rows=rows)
+        check_product(res["qkv"], h, *L0,
+                      *stores(Wqkv, rows, parts=[w.q, w.k, w.v], lib=lib.get(0)),
+                      f"{label} qkv", rows=rows)
 
         L1 = O.plan_tiers(z, *ks["o"])
         assert all(np.array_equal(a, b) for a, b in zip(res["lists"][1], L1)), \
             f"{label}: o lists"
         rows = sample_groups(w.o.shape[1], 8, 2) if rows_per else None
-        check_product(res["o"], z, *L1, *stores(w.o, rows), f"{label} o", rows=rows)
+        check_product(res["o"], z, *L1, *stores(w.o, rows, lib=lib.get(1)), f"{label} o",
+                      rows=rows)
 
     L2 = O.plan_tiers(x, *ks["ffn"])
     assert all(np.array_equal(a, b) for a, b in zip(res["lists"][2], L2)), f"{label}: ffn lists"
     rows = sample_groups(w.inter, 8, 3) if rows_per else None
-    check_product(res["g"], x, *L2, *stores(w.gate, rows, Wgu, gmap), f"{label} gate", rows=rows)
-    check_product(res["u"], x, *L2, *stores(w.up, rows, Wgu, gmap + 128), f"{label} up",
-                  rows=rows)
+    check_product(res["g"], x, *L2, *stores(w.gate, rows, lib=lib[2][:1] if lib else None),
+                  f"{label} gate", rows=rows)
+    check_product(res["u"], x, *L2, *stores(w.up, rows, lib=lib[2][1:] if lib else None),
+                  f"{label} up", rows=rows)
     # a is formed from the GPU's own fp16 g and u
     a_want = O.swiglu_fp16(res["g"], res["u"]).astype(np.float64)
     a_got = res["a"].astype(np.float64)
@@ -168,7 +163,8 @@ def _check_layer(res, w: LayerWeights, ks, h, z, x, ff, af, label, rows_per=None
     L3 = O.plan_tiers(res["a"], *ks["down"])
     assert all(np.array_equal(a, b) for a, b in zip(res["lists"][3], L3)), f"{label}: down lists"
     rows = sample_groups(w.hidden, 8, 4) if rows_per else None
-    check_product(res["down"], res["a"], *L3, *stores(w.down, rows), f"{label} down", rows=rows)
+    check_product(res["down"], res["a"], *L3, *stores(w.down, rows, lib=lib.get(3)),
+                  f"{label} down", rows=rows)
 
 
 def _ks(hidden, inter, split):
@@ -243,6 +239,39 @@ def test_layer_7b_shapes(kernel_choice, af):
         _check_layer(res, w, ks, h, z, x, "fp16", af, f"7B layer {af} token {tok}",
                      rows_per=True)
         log(f"7B layer {af} token {tok} ok")
+
+
+@pytest.mark.parametrize("af", ["sign2", "trellis"])
+def test_per_matrix_codes_of_stacked_and_glu_columns(af):
+    """The sign and trellis codes of stacked q/k/v and GLU-interleaved
+    gate/up stored columns are each matrix's own code: equal, matrix by
+    matrix, to the oracle's packer (sign code) or encoder (trellis) applied
+    to the unstacked matrix (SpAx page section 5.1: codes and scales per
+    weight column, codes before the column start zero; section 5.3: stacked
+    columns stay distinct columns)."""
+    import oracle.spax_trellis as T
+    spax = _spax()
+    from activation_sparse_decode_token_amd.layouts import build_matrix, glu_interleave, stack_rows
+    hidden, n = 512, 6 if af == "trellis" else 64
+    A = {"sign2": spax.FMT_SIGN2, "trellis": spax.FMT_TRELLIS}[af]
+    cb = WL.trellis_codebook(2)
+    cbd = to_dev(cb) if af == "trellis" else None
+    w = {m: WL.weights_fp16(812, 0, m, hidden, n, 0.02) for m in ("q", "k", "v", "gate", "up")}
+    qkv = build_matrix(stack_rows([to_dev(w["q"]), to_dev(w["k"]), to_dev(w["v"])]),
+                       spax.FMT_FP16, A, codebook=cbd, seg_rows=hidden)
+    gu = build_matrix(glu_interleave(to_dev(w["gate"]), to_dev(w["up"])), spax.FMT_FP16, A,
+                      layout=spax.LAYOUT_GLU_INTERLEAVED, codebook=cbd)
+    assert qkv.approx_seg_rows == hidden
+    for M, names, lay in ((qkv, ("q", "k", "v"), "stacked"), (gu, ("gate", "up"), "glu")):
+        codes, scales = to_host(M._keep[2]), to_host(M._keep[3])
+        assert scales.shape == (n, len(names) * (2 if af == "sign2" else 1))
+        for (c, sc), m in zip(split_codes(codes, scales, len(names), lay), names):
+            oc, os_ = O.pack_sign2(w[m]) if af == "sign2" else T.pack_trellis(w[m], cb)
+            assert np.array_equal(c, oc), f"{af} codes of {m}"
+            assert np.array_equal(np.asarray(sc).view(np.uint16),
+                                  np.asarray(os_, dtype=np.float16).view(np.uint16)), \
+                f"{af} scales of {m}"
+    log(f"{af}: per-matrix codes of stacked q/k/v and GLU gate/up equal the oracle's")
 
 
 def test_layer_70b_ffn_shapes(kernel_choice):

@@ -12,7 +12,8 @@ import pytest
 import oracle as O
 import oracle.spax_trellis as T
 import workloads as WL
-from tests.spax_testlib import (RowsOf, TrellisStore, check_product, log, sample_groups, to_dev,
+from tests.spax_testlib import (RowsOf, SegmentedStore, TrellisStore, check_product, log,
+                                 sample_groups, split_codes, to_dev,
                                  to_host)
 
 pytestmark = pytest.mark.gpu
@@ -200,7 +201,7 @@ def test_full_size_7b_attention_trellis():
     benchmark times (a one-group layer step, which ranks x inside the
     product; codes from the GPU encoder): lists bit-exact; whole 128-row
     groups of y against the oracle, which rebuilds those columns from the
-    codes itself."""
+    codes itself (q, k and v each as its own matrix column)."""
     import torch
     import activation_sparse_decode_token_amd as spax
     import activation_sparse_decode_token_amd.layouts as LY
@@ -219,8 +220,16 @@ def test_full_size_7b_attention_trellis():
             else:
                 Wt = np.concatenate([WL.weights_fp16(2, 0, m, R // 3, n, 0.02) for m in stacked],
                                     axis=1)
-            W = build_matrix(to_dev(Wt), spax.FMT_FP16, spax.FMT_TRELLIS, codebook=to_dev(cb))
-            st = TrellisStore(to_host(W._keep[2]), to_host(W._keep[3]), cb)
+            nm = 1 if stacked is None else 3
+            W = build_matrix(to_dev(Wt), spax.FMT_FP16, spax.FMT_TRELLIS, codebook=to_dev(cb),
+                             seg_rows=0 if stacked is None else R // 3)
+            codes, scales = to_host(W._keep[2]), to_host(W._keep[3])
+            if nm == 1:
+                st = TrellisStore(codes, scales, cb)
+            else:
+                # q, k and v are coded as their own columns (SpAx page 5.1)
+                st = SegmentedStore([TrellisStore(c, sc, cb)
+                                     for c, sc in split_codes(codes, scales, nm)])
             rows = sample_groups(R, 8, 14 + R)
             full = O.ColumnStore("fp16", np.ascontiguousarray(Wt[:, rows]))
             L = spax.Layer.make([W, None, None, None], [kf, 0, 0, 0], [ka, 0, 0, 0])
