@@ -249,6 +249,10 @@ bool layer_fits(const spax_layer* L, int32_t* ff, int32_t* af) {
     ++present;
   }
   if (present == 0 || *af == kTrellis) return false;
+  // code-only layers (an int4 full tier): the per-group launches, where all
+  // 16 waves of a workgroup stream the codes, measured faster (70B FFN
+  // layer: 73.8 against 84.5 us per layer step)
+  if (*ff == kInt4) return false;
   return words <= kLayerListCap;
 }
 

@@ -526,7 +526,7 @@ __device__ __forceinline__ void rank_role(const LayerArgs& A, int first, uint32_
 // (more vector work, and two small loads per code load; measured on 7B
 // layers).
 __host__ __device__ constexpr uint32_t form_tile_cost(int fmt) {
-  return fmt == kFp16 ? 1026u : fmt == kInt4 ? 426u : 276u;
+  return fmt == kFp16 ? 1026u : fmt == kInt4 ? 426u : 800u;
 }
 
 // Per-format streaming: fp16 columns load one column per load, lane l
@@ -809,9 +809,25 @@ __device__ __forceinline__ void stream_seq(const LayerArgs& A, bool late, bool f
       for (int q = 0; q < 4; ++q) Tier<FMT>::fma2(acc[q], Fm::piece(d[u], q), fa, fb, kM);
     } else {
       const float f = h2f(xs[u]) * h2f(ss[u]) * Tier<FMT>::kScale;
-      float unused = 0.0f;
+      if constexpr (FMT == kInt2) {
+        // one 32-bit word holds rows 16 w .. 16 w + 15 (row k in bits 2k,
+        // 2k + 1): one shift puts rows k and k + 8 into bits 8..9 of the two
+        // halves, so each pair costs a shift and an and-or (fp16 1 + u / 4)
+        const uint32_t dw[2] = {d[u].x, d[u].y};
 #pragma unroll
-      for (int q = 0; q < 4; ++q) Tier<FMT>::fma(acc[q], unused, Fm::piece(d[u], q), f, kM);
+        for (int w = 0; w < 2; ++w)
+#pragma unroll
+          for (int k = 0; k < 8; ++k) {
+            const uint32_t sh = k <= 4 ? dw[w] << (8 - 2 * k) : dw[w] >> (2 * k - 8);
+            const uint32_t p = (sh & kM) | 0x3C003C00u;
+            acc[2 * w][k] = fmaf(h2f(p & 0xFFFFu), f, acc[2 * w][k]);
+            acc[2 * w + 1][k] = fmaf(h2f(p >> 16), f, acc[2 * w + 1][k]);
+          }
+      } else {
+        float unused = 0.0f;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) Tier<FMT>::fma(acc[q], unused, Fm::piece(d[u], q), f, kM);
+      }
       corr = fmaf(FMT == kInt4 ? 1.5f : 1.375f, f, corr);
     }
     if ((ends >> u) & 1u) {  // wave-uniform
@@ -1117,15 +1133,12 @@ hipError_t launch_pair(const LayerArgs& a, hipStream_t s) {
 
 hipError_t launch_layer(const LayerArgs& a, int32_t full_fmt, int32_t approx_fmt,
                         hipStream_t s) {
+  // (layers with an int4 full tier run the per-group launches)
   if (full_fmt == kFp16) {
     if (approx_fmt == kNone) return launch_pair<kFp16, kNone>(a, s);
     if (approx_fmt == kInt4) return launch_pair<kFp16, kInt4>(a, s);
     if (approx_fmt == kInt2) return launch_pair<kFp16, kInt2>(a, s);
     if (approx_fmt == kSign2) return launch_pair<kFp16, kSign2>(a, s);
-  } else if (full_fmt == kInt4) {
-    if (approx_fmt == kNone) return launch_pair<kInt4, kNone>(a, s);
-    if (approx_fmt == kInt4) return launch_pair<kInt4, kInt4>(a, s);
-    if (approx_fmt == kInt2) return launch_pair<kInt4, kInt2>(a, s);
   }
   return hipErrorInvalidValue;
 }

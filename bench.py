@@ -541,27 +541,36 @@ def layer_kernel_runs(wl: Workload) -> bool:
 
 
 def roofline(spec: Spec, wl: Workload, sec_step: float, mode: str):
-    """The layer kernel's roofline: algorithmic bytes of one layer step over
-    its average launch duration (the timed replays' event time on the launch
-    stream over the launches they hold)."""
-    if mode != "graph" or not layer_kernel_runs(wl):
+    """Roofline of the product kernel: algorithmic bytes per launch over its
+    average launch duration (the timed replays' event time on the launch
+    stream over the launches they hold). With the layer kernel a layer step
+    is one launch; otherwise every group is one fused ranking + product
+    launch (gemv_kernel)."""
+    if mode != "graph":
         return None
-    t_launch = sec_step / wl.slots
-    achieved = wl.layer_bytes() / t_launch / 1e9
-    log(f"layer kernel: {t_launch * 1e6:.2f} us per launch, {achieved:.0f} GB/s on algorithmic "
-        "bytes")
+    layer = layer_kernel_runs(wl)
+    per_slot = 1 if layer else len(group_shapes(spec))
+    launches = wl.slots * per_slot
+    t_launch = sec_step / launches
+    bytes_launch = wl.layer_bytes() / per_slot
+    achieved = bytes_launch / t_launch / 1e9
+    log(f"{'layer' if layer else 'product'} kernel: {t_launch * 1e6:.2f} us per launch, "
+        f"{achieved:.0f} GB/s on algorithmic bytes")
     return {
         "bound": "hbm",
         "achieved": round(achieved, 1),
         "peak": HBM_PEAK_GBS,
         "unit": "GB/s",
         "frac": round(achieved / HBM_PEAK_GBS, 4),
-        "traffic": measured_traffic(spec.config) if spec.approx_fmt in ("int4", "int2") else None,
-        "kernel": "layer_kernel: every group of one decoder layer (ranking, tiered "
-                  "gather-GEMV, SwiGLU) in one launch",
+        "traffic": (measured_traffic(spec.config)
+                    if layer and spec.approx_fmt in ("int4", "int2") else None),
+        "kernel": ("layer_kernel: every group of one decoder layer (ranking, tiered "
+                   "gather-GEMV, SwiGLU) in one launch" if layer else
+                   "gemv_kernel: fused tier selection + tiered gather-GEMV, one launch per "
+                   "group (the mean over the groups' launches)"),
         "avg_launch_us": round(t_launch * 1e6, 3),
-        "launches_per_step": wl.slots,
-        "bytes_per_launch": wl.layer_bytes(),
+        "launches_per_step": launches,
+        "bytes_per_launch": int(bytes_launch),
     }
 
 

@@ -42,9 +42,10 @@ LAYERS = {
     # 7B-shaped layer, 50/25/25
     "7b": (4096, 11008, [(1024, 1024), (1024, 1024), (1024, 1024), (2752, 2752)],
            spax.FMT_FP16, spax.FMT_INT4_G128, (1, 1, 1, 1)),
-    # 70B-shaped FFN, int4 full + int2 approx, 50/30/20
+    # 70B-shaped FFN, fp16 full + int2 approx, 50/30/20 (code-only layers,
+    # with an int4 full tier, run the per-group launches)
     "70b_ffn": (8192, 28672, [(0, 0), (0, 0), (1638, 2458), (5734, 8602)],
-                spax.FMT_INT4_G128, spax.FMT_INT2_G128, (0, 0, 1, 1)),
+                spax.FMT_FP16, spax.FMT_INT2_G128, (0, 0, 1, 1)),
     # ragged tiles, an empty group and a one-column tier
     "ragged": (640, 1408, [(1, 0), (0, 0), (300, 17), (0, 1)],
                spax.FMT_FP16, spax.FMT_SIGN2, (1, 1, 1, 1)),
@@ -148,6 +149,9 @@ def test_schedule_rejects_what_the_layer_kernel_does_not_run():
     L.group[1] = _m(hidden, hidden, spax.FMT_FP16, spax.FMT_INT2_G128)
     with pytest.raises(spax.SpaxError):
         spax.layer_schedule(L, 256)            # two format pairs in one layer
+    L = _layer(hidden, inter, ks, spax.FMT_INT4_G128, spax.FMT_INT2_G128, on)
+    with pytest.raises(spax.SpaxError):
+        spax.layer_schedule(L, 256)            # an int4 full tier: per-group launches
     big = _layer(4096, 11008, [(8192, 8192), (1024, 1024), (1024, 1024), (2752, 2752)])
     with pytest.raises(spax.SpaxError):
         spax.layer_schedule(big, 256)          # lists past the LDS capacity
