@@ -57,11 +57,16 @@ constexpr int kCoherent = 16;
 
 struct LayerShared {
   uint16_t lists[kLayerListCap];             // every group's F then A lists
-  uint16_t keys[kLayerMaxN];                 // ranking: the input's fp16 bits
+  uint16_t keys[kLayerMaxN];                 // ranking: the input's fp16 bits (the
+                                             // four ranking waves), or the 32768-bin
+                                             // key histogram (the whole workgroup)
   float slot[2][kNS][kTileRows];             // streaming waves' partials
   uint32_t hist[256 * kHistCopies];          // ranking: top-level histogram
   uint32_t sub[256 * kHistCopies];           // ranking: the two sub-histograms
   uint32_t rtot[kRankMaxRounds][4];          // ranking: per-round counts
+  uint32_t wtot[kWaves];                     // ranking: per-wave histogram totals
+  uint32_t rsel[4];                          // ranking: t1, q1, t2, q2
+  uint32_t rsum[4];                          // ranking: the four counts over all rounds
   uint32_t need[8];                          // ranking: positions to place
   uint32_t own[4];                           // ranking: positions to store out
   uint64_t rank_out[2];                      // ranking: the caller's lists
@@ -99,6 +104,15 @@ __device__ __forceinline__ void lds_signal_add(uint32_t* p, uint32_t v) {
 __device__ __forceinline__ void lds_signal_store(uint32_t* p, uint32_t v) {
   lds_release();
   __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+}
+
+// A barrier of the whole workgroup that orders its LDS accesses only: a
+// full barrier would also wait for every global store the wave still has in
+// flight (the ranking's tier lists to the caller, read by no one here).
+__device__ __forceinline__ void lds_barrier() {
+  lds_release();
+  __builtin_amdgcn_s_barrier();
+  lds_acquire();
 }
 
 __device__ __forceinline__ void set_status(uint32_t* status, uint32_t bit) {
@@ -166,6 +180,77 @@ __device__ __forceinline__ void lane_counts(const uint4& v, uint32_t t1, uint32_
     const uint32_t k = (w[h >> 1] >> (16 * (h & 1))) & 0x7FFFu;
     c1 += k > t1 ? 1u : (k == t1 ? 0x10000u : 0u);
     c2 += k > t2 ? 1u : (k == t2 ? 0x10000u : 0u);
+  }
+}
+
+
+// What the placement of a ranking needs: the boundaries, the list positions
+// the workgroup reads (two intervals per tier), the positions it stores to
+// the caller's lists and their pointers (set_need).
+struct Placement {
+  uint32_t K1, t1, q1, t2, q2;
+  uint32_t nf0, nf1, nf2, nf3, na0, na1, na2, na3;
+  uint32_t of0, of1, oa0, oa1;
+  int32_t* out_f;
+  int32_t* out_a;
+};
+
+__device__ __forceinline__ Placement load_placement(uint32_t K1, uint32_t t1, uint32_t q1,
+                                                    uint32_t t2, uint32_t q2) {
+  const LayerShared& sm = g_sm;
+  Placement P;
+  P.K1 = K1; P.t1 = t1; P.q1 = q1; P.t2 = t2; P.q2 = q2;
+  const uint4 nf = *reinterpret_cast<const uint4*>(&sm.need[0]);
+  const uint4 na = *reinterpret_cast<const uint4*>(&sm.need[4]);
+  P.nf0 = uniform(nf.x); P.nf1 = uniform(nf.y); P.nf2 = uniform(nf.z); P.nf3 = uniform(nf.w);
+  P.na0 = uniform(na.x); P.na1 = uniform(na.y); P.na2 = uniform(na.z); P.na3 = uniform(na.w);
+  const uint4 ow = *reinterpret_cast<const uint4*>(&sm.own[0]);
+  P.of0 = uniform(ow.x); P.of1 = uniform(ow.y); P.oa0 = uniform(ow.z); P.oa1 = uniform(ow.w);
+  P.out_f = uniform_ptr(reinterpret_cast<int32_t*>(sm.rank_out[0]));
+  P.out_a = uniform_ptr(reinterpret_cast<int32_t*>(sm.rank_out[1]));
+  return P;
+}
+
+// Whether a round whose counts before it are (G1, E1, G2, E2) and through it
+// (G1e, E1e, G2e, E2e) holds a list position the workgroup needs.
+__device__ __forceinline__ bool round_needed(const Placement& P, uint32_t G1, uint32_t E1,
+                                             uint32_t G2, uint32_t E2, uint32_t G1e,
+                                             uint32_t E1e, uint32_t G2e, uint32_t E2e) {
+  // the round's full-tier and approx-tier position ranges
+  const uint32_t fb = G1 + min(E1, P.q1), fe = G1e + min(E1e, P.q1);
+  const uint32_t ab = G2 + min(E2, P.q2) - fb, ae = G2e + min(E2e, P.q2) - fe;
+  return (fb < P.nf1 && fe > P.nf0) || (fb < P.nf3 && fe > P.nf2) ||
+         (ab < P.na1 && ae > P.na0) || (ab < P.na3 && ae > P.na2);
+}
+
+// Places the lane's 8 entries e0 + h (keys v) of a round: x1, x2 are the
+// lane's exclusive counts within the round (as lane_counts packs them),
+// (G1, E1, G2, E2) the counts of the rounds before.
+__device__ __forceinline__ void place_round(const Placement& P, uint16_t* list, const uint4& v,
+                                            uint32_t e0, uint32_t x1, uint32_t x2, uint32_t G1,
+                                            uint32_t E1, uint32_t G2, uint32_t E2) {
+  uint32_t g1 = G1 + (x1 & 0xFFFFu), e1 = E1 + (x1 >> 16);
+  uint32_t g2 = G2 + (x2 & 0xFFFFu), e2 = E2 + (x2 >> 16);
+  const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+  for (int h = 0; h < 8; ++h) {
+    const uint32_t k = (w4[h >> 1] >> (16 * (h & 1))) & 0x7FFFu;
+    const uint32_t fpos = g1 + min(e1, P.q1);
+    const uint32_t apos = g2 + min(e2, P.q2) - fpos;
+    const bool in_f = k > P.t1 || (k == P.t1 && e1 < P.q1);
+    const bool in_fa = k > P.t2 || (k == P.t2 && e2 < P.q2);
+    const uint32_t e = e0 + (uint32_t)h;
+    if (in_f) {
+      list[fpos] = (uint16_t)e;
+      if (fpos >= P.of0 && fpos < P.of1) P.out_f[fpos] = (int32_t)e;
+    } else if (in_fa) {
+      list[P.K1 + apos] = (uint16_t)e;
+      if (apos >= P.oa0 && apos < P.oa1) P.out_a[apos] = (int32_t)e;
+    }
+    g1 += k > P.t1 ? 1u : 0u;
+    e1 += k == P.t1 ? 1u : 0u;
+    g2 += k > P.t2 ? 1u : 0u;
+    e2 += k == P.t2 ? 1u : 0u;
   }
 }
 
@@ -355,14 +440,7 @@ __device__ __attribute__((noinline)) uint32_t rank_group(const uint16_t* __restr
       ex[q] = inc[q] - own[q];
     }
   }
-  const uint4 nf = *reinterpret_cast<const uint4*>(&sm.need[0]);
-  const uint4 na = *reinterpret_cast<const uint4*>(&sm.need[4]);
-  const uint32_t nf0 = uniform(nf.x), nf1 = uniform(nf.y), nf2 = uniform(nf.z), nf3 = uniform(nf.w);
-  const uint32_t na0 = uniform(na.x), na1 = uniform(na.y), na2 = uniform(na.z), na3 = uniform(na.w);
-  const uint4 ow = *reinterpret_cast<const uint4*>(&sm.own[0]);
-  const uint32_t of0 = uniform(ow.x), of1 = uniform(ow.y), oa0 = uniform(ow.z), oa1 = uniform(ow.w);
-  int32_t* out_f = uniform_ptr(reinterpret_cast<int32_t*>(sm.rank_out[0]));
-  int32_t* out_a = uniform_ptr(reinterpret_cast<int32_t*>(sm.rank_out[1]));
+  const Placement P = load_placement(K1, t1, q1, t2, q2);
   for (int r = rw; r < R; r += RW) {
     const uint32_t G1 = uniform((uint32_t)__builtin_amdgcn_readlane((int)ex[0], r));
     const uint32_t E1 = uniform((uint32_t)__builtin_amdgcn_readlane((int)ex[1], r));
@@ -372,40 +450,12 @@ __device__ __attribute__((noinline)) uint32_t rank_group(const uint16_t* __restr
     const uint32_t E1e = uniform((uint32_t)__builtin_amdgcn_readlane((int)inc[1], r));
     const uint32_t G2e = uniform((uint32_t)__builtin_amdgcn_readlane((int)inc[2], r));
     const uint32_t E2e = uniform((uint32_t)__builtin_amdgcn_readlane((int)inc[3], r));
-    // the round's full-tier and approx-tier position ranges
-    const uint32_t fb = G1 + min(E1, q1), fe = G1e + min(E1e, q1);
-    const uint32_t ab = G2 + min(E2, q2) - fb, ae = G2e + min(E2e, q2) - fe;
-    const bool need = (fb < nf1 && fe > nf0) || (fb < nf3 && fe > nf2) ||
-                      (ab < na1 && ae > na0) || (ab < na3 && ae > na2);
-    if (!need) continue;  // wave-uniform
+    if (!round_needed(P, G1, E1, G2, E2, G1e, E1e, G2e, E2e)) continue;  // wave-uniform
     const uint4 v = *reinterpret_cast<const uint4*>(&sm.keys[r * kRankRound + 8 * lane]);
     uint32_t c1, c2;
     lane_counts(v, t1, t2, c1, c2);
-    const uint32_t x1 = wave_incl_scan(c1) - c1, x2 = wave_incl_scan(c2) - c2;
-    uint32_t g1 = G1 + (x1 & 0xFFFFu), e1 = E1 + (x1 >> 16);
-    uint32_t g2 = G2 + (x2 & 0xFFFFu), e2 = E2 + (x2 >> 16);
-    const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
-    const uint32_t e0 = (uint32_t)(r * kRankRound + 8 * lane);
-#pragma unroll
-    for (int h = 0; h < 8; ++h) {
-      const uint32_t k = (w4[h >> 1] >> (16 * (h & 1))) & 0x7FFFu;
-      const uint32_t fpos = g1 + min(e1, q1);
-      const uint32_t apos = g2 + min(e2, q2) - fpos;
-      const bool in_f = k > t1 || (k == t1 && e1 < q1);
-      const bool in_fa = k > t2 || (k == t2 && e2 < q2);
-      const uint32_t e = e0 + (uint32_t)h;
-      if (in_f) {
-        list[fpos] = (uint16_t)e;
-        if (fpos >= of0 && fpos < of1) out_f[fpos] = (int32_t)e;
-      } else if (in_fa) {
-        list[K1 + apos] = (uint16_t)e;
-        if (apos >= oa0 && apos < oa1) out_a[apos] = (int32_t)e;
-      }
-      g1 += k > t1 ? 1u : 0u;
-      e1 += k == t1 ? 1u : 0u;
-      g2 += k > t2 ? 1u : 0u;
-      e2 += k == t2 ? 1u : 0u;
-    }
+    place_round(P, list, v, (uint32_t)(r * kRankRound + 8 * lane), wave_incl_scan(c1) - c1,
+                wave_incl_scan(c2) - c2, G1, E1, G2, E2);
   }
   static_assert(256 * kHistCopies == 4 * kLayerRankThreads, "one 16-byte clear per thread");
   if (rt < kLayerRankThreads) {
@@ -414,6 +464,203 @@ __device__ __attribute__((noinline)) uint32_t rank_group(const uint16_t* __restr
   }
   rank_sync<RW>(epoch, status);
   return epoch;
+}
+
+// Ranks x[0, n) on the whole workgroup (16 waves, no streaming waves beside
+// them) and places the list positions this workgroup needs, with the same
+// result as rank_group (the same K1 largest |x_j| in F, the next K2 - K1 in
+// A, lower index first among equal keys). With every wave ranking there is
+// no room to spare in issue cycles: a wave gets one instruction per four
+// cycles, so the steps that one wave or every wave repeats (finding a bin,
+// scanning 64 rounds) cost as much as the per-key passes. This variant
+// keeps each wave's keys in registers (at most 4 rounds of 512 entries per
+// wave) and puts an exact histogram of all 32768 keys in the keys' LDS area,
+// which removes the second histogram pass and both bin searches. Steps:
+//   1. the keys into registers (rounds rw, rw + 16, ...), the histogram
+//      cleared meanwhile, then one LDS add per real entry (two 16-bit bins
+//      per word: no bin exceeds n <= 32768, nor does any sum of bins below);
+//   2. thread i holds bins [32 i, 32 i + 32): its total, a suffix sum over
+//      the threads (a wave scan, then the waves' totals) gives the entries
+//      above its bins; the thread whose bins hold rank K (1-based, from the
+//      largest key) hands its 32 bins to the lanes of its wave, whose scan
+//      finds the boundary key t and the number q of entries equal to t that
+//      are kept, for K = K1 and K = K2;
+//   3. per round, the counts of key > t1, key == t1, key > t2, key == t2
+//      (the lanes' exclusive counts stay in registers for step 4);
+//   4. one wave scans the counts over the rounds; each wave places the
+//      entries of its rounds that meet a needed range (rank_group step 6).
+// Entries past n are loaded as key 0 and not counted in the histogram; they
+// come after every real entry, so a boundary at key 0 keeps real zeros
+// first (the quota q counts real entries only).
+__device__ __attribute__((noinline)) void rank_all(const uint16_t* __restrict__ x, int n,
+                                                   uint32_t K1, uint32_t K2, int list_off) {
+  x = uniform_ptr(x);
+  n = (int)uniform((uint32_t)n);
+  K1 = uniform(K1);
+  K2 = uniform(K2);
+  list_off = (int)uniform((uint32_t)list_off);
+  LayerShared& sm = g_sm;
+  uint16_t* list = sm.lists + list_off;
+  uint32_t* hist = reinterpret_cast<uint32_t*>(sm.keys);  // bins 2 i and 2 i + 1 in word i
+  const int t = (int)threadIdx.x;
+  const int lane = t & 63;
+  const int rw = (int)uniform((uint32_t)(t >> 6));
+  constexpr int kPer = kRankMaxRounds / kWaves;  // rounds per wave
+  const int R = (n + kRankRound - 1) / kRankRound;
+  const int Rfull = n / kRankRound;
+
+  // 1. keys (loads in flight while the histogram is cleared)
+  const __amdgpu_buffer_rsrc_t rs = tier_rsrc(reinterpret_cast<const uint8_t*>(x), 2u * n);
+  uint4 kv[kPer];
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) {
+    const int r = rw + kWaves * i;
+    kv[i] = make_uint4(0u, 0u, 0u, 0u);
+    if (r < Rfull) {
+      kv[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
+                                            rs, 2u * (uint32_t)(r * kRankRound + 8 * lane), 0, 0));
+    } else if (r < R) {  // the round that holds the end of x, entry by entry
+      const int e = r * kRankRound + 8 * lane;
+      uint32_t wd[4];
+#pragma unroll
+      for (int h = 0; h < 8; h += 2) {
+        uint32_t lo = 0u, hi = 0u;
+        if (e + h < n) lo = __builtin_amdgcn_raw_buffer_load_b16(rs, 2u * (e + h), 0, 0);
+        if (e + h + 1 < n) hi = __builtin_amdgcn_raw_buffer_load_b16(rs, 2u * (e + h + 1), 0, 0);
+        wd[h / 2] = lo | (hi << 16);
+      }
+      kv[i] = make_uint4(wd[0], wd[1], wd[2], wd[3]);
+    }
+  }
+  static_assert(kLayerMaxN / 2 == 16 * kGemvThreads, "four 16-byte clears per thread");
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+    reinterpret_cast<uint4*>(hist)[t + kGemvThreads * j] = make_uint4(0u, 0u, 0u, 0u);
+  if (t == 0)
+    *reinterpret_cast<uint4*>(&sm.rsel[0]) = make_uint4(kAboveAll, 0u, kAboveAll, 0u);
+  lds_barrier();
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) {
+    const int r = rw + kWaves * i;
+    if (r < R) {
+      const uint4 v = make_uint4(kv[i].x & 0x7FFF7FFFu, kv[i].y & 0x7FFF7FFFu,
+                                 kv[i].z & 0x7FFF7FFFu, kv[i].w & 0x7FFF7FFFu);
+      kv[i] = v;
+      const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
+      if (r < Rfull) {  // wave-uniform
+#pragma unroll
+        for (int h = 0; h < 8; ++h) {
+          const uint32_t k = (w4[h >> 1] >> (16 * (h & 1))) & 0xFFFFu;
+          atomicAdd(&hist[k >> 1], 1u << ((k & 1u) << 4));
+        }
+      } else {
+        const int lim = n - (r * kRankRound + 8 * lane);  // real entries of the lane
+#pragma unroll
+        for (int h = 0; h < 8; ++h) {
+          const uint32_t k = (w4[h >> 1] >> (16 * (h & 1))) & 0xFFFFu;
+          if (h < lim) atomicAdd(&hist[k >> 1], 1u << ((k & 1u) << 4));
+        }
+      }
+    }
+  }
+  lds_barrier();
+
+  // 2. boundary keys and quotas
+  {
+    const uint4* hp = reinterpret_cast<const uint4*>(hist) + 4 * t;
+    uint32_t sum = 0u;  // packed: no half reaches 2^16
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const uint4 v = hp[j];
+      sum += v.x + v.y + v.z + v.w;
+    }
+    const uint32_t tot = (sum & 0xFFFFu) + (sum >> 16);
+    const uint32_t incl = wave_incl_scan(tot);
+    const uint32_t wsum = (uint32_t)__builtin_amdgcn_readlane((int)incl, 63);
+    if (lane == 0) sm.wtot[rw] = wsum;
+    lds_barrier();
+    uint32_t above = wsum - incl;  // entries in the bins of higher lanes of this wave
+    const uint4* wp = reinterpret_cast<const uint4*>(sm.wtot);
+#pragma unroll
+    for (int j = 0; j < kWaves / 4; ++j) {
+      const uint4 v = wp[j];
+      above += (4 * j + 0 > rw ? v.x : 0u) + (4 * j + 1 > rw ? v.y : 0u) +
+               (4 * j + 2 > rw ? v.z : 0u) + (4 * j + 3 > rw ? v.w : 0u);
+    }
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+      const uint32_t K = c == 0 ? K1 : K2;
+      const uint64_t m = __ballot(K > 0u && above < K && K <= above + tot);
+      if (m != 0) {  // wave-uniform: this wave holds rank K
+        const int L = (int)__builtin_ctzll(m);
+        const uint32_t ab = (uint32_t)__builtin_amdgcn_readlane((int)above, L);
+        const int b_top = 32 * (64 * rw + L) + 31;  // the holder's highest bin
+        const uint32_t cnt = lane < 32 ? (uint32_t)sm.keys[b_top - lane] : 0u;
+        const uint32_t ci = ab + wave_incl_scan(cnt);
+        const uint64_t f = __ballot(lane < 32 && ci - cnt < K && K <= ci);
+        const int J = (int)__builtin_ctzll(f);
+        const uint32_t q = K - ((uint32_t)__builtin_amdgcn_readlane((int)ci, J) -
+                                (uint32_t)__builtin_amdgcn_readlane((int)cnt, J));
+        if (lane == 0) {
+          sm.rsel[2 * c] = (uint32_t)(b_top - J);
+          sm.rsel[2 * c + 1] = q;
+        }
+      }
+    }
+  }
+  lds_barrier();
+  const uint4 sel = *reinterpret_cast<const uint4*>(&sm.rsel[0]);
+  const uint32_t t1 = uniform(sel.x), q1 = uniform(sel.y), t2 = uniform(sel.z),
+                 q2 = uniform(sel.w);
+
+  // 3. per-round counts
+  uint32_t x1[kPer], x2[kPer];
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) {
+    const int r = rw + kWaves * i;
+    x1[i] = x2[i] = 0u;
+    if (r < R) {
+      uint32_t c1, c2;
+      lane_counts(kv[i], t1, t2, c1, c2);
+      const uint32_t i1 = wave_incl_scan(c1), i2 = wave_incl_scan(c2);
+      x1[i] = i1 - c1;
+      x2[i] = i2 - c2;
+      if (lane == 63)
+        *reinterpret_cast<uint4*>(&sm.rtot[r][0]) =
+            make_uint4(i1 & 0xFFFFu, i1 >> 16, i2 & 0xFFFFu, i2 >> 16);
+    }
+  }
+  lds_barrier();
+
+  // 4. wave 0: exclusive counts before each round, in place (the counts
+  // through round r are those before round r + 1; after the last, the
+  // totals); then placement
+  if (rw == 0) {
+    const uint4 u = lane < R ? *reinterpret_cast<const uint4*>(&sm.rtot[lane][0])
+                             : make_uint4(0u, 0u, 0u, 0u);
+    const uint32_t i0 = wave_incl_scan(u.x), i1 = wave_incl_scan(u.y);
+    const uint32_t i2 = wave_incl_scan(u.z), i3 = wave_incl_scan(u.w);
+    if (lane < R)
+      *reinterpret_cast<uint4*>(&sm.rtot[lane][0]) =
+          make_uint4(i0 - u.x, i1 - u.y, i2 - u.z, i3 - u.w);
+    if (lane == 63) *reinterpret_cast<uint4*>(&sm.rsum[0]) = make_uint4(i0, i1, i2, i3);
+  }
+  lds_barrier();
+  const Placement P = load_placement(K1, t1, q1, t2, q2);
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) {
+    const int r = rw + kWaves * i;
+    if (r >= R) break;  // wave-uniform
+    const uint4 e = *reinterpret_cast<const uint4*>(&sm.rtot[r][0]);
+    const uint4 f = r + 1 < R ? *reinterpret_cast<const uint4*>(&sm.rtot[r + 1][0])
+                              : *reinterpret_cast<const uint4*>(&sm.rsum[0]);
+    const uint32_t G1 = uniform(e.x), E1 = uniform(e.y), G2 = uniform(e.z), E2 = uniform(e.w);
+    if (!round_needed(P, G1, E1, G2, E2, uniform(f.x), uniform(f.y), uniform(f.z),
+                      uniform(f.w)))
+      continue;
+    place_round(P, list, kv[i], (uint32_t)(r * kRankRound + 8 * lane), x1[i], x2[i], G1, E1, G2,
+                E2);
+  }
 }
 
 // Whether group g runs in the launch's second phase: down, when its input
@@ -1068,19 +1315,21 @@ __global__ __launch_bounds__(kGemvThreads) void layer_kernel(LayerArgs A) {
   const uint32_t w = blockIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
   const int first = first_ranked(A, w);
-  if (first >= 0 && t == 0) set_need(A, first, w);
   __syncthreads();
-  // the first phase's segments, by the last wave while the others load the
-  // first ranking's keys (it has no keys to load for inputs up to 7680)
-  if (wave == kWaves - 1) build_segtab(A, w, false);
+  // the first phase's segments and the positions the first ranking places,
+  // by the last wave while the others load the first ranking's keys (the
+  // placement reads the positions after the ranking's barriers)
+  if (wave == kWaves - 1) {
+    build_segtab(A, w, false);
+    if (first >= 0 && t == (kWaves - 1) * 64) set_need(A, first, w);
+  }
   uint32_t epoch = 0u;
   if (first >= 0) {
     const LayerGroupArgs& gr = A.g[first];
-    rank_group<kWaves>(gr.x, gr.n, (uint32_t)gr.k_full, (uint32_t)(gr.k_full + gr.k_approx),
-                       gr.list_off, 0u, A.sync + 2);
+    rank_all(gr.x, gr.n, (uint32_t)gr.k_full, (uint32_t)(gr.k_full + gr.k_approx), gr.list_off);
     if (t == 0) sm.ready[first] = 1u;
   }
-  __syncthreads();  // the first lists and the segment table are in LDS
+  lds_barrier();  // the first lists and the segment table are in LDS
   uint32_t k = 0u;  // segments handed over (streaming and reduction waves)
   // phase 0: every group but a late down; phase 1: down, once every gate/up
   // tile has written a (one call site per role keeps the streaming code
@@ -1092,17 +1341,17 @@ __global__ __launch_bounds__(kGemvThreads) void layer_kernel(LayerArgs A) {
       __syncthreads();
       if (wave == 0) {
         wait_gate_up(A);
-        if (t == 0) set_need(A, SPAX_GROUP_DOWN, w);
       } else if (wave == 1) {
         build_segtab(A, w, true);
+        if (t == 64) set_need(A, SPAX_GROUP_DOWN, w);
       }
       __syncthreads();
       const LayerGroupArgs& gd = A.g[SPAX_GROUP_DOWN];
       if (gd.k_full + gd.k_approx > 0)
-        rank_group<kWaves>(gd.x, gd.n, (uint32_t)gd.k_full,
-                           (uint32_t)(gd.k_full + gd.k_approx), gd.list_off, 0u, A.sync + 2);
+        rank_all(gd.x, gd.n, (uint32_t)gd.k_full, (uint32_t)(gd.k_full + gd.k_approx),
+                 gd.list_off);
       if (t == 0) sm.ready[SPAX_GROUP_DOWN] = 1u;
-      __syncthreads();
+      lds_barrier();
     }
     if (wave < kLayerStreamWaves)
       stream_role<FF, AF>(A, wave, phase == 1, k);

@@ -222,6 +222,38 @@ def test_layer_kernel_7b_on_37_workgroups():
     log("7B layer on 37 workgroups ok")
 
 
+def _tied(case, seed, n):
+    """Inputs with many equal magnitudes: the ranking's ties (lower index
+    first) decide most of the lists."""
+    rs = np.random.default_rng(seed)
+    if case == "all-equal":
+        return np.full(n, -1.5, dtype=np.float16)
+    if case == "signed-zeros":
+        return rs.choice(np.array([0.0, -0.0], dtype=np.float16), n)
+    if case == "small-alphabet":
+        return rs.choice(np.array([0, -0.0, 1, -1, 2, -2, 0.5], dtype=np.float16), n)
+    if case == "subnormal":
+        return (rs.integers(-3, 4, n) * 2.0 ** -24).astype(np.float16)
+    raise ValueError(case)
+
+
+@pytest.mark.parametrize("case", ["all-equal", "signed-zeros", "small-alphabet", "subnormal"])
+def test_layer_kernel_tied_inputs(case):
+    """The layer kernel's rankings on inputs full of ties, with empty tiers,
+    tiers that take every column, and a ragged last round of 512 entries
+    (down's input has 1408 entries): lists equal the oracle's exactly."""
+    hidden, inter = 512, 1408
+    w = LayerWeights(812, 0, hidden, inter, 0.02)
+    for ks in ({"qkv": (128, 128), "o": (0, 200), "ffn": (256, 0), "down": (1, 1406)},
+               {"qkv": (511, 1), "o": (170, 171), "ffn": (0, 512), "down": (704, 0)}):
+        L = _build_layer(w, "fp16", "int4", 0, ks, 0)
+        assert len(_spax().layer_schedule(L, 256)) > 0  # the one-launch layer kernel runs
+        h, z, x = (_tied(case, 812 + i, hidden) for i in range(3))
+        res, _ = _run_layer(L, h, z, x)
+        _check_layer(res, w, ks, h, z, x, "fp16", "int4", f"tied {case} {ks}")
+    log(f"layer kernel on tied inputs ({case}) ok")
+
+
 @pytest.mark.parametrize("af", ["int4", "sign2"])
 def test_layer_7b_shapes(kernel_choice, af):
     """A full-size 7B layer step (the launches the benchmarks time), with the
