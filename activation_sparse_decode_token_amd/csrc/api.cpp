@@ -212,9 +212,6 @@ size_t gemv_ws(const spax_matrix* W) {
 
 // Smallest share of a group's selected bytes worth one workgroup.
 constexpr uint64_t kLayerMinWgBytes = 32768;
-// Processing order of the groups in the layer kernel.
-constexpr int kLayerOrder[4] = {SPAX_GROUP_GATE_UP, SPAX_GROUP_QKV, SPAX_GROUP_O,
-                                SPAX_GROUP_DOWN};
 
 int32_t row_tiles(int32_t rows) { return (rows + kTileRows - 1) / kTileRows; }
 
@@ -274,7 +271,7 @@ void layer_schedule(const spax_layer* L, int32_t Gmax, LayerArgs* A) {
   const bool has_gu = L->group[SPAX_GROUP_GATE_UP].cols > 0;
   int32_t list_off = 0;
   for (int oi = 0; oi < 4; ++oi) {
-    const int g = kLayerOrder[oi];
+    const int g = layer_order(oi);
     const spax_matrix& M = L->group[g];
     if (M.cols <= 0) continue;
     LayerGroupArgs& gr = A->g[g];
@@ -319,6 +316,8 @@ void layer_schedule(const spax_layer* L, int32_t Gmax, LayerArgs* A) {
     gr.n_wg = (int32_t)n;
     gr.unit_q = gr.units / (uint32_t)n;
     gr.unit_r = gr.units % (uint32_t)n;
+    gr.k_magic = div_magic((uint32_t)K);
+    gr.nwg_magic = div_magic((uint32_t)n);
     G = std::max<int64_t>(G, lo[g] + n);
   }
   A->G = (int32_t)G;

@@ -706,8 +706,10 @@ __device__ __forceinline__ void set_need(const LayerArgs& A, int g, uint32_t w) 
 
 // The first group in processing order that workgroup w ranks, or -1.
 __device__ __forceinline__ int first_ranked(const LayerArgs& A, uint32_t w) {
-  for (int oi = 0; oi < A.n_order; ++oi) {
-    const int g = A.order[oi];
+  // (unrolled: every group's fields sit at fixed offsets of the arguments)
+#pragma unroll
+  for (int oi = 0; oi < 4; ++oi) {
+    const int g = layer_order(oi);
     if (layer_meets(A, g, w) && A.g[g].k_full + A.g[g].k_approx > 0 && !late_group(A, g))
       return g;
   }
@@ -825,32 +827,26 @@ struct Form<kSign2> : Form<kInt2> {};
 // order, by one wave: lane i builds entries i, i + 64, ...
 __device__ __forceinline__ void build_segtab(const LayerArgs& A, uint32_t w, bool late) {
   const int lane = (int)threadIdx.x & 63;
-  uint32_t first[4], step[4], cnt[4], u0[4], u1[4];
-  int gid[4];
-  int ng = 0;
-  uint32_t total = 0u;
-  for (int oi = 0; oi < A.n_order; ++oi) {
-    const int g = A.order[oi];
-    uint32_t t_end;
-    if (late_group(A, g) != late ||
-        !layer_group_range(A, g, w, first[ng], step[ng], t_end, u0[ng], u1[ng]))
+  uint32_t base = 0u;
+  // unrolled over the groups: their fields sit at fixed offsets of the
+  // arguments, and the four range computations are independent
+#pragma unroll
+  for (int oi = 0; oi < 4; ++oi) {
+    const int g = layer_order(oi);
+    uint32_t t0, step, t_end, u0, u1;
+    if (late_group(A, g) != late || !layer_group_range(A, g, w, t0, step, t_end, u0, u1))
       continue;
-    cnt[ng] = (t_end - first[ng] + step[ng] - 1u) / step[ng];
-    gid[ng] = g;
-    total += cnt[ng];
-    ++ng;
+    const uint32_t cnt = step == 1u ? t_end - t0 : (t_end - t0 + step - 1u) / step;
+    // (the host keeps every phase within the table)
+    for (uint32_t i = (uint32_t)lane; i < cnt && base + i < (uint32_t)kLayerSegTab; i += 64u) {
+      const LayerSeg sg = layer_make_seg(A, g, w, t0 + i * step, u0, u1);
+      g_sm.segtab[base + i] = make_uint4((uint32_t)sg.g | ((uint32_t)sg.t << 8),
+                                         (uint32_t)sg.f0 | ((uint32_t)sg.f1 << 16),
+                                         (uint32_t)sg.a0 | ((uint32_t)sg.a1 << 16), 0u);
+    }
+    base += cnt;
   }
-  total = min(total, (uint32_t)kLayerSegTab);  // the host keeps every phase within
-  for (uint32_t i = (uint32_t)lane; i < total; i += 64u) {
-    uint32_t r = i;
-    int k = 0;
-    while (k + 1 < ng && r >= cnt[k]) r -= cnt[k++];
-    const LayerSeg s = layer_make_seg(A, gid[k], w, first[k] + r * step[k], u0[k], u1[k]);
-    g_sm.segtab[i] = make_uint4((uint32_t)s.g | ((uint32_t)s.t << 8),
-                                (uint32_t)s.f0 | ((uint32_t)s.f1 << 16),
-                                (uint32_t)s.a0 | ((uint32_t)s.a1 << 16), 0u);
-  }
-  if (lane == 0) g_sm.nseg = total;
+  if (lane == 0) g_sm.nseg = min(base, (uint32_t)kLayerSegTab);
 }
 
 // Entry i of the segment table (wave-uniform).
@@ -1316,13 +1312,12 @@ __global__ __launch_bounds__(kGemvThreads) void layer_kernel(LayerArgs A) {
   const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
   const int first = first_ranked(A, w);
   __syncthreads();
-  // the first phase's segments and the positions the first ranking places,
-  // by the last wave while the others load the first ranking's keys (the
-  // placement reads the positions after the ranking's barriers)
-  if (wave == kWaves - 1) {
-    build_segtab(A, w, false);
-    if (first >= 0 && t == (kWaves - 1) * 64) set_need(A, first, w);
-  }
+  // the first phase's segments (the last wave) and the positions the first
+  // ranking places (the wave before it), while the other waves load the
+  // first ranking's keys (the placement reads the positions after the
+  // ranking's barriers)
+  if (wave == kWaves - 1) build_segtab(A, w, false);
+  if (first >= 0 && t == (kWaves - 2) * 64) set_need(A, first, w);
   uint32_t epoch = 0u;
   if (first >= 0) {
     const LayerGroupArgs& gr = A.g[first];

@@ -29,6 +29,7 @@
 #include <stdint.h>
 #include <hip/hip_runtime.h>
 
+#include "spax.h"
 #include "spax_internal.h"
 
 namespace spax {
@@ -66,6 +67,8 @@ struct LayerGroupArgs {
   int32_t wg_lo, n_wg;      // the group's workgroups [wg_lo, wg_lo + n_wg)
   uint32_t units;           // tiles * (k_full + k_approx) (0: no columns)
   uint32_t unit_q, unit_r;  // units = unit_q * n_wg + unit_r
+  uint32_t k_magic;         // div_magic(k_full + k_approx)
+  uint32_t nwg_magic;       // div_magic(n_wg)
   const uint8_t* full_base;
   int64_t full_stride;
   uint32_t full_bytes;
@@ -107,10 +110,31 @@ struct LayerSeg {
   int32_t w_lo, w_hi;       // the workgroups that meet this tile
 };
 
+// Processing order of the groups (absent ones are skipped): gate/up first,
+// down last.
+__host__ __device__ constexpr int layer_order(int oi) {
+  return oi == 0 ? SPAX_GROUP_GATE_UP : oi == 1 ? SPAX_GROUP_QKV : oi == 2 ? SPAX_GROUP_O
+                                                                          : SPAX_GROUP_DOWN;
+}
+
+// Division by a divisor fixed for the launch: m = div_magic(d) =
+// floor(2^32 / d) (2^32 - 1 for d = 1) makes floor(a m / 2^32) equal
+// floor(a / d) or one less (a m / 2^32 lies in (a / d - 1, a / d]), which
+// one comparison corrects. The kernel's schedule arithmetic then costs a
+// multiply instead of a full 32-bit division.
+inline uint32_t div_magic(uint32_t d) {
+  return d <= 1u ? 0xFFFFFFFFu : (uint32_t)((uint64_t(1) << 32) / d);
+}
+__host__ __device__ inline uint32_t div_by(uint32_t a, uint32_t d, uint32_t m) {
+  uint32_t q = (uint32_t)(((uint64_t)a * m) >> 32);
+  if ((uint64_t)(q + 1u) * d <= a) ++q;
+  return q;
+}
+
 // First unit of run i of a group: floor(U i / n) with U = q n + r, as
 // q i + floor(r i / n) (r i below 2^18).
 __host__ __device__ inline uint32_t layer_run_start(const LayerGroupArgs& gr, uint32_t i) {
-  return gr.unit_q * i + gr.unit_r * i / (uint32_t)gr.n_wg;
+  return gr.unit_q * i + div_by(gr.unit_r * i, (uint32_t)gr.n_wg, gr.nwg_magic);
 }
 
 // The workgroup (index within the group) whose run holds unit u:
@@ -154,9 +178,9 @@ __host__ __device__ inline bool layer_group_range(const LayerArgs& A, int g, uin
   const uint32_t K = (uint32_t)(gr.k_full + gr.k_approx);
   u0 = layer_run_start(gr, i);
   u1 = layer_run_start(gr, i + 1);
-  t_first = u0 / K;
+  t_first = div_by(u0, K, gr.k_magic);
   step = 1u;
-  t_end = (u1 + K - 1u) / K;
+  t_end = div_by(u1 + K - 1u, K, gr.k_magic);
   return t_first < t_end;
 }
 
@@ -176,10 +200,10 @@ __host__ __device__ inline LayerSeg layer_make_seg(const LayerArgs& A, int g, ui
     const uint32_t K = (uint32_t)(gr.k_full + gr.k_approx);
     const uint32_t q0 = (u0 > t * K ? u0 - t * K : 0u);
     const uint32_t q1 = (u1 < (t + 1) * K ? u1 - t * K : K);
-    s.f0 = (int32_t)(q0 * (uint32_t)gr.k_full / K);
-    s.f1 = (int32_t)(q1 * (uint32_t)gr.k_full / K);
-    s.a0 = (int32_t)(q0 * (uint32_t)gr.k_approx / K);
-    s.a1 = (int32_t)(q1 * (uint32_t)gr.k_approx / K);
+    s.f0 = (int32_t)div_by(q0 * (uint32_t)gr.k_full, K, gr.k_magic);
+    s.f1 = (int32_t)div_by(q1 * (uint32_t)gr.k_full, K, gr.k_magic);
+    s.a0 = (int32_t)div_by(q0 * (uint32_t)gr.k_approx, K, gr.k_magic);
+    s.a1 = (int32_t)div_by(q1 * (uint32_t)gr.k_approx, K, gr.k_magic);
     s.w_lo = s.w_hi = -1;
   }
   return s;
