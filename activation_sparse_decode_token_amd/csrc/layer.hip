@@ -466,55 +466,74 @@ __device__ __attribute__((noinline)) uint32_t rank_group(const uint16_t* __restr
   return epoch;
 }
 
-// Ranks x[0, n) on the whole workgroup (16 waves, no streaming waves beside
-// them) and places the list positions this workgroup needs, with the same
-// result as rank_group (the same K1 largest |x_j| in F, the next K2 - K1 in
-// A, lower index first among equal keys). With every wave ranking there is
-// no room to spare in issue cycles: a wave gets one instruction per four
-// cycles, so the steps that one wave or every wave repeats (finding a bin,
-// scanning 64 rounds) cost as much as the per-key passes. This variant
-// keeps each wave's keys in registers (at most 4 rounds of 512 entries per
-// wave) and puts an exact histogram of all 32768 keys in the keys' LDS area,
-// which removes the second histogram pass and both bin searches. Steps:
-//   1. the keys into registers (rounds rw, rw + 16, ...), the histogram
+// Ranks x[0, n) with the same result as rank_group (the same K1 largest
+// |x_j| in F, the next K2 - K1 in A, lower index first among equal keys) and
+// places the list positions this workgroup needs, on RW waves: the whole
+// workgroup (RW = 16, nothing streams beside it) or the four ranking waves
+// beside the streaming waves (RW = 4, inputs up to 4 rounds per wave). A
+// wave gets one instruction per four cycles, and the ranking waves' issue
+// cycles slow the streaming waves that share their SIMDs, so this variant
+// spends as few instructions as it can: each wave's keys stay in registers
+// (at most 4 rounds of 512 entries per wave) and an exact histogram of all
+// 32768 keys sits in the keys' LDS area, which removes rank_group's second
+// histogram pass and both bin searches. Steps:
+//   1. the keys into registers (rounds rw, rw + RW, ...), the histogram
 //      cleared meanwhile, then one LDS add per real entry (two 16-bit bins
 //      per word: no bin exceeds n <= 32768, nor does any sum of bins below);
-//   2. thread i holds bins [32 i, 32 i + 32): its total, a suffix sum over
-//      the threads (a wave scan, then the waves' totals) gives the entries
-//      above its bins; the thread whose bins hold rank K (1-based, from the
-//      largest key) hands its 32 bins to the lanes of its wave, whose scan
-//      finds the boundary key t and the number q of entries equal to t that
-//      are kept, for K = K1 and K = K2;
+//   2. ranking thread i holds bins [B i, B i + B) (B = 32768 / (64 RW)): its
+//      total, a suffix sum over the threads (a wave scan, then the waves'
+//      totals) gives the entries above its bins; the thread whose bins hold
+//      rank K (1-based, from the largest key) hands its B bins to the lanes
+//      of its wave, whose scan finds the boundary key t and the number q of
+//      entries equal to t that are kept, for K = K1 and K = K2;
 //   3. per round, the counts of key > t1, key == t1, key > t2, key == t2
 //      (the lanes' exclusive counts stay in registers for step 4);
-//   4. one wave scans the counts over the rounds; each wave places the
-//      entries of its rounds that meet a needed range (rank_group step 6).
+//   4. the counts' exclusive scans over the rounds (one wave for RW = 16,
+//      read from LDS after a barrier; each wave for RW = 4, where a barrier
+//      costs more than the scan); each wave places the entries of its
+//      rounds that meet a needed range (rank_group step 6).
 // Entries past n are loaded as key 0 and not counted in the histogram; they
 // come after every real entry, so a boundary at key 0 keeps real zeros
-// first (the quota q counts real entries only).
-__device__ __attribute__((noinline)) void rank_all(const uint16_t* __restrict__ x, int n,
-                                                   uint32_t K1, uint32_t K2, int list_off) {
+// first (the quota q counts real entries only). Returns the ranking waves'
+// barrier count (RW = 4).
+template <int RW>
+__device__ __attribute__((noinline)) uint32_t rank_all(const uint16_t* __restrict__ x, int n,
+                                                       uint32_t K1, uint32_t K2, int list_off,
+                                                       uint32_t epoch, uint32_t* status) {
   x = uniform_ptr(x);
   n = (int)uniform((uint32_t)n);
   K1 = uniform(K1);
   K2 = uniform(K2);
   list_off = (int)uniform((uint32_t)list_off);
+  epoch = uniform(epoch);
+  status = uniform_ptr(status);
   LayerShared& sm = g_sm;
   uint16_t* list = sm.lists + list_off;
   uint32_t* hist = reinterpret_cast<uint32_t*>(sm.keys);  // bins 2 i and 2 i + 1 in word i
-  const int t = (int)threadIdx.x;
-  const int lane = t & 63;
-  const int rw = (int)uniform((uint32_t)(t >> 6));
-  constexpr int kPer = kRankMaxRounds / kWaves;  // rounds per wave
+  constexpr int kThreads = 64 * RW;
+  const int rt = (int)threadIdx.x - (kWaves - RW) * 64;  // ranking thread
+  const int lane = rt & 63;
+  const int rw = (int)uniform((uint32_t)(rt >> 6));
+  constexpr int kPer = 4;                                     // rounds per wave
+  constexpr int kBins = kLayerMaxN / kThreads;                // bins per ranking thread
+  constexpr int kWords = kBins / 2;
+  constexpr int kBinsPerLane = kBins > 64 ? kBins / 64 : 1;  // holder search
+  static_assert(kBins % 8 == 0 && kBinsPerLane <= 2, "whole 16-byte reads, two bins per lane");
   const int R = (n + kRankRound - 1) / kRankRound;
   const int Rfull = n / kRankRound;
+  auto sync = [&] {
+    if constexpr (RW == kWaves)
+      lds_barrier();
+    else
+      rank_sync<RW>(epoch, status);
+  };
 
   // 1. keys (loads in flight while the histogram is cleared)
   const __amdgpu_buffer_rsrc_t rs = tier_rsrc(reinterpret_cast<const uint8_t*>(x), 2u * n);
   uint4 kv[kPer];
 #pragma unroll
   for (int i = 0; i < kPer; ++i) {
-    const int r = rw + kWaves * i;
+    const int r = rw + RW * i;
     kv[i] = make_uint4(0u, 0u, 0u, 0u);
     if (r < Rfull) {
       kv[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
@@ -532,16 +551,15 @@ __device__ __attribute__((noinline)) void rank_all(const uint16_t* __restrict__ 
       kv[i] = make_uint4(wd[0], wd[1], wd[2], wd[3]);
     }
   }
-  static_assert(kLayerMaxN / 2 == 16 * kGemvThreads, "four 16-byte clears per thread");
 #pragma unroll
-  for (int j = 0; j < 4; ++j)
-    reinterpret_cast<uint4*>(hist)[t + kGemvThreads * j] = make_uint4(0u, 0u, 0u, 0u);
-  if (t == 0)
+  for (int j = 0; j < kWords / 4; ++j)
+    reinterpret_cast<uint4*>(hist)[rt + kThreads * j] = make_uint4(0u, 0u, 0u, 0u);
+  if (rt == 0)
     *reinterpret_cast<uint4*>(&sm.rsel[0]) = make_uint4(kAboveAll, 0u, kAboveAll, 0u);
-  lds_barrier();
+  sync();
 #pragma unroll
   for (int i = 0; i < kPer; ++i) {
-    const int r = rw + kWaves * i;
+    const int r = rw + RW * i;
     if (r < R) {
       const uint4 v = make_uint4(kv[i].x & 0x7FFF7FFFu, kv[i].y & 0x7FFF7FFFu,
                                  kv[i].z & 0x7FFF7FFFu, kv[i].w & 0x7FFF7FFFu);
@@ -563,14 +581,14 @@ __device__ __attribute__((noinline)) void rank_all(const uint16_t* __restrict__ 
       }
     }
   }
-  lds_barrier();
+  sync();
 
   // 2. boundary keys and quotas
   {
-    const uint4* hp = reinterpret_cast<const uint4*>(hist) + 4 * t;
+    const uint4* hp = reinterpret_cast<const uint4*>(hist) + (kWords / 4) * rt;
     uint32_t sum = 0u;  // packed: no half reaches 2^16
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
+    for (int j = 0; j < kWords / 4; ++j) {
       const uint4 v = hp[j];
       sum += v.x + v.y + v.z + v.w;
     }
@@ -578,15 +596,10 @@ __device__ __attribute__((noinline)) void rank_all(const uint16_t* __restrict__ 
     const uint32_t incl = wave_incl_scan(tot);
     const uint32_t wsum = (uint32_t)__builtin_amdgcn_readlane((int)incl, 63);
     if (lane == 0) sm.wtot[rw] = wsum;
-    lds_barrier();
+    sync();
     uint32_t above = wsum - incl;  // entries in the bins of higher lanes of this wave
-    const uint4* wp = reinterpret_cast<const uint4*>(sm.wtot);
 #pragma unroll
-    for (int j = 0; j < kWaves / 4; ++j) {
-      const uint4 v = wp[j];
-      above += (4 * j + 0 > rw ? v.x : 0u) + (4 * j + 1 > rw ? v.y : 0u) +
-               (4 * j + 2 > rw ? v.z : 0u) + (4 * j + 3 > rw ? v.w : 0u);
-    }
+    for (int j = 0; j < RW; ++j) above += j > rw ? sm.wtot[j] : 0u;
 #pragma unroll
     for (int c = 0; c < 2; ++c) {
       const uint32_t K = c == 0 ? K1 : K2;
@@ -594,21 +607,26 @@ __device__ __attribute__((noinline)) void rank_all(const uint16_t* __restrict__ 
       if (m != 0) {  // wave-uniform: this wave holds rank K
         const int L = (int)__builtin_ctzll(m);
         const uint32_t ab = (uint32_t)__builtin_amdgcn_readlane((int)above, L);
-        const int b_top = 32 * (64 * rw + L) + 31;  // the holder's highest bin
-        const uint32_t cnt = lane < 32 ? (uint32_t)sm.keys[b_top - lane] : 0u;
-        const uint32_t ci = ab + wave_incl_scan(cnt);
-        const uint64_t f = __ballot(lane < 32 && ci - cnt < K && K <= ci);
+        const int b_top = kBins * (64 * rw + L) + kBins - 1;  // the holder's highest bin
+        // lane l takes bins b_top - kBinsPerLane l - (0 .. kBinsPerLane - 1)
+        const bool act = lane * kBinsPerLane < kBins;
+        const int b0 = b_top - kBinsPerLane * lane;
+        const uint32_t c0 = act ? (uint32_t)sm.keys[b0] : 0u;
+        const uint32_t c1 = act && kBinsPerLane == 2 ? (uint32_t)sm.keys[b0 - 1] : 0u;
+        const uint32_t cnt = c0 + c1;
+        const uint32_t ci = ab + wave_incl_scan(cnt);  // through this lane's bins
+        const uint32_t cb = ci - cnt;                   // before them
+        const uint64_t f = __ballot(act && cb < K && K <= ci);
         const int J = (int)__builtin_ctzll(f);
-        const uint32_t q = K - ((uint32_t)__builtin_amdgcn_readlane((int)ci, J) -
-                                (uint32_t)__builtin_amdgcn_readlane((int)cnt, J));
-        if (lane == 0) {
-          sm.rsel[2 * c] = (uint32_t)(b_top - J);
-          sm.rsel[2 * c + 1] = q;
+        if (lane == J) {
+          const bool first = K <= cb + c0;  // in the lane's higher bin
+          sm.rsel[2 * c] = (uint32_t)(first ? b0 : b0 - 1);
+          sm.rsel[2 * c + 1] = first ? K - cb : K - cb - c0;
         }
       }
     }
   }
-  lds_barrier();
+  sync();
   const uint4 sel = *reinterpret_cast<const uint4*>(&sm.rsel[0]);
   const uint32_t t1 = uniform(sel.x), q1 = uniform(sel.y), t2 = uniform(sel.z),
                  q2 = uniform(sel.w);
@@ -617,7 +635,7 @@ __device__ __attribute__((noinline)) void rank_all(const uint16_t* __restrict__ 
   uint32_t x1[kPer], x2[kPer];
 #pragma unroll
   for (int i = 0; i < kPer; ++i) {
-    const int r = rw + kWaves * i;
+    const int r = rw + RW * i;
     x1[i] = x2[i] = 0u;
     if (r < R) {
       uint32_t c1, c2;
@@ -630,37 +648,60 @@ __device__ __attribute__((noinline)) void rank_all(const uint16_t* __restrict__ 
             make_uint4(i1 & 0xFFFFu, i1 >> 16, i2 & 0xFFFFu, i2 >> 16);
     }
   }
-  lds_barrier();
+  sync();
 
-  // 4. wave 0: exclusive counts before each round, in place (the counts
-  // through round r are those before round r + 1; after the last, the
-  // totals); then placement
-  if (rw == 0) {
+  // 4. exclusive counts before each round (lane l: round l); the counts
+  // through round r are those before round r + 1, after the last the totals
+  uint32_t ex[4] = {0u, 0u, 0u, 0u}, inc[4] = {0u, 0u, 0u, 0u};
+  if (RW != kWaves || rw == 0) {
     const uint4 u = lane < R ? *reinterpret_cast<const uint4*>(&sm.rtot[lane][0])
                              : make_uint4(0u, 0u, 0u, 0u);
-    const uint32_t i0 = wave_incl_scan(u.x), i1 = wave_incl_scan(u.y);
-    const uint32_t i2 = wave_incl_scan(u.z), i3 = wave_incl_scan(u.w);
-    if (lane < R)
-      *reinterpret_cast<uint4*>(&sm.rtot[lane][0]) =
-          make_uint4(i0 - u.x, i1 - u.y, i2 - u.z, i3 - u.w);
-    if (lane == 63) *reinterpret_cast<uint4*>(&sm.rsum[0]) = make_uint4(i0, i1, i2, i3);
+    const uint32_t own[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      inc[q] = wave_incl_scan(own[q]);
+      ex[q] = inc[q] - own[q];
+    }
+    if (RW == kWaves) {  // shared through LDS
+      if (lane < R)
+        *reinterpret_cast<uint4*>(&sm.rtot[lane][0]) = make_uint4(ex[0], ex[1], ex[2], ex[3]);
+      if (lane == 63)
+        *reinterpret_cast<uint4*>(&sm.rsum[0]) = make_uint4(inc[0], inc[1], inc[2], inc[3]);
+    }
   }
-  lds_barrier();
+  if constexpr (RW == kWaves) lds_barrier();
   const Placement P = load_placement(K1, t1, q1, t2, q2);
 #pragma unroll
   for (int i = 0; i < kPer; ++i) {
-    const int r = rw + kWaves * i;
+    const int r = rw + RW * i;
     if (r >= R) break;  // wave-uniform
-    const uint4 e = *reinterpret_cast<const uint4*>(&sm.rtot[r][0]);
-    const uint4 f = r + 1 < R ? *reinterpret_cast<const uint4*>(&sm.rtot[r + 1][0])
-                              : *reinterpret_cast<const uint4*>(&sm.rsum[0]);
-    const uint32_t G1 = uniform(e.x), E1 = uniform(e.y), G2 = uniform(e.z), E2 = uniform(e.w);
-    if (!round_needed(P, G1, E1, G2, E2, uniform(f.x), uniform(f.y), uniform(f.z),
-                      uniform(f.w)))
-      continue;
+    uint32_t G1, E1, G2, E2, G1e, E1e, G2e, E2e;
+    if constexpr (RW == kWaves) {
+      const uint4 e = *reinterpret_cast<const uint4*>(&sm.rtot[r][0]);
+      const uint4 f = r + 1 < R ? *reinterpret_cast<const uint4*>(&sm.rtot[r + 1][0])
+                                : *reinterpret_cast<const uint4*>(&sm.rsum[0]);
+      G1 = uniform(e.x); E1 = uniform(e.y); G2 = uniform(e.z); E2 = uniform(e.w);
+      G1e = uniform(f.x); E1e = uniform(f.y); G2e = uniform(f.z); E2e = uniform(f.w);
+    } else {
+      G1 = uniform((uint32_t)__builtin_amdgcn_readlane((int)ex[0], r));
+      E1 = uniform((uint32_t)__builtin_amdgcn_readlane((int)ex[1], r));
+      G2 = uniform((uint32_t)__builtin_amdgcn_readlane((int)ex[2], r));
+      E2 = uniform((uint32_t)__builtin_amdgcn_readlane((int)ex[3], r));
+      G1e = uniform((uint32_t)__builtin_amdgcn_readlane((int)inc[0], r));
+      E1e = uniform((uint32_t)__builtin_amdgcn_readlane((int)inc[1], r));
+      G2e = uniform((uint32_t)__builtin_amdgcn_readlane((int)inc[2], r));
+      E2e = uniform((uint32_t)__builtin_amdgcn_readlane((int)inc[3], r));
+    }
+    if (!round_needed(P, G1, E1, G2, E2, G1e, E1e, G2e, E2e)) continue;
     place_round(P, list, kv[i], (uint32_t)(r * kRankRound + 8 * lane), x1[i], x2[i], G1, E1, G2,
                 E2);
   }
+  if constexpr (RW != kWaves) {
+    // the ranking waves' next use of the shared arrays comes after this
+    // barrier (the lists are complete for the ready flag)
+    sync();
+  }
+  return epoch;
 }
 
 // Whether group g runs in the launch's second phase: down, when its input
@@ -748,7 +789,11 @@ __device__ __forceinline__ void rank_role(const LayerArgs& A, int first, uint32_
     const uint32_t K1 = (uint32_t)gr.k_full, K2 = (uint32_t)(gr.k_full + gr.k_approx);
     if (K2 == 0u) continue;  // no lists: the group's segments are empty
     if (rt == 0) set_need(A, g, w);
-    epoch = rank_group<kLayerRankWaves>(gr.x, gr.n, K1, K2, gr.list_off, epoch, status);
+    // (inputs past four rounds per ranking wave: the LDS-keys ranking)
+    if (gr.n <= 4 * kRankRound * kLayerRankWaves)
+      epoch = rank_all<kLayerRankWaves>(gr.x, gr.n, K1, K2, gr.list_off, epoch, status);
+    else
+      epoch = rank_group<kLayerRankWaves>(gr.x, gr.n, K1, K2, gr.list_off, epoch, status);
     if (rt == 0) lds_signal_store(&g_sm.ready[g], 1u);
   }
 }
@@ -1321,7 +1366,8 @@ __global__ __launch_bounds__(kGemvThreads) void layer_kernel(LayerArgs A) {
   uint32_t epoch = 0u;
   if (first >= 0) {
     const LayerGroupArgs& gr = A.g[first];
-    rank_all(gr.x, gr.n, (uint32_t)gr.k_full, (uint32_t)(gr.k_full + gr.k_approx), gr.list_off);
+    rank_all<kWaves>(gr.x, gr.n, (uint32_t)gr.k_full, (uint32_t)(gr.k_full + gr.k_approx),
+                     gr.list_off, 0u, A.sync + 2);
     if (t == 0) sm.ready[first] = 1u;
   }
   lds_barrier();  // the first lists and the segment table are in LDS
@@ -1343,8 +1389,8 @@ __global__ __launch_bounds__(kGemvThreads) void layer_kernel(LayerArgs A) {
       __syncthreads();
       const LayerGroupArgs& gd = A.g[SPAX_GROUP_DOWN];
       if (gd.k_full + gd.k_approx > 0)
-        rank_all(gd.x, gd.n, (uint32_t)gd.k_full, (uint32_t)(gd.k_full + gd.k_approx),
-                 gd.list_off);
+        rank_all<kWaves>(gd.x, gd.n, (uint32_t)gd.k_full, (uint32_t)(gd.k_full + gd.k_approx),
+                         gd.list_off, 0u, A.sync + 2);
       if (t == 0) sm.ready[SPAX_GROUP_DOWN] = 1u;
       lds_barrier();
     }
