@@ -46,7 +46,7 @@ EXPORTS = (
     "spax_pack_trellis_host", "spax_pack_trellis", "spax_pack_trellis_workspace_bytes",
     "spax_workspace_clear", "spax_status_string", "spax_last_error", "spax_version",
     "spax_copy_init", "spax_copy_release", "spax_layer_schedule", "spax_workspace_status",
-    "spax_layer_step_static",
+    "spax_layer_step_static", "spax_sq_error",
 )
 
 library_path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libspax.so")
@@ -201,6 +201,8 @@ def _declare(L: ctypes.CDLL) -> None:
     L.spax_layer_step.restype = ctypes.c_int
     L.spax_layer_step_static.argtypes = [ctypes.POINTER(Layer), ctypes.POINTER(LayerIO), vp]
     L.spax_layer_step_static.restype = ctypes.c_int
+    L.spax_sq_error.argtypes = [vp, vp, ctypes.c_int64, vp, i32, vp]
+    L.spax_sq_error.restype = ctypes.c_int
     L.spax_pack_g128.argtypes = [vp, i32, i32, i32, vp, vp, vp]
     L.spax_pack_g128.restype = ctypes.c_int
     L.spax_pack_sign2.argtypes = [vp, i32, i32, vp, vp, vp]
@@ -326,6 +328,13 @@ def workspace_status(ws, stream=None, reset: bool = False) -> int:
     _check(lib().spax_workspace_status(_ptr(ws), _stream(stream), int(bool(reset)),
                                        ctypes.byref(v)), "spax_workspace_status")
     return int(v.value)
+
+
+def sq_error(y, ref, n, acc, accumulate: bool = False, stream=None) -> None:
+    """spax_sq_error: sum_i (y_i - ref_i)^2 in fp64 into (or onto) acc[0]."""
+    _check(lib().spax_sq_error(_ptr(y), _ptr(ref), int(n), _ptr(acc), int(bool(accumulate)),
+                               _stream(stream)),
+           "spax_sq_error")
 
 
 def pack_g128(w, rows, cols, fmt, codes, scales, stream=None) -> None:

@@ -11,7 +11,9 @@ setting with the smallest error.
 
 Every product runs in the library (spax_plan_tiers, then spax_tiered_gemv);
 a token's dense reference is the library's product with every column in the
-top tier. The squared errors are summed on the host in fp64. Budgets are
+top tier. The squared errors are summed in fp64 by the library too
+(spax_sq_error, one accumulator over the tokens), so one evaluation of a
+setting enqueues its tokens' work and synchronises once, to read the sum. Budgets are
 integer percentages and Eq. 5 is evaluated in exact integer arithmetic, so
 the grid of tier sizes is exact. A group's error is summed over its
 calibration tokens and all its stored rows (stacked q, k, v; interleaved
@@ -24,10 +26,9 @@ from __future__ import annotations
 from fractions import Fraction
 from typing import List, Sequence, Tuple
 
-import numpy as np
 
 from . import (FMT_FP16, FMT_INT2_G128, FMT_INT4_G128, FMT_NONE, FMT_SIGN2, FMT_TRELLIS,
-               Matrix, gemv_workspace_bytes, plan_tiers, tiered_gemv)
+               Matrix, gemv_workspace_bytes, plan_tiers, sq_error, tiered_gemv)
 
 __all__ = ["column_bytes", "rho_of", "k_mid_for_budget", "grid", "Group", "step2", "step1",
            "layer_budget"]
@@ -91,24 +92,33 @@ class Group:
         self.F = torch.empty(self.n, dtype=torch.int32, device=dev)
         self.A = torch.empty(self.n, dtype=torch.int32, device=dev)
         self.y = torch.empty(W.rows, dtype=torch.float16, device=dev)
-        self.dense = [self._product(x, self.n, 0) for x in self.xs]
-
-    def _product(self, x, k_top: int, k_mid: int) -> np.ndarray:
-        import torch
-        plan_tiers(x, self.n, k_top, k_mid, self.F, self.A, self.stream)
-        tiered_gemv(self.W, x, self.F, k_top, self.A, k_mid, self.y, self.ws,
-                    stream=self.stream)
+        self.acc = torch.zeros(1, dtype=torch.float64, device=dev)
+        self.dense = []
+        for x in self.xs:  # the dense references stay on the device
+            d = torch.empty(W.rows, dtype=torch.float16, device=dev)
+            self._product(x, self.n, 0, d)
+            self.dense.append(d)
         torch.cuda.synchronize()
-        return self.y.cpu().numpy().astype(np.float64)
+
+    def _product(self, x, k_top: int, k_mid: int, y) -> None:
+        """Enqueues the tiered product of x into y (no synchronisation)."""
+        plan_tiers(x, self.n, k_top, k_mid, self.F, self.A, self.stream)
+        tiered_gemv(self.W, x, self.F, k_top, self.A, k_mid, y, self.ws, stream=self.stream)
 
     def dense_bytes(self) -> int:
         return self.n * column_bytes(self.W.full_fmt, self.W.rows)
 
     def error(self, k_top: int, k_mid: int) -> float:
-        """sum over tokens of ||y_tiered - y_dense||^2 over the stored rows."""
+        """sum over tokens of ||y_tiered - y_dense||^2 over the stored rows:
+        every token's product and squared distance on the stream, then one
+        synchronisation to read the fp64 sum."""
+        import torch
         self.evaluations += 1
-        return float(sum(((self._product(x, k_top, k_mid) - d) ** 2).sum()
-                         for x, d in zip(self.xs, self.dense)))
+        for i, (x, d) in enumerate(zip(self.xs, self.dense)):
+            self._product(x, k_top, k_mid, self.y)
+            sq_error(self.y, d, self.W.rows, self.acc, accumulate=i > 0, stream=self.stream)
+        torch.cuda.synchronize()
+        return float(self.acc.cpu()[0])
 
 
 def step2(g: Group, budget_pct: int, steps: int = 10):

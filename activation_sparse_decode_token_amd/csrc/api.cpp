@@ -783,6 +783,17 @@ int spax_workspace_status(void* ws, hipStream_t stream, int32_t reset, uint32_t*
   return e == hipSuccess ? SPAX_OK : hip_fail(e);
 }
 
+int spax_sq_error(const uint16_t* y, const uint16_t* ref, int64_t n, double* acc,
+                  int32_t accumulate, hipStream_t stream) {
+  if (!acc || (n > 0 && (!y || !ref))) return SPAX_ENULL;
+  if (n < 0) return SPAX_EINVAL;
+  if ((reinterpret_cast<uintptr_t>(y) | reinterpret_cast<uintptr_t>(ref)) % 2 ||
+      reinterpret_cast<uintptr_t>(acc) % 8)
+    return SPAX_EALIGN;
+  const hipError_t e = launch_sq_error(y, ref, n, acc, accumulate, stream);
+  return e == hipSuccess ? SPAX_OK : hip_fail(e);
+}
+
 int spax_pack_g128(const uint16_t* w, int32_t rows, int32_t cols, int32_t fmt, uint8_t* codes,
                    uint16_t* scales, hipStream_t stream) {
   if (fmt != kInt4 && fmt != kInt2) return SPAX_EFORMAT;

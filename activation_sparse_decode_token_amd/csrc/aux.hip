@@ -425,6 +425,30 @@ __global__ __launch_bounds__(kTrelThreads) void trellis_encode_kernel(
   }
 }
 
+// Squared l2 distance of two fp16 vectors, added to (or stored in) one fp64
+// value: one workgroup; thread t sums the terms t, t + 1024, ... in order,
+// then a fixed tree over the threads (the same bits on every call).
+constexpr int kSqThreads = 1024;
+__global__ __launch_bounds__(kSqThreads) void sq_error_kernel(const uint16_t* __restrict__ y,
+                                                              const uint16_t* __restrict__ r,
+                                                              int64_t n, double* acc,
+                                                              int accumulate) {
+  __shared__ double part[kSqThreads];
+  const int t = (int)threadIdx.x;
+  double s = 0.0;
+  for (int64_t i = t; i < n; i += kSqThreads) {
+    const double d = (double)h2f(y[i]) - (double)h2f(r[i]);  // exact in fp64
+    s = fma(d, d, s);
+  }
+  part[t] = s;
+  __syncthreads();
+  for (int h = kSqThreads / 2; h > 0; h >>= 1) {
+    if (t < h) part[t] += part[t + h];
+    __syncthreads();
+  }
+  if (t == 0) *acc = accumulate ? *acc + part[0] : part[0];
+}
+
 __global__ void clear_kernel(uint32_t* __restrict__ p, int64_t n) {
   for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
        i += (int64_t)gridDim.x * blockDim.x)
@@ -475,6 +499,13 @@ hipError_t launch_pack_trellis(const uint16_t* w, int32_t rows, int32_t cols,
     if (e != hipSuccess) return e;
   }
   return hipSuccess;
+}
+
+hipError_t launch_sq_error(const uint16_t* y, const uint16_t* r, int64_t n, double* acc,
+                           int32_t accumulate, hipStream_t s) {
+  hipLaunchKernelGGL(sq_error_kernel, dim3(1), dim3(kSqThreads), 0, s, y, r, n, acc,
+                     (int)accumulate);
+  return hipGetLastError();
 }
 
 hipError_t launch_clear(void* ws, size_t bytes, hipStream_t s) {

@@ -152,6 +152,8 @@ hipError_t launch_pack_trellis(const uint16_t* w, int32_t rows, int32_t cols,
                                void* ws, size_t ws_bytes, hipStream_t s);
 
 hipError_t launch_clear(void* ws, size_t bytes, hipStream_t s);
+hipError_t launch_sq_error(const uint16_t* y, const uint16_t* r, int64_t n, double* acc,
+                           int32_t accumulate, hipStream_t s);
 // Bytes at the start of a workspace that must start at zero (arrival
 // counters, the layer kernel's sync words, the sliced selection's counts).
 size_t workspace_head_bytes();

@@ -338,6 +338,21 @@ int spax_layer_schedule(const spax_layer* L, int32_t workgroups, int32_t* out, i
 int spax_workspace_status(void* ws, hipStream_t stream, int32_t reset, uint32_t* status);
 
 /* ---- offline helpers ---------------------------------------------------- */
+/* spax_sq_error -- the squared l2 distance of two fp16 vectors, for the
+ * offline calibration of the tier sizes (SpAx page section 5.2, steps 1-2:
+ * the tier sizes that keep the layer's l2 output error against the dense
+ * product smallest): sum_i (y_i - ref_i)^2, each difference and square formed
+ * in fp64, stored to *acc (accumulate == 0) or added to it (accumulate != 0).
+ * One workgroup in a fixed order: repeated calls give the same bits. Several
+ * calls on one stream (one per calibration token) need one synchronisation
+ * before *acc is read.
+ *   y, ref  device fp16 [n] (2-byte aligned; may be null when n == 0);
+ *   acc  device fp64 (8-byte aligned), read and written by the kernel;
+ *   n >= 0 (0 sums nothing: *acc is set to 0 or kept).
+ *   Errors: SPAX_ENULL, SPAX_EINVAL (n < 0), SPAX_EALIGN, SPAX_EHIP.        */
+int spax_sq_error(const uint16_t* y, const uint16_t* ref, int64_t n, double* acc,
+                  int32_t accumulate, hipStream_t stream);
+
 /* spax_pack_g128 -- encode the compressed copy of a matrix (SpAx page
  * section 5, Figure 2 step 1: every column is encoded offline, on its own).
  *   w      device fp16 [cols][rows] (column-major), rows % 128 == 0.

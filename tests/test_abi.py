@@ -196,6 +196,19 @@ def test_static_layer_step_rejects_what_its_scratch_cannot_hold():
              None) == -1
 
 
+def test_sq_error_argument_checks():
+    """spax_sq_error refuses bad arguments before any GPU call."""
+    f = spax.lib().spax_sq_error
+    assert f(None, P, 8, P, 0, None) == -2
+    assert f(P, None, 8, P, 0, None) == -2
+    assert f(P, P, 8, None, 0, None) == -2
+    assert f(P, P, -1, P, 0, None) == -1
+    assert f(None, None, 0, None, 0, None) == -2  # the accumulator is always required
+    assert f(P + 1, P, 8, P, 0, None) == -3
+    assert f(P, P + 1, 8, P, 0, None) == -3
+    assert f(P, P, 8, P + 4, 0, None) == -3
+
+
 def test_python_wrapper_raises_with_status():
     with pytest.raises(spax.SpaxError) as ei:
         spax.plan_tiers(None, 10, 1, 1, P, P, stream=0)

@@ -40,6 +40,34 @@ def _layer():
     return stored, xs
 
 
+@pytest.mark.parametrize("n", [0, 1, 1023, 1025, 57344])
+def test_sq_error_kernel(n):
+    """spax_sq_error against the fp64 sum of squared differences formed on
+    the host (each difference of two fp16 values is exact in fp64; the sums
+    differ only in their order); accumulate mode adds to the stored value;
+    two calls give the same bits."""
+    import torch
+    import activation_sparse_decode_token_amd as spax
+    rs = np.random.default_rng(850 + n)
+    y = rs.standard_normal(n).astype(np.float16)
+    r = (y.astype(np.float32) + 0.01 * rs.standard_normal(n)).astype(np.float16)
+    r[: n // 7] = y[: n // 7]  # some equal pairs
+    want = float(((y.astype(np.float64) - r.astype(np.float64)) ** 2).sum())
+    acc = torch.full((1,), 123.5, dtype=torch.float64, device="cuda:0")
+    yd, rd = to_dev(y), to_dev(r)
+    spax.sq_error(yd, rd, n, acc)
+    torch.cuda.synchronize()
+    got = float(acc.cpu()[0])
+    assert abs(got - want) <= 1e-12 * want + 1e-300, (got, want)
+    spax.sq_error(yd, rd, n, acc, accumulate=True)
+    torch.cuda.synchronize()
+    assert float(acc.cpu()[0]) == got + got
+    spax.sq_error(yd, rd, n, acc)
+    torch.cuda.synchronize()
+    assert float(acc.cpu()[0]) == got  # the same bits again
+    log(f"sq_error n={n}: {got:.6g} (host {want:.6g})")
+
+
 def test_step2_grid_matches_the_oracle():
     import activation_sparse_decode_token_amd.calibrate as K
     stored, xs = _layer()
