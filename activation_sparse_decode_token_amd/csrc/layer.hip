@@ -67,6 +67,7 @@ struct LayerShared {
   uint32_t wtot[kWaves];                     // ranking: per-wave histogram totals
   uint32_t rsel[4];                          // ranking: t1, q1, t2, q2
   uint32_t rsum[4];                          // ranking: the four counts over all rounds
+  uint16_t spare[64];                        // ranking: per-lane target of unplaced entries
   uint32_t need[8];                          // ranking: positions to place
   uint32_t own[4];                           // ranking: positions to store out
   uint64_t rank_out[2];                      // ranking: the caller's lists
@@ -225,27 +226,39 @@ __device__ __forceinline__ bool round_needed(const Placement& P, uint32_t G1, ui
 
 // Places the lane's 8 entries e0 + h (keys v) of a round: x1, x2 are the
 // lane's exclusive counts within the round (as lane_counts packs them),
-// (G1, E1, G2, E2) the counts of the rounds before.
+// (G1, E1, G2, E2) the counts of the rounds before. Without branches: an
+// entry of neither tier writes to its lane's spare slot, and a workgroup
+// that stores positions to the caller's lists stores every entry through a
+// buffer resource, at an offset past the list's end (a store the hardware
+// drops) unless its position is one the workgroup owns.
 __device__ __forceinline__ void place_round(const Placement& P, uint16_t* list, const uint4& v,
                                             uint32_t e0, uint32_t x1, uint32_t x2, uint32_t G1,
                                             uint32_t E1, uint32_t G2, uint32_t E2) {
   uint32_t g1 = G1 + (x1 & 0xFFFFu), e1 = E1 + (x1 >> 16);
   uint32_t g2 = G2 + (x2 & 0xFFFFu), e2 = E2 + (x2 >> 16);
   const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
+  const int lane = (int)threadIdx.x & 63;
+  uint16_t* spare = &g_sm.spare[lane];
+  const bool owner = P.of0 < P.of1 || P.oa0 < P.oa1;  // wave-uniform
+  const __amdgpu_buffer_rsrc_t rf =
+      tier_rsrc(reinterpret_cast<const uint8_t*>(P.out_f), 4u * P.of1);
+  const __amdgpu_buffer_rsrc_t ra =
+      tier_rsrc(reinterpret_cast<const uint8_t*>(P.out_a), 4u * P.oa1);
 #pragma unroll
   for (int h = 0; h < 8; ++h) {
     const uint32_t k = (w4[h >> 1] >> (16 * (h & 1))) & 0x7FFFu;
     const uint32_t fpos = g1 + min(e1, P.q1);
     const uint32_t apos = g2 + min(e2, P.q2) - fpos;
+    // (an entry of F is also among the K2 largest: in_f implies in_fa)
     const bool in_f = k > P.t1 || (k == P.t1 && e1 < P.q1);
     const bool in_fa = k > P.t2 || (k == P.t2 && e2 < P.q2);
     const uint32_t e = e0 + (uint32_t)h;
-    if (in_f) {
-      list[fpos] = (uint16_t)e;
-      if (fpos >= P.of0 && fpos < P.of1) P.out_f[fpos] = (int32_t)e;
-    } else if (in_fa) {
-      list[P.K1 + apos] = (uint16_t)e;
-      if (apos >= P.oa0 && apos < P.oa1) P.out_a[apos] = (int32_t)e;
+    *(in_fa ? list + (in_f ? fpos : P.K1 + apos) : spare) = (uint16_t)e;
+    if (owner) {
+      const bool sf = in_f && fpos >= P.of0;
+      const bool sa = !in_f && in_fa && apos >= P.oa0;
+      __builtin_amdgcn_raw_buffer_store_b32(e, rf, sf ? 4u * fpos : 0xFFFFFFF0u, 0, 0);
+      __builtin_amdgcn_raw_buffer_store_b32(e, ra, sa ? 4u * apos : 0xFFFFFFF0u, 0, 0);
     }
     g1 += k > P.t1 ? 1u : 0u;
     e1 += k == P.t1 ? 1u : 0u;
