@@ -342,17 +342,15 @@ __device__ __attribute__((noinline)) uint32_t rank_group(const uint16_t* __restr
     }
   }
   if (Rfull < R && rw == Rfull % RW) {
+    // the round that holds the end of x: loads past x's end (the buffer's
+    // range) return 0, the padding's key, so no branch separates them
     const int e = Rfull * kRankRound + 8 * lane;
-    uint32_t wd[4];
+    uint32_t hw[8];
 #pragma unroll
-    for (int h = 0; h < 8; h += 2) {
-      uint32_t lo = 0u, hi = 0u;
-      if (e + h < n) lo = __builtin_amdgcn_raw_buffer_load_b16(rs, 2u * (e + h), 0, 0);
-      if (e + h + 1 < n)
-        hi = __builtin_amdgcn_raw_buffer_load_b16(rs, 2u * (e + h + 1), 0, 0);
-      wd[h / 2] = lo | (hi << 16);
-    }
-    const uint4 v = make_uint4(wd[0], wd[1], wd[2], wd[3]);
+    for (int h = 0; h < 8; ++h)
+      hw[h] = __builtin_amdgcn_raw_buffer_load_b16(rs, 2u * (uint32_t)(e + h), 0, 0);
+    const uint4 v = make_uint4(hw[0] | (hw[1] << 16), hw[2] | (hw[3] << 16),
+                               hw[4] | (hw[5] << 16), hw[6] | (hw[7] << 16));
     *reinterpret_cast<uint4*>(&sm.keys[e]) = v;
     hist8(v, copy);
   }
@@ -557,17 +555,18 @@ __device__ __attribute__((noinline)) uint32_t rank_all(const uint16_t* __restric
     if (r < Rfull) {
       kv[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
                                             rs, 2u * (uint32_t)(r * kRankRound + 8 * lane), 0, 0));
-    } else if (r < R) {  // the round that holds the end of x, entry by entry
-      const int e = r * kRankRound + 8 * lane;
-      uint32_t wd[4];
+    } else if (r < R) {
+      // the round that holds the end of x, entry by entry: the buffer's
+      // range ends at x's end and a load past it returns 0, the key of the
+      // padding, so all eight loads go out at once with no branch between
+      // them (branches made the compiler wait for each pair in turn)
+      const uint32_t e = (uint32_t)(r * kRankRound + 8 * lane);
+      uint32_t hw[8];
 #pragma unroll
-      for (int h = 0; h < 8; h += 2) {
-        uint32_t lo = 0u, hi = 0u;
-        if (e + h < n) lo = __builtin_amdgcn_raw_buffer_load_b16(rs, 2u * (e + h), 0, 0);
-        if (e + h + 1 < n) hi = __builtin_amdgcn_raw_buffer_load_b16(rs, 2u * (e + h + 1), 0, 0);
-        wd[h / 2] = lo | (hi << 16);
-      }
-      kv[i] = make_uint4(wd[0], wd[1], wd[2], wd[3]);
+      for (int h = 0; h < 8; ++h)
+        hw[h] = __builtin_amdgcn_raw_buffer_load_b16(rs, 2u * (e + (uint32_t)h), 0, 0);
+      kv[i] = make_uint4(hw[0] | (hw[1] << 16), hw[2] | (hw[3] << 16), hw[4] | (hw[5] << 16),
+                         hw[6] | (hw[7] << 16));
     }
   }
 #pragma unroll
