@@ -254,6 +254,29 @@ def test_layer_kernel_tied_inputs(case):
     log(f"layer kernel on tied inputs ({case}) ok")
 
 
+def test_layer_kernel_ragged_down_many_contributors():
+    """Down with a ragged last row tile (640 rows: 512 + 128) whose tiles
+    have far more than 32 contributors (every workgroup meets both): the
+    last eight contributors to arrive share each tile's final sum in 64-row
+    slices, slices past the last row store nothing, and the partials are
+    loaded in batches of 32 contributors."""
+    hidden, inter = 640, 5632          # an FFN layer (stacked q/k/v take whole tiles)
+    w = LayerWeights(813, 0, hidden, inter, 0.02, attn=False)
+    ks = _ks(hidden, inter, WL.TierSplit(40, 30, 30))
+    ks["qkv"] = ks["o"] = (0, 0)
+    L = _build_layer(w, "fp16", "int4", 0, ks, 0)
+    sched = _spax().layer_schedule(L, 256)
+    assert len(sched) > 0  # the one-launch layer kernel runs
+    down = sched[sched[:, 1] == _spax().GROUP_DOWN]
+    assert sorted(set(down[:, 2])) == [0, 1]
+    assert (down[:, 8] - down[:, 7] + 1).min() > 32, "tiles with more than 32 contributors"
+    for tok in range(2):
+        x = WL.laplace_fp16(813, 0, "x", tok, hidden)
+        res, _ = _run_layer(L, None, None, x)
+        _check_layer(res, w, ks, None, None, x, "fp16", "int4", f"ragged down token {tok}")
+    log("layer kernel ragged down with many contributors ok")
+
+
 @pytest.mark.parametrize("af", ["int4", "sign2"])
 def test_layer_7b_shapes(kernel_choice, af):
     """A full-size 7B layer step (the launches the benchmarks time), with the
