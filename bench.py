@@ -65,30 +65,35 @@ KERNEL = 0
 PCIE5_X16_GBS = 64.0
 
 
-# counter summaries of the layer kernel per workload (FETCH_SIZE and
-# WRITE_SIZE runs), valid while the kernel sources are unchanged
+# counter summaries per workload (FETCH_SIZE and WRITE_SIZE runs), valid while
+# the sources of the kernel they measured are unchanged: the layer kernel, and
+# the per-group product (gemv_kernel)
 PMC_SUMMARY = {4: os.path.join(ROOT, "profiles", "layer_kernel_7b_stream_pmc.txt"),
                5: os.path.join(ROOT, "profiles", "layer_kernel_70b_ffn_pmc.txt"),
                2: os.path.join(ROOT, "profiles", "layer_kernel_7b_attention_pmc.txt")}
+GEMV_PMC_SUMMARY = {5: os.path.join(ROOT, "profiles", "gemv_kernel_70b_ffn_pmc.txt"),
+                    2: os.path.join(ROOT, "profiles", "gemv_kernel_7b_attention_pmc.txt")}
 KERNEL_SOURCES = ("layer.hip", "layer_plan.h", "block_common.h", "spax_internal.h", "api.cpp")
+GEMV_SOURCES = ("gemv.hip", "block_common.h", "stream_common.h", "spax_internal.h", "api.cpp")
 
 
-def kernel_source_hash() -> str:
+def kernel_source_hash(sources=KERNEL_SOURCES) -> str:
     import hashlib
     h = hashlib.sha256()
-    for f in KERNEL_SOURCES:
+    for f in sources:
         with open(os.path.join(ROOT, "activation_sparse_decode_token_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()
 
 
-def measured_traffic(config: int):
-    """HBM bytes per launch of the layer kernel from the committed counter
-    summary of this workload (FETCH_SIZE and WRITE_SIZE, scaled by a plain
-    copy's reading), or None when there is none or the kernel sources
-    changed since the counters were taken."""
+def measured_traffic(config: int, layer: bool = True):
+    """HBM bytes per launch of the layer kernel (layer) or of the per-group
+    product from the committed counter summary of this workload (FETCH_SIZE
+    and WRITE_SIZE, scaled by a plain copy's reading), or None when there is
+    none or that kernel's sources changed since the counters were taken."""
+    table, sources = (PMC_SUMMARY, KERNEL_SOURCES) if layer else (GEMV_PMC_SUMMARY, GEMV_SOURCES)
     try:
-        text = open(PMC_SUMMARY[config]).read()
+        text = open(table[config]).read()
     except (OSError, KeyError):
         return None
     vals = {}
@@ -97,7 +102,7 @@ def measured_traffic(config: int):
             vals["traffic"] = float(line.split(":", 1)[1])
         elif line.startswith("kernel sources sha256"):
             vals["sha"] = line.rsplit(":", 1)[1].strip()
-    if vals.get("sha") != kernel_source_hash() or "traffic" not in vals:
+    if vals.get("sha") != kernel_source_hash(sources) or "traffic" not in vals:
         return None
     return int(vals["traffic"])
 
@@ -562,8 +567,8 @@ def roofline(spec: Spec, wl: Workload, sec_step: float, mode: str):
         "peak": HBM_PEAK_GBS,
         "unit": "GB/s",
         "frac": round(achieved / HBM_PEAK_GBS, 4),
-        "traffic": (measured_traffic(spec.config)
-                    if layer and spec.approx_fmt in ("int4", "int2") else None),
+        "traffic": (measured_traffic(spec.config, layer)
+                    if spec.approx_fmt in ("int4", "int2") else None),
         "kernel": ("layer_kernel: every group of one decoder layer (ranking, tiered "
                    "gather-GEMV, SwiGLU) in one launch" if layer else
                    "gemv_kernel: fused tier selection + tiered gather-GEMV, one launch per "

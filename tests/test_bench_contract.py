@@ -6,6 +6,8 @@ import os
 import subprocess
 import sys
 
+import pytest
+
 import bench
 import workloads as WL
 from workloads.accounting import gemv_algorithmic_bytes
@@ -59,21 +61,25 @@ def test_config4_layer_bytes_by_hand():
 
 
 def test_traffic_is_null_once_the_kernel_changed(monkeypatch):
-    monkeypatch.setattr(bench, "kernel_source_hash", lambda: "0" * 64)
-    for config in bench.PMC_SUMMARY:
-        assert bench.measured_traffic(config) is None
+    monkeypatch.setattr(bench, "kernel_source_hash", lambda *a: "0" * 64)
+    for layer, table in ((True, bench.PMC_SUMMARY), (False, bench.GEMV_PMC_SUMMARY)):
+        for config in table:
+            assert bench.measured_traffic(config, layer) is None
 
 
-def test_traffic_comes_from_the_committed_summary():
-    for config, path in bench.PMC_SUMMARY.items():
+@pytest.mark.parametrize("layer", [True, False])
+def test_traffic_comes_from_the_committed_summary(layer):
+    table, sources = ((bench.PMC_SUMMARY, bench.KERNEL_SOURCES) if layer else
+                      (bench.GEMV_PMC_SUMMARY, bench.GEMV_SOURCES))
+    for config, path in table.items():
         if not os.path.exists(path):
-            assert bench.measured_traffic(config) is None
+            assert bench.measured_traffic(config, layer) is None
             continue
         text = open(path).read()
         sha = next(line for line in text.splitlines()
                    if line.startswith("kernel sources sha256")).rsplit(":", 1)[1].strip()
-        t = bench.measured_traffic(config)
-        if sha == bench.kernel_source_hash():
+        t = bench.measured_traffic(config, layer)
+        if sha == bench.kernel_source_hash(sources):
             assert t is not None and t > 0
         else:
             assert t is None
