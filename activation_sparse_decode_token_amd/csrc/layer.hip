@@ -823,9 +823,10 @@ __device__ __forceinline__ void rank_role(const LayerArgs& A, int first, uint32_
 // list positions. A wave streams all its shares as one sequence through a
 // ring of loads in registers: the load for ring slot u is issued as soon as
 // slot u's previous load has been added, across segment boundaries, so the
-// ring never drains between segments. The rings are short (4 KB in flight
-// per wave): with more requests in flight the chip's scattered 1 KB reads
-// got slower, not faster (measured on 7B layers). When a segment's last load has been
+// ring never drains between segments. The rings are short (3 KB of fp16
+// columns in flight per wave): with more requests in flight the chip's
+// scattered 1 KB reads got slower, not faster, and with 2 the ring drained
+// (measured on 7B layers). When a segment's last load has been
 // added, the wave hands its fp32 partial of the tile's 512 rows to the
 // reduction wave through LDS (two slot sets, so a wave can run one segment
 // ahead) and starts the next sum. A share with no positions still costs one
@@ -853,7 +854,7 @@ struct Form;
 template <>
 struct Form<kFp16> {
   using V = uint4;
-  static constexpr int kRing = 4;
+  static constexpr int kRing = 3;
   static constexpr int kPos = 1;  // list positions per load
 };
 template <>
